@@ -1,0 +1,79 @@
+"""Exact rational brute force for tiny inputs (pins the fp64 oracle).
+
+TEST INFRASTRUCTURE, like the rest of this package: only the test-suite may
+use it.
+
+bf16 and fp32 inputs are dyadic rationals, so every product and sum in the
+DoRA row norm [P2 "The Problem": ||W + sBA||_row] and in the compose
+[P1 "DoRA优化技术解析" §2.1] is computed here exactly with
+``fractions.Fraction``; the square root is taken to 50 significant digits
+with ``decimal``. Nothing here uses floating-point arithmetic on results.
+"""
+
+from __future__ import annotations
+
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+__all__ = ["exact_row_sq_norms", "exact_sqrt", "exact_compose", "round_fraction_bf16"]
+
+
+def _fr(v) -> Fraction:
+    return Fraction(float(v))
+
+
+def exact_row_sq_norms(W, A, B, s):
+    """sum_k (W[j,k] + s * sum_l B[j,l] A[l,k])^2 for every row j, exactly."""
+    d_out = len(W)
+    d_in = len(W[0]) if d_out else 0
+    r = len(A)
+    sf = _fr(s)
+    Af = [[_fr(A[l][k]) for k in range(d_in)] for l in range(r)]
+    out = []
+    for j in range(d_out):
+        Bj = [_fr(B[j][l]) for l in range(r)]
+        acc = Fraction(0)
+        for k in range(d_in):
+            ba = sum((Bj[l] * Af[l][k] for l in range(r)), Fraction(0))
+            v = _fr(W[j][k]) + sf * ba
+            acc += v * v
+        out.append(acc)
+    return out
+
+
+def exact_sqrt(q: Fraction, digits: int = 50) -> Decimal:
+    """Square root of a non-negative rational to ``digits`` significant digits."""
+    getcontext().prec = digits + 10
+    return (Decimal(q.numerator) / Decimal(q.denominator)).sqrt()
+
+
+def exact_compose(base, lora, g, s):
+    """(g-1)*base + g*(s*lora) for one element, exactly."""
+    gf = _fr(g)
+    return (gf - 1) * _fr(base) + gf * (_fr(s) * _fr(lora))
+
+
+def round_fraction_bf16(q: Fraction) -> Fraction:
+    """Round an exact rational to bfloat16 (8 significant bits), ties to even.
+
+    Independent of the oracle's float-based rounding: the binade is found by
+    exact comparison with powers of two and the tie is decided on integers.
+    Handles the normal range only (the tests never leave it).
+    """
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = 0
+    while a >= 2 ** (e + 1):
+        e += 1
+    while a < Fraction(2) ** e:
+        e -= 1
+    # a in [2^e, 2^(e+1)); spacing 2^(e-7)
+    spacing = Fraction(2) ** (e - 7)
+    n = a / spacing                       # in [128, 256)
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * spacing

@@ -1,0 +1,341 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+Exact rational brute force, hand-derived closed forms, invariants of the
+definition, library routines for the special cases, and the values the
+pages print for the memory closed forms (tests/golden/table1_memory.json).
+A final test plants plausible mistakes in copies of the oracle and checks
+that these pins reject each one.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bruteforce as bf
+from oracle import dora_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bf16_like(rng, shape, scale):
+    """Random values that are exactly representable in bf16 (small integers / 2^k)."""
+    return rng.integers(-127, 128, size=shape).astype(np.float64) * scale
+
+
+def _f32_like(rng, shape, scale):
+    return rng.standard_normal(shape).astype(np.float32).astype(np.float64) * scale
+
+
+# ---------------------------------------------------------------- norm ----
+
+@pytest.mark.parametrize(
+    "d_out,d_in,r,s,kind",
+    [
+        (4, 16, 3, 2.0, "bf16"),
+        (8, 64, 8, 0.5, "bf16"),
+        (5, 7, 9, -1.25, "f32"),      # r > d_in, negative s
+        (3, 33, 1, 0.3, "f32"),       # s not a power of two
+        (6, 20, 4, 0.0, "bf16"),
+    ],
+)
+def test_dense_norm_matches_exact_bruteforce(d_out, d_in, r, s, kind):
+    rng = np.random.default_rng(1234 + d_out * 7 + r)
+    mk = _bf16_like if kind == "bf16" else _f32_like
+    W = mk(rng, (d_out, d_in), 2.0 ** -7)
+    A = mk(rng, (r, d_in), 2.0 ** -7)
+    B = mk(rng, (d_out, r), 2.0 ** -9)
+    exact = bf.exact_row_sq_norms(W.tolist(), A.tolist(), B.tolist(), s)
+    got = O.dense_row_norm(W, A, B, s)
+    got_alg = O.algorithm1_row_norm(W, A, B, s, budget_bytes=64 * 4 * max(d_out, 1))
+    for j in range(d_out):
+        ref = float(bf.exact_sqrt(exact[j]))
+        assert got[j] == pytest.approx(ref, rel=1e-14, abs=0.0)
+        assert got_alg[j] == pytest.approx(ref, rel=1e-12, abs=1e-300)
+
+
+def test_norm_hand_worked_example():
+    # W + s*B@A with s = 1/2:
+    #   B@A = [[1,0,0],[0,1,1],[2,-1,-1]]
+    #   W + B@A/2 = [[3.5,4,0],[1,2.5,2.5],[1,-0.5,-0.5]]
+    #   squared row norms 113/4, 27/2, 3/2.
+    W = np.array([[3, 4, 0], [1, 2, 2], [0, 0, 0]], float)
+    A = np.array([[1, 0, 0], [0, 1, 1]], float)
+    B = np.array([[1, 0], [0, 1], [2, -1]], float)
+    expect_sq = [Fraction(113, 4), Fraction(27, 2), Fraction(3, 2)]
+    assert bf.exact_row_sq_norms(W.tolist(), A.tolist(), B.tolist(), 0.5) == expect_sq
+    got = O.dense_row_norm(W, A, B, 0.5)
+    np.testing.assert_allclose(got ** 2, [float(q) for q in expect_sq], rtol=1e-15)
+    base, cross, ba, G = O.factored_terms(W, A, B)
+    # base = ||W_j||^2; cross = <W_j,(BA)_j>; ba = ||(BA)_j||^2, by hand:
+    np.testing.assert_array_equal(base, [25, 9, 0])
+    np.testing.assert_array_equal(cross, [3, 4, 0])
+    np.testing.assert_array_equal(ba, [1, 2, 6])
+    np.testing.assert_array_equal(G, [[1, 0], [0, 2]])
+
+
+@pytest.mark.parametrize("budget_cols", [64, 128, 192, 10_000])
+def test_algorithm1_equals_dense_for_any_chunking(budget_cols):
+    rng = np.random.default_rng(7)
+    d_out, d_in, r, s = 37, 201, 13, 0.75      # ragged last chunk
+    W = rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)
+    A = rng.standard_normal((r, d_in)) / np.sqrt(d_in)
+    B = rng.standard_normal((d_out, r)) * 0.02
+    budget = budget_cols * 4 * d_out
+    np.testing.assert_allclose(
+        O.algorithm1_row_norm(W, A, B, s, budget), O.dense_row_norm(W, A, B, s), rtol=1e-13
+    )
+
+
+def test_s_zero_is_plain_row_norm():
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((19, 50))
+    A = rng.standard_normal((6, 50))
+    B = rng.standard_normal((19, 6))
+    ref = np.linalg.norm(W, axis=1)
+    np.testing.assert_allclose(O.dense_row_norm(W, A, B, 0.0), ref, rtol=1e-15)
+    np.testing.assert_allclose(O.algorithm1_row_norm(W, A, B, 0.0), ref, rtol=1e-15)
+
+
+@pytest.mark.parametrize("zero", ["A", "B"])
+def test_zero_factor_kills_cross_and_gram(zero):
+    # LoRA starts with B = 0; then W + sBA = W.
+    rng = np.random.default_rng(4)
+    W = rng.standard_normal((11, 40))
+    A = rng.standard_normal((5, 40))
+    B = rng.standard_normal((11, 5))
+    if zero == "A":
+        A[:] = 0.0
+    else:
+        B[:] = 0.0
+    _, cross, ba, _ = O.factored_terms(W, A, B)
+    assert np.all(cross == 0.0) and np.all(ba == 0.0)
+    np.testing.assert_allclose(O.dense_row_norm(W, A, B, 1.5), np.linalg.norm(W, axis=1), rtol=1e-15)
+
+
+def test_identity_A_closed_form():
+    # A = [I_r | 0]: (BA)_j = [B_j, 0,...], so ||W+sBA||_j^2 = sum_{k<r}(W_jk+sB_jk)^2 + sum_{k>=r} W_jk^2.
+    rng = np.random.default_rng(5)
+    d_out, d_in, r, s = 9, 30, 4, -0.5
+    W = rng.standard_normal((d_out, d_in))
+    B = rng.standard_normal((d_out, r))
+    A = np.zeros((r, d_in))
+    A[:, :r] = np.eye(r)
+    head = W[:, :r] + s * B
+    ref = np.sqrt(np.sum(head ** 2, axis=1) + np.sum(W[:, r:] ** 2, axis=1))
+    np.testing.assert_allclose(O.dense_row_norm(W, A, B, s), ref, rtol=1e-15)
+    np.testing.assert_allclose(O.algorithm1_row_norm(W, A, B, s), ref, rtol=1e-14)
+
+
+def test_rank_one_and_zero_W_closed_forms():
+    rng = np.random.default_rng(6)
+    d_out, d_in, s = 8, 25, 1.75
+    A = rng.standard_normal((1, d_in))
+    B = rng.standard_normal((d_out, 1))
+    W = rng.standard_normal((d_out, d_in))
+    _, _, ba, G = O.factored_terms(W, A, B)
+    nA2 = float(np.dot(A[0], A[0]))
+    np.testing.assert_allclose(ba, B[:, 0] ** 2 * nA2, rtol=1e-14)
+    np.testing.assert_allclose(G, [[nA2]], rtol=1e-15)
+    W0 = np.zeros_like(W)
+    ref = abs(s) * np.abs(B[:, 0]) * np.sqrt(nA2)
+    np.testing.assert_allclose(O.dense_row_norm(W0, A, B, s), ref, rtol=1e-14)
+    np.testing.assert_allclose(O.algorithm1_row_norm(W0, A, B, s), ref, rtol=1e-13)
+
+
+def test_rotation_invariance_and_row_permutation():
+    rng = np.random.default_rng(8)
+    d_out, d_in, r, s = 14, 24, 5, 0.9
+    W = rng.standard_normal((d_out, d_in))
+    A = rng.standard_normal((r, d_in))
+    B = rng.standard_normal((d_out, r))
+    Q, _ = np.linalg.qr(rng.standard_normal((d_in, d_in)))
+    base = O.dense_row_norm(W, A, B, s)
+    np.testing.assert_allclose(O.dense_row_norm(W @ Q, A @ Q, B, s), base, rtol=1e-13)
+    np.testing.assert_allclose(O.algorithm1_row_norm(W @ Q, A @ Q, B, s), base, rtol=1e-13)
+    p = rng.permutation(d_out)
+    np.testing.assert_array_equal(O.dense_row_norm(W[p], A, B[p], s), base[p])
+
+
+def test_factored_terms_are_the_dense_inner_products():
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((10, 33))
+    A = rng.standard_normal((7, 33))
+    B = rng.standard_normal((10, 7))
+    base, cross, ba, G = O.factored_terms(W, A, B, budget_bytes=64 * 4 * 10)
+    BA = np.zeros((10, 33))
+    for j in range(10):              # BA row by row, as explicit sums
+        for l in range(7):
+            BA[j] += B[j, l] * A[l]
+    np.testing.assert_allclose(base, [np.dot(w, w) for w in W], rtol=1e-14)
+    np.testing.assert_allclose(cross, [np.dot(W[j], BA[j]) for j in range(10)], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ba, [np.dot(BA[j], BA[j]) for j in range(10)], rtol=1e-12)
+    np.testing.assert_allclose(G, G.T, rtol=0, atol=1e-13)
+    assert np.all(np.linalg.eigvalsh(G) > -1e-12)
+
+
+def test_norm_clamp_and_cancellation_to_zero():
+    # W = -s B A exactly: the true norm is 0.
+    rng = np.random.default_rng(10)
+    A = _bf16_like(rng, (3, 16), 2.0 ** -4)
+    B = _bf16_like(rng, (5, 3), 2.0 ** -4)
+    s = 0.5
+    W = -s * (B @ A)
+    assert np.all(O.dense_row_norm(W, A, B, s) == 0.0)
+    alg = O.algorithm1_row_norm(W, A, B, s)
+    assert np.all(np.isfinite(alg)) and np.all(alg >= 0.0) and np.all(alg < 1e-6)
+
+
+# ------------------------------------------------------- chunk + memory ----
+
+def test_chunk_size_rule():
+    MiB = 1 << 20
+    assert O.chunk_size(8192, 8192, 256 * MiB) == 8192          # [d_out,cs] fp32 = 256 MiB
+    assert O.chunk_size(28672, 8192, 256 * MiB) == 2304         # floor(2340.57) -> 64-aligned
+    assert O.chunk_size(512, 3584, 256 * MiB) == 3584           # capped at d_in
+    assert O.chunk_size(4096, 4096, 1 * MiB) == 64              # never below 64
+    assert O.chunk_size(100, 40, 256 * MiB) == 40               # d_in below one chunk
+    assert O.chunk_size(1000, 8192, 700_000) == 128             # 175 -> 128
+
+
+def test_table1_memory_matches_printed_values():
+    with open(os.path.join(GOLDEN, "table1_memory.json")) as f:
+        gold = json.load(f)
+    MiB = float(1 << 20)
+    for c in gold["cases"]:
+        mem = O.table1_memory(c["d_out"], c["d_in"], c["r"], c["elem_bytes"])
+        assert mem["dense"] / MiB == c["dense_MiB"]
+        assert round(mem["factored"] / MiB, 1) == c["factored_MiB"]
+        assert round(mem["dense"] / mem["factored"], c["ratio_digits"]) == c["ratio_printed"]
+        assert mem["gram"] / MiB == c["gram_MiB"]
+        assert mem["chunk"] / MiB == c["chunk_buffer_near_MiB"]
+    ub = gold["gram_upper_bound"]
+    g = O.table1_memory(8192, 8192, ub["r"], ub["elem_bytes"])["gram"]
+    assert g / 1e6 <= ub["at_most_MB"]
+
+
+# ------------------------------------------------------------ g = m/... ----
+
+def test_magnitude_scale_cases():
+    m = np.array([2.0, 3.0, 5.0, 7.0])
+    wn = np.array([4.0, 0.0, 1e-9, np.nan])
+    g = O.magnitude_scale(m, wn, 1e-6)
+    assert g[0] == 0.5
+    assert g[1] == 3.0 / 1e-6 and g[2] == 5.0 / 1e-6
+    assert np.isnan(g[3])
+
+
+# -------------------------------------------------------------- compose ----
+
+def test_compose_hand_worked_example():
+    # (g-1)*base + g*s*lora with g = [1.25, 0.75], s = 2:
+    #   col 0: 0.25*1 + 1.25*2*0.5 = 1.5;  col 1: -0.25*-2 + 0.75*2*4 = 6.5
+    out = O.compose([[1.0, -2.0]], [[0.5, 4.0]], [1.25, 0.75], 2.0)
+    np.testing.assert_array_equal(out, [[1.5, 6.5]])
+
+
+def test_compose_special_cases():
+    rng = np.random.default_rng(11)
+    base = rng.standard_normal((6, 9))
+    lora = rng.standard_normal((6, 9))
+    g = 1.0 + 0.01 * rng.standard_normal(9)
+    s = 0.5
+    np.testing.assert_array_equal(O.compose(base, lora, np.ones(9), s), s * lora)
+    np.testing.assert_array_equal(O.compose(base, lora, g, 0.0), (g - 1.0)[None] * base)
+    np.testing.assert_array_equal(O.compose(base, np.zeros_like(lora), g, s), (g - 1.0)[None] * base)
+    np.testing.assert_array_equal(O.compose(np.zeros_like(base), lora, g, s), g[None] * (s * lora))
+    # algebraically equal to the naive form
+    np.testing.assert_allclose(O.compose(base, lora, g, s), O.compose_naive(base, lora, g, s),
+                               rtol=1e-9, atol=1e-14)
+
+
+def test_compose_matches_exact_rational_rounding():
+    rng = np.random.default_rng(12)
+    n = 3000
+    base = O.bf16_round(rng.standard_normal(n))
+    lora = O.bf16_round(0.1 * rng.standard_normal(n))
+    g = O.f32_round(1.0 + 0.0015 * rng.standard_normal(n))
+    s = 0.5
+    got = O.bf16_round(O.compose(base[None], lora[None], g, s))[0]
+    for i in range(n):
+        q = bf.exact_compose(base[i], lora[i], g[i], s)
+        assert float(bf.round_fraction_bf16(q)) == got[i], i
+
+
+def test_bf16_round_matches_torch_and_ties():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    # exact midpoints between neighbouring bf16 values: ties go to even
+    hi = (x.view(np.uint32) & np.uint32(0xFFFF0000))
+    ties = (hi | np.uint32(0x8000)).view(np.float32)
+    allx = np.concatenate([x, ties, np.float32([0.0, -0.0, 1e-40, 3.0e38, -3.0e38])])
+    ref = torch.from_numpy(allx).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(allx.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    for v in [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.1, 1.0 / 3.0]:
+        assert O.bf16_round(v) == float(bf.round_fraction_bf16(Fraction(v)))
+
+
+def test_stable_compose_beats_naive_near_one():
+    # Near g = 1 the naive form cancels; the stable form keeps (g-1) explicit.
+    rng = np.random.default_rng(14)
+    T, d = 512, 1024
+    base = O.bf16_round(rng.standard_normal((T, d)))
+    lora = O.bf16_round(0.1 * rng.standard_normal((T, d)))
+    g = O.f32_round(1.0 + 0.0015 * rng.standard_normal(d))
+    s = 0.5
+    ref = O.compose(base, lora, g, s)
+    e_st = np.max(np.abs(O.compose_f32_stable(base, lora, g, s) - ref))
+    e_nv = np.max(np.abs(O.compose_f32_naive(base, lora, g, s) - ref))
+    assert e_st < e_nv / 2
+
+
+# ------------------------------------------------------ planted mistakes ----
+
+def test_pins_reject_planted_mistakes():
+    """Each mutant of the oracle must fail at least one of the checks above."""
+    rng = np.random.default_rng(15)
+    W = _bf16_like(rng, (4, 12), 2.0 ** -6)
+    A = _bf16_like(rng, (3, 12), 2.0 ** -6)
+    B = _bf16_like(rng, (4, 3), 2.0 ** -6)
+    s = 0.5
+    exact = np.array([float(bf.exact_sqrt(q)) for q in bf.exact_row_sq_norms(W.tolist(), A.tolist(), B.tolist(), s)])
+
+    def norm_ok(fn):
+        return np.allclose(fn(W, A, B, s), exact, rtol=1e-12, atol=0)
+
+    norm_mutants = {
+        "minus sign": lambda W, A, B, s: O.dense_row_norm(W, A, -B, s),
+        "dropped s": lambda W, A, B, s: O.dense_row_norm(W, A, B, 1.0),
+        "transposed product": lambda W, A, B, s: np.sqrt(np.sum((W + s * (B @ A)[::-1]) ** 2, 1)),
+        "cross without 2": lambda W, A, B, s: np.sqrt(
+            (lambda t: t[0] + s * t[1] + s * s * t[2])(O.factored_terms(W, A, B))),
+        "no gram term": lambda W, A, B, s: np.sqrt(
+            (lambda t: t[0] + 2 * s * t[1])(O.factored_terms(W, A, B))),
+        "s instead of s^2": lambda W, A, B, s: np.sqrt(
+            (lambda t: t[0] + 2 * s * t[1] + s * t[2])(O.factored_terms(W, A, B))),
+    }
+    assert norm_ok(O.dense_row_norm) and norm_ok(O.algorithm1_row_norm)
+    for name, fn in norm_mutants.items():
+        assert not norm_ok(fn), name
+
+    base = np.array([[1.0, -2.0]])
+    lora = np.array([[0.5, 4.0]])
+    gg = np.array([1.25, 0.75])
+
+    def compose_ok(fn):
+        return (np.array_equal(fn(base, lora, gg, 2.0), [[1.5, 6.5]])
+                and np.array_equal(fn(base, lora, np.ones(2), 2.0), 2.0 * lora))
+
+    compose_mutants = {
+        "g+1": lambda b, l, g, s: (g[None] + 1) * b + g[None] * s * l,
+        "dropped s": lambda b, l, g, s: (g[None] - 1) * b + g[None] * l,
+        "dropped g on lora": lambda b, l, g, s: (g[None] - 1) * b + s * l,
+        "returns output not delta": lambda b, l, g, s: g[None] * (s * l + b),
+    }
+    assert compose_ok(O.compose)
+    for name, fn in compose_mutants.items():
+        assert not compose_ok(fn), name
