@@ -1,0 +1,220 @@
+"""ctypes binding of libdora (include/dora.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+layout, their data pointers and the current HIP stream are handed to the C
+ABI, and outputs are allocated with torch. Every step of the computation
+runs in libdora's kernels; there is no fallback path. If ``libdora.so`` is
+missing, every call raises.
+
+The function names match the C entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH",
+    "DoraError",
+    "load",
+    "dora_version",
+    "dora_status_string",
+    "dora_norm_chunk_size",
+    "dora_norm_workspace_size",
+    "dora_norm_plan_info",
+    "dora_factored_norm",
+    "dora_magnitude_scale",
+    "dora_compose",
+    "DORA_BF16",
+    "DORA_F32",
+    "PLAN_FIELDS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdora.so")
+
+DORA_BF16 = 0
+DORA_F32 = 1
+DEFAULT_BUDGET = 256 << 20
+
+PLAN_FIELDS = (
+    "mode", "tile_cfg", "tile_rows", "tile_cols", "stage_depth", "row_tiles_w",
+    "row_tiles_a", "col_tiles", "stages", "ranges", "workgroups_per_range",
+    "max_segments", "workspace_bytes", "grid", "lds_bytes",
+)
+
+_lib = None
+_c_i64 = ctypes.c_int64
+_c_sz = ctypes.c_size_t
+_c_p = ctypes.c_void_p
+_c_f = ctypes.c_float
+_c_i = ctypes.c_int
+
+
+class DoraError(RuntimeError):
+    """A libdora call returned a non-zero status."""
+
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func}: {dora_status_string(status)} (status {status})")
+
+
+def load():
+    """Load libdora.so (after torch, so it binds to torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m dora_weight_norm_amd.build` "
+            "or __graft_entry__.build()"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "dora_status_string": (ctypes.c_char_p, [_c_i]),
+        "dora_version": (_c_i, []),
+        "dora_norm_chunk_size": (_c_i, [_c_i64, _c_i64, _c_sz, ctypes.POINTER(_c_i64)]),
+        "dora_norm_workspace_size": (_c_i, [_c_i64, _c_i64, _c_i64, _c_i, _c_f, _c_sz, ctypes.POINTER(_c_sz)]),
+        "dora_norm_plan_info": (_c_i, [_c_i64, _c_i64, _c_i64, _c_i, _c_f, _c_sz, ctypes.POINTER(_c_i64), _c_i]),
+        "dora_factored_norm": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i64, _c_i64, _c_i64, _c_f, _c_sz, _c_p, _c_sz,
+                                      _c_p, _c_p, _c_f, _c_p, _c_p]),
+        "dora_magnitude_scale": (_c_i, [_c_p, _c_p, _c_f, _c_i64, _c_p, _c_p]),
+        "dora_compose": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(load(), name)(*args)
+    if st != 0:
+        raise DoraError(name, st)
+
+
+def dora_version() -> int:
+    return load().dora_version()
+
+
+def dora_status_string(status: int) -> str:
+    return load().dora_status_string(status).decode()
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in (torch.bfloat16, "bf16", DORA_BF16):
+        return DORA_BF16
+    if dtype in (torch.float32, "f32", DORA_F32):
+        return DORA_F32
+    raise TypeError(f"unsupported dtype {dtype}; libdora takes bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def dora_norm_chunk_size(d_out: int, d_in: int, budget_bytes: int = DEFAULT_BUDGET) -> int:
+    cs = _c_i64()
+    _call("dora_norm_chunk_size", d_out, d_in, budget_bytes, ctypes.byref(cs))
+    return cs.value
+
+
+def dora_norm_workspace_size(d_out: int, d_in: int, r: int, dtype, s: float,
+                             budget_bytes: int = DEFAULT_BUDGET) -> int:
+    ws = _c_sz()
+    _call("dora_norm_workspace_size", d_out, d_in, r, _dtype_code(dtype), s, budget_bytes, ctypes.byref(ws))
+    return ws.value
+
+
+def dora_norm_plan_info(d_out: int, d_in: int, r: int, dtype, s: float,
+                        budget_bytes: int = DEFAULT_BUDGET) -> dict:
+    buf = (_c_i64 * len(PLAN_FIELDS))()
+    _call("dora_norm_plan_info", d_out, d_in, r, _dtype_code(dtype), s, budget_bytes, buf, len(PLAN_FIELDS))
+    return dict(zip(PLAN_FIELDS, list(buf)))
+
+
+def dora_factored_norm(W, A, B, s: float, budget_bytes: int = DEFAULT_BUDGET, m=None, eps: float = 1e-6,
+                       workspace=None, wnorm=None, g=None, stream=None):
+    """wnorm = ||W + s B A||_row (fp32) and, if m is given, g = m / max(wnorm, eps).
+
+    W [d_out, d_in], A [r, d_in], B [d_out, r], all bfloat16 or all float32,
+    on the GPU. Returns (wnorm, g); g is None when m is None.
+    """
+    for t, nm in ((W, "W"), (A, "A"), (B, "B")):
+        _dev(t, nm)
+    if W.dim() != 2 or A.dim() != 2 or B.dim() != 2:
+        raise ValueError("W, A, B must be 2-D")
+    d_out, d_in = W.shape
+    r = A.shape[0]
+    if A.shape[1] != d_in or tuple(B.shape) != (d_out, r):
+        raise ValueError(f"shape mismatch: W {tuple(W.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if not (W.dtype == A.dtype == B.dtype):
+        raise TypeError("W, A, B must share one dtype")
+    dt = _dtype_code(W.dtype)
+    dev = W.device
+    ws_bytes = dora_norm_workspace_size(d_out, d_in, r, dt, s, budget_bytes)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if wnorm is None:
+        wnorm = torch.empty(d_out, dtype=torch.float32, device=dev)
+    if m is not None:
+        _dev(m, "m")
+        if m.dtype != torch.float32 or m.shape != (d_out,):
+            raise ValueError("m must be float32 [d_out]")
+        if g is None:
+            g = torch.empty(d_out, dtype=torch.float32, device=dev)
+    _call("dora_factored_norm", _ptr(W), _ptr(A), _ptr(B), dt, d_out, d_in, r, s, budget_bytes,
+          _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+          _ptr(wnorm), _ptr(m), eps, _ptr(g) if m is not None else None, _stream(stream))
+    return wnorm, (g if m is not None else None)
+
+
+def dora_magnitude_scale(m, wnorm, eps: float = 1e-6, g=None, stream=None):
+    """g = m / max(wnorm, eps), fp32 [d_out]."""
+    _dev(m, "m")
+    _dev(wnorm, "wnorm")
+    if g is None:
+        g = torch.empty_like(m)
+    _call("dora_magnitude_scale", _ptr(m), _ptr(wnorm), eps, m.numel(), _ptr(g), _stream(stream))
+    return g
+
+
+def dora_compose(base, lora, g, s: float, out=None, stream=None):
+    """out = (g - 1) * base + g * (s * lora), with g [d_out] scaling columns of [T, d_out]."""
+    for t, nm in ((base, "base"), (lora, "lora"), (g, "g")):
+        _dev(t, nm)
+    if base.shape != lora.shape or base.dtype != lora.dtype:
+        raise ValueError("base and lora must share shape and dtype")
+    if base.dim() != 2:
+        raise ValueError("base and lora must be [T, d_out]")
+    T, d_out = base.shape
+    if g.dtype != torch.float32 or g.shape != (d_out,):
+        raise ValueError("g must be float32 [d_out]")
+    dt = _dtype_code(base.dtype)
+    if out is None:
+        out = torch.empty_like(base)
+    else:
+        _dev(out, "out")
+        if out.shape != base.shape or out.dtype != base.dtype:
+            raise ValueError("out must match base")
+    _call("dora_compose", _ptr(base), _ptr(lora), _ptr(g), s, dt, T, d_out, _ptr(out), _stream(stream))
+    return out

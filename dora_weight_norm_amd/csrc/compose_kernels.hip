@@ -1,0 +1,145 @@
+// Stable DoRA magnitude compose on gfx950:
+//
+//   out[t,j] = (g[j] - 1) * base[t,j] + g[j] * (s * lora[t,j])
+//
+// ("DoRA优化技术解析：从内存瓶颈到高效实现", cyqw.cn, §2.1, §2.1.1, §5.2.)
+// One HBM pass: base and lora are streamed once, out written once, g read
+// once per thread into registers. Each thread owns one 16-byte column strip
+// (8 bf16 or 4 fp32 columns) and walks rows with a stride of the grid's
+// row count, keeping several rows' loads in flight. Loads and stores are
+// non-temporal: nothing here is reused, so it should not displace anything
+// from the L2 or the Infinity Cache. Arithmetic is fp32: s*lora first, then
+// one fused multiply-add g*(s*lora) + (g-1)*base, rounded once (RNE) to the
+// storage type.
+#include "dora_device.h"
+#include "dora_launch.h"
+
+namespace dora {
+
+namespace {
+
+constexpr int kUnroll = 4;
+
+template <typename T, int VEC>
+struct Strip;
+template <typename T>
+struct Strip<T, 1> {
+  using V = T;
+};
+template <>
+struct Strip<bf16_t, 8> {
+  using V = u32x4;
+};
+template <>
+struct Strip<float, 4> {
+  using V = u32x4;
+};
+
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack(const typename Strip<T, VEC>::V& v, float (&f)[VEC]) {
+  if constexpr (VEC == 1) {
+    f[0] = to_f32(v);
+  } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ typename Strip<T, VEC>::V pack(const float (&f)[VEC]) {
+  if constexpr (VEC == 1) {
+    return from_f32<T>(f[0]);
+  } else if constexpr (sizeof(T) == 2) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (uint32_t)f32_to_bf16_rne(f[2 * i]) | ((uint32_t)f32_to_bf16_rne(f[2 * i + 1]) << 16);
+    return v;
+  } else {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+    return v;
+  }
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void compose_kernel(const T* base, const T* lora, const float* __restrict__ g,
+                                                      float s, int64_t T_rows, int64_t d_out, T* out) {
+  using V = typename Strip<T, VEC>::V;
+  const int64_t cg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (cg >= d_out / VEC) return;
+  const int64_t c0 = cg * VEC;
+  float gv[VEC], gm1[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    gv[e] = g[c0 + e];
+    gm1[e] = gv[e] - 1.0f;
+  }
+  const int64_t step = (int64_t)gridDim.y * kUnroll;
+  for (int64_t t0 = (int64_t)blockIdx.y * kUnroll; t0 < T_rows; t0 += step) {
+    V bv[kUnroll], lv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t0 + u < T_rows) {
+        const int64_t off = (t0 + u) * d_out + c0;
+        bv[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(base + off));
+        lv[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(lora + off));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t0 + u < T_rows) {
+        float b[VEC], l[VEC], o[VEC];
+        unpack<T, VEC>(bv[u], b);
+        unpack<T, VEC>(lv[u], l);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float sl = s * l[e];
+          o[e] = fmaf(gv[e], sl, gm1[e] * b[e]);
+        }
+        const int64_t off = (t0 + u) * d_out + c0;
+        __builtin_nontemporal_store(pack<T, VEC>(o), reinterpret_cast<V*>(out + off));
+      }
+    }
+  }
+}
+
+template <typename T, int VEC>
+hipError_t launch(const void* base, const void* lora, const float* g, float s, int64_t T_rows, int64_t d_out,
+                  void* out, hipStream_t st) {
+  const int64_t ncg = d_out / VEC;
+  int64_t tpb = ((ncg + 63) / 64) * 64;
+  if (tpb > 256) tpb = 256;
+  const int64_t bx = (ncg + tpb - 1) / tpb;
+  // About 8 resident workgroups per compute unit over 256 CUs.
+  int64_t by = 2048 / bx;
+  if (by < 1) by = 1;
+  const int64_t row_iters = (T_rows + kUnroll - 1) / kUnroll;
+  if (by > row_iters) by = row_iters;
+  if (by > 65535) by = 65535;
+  hipLaunchKernelGGL((compose_kernel<T, VEC>), dim3((unsigned)bx, (unsigned)by), dim3((unsigned)tpb), 0, st,
+                     static_cast<const T*>(base), static_cast<const T*>(lora), g, s, T_rows, d_out,
+                     static_cast<T*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
+                          int64_t d_out, void* out, bool vec, hipStream_t st) {
+  if (dtype == 0) {
+    return vec ? launch<bf16_t, 8>(base, lora, g, s, T, d_out, out, st)
+               : launch<bf16_t, 1>(base, lora, g, s, T, d_out, out, st);
+  }
+  return vec ? launch<float, 4>(base, lora, g, s, T, d_out, out, st)
+             : launch<float, 1>(base, lora, g, s, T, d_out, out, st);
+}
+
+}  // namespace dora

@@ -1,0 +1,126 @@
+// Device-side helpers shared by the libdora kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dora {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Storage types: bf16 is carried as its 16 raw bits.
+typedef uint16_t bf16_t;
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<bf16_t> {
+  static constexpr int esz = 2;
+  static constexpr int epc = 8;         // elements per 16-byte chunk
+  static constexpr int frag_chunks = 1; // 16-byte chunks per MFMA operand fragment
+};
+template <>
+struct Elem<float> {
+  static constexpr int esz = 4;
+  static constexpr int epc = 4;
+  static constexpr int frag_chunks = 2;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16_rne(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+__device__ __forceinline__ float to_f32(bf16_t v) { return bf16_bits_to_f32(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float f);
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return f32_to_bf16_rne(f); }
+template <>
+__device__ __forceinline__ float from_f32<float>(float f) { return f; }
+
+// Sum of squares of the elements held in one 16-byte chunk.
+__device__ __forceinline__ float chunk_sumsq(const u32x4& v, bf16_t) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16);
+    const float hi = __uint_as_float(v[i] & 0xffff0000u);
+    s0 = fmaf(lo, lo, s0);
+    s1 = fmaf(hi, hi, s1);
+  }
+  return s0 + s1;
+}
+__device__ __forceinline__ float chunk_sumsq(const u32x4& v, float) {
+  const float a = __uint_as_float(v[0]), b = __uint_as_float(v[1]);
+  const float c = __uint_as_float(v[2]), d = __uint_as_float(v[3]);
+  return fmaf(a, a, b * b) + fmaf(c, c, d * d);
+}
+
+// One 16-byte chunk of a row: elements [k, k+EPC) of `row`, zero-filled past
+// d_in or when the row is out of range. `vec` means the row start and d_in
+// allow an aligned 16-byte load.
+template <typename T>
+__device__ __forceinline__ u32x4 load_chunk(const T* row, int64_t k, int64_t d_in, bool row_ok,
+                                            bool vec) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (!row_ok || k >= d_in) return v;
+  if (vec) return *reinterpret_cast<const u32x4*>(row + k);
+  constexpr int EPC = Elem<T>::epc;
+  T tmp[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) tmp[e] = (k + e < d_in) ? row[k + e] : T(0);
+  __builtin_memcpy(&v, tmp, 16);
+  return v;
+}
+
+// XOR swizzle of 16-byte chunks inside LDS rows of CPR chunks, so that the
+// 32 rows one MFMA fragment read touches spread over all LDS banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (CPR == 8) {
+    return c ^ (row & 7);
+  } else {
+    static_assert(CPR == 4, "LDS rows are 64 or 128 bytes");
+    return c ^ ((row >> 1) & 3);
+  }
+}
+
+// acc += A_frag * B_frag over one 16-deep slice of K.
+// bf16: one v_mfma_f32_32x32x16_bf16. fp32: eight v_mfma_f32_32x32x2_f32,
+// element e of both fragments forming the e-th pair of K indices.
+template <typename T>
+struct Mfma;
+template <>
+struct Mfma<bf16_t> {
+  static __device__ __forceinline__ f32x16 run(const u32x4* a, const u32x4* b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                   __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<float> {
+  static __device__ __forceinline__ f32x16 run(const u32x4* a, const u32x4* b, f32x16 c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[h][e]), __uint_as_float(b[h][e]),
+                                                 c, 0, 0, 0);
+    return c;
+  }
+};
+
+// Row (within a 32x32 block) of accumulator register v for this lane:
+// lanes 0-31 hold rows {0-3, 8-11, 16-19, 24-27}, lanes 32-63 the other four
+// of each group of eight; the column is lane % 32.
+__device__ __forceinline__ int acc_row(int v, int lgrp) { return 8 * (v >> 2) + 4 * lgrp + (v & 3); }
+
+}  // namespace dora

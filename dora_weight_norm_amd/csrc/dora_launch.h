@@ -1,0 +1,21 @@
+// Kernel launchers behind the C ABI (host side, defined in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dora_plan.h"
+
+namespace dora {
+
+hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A, const void* B, void* ws,
+                                float s, const float* m, float eps, float* wnorm, float* g, hipStream_t st);
+hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t d_in, bool vec, const float* m,
+                               float eps, float* wnorm, float* g, hipStream_t st);
+hipError_t launch_magnitude(const float* m, const float* wnorm, float eps, int64_t n, float* g, hipStream_t st);
+hipError_t launch_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
+                          int64_t d_out, void* out, bool vec, hipStream_t st);
+size_t main_kernel_lds_bytes(int cfg);
+
+}  // namespace dora

@@ -1,0 +1,175 @@
+/*
+ * libdora: the DoRA forward hot path on AMD Instinct MI355X (gfx950).
+ *
+ * DoRA writes an adapted weight as W' = m * (W + sBA) / ||W + sBA||_row
+ * ("Scaling DoRA: High-Rank Adaptation via Factored Norms and Fused Kernels",
+ * summary on alanhou.org, "The Problem"). This library computes the two
+ * pieces of that forward pass that dominate its cost:
+ *
+ *   dora_factored_norm  the row norm ||W + sBA||_row without forming BA,
+ *                       through ||W||^2 + 2s<W,BA> + s^2||BA||^2 with
+ *                       U = W A^T and G = A A^T ("DoRA优化技术解析：从内存瓶颈到
+ *                       高效实现", cyqw.cn, §1.2, §1.2.1, §5.1 Algorithm 1),
+ *                       and optionally g = m / max(wnorm, eps) (same page,
+ *                       §1.2.2);
+ *   dora_compose        the stable magnitude compose
+ *                       (g - 1) * base + g * (s * lora) in one pass
+ *                       (same page, §2.1, §2.1.1, §5.2).
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are dense, row-major and contiguous. Layouts follow LoRA:
+ *     W [d_out, d_in], A [r, d_in], B [d_out, r]; activations [T, d_out].
+ *   - Device pointers are device memory the caller owns (e.g. torch
+ *     tensors). The library allocates nothing and keeps no state between
+ *     calls; it never frees or retains a pointer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued asynchronously on it; results are valid once
+ *     the stream has reached that point.
+ *   - Errors: arguments are checked on the host before any launch. A
+ *     failed check returns a non-zero dora_status and enqueues nothing.
+ *     A HIP launch error returns DORA_ERR_HIP. No exception crosses this
+ *     ABI and no call aborts the process.
+ *   - Results are bitwise reproducible from run to run for the same
+ *     arguments: reductions use a fixed order and no floating-point
+ *     atomics.
+ */
+#ifndef DORA_H_
+#define DORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dora_status {
+  DORA_OK = 0,
+  DORA_ERR_INVALID_ARG = 1,       /* null pointer, negative size, bad alias  */
+  DORA_ERR_UNSUPPORTED_DTYPE = 2, /* dtype code not in dora_dtype            */
+  DORA_ERR_BUDGET = 3,            /* workspace needed exceeds the budget     */
+  DORA_ERR_WORKSPACE = 4,         /* workspace pointer too small / misaligned */
+  DORA_ERR_HIP = 5                /* a HIP runtime or launch call failed     */
+} dora_status;
+
+typedef enum dora_dtype {
+  DORA_BF16 = 0, /* bfloat16 storage, fp32 arithmetic */
+  DORA_F32 = 1   /* binary32 storage and arithmetic   */
+} dora_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dora_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int dora_version(void);
+
+/*
+ * Chunk width of the factored norm's d_in loop, as the cyqw.cn page defines
+ * it (§5.1 Algorithm 1, step 1): the fp32 chunk buffer [d_out, cs] must fit
+ * `budget_bytes`, aligned to 64 elements. cs = min(d_in, max(64,
+ * 64 * floor(floor(budget / (4 d_out)) / 64))); cs = d_in when d_out or
+ * d_in is 0. Host only; never touches the GPU.
+ * Returns DORA_ERR_INVALID_ARG for negative sizes or cs == NULL.
+ */
+dora_status dora_norm_chunk_size(int64_t d_out, int64_t d_in, size_t budget_bytes,
+                                 int64_t* cs);
+
+/*
+ * Bytes of device workspace dora_factored_norm needs for this shape.
+ * The planner picks the most parallel split whose workspace fits
+ * `budget_bytes`; the same arguments always give the same plan.
+ * s == 0 or r == 0 needs no workspace (the cross and Gram terms are
+ * skipped, cyqw.cn §5.1 notes). Host only; never touches the GPU.
+ * Returns DORA_ERR_BUDGET if even the least parallel plan does not fit,
+ * DORA_ERR_INVALID_ARG for negative sizes or ws_bytes == NULL,
+ * DORA_ERR_UNSUPPORTED_DTYPE for an unknown dtype.
+ */
+dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int dtype,
+                                     float s, size_t budget_bytes, size_t* ws_bytes);
+
+/*
+ * The plan dora_factored_norm would use, for diagnostics and benchmarks.
+ * Fills info[0 .. n_info-1] with, in order: mode (0 nothing to do, 1 row
+ * sum of squares only, 2 factored), tile configuration, tile rows, tile
+ * columns, stage depth along d_in, row tiles over W, row tiles over A,
+ * column tiles, stages, d_in ranges, workgroups per range, most workgroups
+ * sharing one (range, tile), workspace bytes, main-kernel grid, main-kernel
+ * LDS bytes; entries past the last field are set to -1.
+ * Before returning it replays the work split on the host and checks that
+ * every (range, tile, stage) unit has exactly one owner and that the
+ * reduction enumerates exactly the partials the producers write;
+ * DORA_ERR_INVALID_ARG if not. Host only; never touches the GPU.
+ */
+dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s,
+                                size_t budget_bytes, int64_t* info, int n_info);
+
+/*
+ * Factored row norm and magnitude scale (cyqw.cn §1.2, §1.2.1, §1.2.2,
+ * §5.1 Algorithm 1; alanhou.org "Factored Norm").
+ *
+ *   wnorm[j] = sqrt(max(base[j] + 2s*cross[j] + s^2*ba[j], 0))
+ *     base[j]  = sum_k W[j,k]^2
+ *     cross[j] = sum_l B[j,l] * U[j,l],      U = W A^T   [d_out, r]
+ *     ba[j]    = sum_l (B G)[j,l] * B[j,l],  G = A A^T   [r, r]
+ *   g[j]     = m[j] / max(wnorm[j], eps)      (only if m != NULL)
+ *
+ * Inputs W, A, B are device pointers of storage type `dtype`; all
+ * accumulation is fp32. U never leaves the matrix-core accumulators; BA is
+ * never formed. wnorm (and g) are fp32 [d_out] device arrays written by the
+ * call. m is an fp32 [d_out] device array or NULL (then g is not written
+ * and may be NULL). A NaN in the inputs propagates to wnorm and g.
+ *
+ * `workspace` must hold at least dora_norm_workspace_size(...) bytes
+ * (256-byte aligned) for the same (d_out, d_in, r, dtype, s, budget);
+ * it may be NULL when that size is 0. Its contents on entry are ignored.
+ *
+ * Sizes may be 0: d_out == 0 does nothing; d_in == 0 gives wnorm = 0;
+ * r == 0 or s == 0 gives wnorm = ||W||_row.
+ *
+ * Errors: DORA_ERR_INVALID_ARG (negative size, non-finite s or eps, eps <= 0,
+ * required pointer NULL, output overlapping an input), DORA_ERR_UNSUPPORTED_DTYPE,
+ * DORA_ERR_BUDGET (plan does not fit budget_bytes), DORA_ERR_WORKSPACE
+ * (workspace_bytes too small or pointer misaligned), DORA_ERR_HIP.
+ */
+dora_status dora_factored_norm(const void* W, const void* A, const void* B, int dtype,
+                               int64_t d_out, int64_t d_in, int64_t r, float s,
+                               size_t budget_bytes, void* workspace, size_t workspace_bytes,
+                               float* wnorm, const float* m, float eps, float* g,
+                               void* stream);
+
+/*
+ * g[j] = m[j] / max(wnorm[j], eps), fp32, on the device (cyqw.cn §1.2.2:
+ * the magnitude division is kept apart from the fused kernels). A NaN
+ * wnorm gives a NaN g. g may alias m or wnorm exactly.
+ * Errors: DORA_ERR_INVALID_ARG (NULL pointer with d_out > 0, negative
+ * d_out, eps not finite or <= 0), DORA_ERR_HIP.
+ */
+dora_status dora_magnitude_scale(const float* m, const float* wnorm, float eps,
+                                 int64_t d_out, float* g, void* stream);
+
+/*
+ * Stable magnitude compose (cyqw.cn §2.1, §2.1.1, §5.2):
+ *
+ *   out[t,j] = (g[j] - 1) * base[t,j] + g[j] * (s * lora[t,j])
+ *
+ * base, lora and out are [T, d_out] device arrays of storage type `dtype`;
+ * g is an fp32 [d_out] device array. Arithmetic is fp32: s*lora is formed
+ * first, then one fused multiply-add g*(s*lora) + (g-1)*base, rounded once
+ * to the output type (round-to-nearest-even). One pass: base, lora and g
+ * are read once and out is written once.
+ * The result is the delta the DoRA layer adds to its base output.
+ *
+ * out may alias base or lora exactly (in-place); partial overlap is
+ * rejected. T == 0 or d_out == 0 does nothing.
+ * Errors: DORA_ERR_INVALID_ARG (NULL pointer with T*d_out > 0, negative
+ * size, non-finite s, partial overlap), DORA_ERR_UNSUPPORTED_DTYPE,
+ * DORA_ERR_HIP.
+ */
+dora_status dora_compose(const void* base, const void* lora, const float* g, float s,
+                         int dtype, int64_t T, int64_t d_out, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DORA_H_ */

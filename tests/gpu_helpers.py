@@ -1,0 +1,83 @@
+"""Shared pieces of the GPU parity tests (inputs, oracle references, bounds)."""
+
+import numpy as np
+import torch
+
+from dora_weight_norm_amd import binding as bnd
+from dora_weight_norm_amd import inputs as I
+from oracle import dora_oracle as O
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+NORM_RTOL = 1e-5          # wnorm vs the fp64 oracle, relative
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def dev(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """Storage-exact float32 values -> device tensor of the storage dtype (exact)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda").to(TORCH_DT[dtype])
+
+
+def norm_case(d_out, d_in, r, dtype, seed):
+    W, A, B = I.norm_inputs(d_out, d_in, r, dtype, seed)
+    return W, A, B
+
+
+def magnitude(wnorm_ref: np.ndarray, seed: int) -> np.ndarray:
+    """m = fp32(wnorm * (1 + 0.0015 N(0,1))), from the oracle's wnorm."""
+    noise = I.m_noise(wnorm_ref.shape[0], seed)
+    return (wnorm_ref * (1.0 + I.G_SPREAD * noise)).astype(np.float32)
+
+
+def check_norm(wnorm_gpu: np.ndarray, ref: np.ndarray, rtol: float = NORM_RTOL):
+    wnorm_gpu = wnorm_gpu.astype(np.float64)
+    err = np.abs(wnorm_gpu - ref)
+    bad = err > rtol * np.abs(ref)
+    assert not bad.any(), (
+        f"{bad.sum()} of {bad.size} rows off; worst rel {np.max(err / np.maximum(np.abs(ref), 1e-300)):.3e} "
+        f"at row {int(np.argmax(err / np.maximum(np.abs(ref), 1e-300)))}")
+    return float(np.max(err / np.maximum(np.abs(ref), 1e-300)))
+
+
+def check_g(g_gpu: np.ndarray, m: np.ndarray, wnorm_ref: np.ndarray, eps: float):
+    g_ref = O.magnitude_scale(m, wnorm_ref, eps)
+    rel = np.abs(g_gpu.astype(np.float64) - g_ref) / np.abs(g_ref)
+    # wnorm's bound plus one fp32 rounding of the division
+    assert np.max(rel) <= NORM_RTOL + 2.0 ** -23, np.max(rel)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (normal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, np.frexp(ax)[1] - 8)
+
+
+def ulp32(x: np.ndarray) -> np.ndarray:
+    """Spacing of binary32 numbers at |x| (normal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, np.frexp(ax)[1] - 24)
+
+
+def check_compose(out_gpu: torch.Tensor, base, lora, g, s, dtype):
+    """The bar: within 1 bf16 ulp of the oracle's output, for every storage type.
+
+    bf16: |out - RNE_bf16(ref)| <= 1 bf16 ulp.
+    f32 : additionally the bound the evaluation order implies,
+          fma(g, RN(s*lora), RN((g-1)*base)): half an ulp of each rounded
+          operand plus one ulp of the result. Returns the worst error in bf16 ulps.
+    """
+    ref = O.compose(base, lora, g, s)
+    got = out_gpu.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - O.round_to_dtype(ref, dtype))
+    ub = bf16_ulp(ref)
+    assert np.all(err <= ub), f"max err {np.max(err / ub):.2f} bf16 ulp"
+    if dtype == "f32":
+        g2 = np.asarray(g, np.float64)[None, :]
+        t = np.abs((g2 - 1.0) * base)
+        sl = np.abs(s * np.asarray(lora, np.float64))
+        tol = 0.5 * ulp32(t) + 0.5 * ulp32(sl) * np.abs(g2) + ulp32(np.maximum(np.abs(ref), np.abs(got)))
+        e32 = np.abs(got - ref)
+        assert np.all(e32 <= tol), f"fp32 bound exceeded by {np.max(e32 / tol):.2f}x"
+    return float(np.max(err / ub))

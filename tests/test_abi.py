@@ -1,0 +1,142 @@
+"""C ABI checks that need no GPU: symbols, host planner, argument errors.
+
+Every call here returns before anything is enqueued (host-only entry points,
+or argument checks that fail), so no HIP device is touched.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dora_weight_norm_amd import binding as bnd
+from dora_weight_norm_amd import inputs as I
+from oracle import dora_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MiB = 1 << 20
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bnd.LIB_PATH), reason="libdora.so not built")
+
+
+def _declared():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"\b(dora_\w+)\s*\(", txt)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bnd.load()
+    names = _declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert bnd.dora_version() == 10000
+    for st in range(6):
+        assert bnd.dora_status_string(st)
+
+
+@pytest.mark.parametrize("d_out,d_in,budget", [
+    (8192, 8192, 256 * MiB), (28672, 8192, 256 * MiB), (512, 3584, 256 * MiB), (4096, 4096, MiB),
+    (100, 40, 256 * MiB), (1000, 8192, 700_000), (1, 1, 0), (0, 10, 5), (7, 0, 5), (3, 1 << 20, 1 << 40),
+])
+def test_chunk_size_matches_oracle_rule(d_out, d_in, budget):
+    assert bnd.dora_norm_chunk_size(d_out, d_in, budget) == O.chunk_size(d_out, d_in, budget)
+
+
+@pytest.mark.parametrize("name", sorted(I.WORKLOADS))
+def test_plans_of_the_workloads(name):
+    w = I.WORKLOADS[name]
+    info = bnd.dora_norm_plan_info(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
+    assert info["mode"] == 2
+    assert info["workspace_bytes"] <= w.budget
+    assert info["workspace_bytes"] == bnd.dora_norm_workspace_size(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
+    assert info["grid"] <= 256 and info["lds_bytes"] <= 160 * 1024
+    assert info["tile_cols"] * info["col_tiles"] >= w.r
+
+
+def test_plan_self_check_on_many_shapes():
+    rng = np.random.default_rng(0)
+    shapes = [(1, 1, 1), (1, 64, 1), (33, 65, 7), (256, 256, 8), (512, 3584, 768), (4096, 4096, 64),
+              (8192, 8192, 384), (28672, 8192, 512), (8192, 8192, 768), (640, 1024, 1000), (5, 100000, 3)]
+    shapes += [tuple(int(v) for v in (rng.integers(1, 5000), rng.integers(1, 9000), rng.integers(1, 1100)))
+               for _ in range(40)]
+    for (d_out, d_in, r) in shapes:
+        for dt in ("bf16", "f32"):
+            info = bnd.dora_norm_plan_info(d_out, d_in, r, dt, 0.5, 256 * MiB)
+            assert info["mode"] == 2
+            assert info["tile_cols"] * info["col_tiles"] >= r
+
+
+def test_trivial_modes_need_no_workspace():
+    assert bnd.dora_norm_plan_info(0, 10, 4, "bf16", 1.0)["mode"] == 0
+    for args in [(10, 20, 4, "bf16", 0.0), (10, 20, 0, "bf16", 1.0), (10, 0, 4, "f32", 1.0)]:
+        info = bnd.dora_norm_plan_info(*args)
+        assert info["mode"] == 1 and info["workspace_bytes"] == 0
+
+
+def test_budget_fallback_and_error():
+    full = bnd.dora_norm_plan_info(8192, 8192, 384, "bf16", 0.5, 256 * MiB)
+    small = bnd.dora_norm_plan_info(8192, 8192, 384, "bf16", 0.5, 2 * MiB)
+    assert small["workspace_bytes"] <= 2 * MiB < full["workspace_bytes"]
+    assert small["grid"] < full["grid"]
+    with pytest.raises(bnd.DoraError) as e:
+        bnd.dora_norm_workspace_size(8192, 8192, 384, "bf16", 0.5, 1024)
+    assert e.value.status == 3
+
+
+def _raw_norm(**kw):
+    a = dict(W=0x100000, A=0x200000, B=0x300000, dtype=0, d_out=16, d_in=32, r=4, s=0.5,
+             budget=256 * MiB, ws=None, ws_bytes=0, wnorm=0x400000, m=None, eps=1e-6, g=None)
+    a.update(kw)
+    lib = bnd.load()
+    P = ctypes.c_void_p
+    return lib.dora_factored_norm(P(a["W"]), P(a["A"]), P(a["B"]), a["dtype"], a["d_out"], a["d_in"], a["r"],
+                                  a["s"], a["budget"], P(a["ws"]), a["ws_bytes"], P(a["wnorm"]), P(a["m"]),
+                                  a["eps"], P(a["g"]), None)
+
+
+def test_norm_argument_errors_return_before_launch():
+    assert _raw_norm(dtype=7) == 2
+    assert _raw_norm(d_out=-1) == 1
+    assert _raw_norm(s=float("nan")) == 1
+    assert _raw_norm(m=0x500000, g=0x600000, eps=0.0) == 1
+    assert _raw_norm(m=0x500000, g=None) == 1
+    assert _raw_norm(wnorm=None) == 1
+    assert _raw_norm(A=None) == 1
+    assert _raw_norm(wnorm=0x100010) == 1                  # output inside W
+    assert _raw_norm(W=0x100001) == 1                      # misaligned element
+    assert _raw_norm(d_out=8192, d_in=8192, r=384, budget=1024) == 3
+    assert _raw_norm(ws=None, ws_bytes=0) == 4             # workspace required
+    assert _raw_norm(d_out=0) == 0                         # nothing to do
+
+
+def test_compose_argument_errors_return_before_launch():
+    lib = bnd.load()
+    P = ctypes.c_void_p
+
+    def call(base=0x100000, lora=0x200000, g=0x300000, s=0.5, dtype=0, T=4, d_out=8, out=0x400000):
+        return lib.dora_compose(P(base), P(lora), P(g), s, dtype, T, d_out, P(out), None)
+
+    assert call(dtype=9) == 2
+    assert call(T=-1) == 1
+    assert call(s=float("inf")) == 1
+    assert call(base=None) == 1
+    assert call(out=0x100002) == 1          # partial overlap with base
+    assert call(out=0x300000 - 4) == 1      # overlaps g
+    assert call(T=0) == 0 and call(d_out=0) == 0
+
+
+def test_magnitude_argument_errors():
+    lib = bnd.load()
+    P = ctypes.c_void_p
+    assert lib.dora_magnitude_scale(P(0x1000), P(0x2000), 0.0, 4, P(0x3000), None) == 1
+    assert lib.dora_magnitude_scale(P(0x1000), P(0x2000), 1e-6, -1, P(0x3000), None) == 1
+    assert lib.dora_magnitude_scale(None, None, 1e-6, 0, None, None) == 0
+    assert lib.dora_magnitude_scale(P(0x1000), P(0x1004), 1e-6, 4, P(0x1004), None) == 1   # g overlaps m

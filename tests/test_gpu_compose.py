@@ -1,0 +1,98 @@
+"""GPU parity of dora_compose against the fp64 oracle (<= 1 ulp of the output).
+
+Both sides take the same fp32 g. Whole tensors for the smaller workloads;
+sampled rows (every column) for the largest ones. Ragged widths, unaligned
+pointers, in-place calls and the closed-form special cases are covered too.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from dora_weight_norm_amd import binding as bnd
+from dora_weight_norm_amd import inputs as I
+from oracle import dora_oracle as O
+
+from gpu_helpers import check_compose, dev, magnitude, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny_f32_256x256_r8", "qproj_4096x4096_r64", "kv_512x3584_r768"]
+LARGE = ["headline_8192x8192_r384", "mlp_28672x8192_r512", "square_8192x8192_r768"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_compose_workload_whole(name):
+    w = I.WORKLOADS[name]
+    say(f"[compose] {name} T={w.T} d_out={w.d_out} {w.dtype}")
+    base, lora, g = I.compose_inputs(w.T, w.d_out, w.dtype, w.seed)
+    out = bnd.dora_compose(dev(base, w.dtype), dev(lora, w.dtype), torch.from_numpy(g).cuda(), w.s)
+    torch.cuda.synchronize()
+    worst = check_compose(out, base, lora, g, w.s, w.dtype)
+    say(f"    worst {worst:.2f} ulp")
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_compose_workload_sampled_rows(name):
+    w = I.WORKLOADS[name]
+    say(f"[compose-full] {name} T={w.T} d_out={w.d_out}")
+    base, lora, g = I.compose_inputs(w.T, w.d_out, w.dtype, w.seed)
+    out = bnd.dora_compose(dev(base, w.dtype), dev(lora, w.dtype), torch.from_numpy(g).cuda(), w.s)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, w.T - 1], rng.choice(w.T, 61, replace=False)]))
+    worst = check_compose(out[torch.from_numpy(rows).cuda()], base[rows], lora[rows], g, w.s, w.dtype)
+    say(f"    {len(rows)} rows, worst {worst:.2f} ulp")
+
+
+@pytest.mark.parametrize("T,d_out,dtype", [(37, 1001, "bf16"), (5, 3, "f32"), (129, 520, "bf16"),
+                                           (64, 250, "f32"), (1, 8, "bf16")])
+def test_compose_ragged_shapes(T, d_out, dtype):
+    base, lora, g = I.compose_inputs(T, d_out, dtype, 31)
+    out = bnd.dora_compose(dev(base, dtype), dev(lora, dtype), torch.from_numpy(g).cuda(), 0.5)
+    check_compose(out, base, lora, g, 0.5, dtype)
+
+
+def test_compose_unaligned_and_in_place():
+    T, d_out = 48, 4096
+    base, lora, g = I.compose_inputs(T, d_out, "bf16", 32)
+    gt = torch.from_numpy(g).cuda()
+    flat = torch.zeros(2 * T * d_out + 1, dtype=torch.bfloat16, device="cuda")
+    b_un = flat[1:1 + T * d_out].view(T, d_out)
+    b_un.copy_(dev(base, "bf16"))
+    out = bnd.dora_compose(b_un, dev(lora, "bf16"), gt, 2.0)
+    check_compose(out, base, lora, g, 2.0, "bf16")
+    bt = dev(base, "bf16")
+    res = bnd.dora_compose(bt, dev(lora, "bf16"), gt, 2.0, out=bt)      # out aliases base
+    torch.cuda.synchronize()
+    assert res.data_ptr() == bt.data_ptr()
+    check_compose(bt, base, lora, g, 2.0, "bf16")
+    lt = dev(lora, "bf16")
+    bnd.dora_compose(dev(base, "bf16"), lt, gt, 2.0, out=lt)          # out aliases lora
+    check_compose(lt, base, lora, g, 2.0, "bf16")
+
+
+def test_compose_closed_forms():
+    T, d_out = 16, 1024
+    base, lora, g = I.compose_inputs(T, d_out, "bf16", 33)
+    ones = torch.ones(d_out, dtype=torch.float32, device="cuda")
+    out = bnd.dora_compose(dev(base, "bf16"), dev(lora, "bf16"), ones, 0.5)
+    # g = 1: out = s*lora exactly (s is a power of two)
+    assert torch.equal(out.float().cpu(), torch.from_numpy(lora * np.float32(0.5)))
+    out = bnd.dora_compose(dev(base, "bf16"), dev(lora, "bf16"), torch.from_numpy(g).cuda(), 0.0)
+    check_compose(out, base, lora, g, 0.0, "bf16")
+    z = torch.zeros(0, d_out, dtype=torch.bfloat16, device="cuda")
+    assert bnd.dora_compose(z, z, ones, 0.5).shape == (0, d_out)
+
+
+def test_norm_then_compose_path():
+    """The whole forward path: g from the library's norm feeds the compose."""
+    w = I.WORKLOADS["kv_512x3584_r768"]
+    W, A, B = I.norm_inputs(w.d_out, w.d_in, w.r, w.dtype, w.seed)
+    ref = O.dense_row_norm(W, A, B, w.s)
+    m = magnitude(ref, w.seed)
+    _, g = bnd.dora_factored_norm(dev(W, w.dtype), dev(A, w.dtype), dev(B, w.dtype), w.s,
+                                  m=torch.from_numpy(m).cuda(), eps=w.eps)
+    base, lora, _ = I.compose_inputs(512, w.d_out, w.dtype, w.seed)
+    out = bnd.dora_compose(dev(base, w.dtype), dev(lora, w.dtype), g, w.s)
+    check_compose(out, base, lora, g.cpu().numpy(), w.s, w.dtype)

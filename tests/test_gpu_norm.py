@@ -1,0 +1,167 @@
+"""GPU parity of dora_factored_norm against the fp64 oracle.
+
+wnorm within 1e-5 relative of the oracle (inputs are storage-exact), g within
+that plus one fp32 division rounding. Small and mid sizes compare every row
+and span several tiles with ragged edges; the full workload sizes compare a
+sample of rows, each of which the oracle computes on its own.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from dora_weight_norm_amd import binding as bnd
+from dora_weight_norm_amd import inputs as I
+from oracle import dora_oracle as O
+
+from gpu_helpers import check_g, check_norm, dev, magnitude, say
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+# (name, d_out, d_in, r, dtype, s, seed)
+CASES = [
+    ("tiny_f32_256x256_r8", 256, 256, 8, "f32", 2.0, 0),       # the tiny workload, whole
+    ("ragged_vec", 300, 1000, 40, "bf16", 0.5, 5),             # d_in % 64 != 0, 16-byte rows
+    ("ragged_scalar", 257, 1001, 13, "bf16", 0.75, 6),         # d_in % 8 != 0: element loads
+    ("r384_tiles", 1000, 2048, 384, "bf16", 0.5, 7),
+    ("r512_tiles", 700, 1536, 512, "bf16", 0.5, 8),
+    ("r700_tiles", 300, 1024, 700, "bf16", 0.25, 9),
+    ("r1000_two_col_tiles", 640, 1024, 1000, "bf16", 0.25, 10),
+    ("f32_two_col_tiles", 100, 200, 200, "f32", 1.0, 11),
+    ("f32_ragged_neg_s", 77, 99, 5, "f32", -0.5, 12),
+    ("r_above_d_out", 40, 512, 300, "bf16", 1.0, 13),
+    ("r_above_d_in", 64, 96, 160, "bf16", 0.5, 14),
+    ("one_row", 1, 64, 1, "bf16", 2.0, 15),
+    ("kv_512x3584_r768", 512, 3584, 768, "bf16", 0.25, 40),   # workload, whole
+    ("qproj_4096x4096_r64", 4096, 4096, 64, "bf16", 2.0, 1),  # workload, whole
+]
+
+
+def _run(W, A, B, dtype, s, m=None, budget=256 << 20):
+    wn, g = bnd.dora_factored_norm(dev(W, dtype), dev(A, dtype), dev(B, dtype), s, budget_bytes=budget,
+                                   m=None if m is None else torch.from_numpy(m).cuda(), eps=EPS)
+    torch.cuda.synchronize()
+    return wn.cpu().numpy(), (None if g is None else g.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_norm_matches_oracle(case):
+    name, d_out, d_in, r, dtype, s, seed = case
+    say(f"[norm] {name} d_out={d_out} d_in={d_in} r={r} {dtype} s={s}")
+    W, A, B = I.norm_inputs(d_out, d_in, r, dtype, seed)
+    ref = O.dense_row_norm(W, A, B, s)
+    m = magnitude(ref, seed)
+    wn, g = _run(W, A, B, dtype, s, m)
+    worst = check_norm(wn, ref)
+    check_g(g, m, ref, EPS)
+    say(f"    worst rel err {worst:.2e}")
+
+
+FULL = ["headline_8192x8192_r384", "mlp_28672x8192_r512", "square_8192x8192_r768"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_norm_full_size_sampled_rows(name):
+    w = I.WORKLOADS[name]
+    say(f"[norm-full] {name}")
+    W, A, B = I.norm_inputs(w.d_out, w.d_in, w.r, w.dtype, w.seed)
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([np.arange(0, 64), np.arange(w.d_out - 64, w.d_out),
+                                     rng.choice(w.d_out, 384, replace=False)]))
+    ref_rows = O.dense_row_norm(W[rows], A, B[rows], w.s)
+    m = np.ones(w.d_out, np.float32)
+    m[rows] = magnitude(ref_rows, w.seed)[: len(rows)]
+    wn, g = _run(W, A, B, w.dtype, w.s, m, w.budget)
+    worst = check_norm(wn[rows], ref_rows)
+    check_g(g[rows], m[rows], ref_rows, EPS)
+    assert np.all(np.isfinite(wn)) and np.all(wn > 0)
+    say(f"    {len(rows)} rows, worst rel err {worst:.2e}")
+
+
+def test_s_zero_and_zero_sizes():
+    W, A, B = I.norm_inputs(130, 300, 12, "bf16", 20)
+    wn, _ = _run(W, A, B, "bf16", 0.0)
+    check_norm(wn, O.dense_row_norm(W, A, B, 0.0))
+    # r == 0
+    wn, _ = _run(W, A[:0], B[:, :0], "bf16", 0.5)
+    check_norm(wn, np.linalg.norm(W.astype(np.float64), axis=1))
+    # d_in == 0: every row norm is 0 and g = m / eps
+    m = np.full(130, 2.0, np.float32)
+    wn, g = _run(W[:, :0], A[:, :0], B, "bf16", 0.5, m)
+    assert np.all(wn == 0.0) and np.allclose(g, 2.0 / EPS, rtol=1e-7)
+    # d_out == 0
+    wn, _ = _run(W[:0], A, B[:0], "bf16", 0.5)
+    assert wn.shape == (0,)
+
+
+def test_exact_cancellation_gives_zero_norm():
+    rng = np.random.default_rng(21)
+    r, d_in, d_out, s = 3, 256, 96, 0.5
+    A = rng.integers(-1, 2, (r, d_in)).astype(np.float32) * np.float32(2.0 ** -4)
+    B = rng.integers(-1, 2, (d_out, r)).astype(np.float32) * np.float32(2.0 ** -4)
+    W = (-s * (B.astype(np.float64) @ A)).astype(np.float32)   # exact in bf16
+    assert np.array_equal(O.bf16_round(W), W)
+    m = np.full(d_out, 1.5, np.float32)
+    wn, g = _run(W, A, B, "bf16", s, m)
+    base = np.sqrt(np.sum(W.astype(np.float64) ** 2, axis=1))
+    assert np.all(np.isfinite(wn)) and np.all(wn >= 0.0)
+    assert np.all(wn <= 1e-3 * np.maximum(base, 1e-30) + 1e-6)
+    d = np.maximum(wn, np.float32(EPS))
+    assert np.allclose(g, m / d, rtol=1e-6)
+
+
+def test_nan_row_propagates_only_to_its_row():
+    W, A, B = I.norm_inputs(200, 512, 16, "bf16", 22)
+    W[7, 100] = np.nan
+    m = np.ones(200, np.float32)
+    wn, g = _run(W, A, B, "bf16", 0.5, m)
+    assert np.isnan(wn[7]) and np.isnan(g[7])
+    keep = np.arange(200) != 7
+    W2 = W.copy()
+    W2[7] = 0
+    check_norm(wn[keep], O.dense_row_norm(W2, A, B, 0.5)[keep])
+
+
+def test_deterministic_and_budget_invariant():
+    W, A, B = I.norm_inputs(1500, 4096, 384, "bf16", 23)
+    a, _ = _run(W, A, B, "bf16", 0.5)
+    b, _ = _run(W, A, B, "bf16", 0.5)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    small = bnd.dora_norm_plan_info(1500, 4096, 384, "bf16", 0.5, 2 << 20)
+    big = bnd.dora_norm_plan_info(1500, 4096, 384, "bf16", 0.5, 256 << 20)
+    assert small["grid"] != big["grid"]
+    c, _ = _run(W, A, B, "bf16", 0.5, budget=2 << 20)
+    assert np.max(np.abs(c.astype(np.float64) - a) / a) <= 1e-6
+    check_norm(c, O.dense_row_norm(W, A, B, 0.5))
+
+
+def test_power_of_two_scale_moves_into_B_bitwise():
+    W, A, B = I.norm_inputs(600, 2048, 128, "bf16", 24)
+    for k in (-2, 1):
+        s = 2.0 ** k
+        a, _ = _run(W, A, B, "bf16", s)
+        b, _ = _run(W, A, (B * np.float32(s)).astype(np.float32), "bf16", 1.0)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), k
+
+
+def test_unaligned_inputs_use_element_loads():
+    d_out, d_in, r = 150, 512, 24
+    W, A, B = I.norm_inputs(d_out, d_in, r, "bf16", 25)
+    ref = O.dense_row_norm(W, A, B, 0.5)
+
+    def shifted(x):
+        flat = torch.zeros(x.size + 1, dtype=torch.bfloat16, device="cuda")
+        flat[1:] = torch.from_numpy(x.ravel()).cuda().to(torch.bfloat16)
+        return flat[1:].view(*x.shape)
+
+    wn, _ = bnd.dora_factored_norm(shifted(W), shifted(A), shifted(B), 0.5)
+    check_norm(wn.cpu().numpy(), ref)
+
+
+def test_budget_too_small_raises():
+    W, A, B = I.norm_inputs(512, 512, 64, "bf16", 26)
+    with pytest.raises(bnd.DoraError) as e:
+        bnd.dora_factored_norm(dev(W, "bf16"), dev(A, "bf16"), dev(B, "bf16"), 0.5, budget_bytes=4096)
+    assert e.value.status == 3
