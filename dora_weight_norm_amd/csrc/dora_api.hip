@@ -74,6 +74,8 @@ void layout(NormPlan& p) {
   off = align_up(off + (size_t)(p.r32 * p.r32) * (p.dtype == DORA_BF16 ? 2 : 4), kAlign);
   p.off_glo = off;
   if (p.dtype == DORA_BF16) off = align_up(off + (size_t)(p.r32 * p.r32) * 2, kAlign);
+  p.off_ba = off;
+  off = align_up(off + (size_t)((int64_t)p.n_cb * p.ld_w) * 4, kAlign);
   p.ws_bytes = off;
 }
 
@@ -118,6 +120,7 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.ga_rows = (int64_t)p.n_mt_a * p.mt;
   p.ga_cols = (int64_t)p.n_nt * p.ntc;
   p.r32 = ceil_div(r, 32) * 32;
+  p.n_cb = (int)ceil_div(p.r32, dora::kGramCB);
 
   // Most parallel split first: one d_in range per die, every compute unit
   // busy. Then fewer workgroups, which shrink the partials.
@@ -126,6 +129,11 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   for (const auto& c : cand) {
     p.X = c[0];
     p.P = c[1];
+    // Never more workgroups per range than work units in its smallest range:
+    // then no workgroup is empty, and the partials of a tile are exactly
+    // those of workgroups slot_of(first unit) .. slot_of(last unit).
+    const int64_t u_min = dora::n_tiles(p) * (p.n_kt / p.X);
+    if (u_min < p.P) p.P = (int)u_min;
     p.maxseg = compute_maxseg(p);
     layout(p);
     if (p.ws_bytes <= budget) {
@@ -168,11 +176,9 @@ bool plan_self_check(const NormPlan& p) {
     for (int64_t t = 0; t < T; ++t) {
       const int sa = dora::slot_of(U, p.P, t * nk), sb = dora::slot_of(U, p.P, t * nk + nk - 1);
       for (int sl = sa; sl <= sb; ++sl) {
-        const bool nonempty = dora::unit_lo(U, p.P, sl) != dora::unit_lo(U, p.P, sl + 1);
         const int k = sl - sa;
         if (k >= p.maxseg) return false;
-        const int prod = seg_of[(size_t)(t * p.maxseg + k)];
-        if (nonempty != (prod == sl)) return false;
+        if (seg_of[(size_t)(t * p.maxseg + k)] != sl) return false;   // every slot in range produced
       }
       for (int k = sb - sa + 1; k < p.maxseg; ++k)
         if (seg_of[(size_t)(t * p.maxseg + k)] != -1) return false;

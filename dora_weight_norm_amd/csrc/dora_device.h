@@ -46,17 +46,18 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return f32_to_bf16
 template <>
 __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 
-// Sum of squares of the elements held in one 16-byte chunk.
+// Sum of squares of the elements held in one 16-byte chunk. For bf16 the
+// pairs go through v_dot2_f32_bf16 (each bf16 square is exact in fp32). The
+// chunk is reinterpreted as a whole: bit-casting its 32-bit elements one by
+// one inside an unrolled loop was compiled into four dots of element 0.
 __device__ __forceinline__ float chunk_sumsq(const u32x4& v, bf16_t) {
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(v[i] << 16);
-    const float hi = __uint_as_float(v[i] & 0xffff0000u);
-    s0 = fmaf(lo, lo, s0);
-    s1 = fmaf(hi, hi, s1);
-  }
-  return s0 + s1;
+  const bf16x8 h = __builtin_bit_cast(bf16x8, v);
+  float q = 0.f;
+  q = __builtin_amdgcn_fdot2_f32_bf16(h.s01, h.s01, q, false);
+  q = __builtin_amdgcn_fdot2_f32_bf16(h.s23, h.s23, q, false);
+  q = __builtin_amdgcn_fdot2_f32_bf16(h.s45, h.s45, q, false);
+  q = __builtin_amdgcn_fdot2_f32_bf16(h.s67, h.s67, q, false);
+  return q;
 }
 __device__ __forceinline__ float chunk_sumsq(const u32x4& v, float) {
   const float a = __uint_as_float(v[0]), b = __uint_as_float(v[1]);
@@ -122,5 +123,43 @@ struct Mfma<float> {
 // lanes 0-31 hold rows {0-3, 8-11, 16-19, 24-27}, lanes 32-63 the other four
 // of each group of eight; the column is lane % 32.
 __device__ __forceinline__ int acc_row(int v, int lgrp) { return 8 * (v >> 2) + 4 * lgrp + (v & 3); }
+
+// Lane exchange inside each 32-lane half: value of lane (i ^ M).
+template <int M>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (M << 10)));
+}
+
+// Sum 16 per-lane values over the 32 lanes of each wave half, returning in
+// lane i (of its half) the total of value index (i >> 1). Each exchange
+// halves the values a lane keeps, so the 16 sums cost 16 lane exchanges.
+// The summation order is fixed, so results are reproducible.
+__device__ __forceinline__ float sum32_transpose(const float (&p)[16], int lane) {
+  const int i = lane & 31;
+  float q8[8], q4[4], q2[2];
+  const bool b4 = (i & 16) != 0, b3 = (i & 8) != 0, b2 = (i & 4) != 0, b1 = (i & 2) != 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float keep = b4 ? p[8 + j] : p[j];
+    const float send = b4 ? p[j] : p[8 + j];
+    q8[j] = keep + swz_xor<16>(send);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float keep = b3 ? q8[4 + j] : q8[j];
+    const float send = b3 ? q8[j] : q8[4 + j];
+    q4[j] = keep + swz_xor<8>(send);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float keep = b2 ? q4[2 + j] : q4[j];
+    const float send = b2 ? q4[j] : q4[2 + j];
+    q2[j] = keep + swz_xor<4>(send);
+  }
+  const float keep = b1 ? q2[1] : q2[0];
+  const float send = b1 ? q2[0] : q2[1];
+  const float q1 = keep + swz_xor<2>(send);
+  return q1 + swz_xor<1>(q1);
+}
 
 }  // namespace dora

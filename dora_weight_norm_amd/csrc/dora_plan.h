@@ -20,6 +20,8 @@ namespace dora {
 constexpr int kDies = 8;
 constexpr int kGrid = 256;           // one norm workgroup per compute unit
 constexpr int kThreads = 256;        // 4 waves of 64
+constexpr int kGramCB = 64;          // columns of G per Gram-term workgroup
+constexpr int kGramRows = 256;       // rows of B per Gram-term workgroup (32 per wave, 8 waves)
 
 // Tile shapes of the norm's main kernel. The workgroup is WM x WN waves;
 // each wave owns MB x NB blocks of 32x32 fp32 accumulators. KT is the d_in
@@ -74,19 +76,28 @@ struct NormPlan {
   int64_t ga_rows;      // n_mt_a * mt
   int64_t ga_cols;      // n_nt * ntc
   int64_t r32;          // r rounded up to 32: side of the reduced Gram matrix
-  size_t off_base, off_cross, off_g, off_ghi, off_glo;
+  int n_cb;             // 64-column blocks of G in the Gram-term kernel
+  size_t off_base, off_cross, off_g, off_ghi, off_glo, off_ba;
   size_t ws_bytes;
 };
 
+// The split below is integer arithmetic on counts that fit 32 bits for any
+// realistic shape; the 64-bit forms are kept for the rest (the division is
+// done in 32 bits whenever both operands fit, which is much cheaper on the GPU).
+DORA_HD int64_t div_u(int64_t a, int64_t b) {
+  if (((uint64_t)a | (uint64_t)b) < (1ull << 32)) return (int64_t)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
 // First stage of d_in range x (ranges split n_kt stages as evenly as integers allow).
-DORA_HD int64_t range_lo(int64_t n_kt, int X, int x) { return (n_kt * x) / X; }
+DORA_HD int64_t range_lo(int64_t n_kt, int X, int x) { return div_u(n_kt * x, X); }
 
 // Work units of one range are (tile, stage) pairs, tile-major. Workgroup s
 // of P takes units [unit_lo(s), unit_lo(s+1)).
-DORA_HD int64_t unit_lo(int64_t U, int P, int s) { return (U * s) / P; }
+DORA_HD int64_t unit_lo(int64_t U, int P, int s) { return div_u(U * s, P); }
 
 // The workgroup whose unit range holds unit w (0 <= w < U).
-DORA_HD int slot_of(int64_t U, int P, int64_t w) { return (int)(((w + 1) * P - 1) / U); }
+DORA_HD int slot_of(int64_t U, int P, int64_t w) { return (int)div_u((w + 1) * P - 1, U); }
 
 DORA_HD int64_t n_tiles(const NormPlan& p) { return (int64_t)(p.n_mt_w + p.n_mt_a) * p.n_nt; }
 

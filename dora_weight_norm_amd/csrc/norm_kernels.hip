@@ -4,20 +4,21 @@
 // ("DoRA优化技术解析：从内存瓶颈到高效实现", cyqw.cn, §1.2 and §1.2.1;
 // "Scaling DoRA", alanhou.org, "Factored Norm").
 //
-// Three launches:
+// Four launches:
 //   norm_main    one pass over W and A on the matrix cores. Rows of W and
 //                rows of A are stacked as one M dimension and contracted
 //                against A over d_in. W rows give U = W A^T, which is dotted
 //                with B row by row in the epilogue (cross term) and never
-//                stored; the same W fragments are squared on the vector ALU
-//                (base term). A rows give G = A A^T partials.
+//                stored; the same W fragments are squared (base term). A
+//                rows give G = A A^T partials.
 //                d_in is split into one range per die so each die's L2 holds
 //                the slice of A its 32 workgroups share; inside a range the
 //                (tile, stage) work units are cut evenly across workgroups.
 //   gram_reduce  sums the G partials in a fixed order; for bf16 it stores G
 //                as an unevaluated sum of two bf16 matrices, G ~ Ghi + Glo.
-//   norm_finish  (B G) on the matrix cores (B Ghi + B Glo), dotted with B
-//                (Gram term); sums the base/cross partials in a fixed order;
+//   gram_term    (B G) on the matrix cores (B Ghi + B Glo), dotted with B,
+//                per 64-column block of G (Gram term partials).
+//   assemble     fixed-order sums of all partials;
 //                wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and
 //                g = m / max(wnorm, eps) without contraction, with correctly
 //                rounded sqrt and division (same page, §1.2.2, §5.2, §6.2).
@@ -297,10 +298,21 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
           if (lgrp == 0) red_b[wmi * MB * 32 + a * 32 + lrow] = q;
         }
       // Cross term, one 32-row block per wave row at a time: U goes to LDS
-      // straight from the accumulators, then each row is dotted with B.
+      // straight from the accumulators, then each row is dotted with B. The
+      // B chunks of the next round are loaded while this round is reduced.
       const int ur = tid / C::TPR, part = tid % C::TPR;   // row in the round, column part
       const int uwm = ur / 32, ua = ur % 32;
       const int64_t gc0 = n0 + (int64_t)part * C::CPTH;
+      constexpr int NBC = C::CPTH / EPC;                  // B chunks per thread per round
+      u32x4 bcur[NBC], bnxt[NBC];
+      auto load_b = [&](int a, u32x4 (&dst)[NBC]) __attribute__((always_inline)) {
+        const int lr = uwm * MB * 32 + a * 32 + ua;
+        const T* brow = B + (mrow0 + lr) * p.r;
+        const bool row_ok = lr < m_lim;
+#pragma unroll
+        for (int c = 0; c < NBC; ++c) dst[c] = load_chunk(brow, gc0 + c * EPC, p.r, row_ok, VEC);
+      };
+      load_b(0, bcur);
 #pragma unroll
       for (int a = 0; a < MB; ++a) {
 #pragma unroll
@@ -312,25 +324,22 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
             *reinterpret_cast<float*>(s0 + rr * C::UPITCH + cc * 4) = acc[a][b][v];
           }
         __syncthreads();
+        if (a + 1 < MB) load_b(a + 1, bnxt);
         const int lr = uwm * MB * 32 + a * 32 + ua;       // tile row of this thread
-        const int64_t grow = mrow0 + lr;
-        const T* brow = B + grow * p.r;
-        const bool row_ok = lr < m_lim;
         float dsum = 0.f;
 #pragma unroll
-        for (int c = 0; c < C::CPTH; c += EPC) {
-          const u32x4 bv = load_chunk(brow, gc0 + c, p.r, row_ok, VEC);
-          const float* up = reinterpret_cast<const float*>(s0 + ur * C::UPITCH + (part * C::CPTH + c) * 4);
+        for (int c = 0; c < NBC; ++c) {
+          const float* up = reinterpret_cast<const float*>(s0 + ur * C::UPITCH + (part * C::CPTH + c * EPC) * 4);
           float bf[EPC];
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              bf[2 * e] = __uint_as_float(bv[e] << 16);
-              bf[2 * e + 1] = __uint_as_float(bv[e] & 0xffff0000u);
+              bf[2 * e] = __uint_as_float(bcur[c][e] << 16);
+              bf[2 * e + 1] = __uint_as_float(bcur[c][e] & 0xffff0000u);
             }
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bf[e] = __uint_as_float(bv[e]);
+            for (int e = 0; e < 4; ++e) bf[e] = __uint_as_float(bcur[c][e]);
           }
 #pragma unroll
           for (int e = 0; e < EPC; ++e) dsum = fmaf(up[e], bf[e], dsum);
@@ -339,6 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
         for (int off = C::TPR / 2; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
         if (part == 0) red_c[lr] = dsum;
         __syncthreads();
+#pragma unroll
+        for (int c = 0; c < NBC; ++c) bcur[c] = bnxt[c];
       }
       for (int R = tid; R < MT; R += kThreads) {
         const int64_t grow = mrow0 + R;
@@ -365,31 +376,35 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
 }
 
 // ---------------------------------------------------------------------------
-// gram_reduce: G[i][j] = sum over ranges and segments, fixed order.
+// gram_reduce: G[i][j] = sum over d_in ranges and segments, fixed order.
+// Eight lanes per element, lane x summing range x's segments; the eight
+// range sums are then combined by a fixed xor tree.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t idx = gid >> 3;
+  const int x = (int)(gid & 7);
   const int64_t r32 = p.r32;
-  if (idx >= r32 * r32) return;
-  const int64_t i = idx / r32, j = idx % r32;
+  const bool live = idx < r32 * r32;
+  const int64_t i = live ? idx / r32 : 0, j = live ? idx % r32 : 0;
   const float* part_g = reinterpret_cast<const float*>(ws + p.off_g);
   float acc = 0.f;
-  if (i < p.r && j < p.r) {
+  if (live && x < p.X && i < p.r && j < p.r) {
     const int ma = (int)(i / p.mt), n = (int)(j / p.ntc);
     const int64_t t = (int64_t)(p.n_mt_w + ma) * p.n_nt + n;
-    for (int x = 0; x < p.X; ++x) {
-      const int64_t kb = range_lo(p.n_kt, p.X, x);
-      const int64_t nk = range_lo(p.n_kt, p.X, x + 1) - kb;
-      const int64_t U = n_tiles(p) * nk;
-      const int sa = slot_of(U, p.P, t * nk), sb = slot_of(U, p.P, t * nk + nk - 1);
-      for (int s = sa; s <= sb; ++s) {
-        if (unit_lo(U, p.P, s) == unit_lo(U, p.P, s + 1)) continue;
-        const int64_t ps = (int64_t)x * p.maxseg + (s - sa);
-        acc += part_g[(ps * p.ga_rows + i) * p.ga_cols + j];
-      }
+    const int64_t nk = range_lo(p.n_kt, p.X, x + 1) - range_lo(p.n_kt, p.X, x);
+    const int64_t U = n_tiles(p) * nk;
+    const int sa = slot_of(U, p.P, t * nk), sb = slot_of(U, p.P, t * nk + nk - 1);
+    for (int s = sa; s <= sb; ++s) {
+      const int64_t ps = (int64_t)x * p.maxseg + (s - sa);
+      acc += part_g[(ps * p.ga_rows + i) * p.ga_cols + j];
     }
   }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  if (!live || x != 0) return;
   if constexpr (sizeof(T) == 2) {
     bf16_t* ghi = reinterpret_cast<bf16_t*>(ws + p.off_ghi);
     bf16_t* glo = reinterpret_cast<bf16_t*>(ws + p.off_glo);
@@ -403,127 +418,167 @@ __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(NormPlan p, char*
 }
 
 // ---------------------------------------------------------------------------
-// norm_finish: ba = rowsum((B G) * B), base/cross partial sums, assembly.
-// One workgroup per 32 rows; wave w takes column blocks w, w+4, ...
+// gram_term: ba[j] = sum_l (B G)[j,l] B[j,l], split over 64-column blocks of G.
+// Workgroup (row group, column block): the block's 64 rows of G (G is
+// symmetric, so they are its columns, K-contiguous) are staged in LDS once
+// per K chunk; each wave contracts 32 rows of B with them on the matrix
+// cores (bf16: B Ghi + B Glo), dots the result with B's entries in those
+// columns, and writes one partial per row and column block.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void norm_finish_kernel(NormPlan p, const T* __restrict__ B,
-                                                               const char* __restrict__ ws, float s,
-                                                               const float* m, float eps,
-                                                               float* wnorm, float* g) {
-  constexpr int EPC = Elem<T>::epc, FC = Elem<T>::frag_chunks;
-  constexpr int NBG = 4;   // column blocks per wave per pass
-  __shared__ float red[4 * 16 * 64];
+struct GramCfg {
+  static constexpr int KC = 192;                          // K chunk staged at once
+  static constexpr int NG = sizeof(T) == 2 ? 2 : 1;       // hi and lo parts
+  static constexpr int EPC = Elem<T>::epc;
+  static constexpr int RBYTES = KC * (int)sizeof(T);      // bytes of one staged G row
+  static constexpr int CPRG = RBYTES / 16;                // 16-byte chunks per staged row
+  static constexpr int PART = kGramCB * RBYTES;           // bytes of one staged part
+  static constexpr int LDS = NG * PART;
+  static constexpr int NBLK = LDS / 1024;                 // direct-load blocks per chunk
+  static constexpr int WAVES = kGramRows / 32;
+  static constexpr int NKS = KC / 16;                     // K16 steps per chunk
+  static constexpr int FC = Elem<T>::frag_chunks;
+  static_assert(NBLK % WAVES == 0 && PART % 1024 == 0, "staging splits evenly over the waves");
+  static_assert(CPRG % 8 == 0, "swizzle stays inside a staged row");
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <typename T>
+__global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p, const T* __restrict__ B,
+                                                                     char* __restrict__ ws) {
+  using C = GramCfg<T>;
+  constexpr int EPC = C::EPC, FC = C::FC;
+  __shared__ __attribute__((aligned(1024))) char sg[C::LDS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, lgrp = lane >> 5;
-  const int64_t j0 = (int64_t)blockIdx.x * 32;
   const int64_t r = p.r, r32 = p.r32;
-  const bool bvec = p.vec_b != 0;
-  const int nblk = (int)(r32 / 32);
+  const int64_t c0 = (int64_t)blockIdx.y * kGramCB;
+  const int64_t j0 = (int64_t)blockIdx.x * kGramRows + wave * 32;
   const int64_t arow = j0 + lrow;
   const bool arow_ok = arow < p.d_out;
   const T* brow = B + arow * r;
+  const bool bvec = p.vec_b != 0;
 
-  float pr[16];
+  // B's entries in this block's columns for the epilogue, fetched up front.
+  float bval[2][16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) pr[v] = 0.f;
+  for (int q = 0; q < 2; ++q) {
+    const int64_t col = c0 + q * 32 + lrow;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = j0 + acc_row(v, lgrp);
+      bval[q][v] = (row < p.d_out && col < r) ? to_f32(B[row * r + col]) : 0.f;
+    }
+  }
 
-  for (int g0 = 0; g0 < nblk; g0 += 4 * NBG) {
-    f32x16 acc[NBG];
+  f32x16 acc[2];
 #pragma unroll
-    for (int q = 0; q < NBG; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[q][v] = 0.f;
-    for (int64_t k0 = 0; k0 < r32; k0 += 16) {
-      u32x4 fa[FC];
+    for (int v = 0; v < 16; ++v) acc[q][v] = 0.f;
+
+  for (int64_t k0 = 0; k0 < r32; k0 += C::KC) {
+    u32x4 fa[C::NKS][FC];   // this lane's B fragments for the chunk
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
       for (int f = 0; f < FC; ++f)
-        fa[f] = load_chunk(brow, k0 + (int64_t)(lgrp * FC + f) * EPC, r, arow_ok, bvec);
+        fa[ks][f] = load_chunk(brow, k0 + ks * 16 + (int64_t)(lgrp * FC + f) * EPC, r, arow_ok, bvec);
+    __syncthreads();   // the previous chunk is fully consumed
+    // Stage rows c0.. of G (hi, lo) for k in [k0, k0 + KC) by direct loads;
+    // each lane fetches the chunk that lands on its LDS slot under the swizzle.
 #pragma unroll
-      for (int q = 0; q < NBG; ++q) {
-        const int nb = g0 + q * 4 + wave;
-        if (nb >= nblk) continue;
-        const int64_t grow = (int64_t)nb * 32 + lrow;
-        if constexpr (sizeof(T) == 2) {
-          const bf16_t* ghi = reinterpret_cast<const bf16_t*>(ws + p.off_ghi) + grow * r32 + k0 + lgrp * 8;
-          const bf16_t* glo = reinterpret_cast<const bf16_t*>(ws + p.off_glo) + grow * r32 + k0 + lgrp * 8;
-          u32x4 fh = *reinterpret_cast<const u32x4*>(ghi);
-          u32x4 fl = *reinterpret_cast<const u32x4*>(glo);
-          acc[q] = Mfma<T>::run(fa, &fh, acc[q]);
-          acc[q] = Mfma<T>::run(fa, &fl, acc[q]);
-        } else {
-          const float* g32 = reinterpret_cast<const float*>(ws + p.off_ghi) + grow * r32 + k0 + lgrp * 8;
-          u32x4 fb[2];
-          fb[0] = *reinterpret_cast<const u32x4*>(g32);
-          fb[1] = *reinterpret_cast<const u32x4*>(g32 + 4);
-          acc[q] = Mfma<T>::run(fa, fb, acc[q]);
-        }
-      }
+    for (int i = 0; i < C::NBLK / C::WAVES; ++i) {
+      const int blk = i * C::WAVES + wave;
+      const int part = blk / (C::PART / 1024);
+      const int slot16 = (blk % (C::PART / 1024)) * 64 + lane;
+      const int row = slot16 / C::CPRG, ch = (slot16 % C::CPRG) ^ (row & 7);
+      int64_t grow = c0 + row, gk = k0 + (int64_t)ch * EPC;
+      grow = grow < r32 ? grow : r32 - 1;          // past the matrix: a real row, never used
+      gk = gk < r32 ? gk : r32 - EPC;
+      const char* src = ws + (part == 0 ? p.off_ghi : p.off_glo) + (grow * r32 + gk) * (int64_t)sizeof(T);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(sg + blk * 1024), 16, 0, 0);
     }
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < NBG; ++q) {
-      const int nb = g0 + q * 4 + wave;
-      if (nb >= nblk) continue;
-      const int64_t col = (int64_t)nb * 32 + lrow;
-      if (col >= r) continue;
+    for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = j0 + acc_row(v, lgrp);
-        if (row < p.d_out) pr[v] = fmaf(acc[q][v], to_f32(B[row * r + col]), pr[v]);
+      for (int q = 0; q < 2; ++q) {
+        const int row = q * 32 + lrow;
+#pragma unroll
+        for (int part = 0; part < C::NG; ++part) {
+          u32x4 fb[FC];
+#pragma unroll
+          for (int f = 0; f < FC; ++f) {
+            const int ch = ks * 2 * FC + lgrp * FC + f;
+            fb[f] = *reinterpret_cast<const u32x4*>(sg + part * C::PART + row * C::RBYTES + ((ch ^ (row & 7)) * 16));
+          }
+          acc[q] = Mfma<T>::run(fa[ks], fb, acc[q]);
+        }
       }
     }
   }
 
+  // Dot with B's entries in this block's columns, then sum over the columns.
+  float pa[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = pr[v];
-  __syncthreads();
+  for (int v = 0; v < 16; ++v) pa[v] = fmaf(acc[0][v], bval[0][v], acc[1][v] * bval[1][v]);
+  const float tot = sum32_transpose(pa, lane);
+  const int64_t row = j0 + acc_row((lane & 31) >> 1, lgrp);
+  if ((lane & 1) == 0 && row < p.d_out)
+    reinterpret_cast<float*>(ws + p.off_ba)[(int64_t)blockIdx.y * p.ld_w + row] = tot;
+}
 
-  if (tid < 32) {
-    const int R = tid;
-    const int64_t j = j0 + R;
-    if (j < p.d_out) {
-      const int v = (R / 8) * 4 + (R & 3);
-      const int gq = (R & 7) / 4;
-      float ba = 0.f;
-      for (int w = 0; w < 4; ++w) {
-        const float* src = red + (w * 16 + v) * 64 + gq * 32;
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 32; ++i) s4[i & 3] += src[i];
-        ba += (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      }
-      const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
-      const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
-      const int mt_idx = (int)(j / p.mt);
-      float base = 0.f, cross = 0.f;
-      for (int x = 0; x < p.X; ++x) {
-        const int64_t kb = range_lo(p.n_kt, p.X, x);
-        const int64_t nk = range_lo(p.n_kt, p.X, x + 1) - kb;
-        const int64_t U = n_tiles(p) * nk;
-        for (int n = 0; n < p.n_nt; ++n) {
-          const int64_t t = (int64_t)mt_idx * p.n_nt + n;
-          const int sa = slot_of(U, p.P, t * nk), sb = slot_of(U, p.P, t * nk + nk - 1);
-          for (int sl = sa; sl <= sb; ++sl) {
-            if (unit_lo(U, p.P, sl) == unit_lo(U, p.P, sl + 1)) continue;
-            const int64_t ps = (int64_t)x * p.maxseg + (sl - sa);
-            cross += part_cross[(ps * p.n_nt + n) * p.ld_w + j];
-            if (n == 0) base += part_base[ps * p.ld_w + j];
-          }
-        }
-      }
-      // wnorm = sqrt(max(base + 2s*cross + s^2*ba, 0)), each operation rounded.
-      const float two_s = s + s;
-      const float s2 = __fmul_rn(s, s);
-      float val = __fadd_rn(__fadd_rn(base, __fmul_rn(two_s, cross)), __fmul_rn(s2, ba));
-      val = (val < 0.f) ? 0.f : val;
-      const float wn = sqrtf(val);
-      wnorm[j] = wn;
-      if (m != nullptr) {
-        const float d = (wn < eps) ? eps : wn;
-        g[j] = m[j] / d;
+// ---------------------------------------------------------------------------
+// assemble: per row, fixed-order sums of the partials, then
+// wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and g = m / max(wnorm, eps),
+// every operation separately rounded (no contraction), sqrt and division
+// correctly rounded.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void assemble_kernel(NormPlan p, const char* __restrict__ ws, float s,
+                                                            const float* m, float eps, float* wnorm, float* g) {
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t j = gid >> 3;
+  const int x = (int)(gid & 7);
+  const bool live = j < p.d_out;
+  const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
+  const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
+  const float* part_ba = reinterpret_cast<const float*>(ws + p.off_ba);
+  // Lane x: range x's base and cross partials.
+  float base = 0.f, cross = 0.f;
+  if (live && x < p.X) {
+    const int mt_idx = (int)(j / p.mt);
+    const int64_t nk = range_lo(p.n_kt, p.X, x + 1) - range_lo(p.n_kt, p.X, x);
+    const int64_t U = n_tiles(p) * nk;
+    for (int n = 0; n < p.n_nt; ++n) {
+      const int64_t t = (int64_t)mt_idx * p.n_nt + n;
+      const int sa = slot_of(U, p.P, t * nk), sb = slot_of(U, p.P, t * nk + nk - 1);
+      for (int sl = sa; sl <= sb; ++sl) {
+        const int64_t ps = (int64_t)x * p.maxseg + (sl - sa);
+        cross += part_cross[(ps * p.n_nt + n) * p.ld_w + j];
+        if (n == 0) base += part_base[ps * p.ld_w + j];
       }
     }
+  }
+  base += __shfl_xor(base, 1, 64);
+  base += __shfl_xor(base, 2, 64);
+  base += __shfl_xor(base, 4, 64);
+  cross += __shfl_xor(cross, 1, 64);
+  cross += __shfl_xor(cross, 2, 64);
+  cross += __shfl_xor(cross, 4, 64);
+  if (!live || x != 0) return;
+  float ba = 0.f;
+  for (int cb = 0; cb < p.n_cb; ++cb) ba += part_ba[(int64_t)cb * p.ld_w + j];
+  const float two_s = s + s;
+  const float s2 = __fmul_rn(s, s);
+  float val = __fadd_rn(__fadd_rn(base, __fmul_rn(two_s, cross)), __fmul_rn(s2, ba));
+  val = (val < 0.f) ? 0.f : val;
+  const float wn = sqrtf(val);
+  wnorm[j] = wn;
+  if (m != nullptr) {
+    const float d = (wn < eps) ? eps : wn;
+    g[j] = m[j] / d;
   }
 }
 
@@ -583,12 +638,16 @@ template <typename T>
 hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, const float* m, float eps,
                        float* wnorm, float* g, hipStream_t st) {
   const int64_t n_g = p.r32 * p.r32;
-  hipLaunchKernelGGL((gram_reduce_kernel<T>), dim3((unsigned)((n_g + kThreads - 1) / kThreads)),
+  hipLaunchKernelGGL((gram_reduce_kernel<T>), dim3((unsigned)((8 * n_g + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, st, p, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((norm_finish_kernel<T>), dim3((unsigned)((p.d_out + 31) / 32)), dim3(kThreads), 0, st,
-                     p, static_cast<const T*>(B), ws, s, m, eps, wnorm, g);
+  hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)p.n_cb),
+                     dim3(kGramRows * 2), 0, st, p, static_cast<const T*>(B), ws);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((8 * p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                     p, ws, s, m, eps, wnorm, g);
   return hipGetLastError();
 }
 
