@@ -82,6 +82,15 @@ __device__ __forceinline__ u32x4 load_chunk(const T* row, int64_t k, int64_t d_i
   return v;
 }
 
+// One 16-byte-per-lane direct load into LDS: lane l's 16 bytes from
+// base + voff + soff land at lds + 16*l. The buffer descriptor spans
+// [base, base + nbytes); a lane whose offset lies past it reads zeros.
+__device__ __forceinline__ void lds_load16(const void* base, int nbytes, void* lds, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes,
+                                                                        0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 // XOR swizzle of 16-byte chunks inside LDS rows of CPR chunks, so that the
 // 32 rows one MFMA fragment read touches spread over all LDS banks.
 template <int CPR>

@@ -23,7 +23,7 @@ constexpr int kThreads = 256;        // 4 waves of 64
 constexpr int kGramCB = 64;          // columns of G per Gram-term workgroup
 constexpr int kGramRows = 256;       // rows of B per Gram-term workgroup (32 per wave, 8 waves)
 
-// Tile shapes of the norm's main kernel. The workgroup is WM x WN waves;
+// Tile shapes of the norm's main kernel. The workgroup is WM x WN waves (4 or 8);
 // each wave owns MB x NB blocks of 32x32 fp32 accumulators. KT is the d_in
 // depth of one LDS stage, in elements.
 struct TileShape {
@@ -47,7 +47,7 @@ DORA_HD TileShape tile_shape(int cfg) {
     case kBf16R64: return TileShape{2, 2, 4, 1, 64};
     case kBf16R128: return TileShape{1, 4, 4, 1, 64};
     case kBf16R256: return TileShape{1, 4, 4, 2, 64};
-    case kBf16R384: return TileShape{1, 4, 4, 3, 64};
+    case kBf16R384: return TileShape{2, 4, 2, 3, 64};
     case kBf16R512: return TileShape{1, 4, 2, 4, 64};
     case kBf16R768: return TileShape{1, 4, 2, 6, 32};
     case kF32R32: return TileShape{4, 1, 1, 1, 32};

@@ -51,29 +51,31 @@ struct MainCfg {
   static constexpr int RB = KT * ESZ;           // bytes of one LDS row
   static constexpr int CPR = RB / 16;           // 16-byte chunks per LDS row
   static constexpr int KSTEPS = KT / 16;
+  static constexpr int NW = WM * WN;            // waves per workgroup
+  static constexpr int NT = NW * 64;            // threads per workgroup
   static constexpr int ROWS = MT + NTC;
   static constexpr int STAGE = ROWS * RB;
   static constexpr int NCH = ROWS * CPR;
-  static constexpr int CPT = NCH / kThreads;    // chunks per thread (register path)
-  static constexpr int RSTEP = kThreads / CPR;  // row step between a thread's chunks
+  static constexpr int CPT = NCH / NT;          // chunks per thread (register path)
+  static constexpr int RSTEP = NT / CPR;        // row step between a thread's chunks
   static constexpr int RPB = 1024 / RB;         // LDS rows per 1 KiB direct-load block
   static constexpr int MBLK = MT * RB / 1024;   // direct-load blocks of the M rows
   static constexpr int NBLKS = NTC * RB / 1024; // direct-load blocks of the N rows
-  static constexpr int BPW_M = MBLK / 4, BPW_N = NBLKS / 4, BPW = BPW_M + BPW_N;
-  // Epilogue: U rows of one 32-row block per wave row (WM*32 rows) in fp32.
-  static constexpr int UR = WM * 32;            // rows handled per epilogue round
+  static constexpr int BPW_M = MBLK / NW, BPW_N = NBLKS / NW, BPW = BPW_M + BPW_N;
+  // Epilogue: one 32-row block of U at a time, in fp32.
+  static constexpr int UR = 32;                 // rows handled per epilogue round
   static constexpr int UPITCH = NTC * 4 + 16;   // bytes per U row in LDS
-  static constexpr int TPR = kThreads / UR;     // threads per row in the dot product
+  static constexpr int TPR = NT / UR;           // threads per row in the dot product
   static constexpr int CPTH = NTC / TPR;        // columns per thread in the dot product
   static constexpr int UBUF = UR * UPITCH;
   static constexpr int RED = 2 * MT * 4;        // cross and base row sums
   static constexpr int L0 = CMax<STAGE, UBUF>::v;
   static constexpr int L1 = CMax<STAGE, RED>::v;
-  static_assert(WM * WN == 4, "four waves");
-  static_assert(NCH % kThreads == 0, "stage must split evenly over the threads");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(NCH % NT == 0, "stage must split evenly over the threads");
   static_assert(MT % RSTEP == 0, "M rows end on a thread-row boundary");
   static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
-  static_assert(MBLK % 4 == 0 && NBLKS % 4 == 0, "direct-load blocks split evenly over the waves");
+  static_assert(MBLK % NW == 0 && NBLKS % NW == 0, "direct-load blocks split evenly over the waves");
   static_assert(CPTH % EPC == 0 && (TPR & (TPR - 1)) == 0, "dot-product split");
   static_assert(L0 + L1 <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 };
@@ -90,13 +92,13 @@ struct MainCfg {
 // stage, or inputs that do not allow aligned 16-byte loads (VEC == false),
 // go through registers with explicit zero fill.
 template <typename T, int WM, int WN, int MB, int NB, int KT, bool VEC>
-__global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, const T* __restrict__ W,
+__global__ __launch_bounds__(WM * WN * 64, 1) void norm_main_kernel(NormPlan p, const T* __restrict__ W,
                                                                  const T* __restrict__ A,
                                                                  const T* __restrict__ B,
                                                                  char* __restrict__ ws) {
   using C = MainCfg<T, WM, WN, MB, NB, KT>;
   constexpr int MT = C::MT, NTC = C::NTC, RB = C::RB, CPR = C::CPR, FC = C::FC, EPC = C::EPC;
-  constexpr int ESZ = C::ESZ;
+  constexpr int ESZ = C::ESZ, NW = C::NW, NT = C::NT;
   __shared__ __attribute__((aligned(1024))) char s0[C::L0];
   __shared__ __attribute__((aligned(1024))) char s1[C::L1];
 
@@ -138,20 +140,22 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
     const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
     const bool do_sq = is_w && n == 0;
 
-    // Byte offsets (k = 0) of this lane's direct-load chunks, from the tile's
-    // first row; one per 1 KiB block this wave loads.
+    // Direct loads go through one buffer descriptor per operand, spanning
+    // exactly the tile's valid rows: a lane whose row lies past the matrix
+    // edge is out of range and reads zeros. doff holds each lane's byte
+    // offset (at k = 0) for every 1 KiB LDS block this wave loads.
+    const int m_bytes = (int)((uint32_t)m_lim * (uint32_t)row_bytes);
+    const int n_bytes = (int)((uint32_t)n_lim * (uint32_t)row_bytes);
     uint32_t doff[C::BPW];
     {
       const int sub = lane / CPR, phys = lane % CPR;
 #pragma unroll
       for (int i = 0; i < C::BPW; ++i) {
         const bool mrow = i < C::BPW_M;
-        const int blk = mrow ? i * 4 + wave : C::MBLK + (i - C::BPW_M) * 4 + wave;
+        const int blk = mrow ? i * NW + wave : C::MBLK + (i - C::BPW_M) * NW + wave;
         const int row = blk * C::RPB + sub;
         const int lr = mrow ? row : row - MT;
-        const int lim = mrow ? m_lim : n_lim;
-        const int rr = lr < lim ? lr : lim - 1;
-        doff[i] = (uint32_t)rr * (uint32_t)row_bytes + (uint32_t)(swz<CPR>(row, phys) * 16);
+        doff[i] = (uint32_t)lr * (uint32_t)row_bytes + (uint32_t)(swz<CPR>(row, phys) * 16);
       }
     }
 
@@ -162,39 +166,36 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-    float sq[MB];
+    // Base term: wave wni squares blocks a = (wni % MB) + i*WN of its rows
+    // (every block exactly once when MB >= WN; waves past MB repeat a block
+    // and their sums are dropped).
+    constexpr int SQB = MB >= WN ? MB / WN : 1;
+    float sq[SQB];
 #pragma unroll
-    for (int a = 0; a < MB; ++a) sq[a] = 0.f;
+    for (int i = 0; i < SQB; ++i) sq[i] = 0.f;
 
-    // Direct loads of stage kt. In a ragged last stage (only when d_in is not
-    // a multiple of KT) lanes whose chunk lies past d_in are masked off the
-    // load and write zeros to their LDS slot instead.
     auto dma_stage = [&](int64_t kt, char* sb) __attribute__((always_inline)) {
-      const char* mb_ = reinterpret_cast<const char*>(msrc) + kt * (KT * ESZ);
-      const char* nb_ = reinterpret_cast<const char*>(nsrc) + kt * (KT * ESZ);
+      const uint32_t koff = (uint32_t)(kt * (KT * ESZ));
       const bool full = (kt + 1) * KT <= d_in;
       if (full) {
 #pragma unroll
         for (int i = 0; i < C::BPW; ++i) {
           const bool mrow = i < C::BPW_M;
-          const int blk = mrow ? i * 4 + wave : C::MBLK + (i - C::BPW_M) * 4 + wave;
-          const char* src = (mrow ? mb_ : nb_) + doff[i];
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                           (__attribute__((address_space(3))) void*)(sb + blk * 1024), 16, 0, 0);
+          const int blk = mrow ? i * NW + wave : C::MBLK + (i - C::BPW_M) * NW + wave;
+          lds_load16(mrow ? (const void*)msrc : (const void*)nsrc, mrow ? m_bytes : n_bytes, sb + blk * 1024, doff[i],
+                     koff);
         }
       } else {
         const int sub = lane / CPR, phys = lane % CPR;
 #pragma unroll
         for (int i = 0; i < C::BPW; ++i) {
           const bool mrow = i < C::BPW_M;
-          const int blk = mrow ? i * 4 + wave : C::MBLK + (i - C::BPW_M) * 4 + wave;
-          const char* src = (mrow ? mb_ : nb_) + doff[i];
+          const int blk = mrow ? i * NW + wave : C::MBLK + (i - C::BPW_M) * NW + wave;
           char* dst = sb + blk * 1024;
           const int row = blk * C::RPB + sub;
           const int64_t k = kt * KT + (int64_t)swz<CPR>(row, phys) * EPC;
           if (k < d_in) {
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            lds_load16(mrow ? (const void*)msrc : (const void*)nsrc, mrow ? m_bytes : n_bytes, dst, doff[i], koff);
           } else {
             *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
           }
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
     };
 
     auto reg_stage = [&](int64_t kt, char* sb) __attribute__((always_inline)) {
-      const int cch = tid % CPR, row0 = tid / CPR;
+      const int cch = tid % CPR, row0 = tid / CPR;   // NT threads cover RSTEP rows per pass
       const int64_t k = kt * KT + (int64_t)cch * EPC;
       u32x4 st[C::CPT];
 #pragma unroll
@@ -223,41 +224,47 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
       }
     };
 
-    auto compute = [&](const char* sb) __attribute__((always_inline)) {
+    // One stage on the matrix cores. Fragments are double-buffered across
+    // the K16 steps: step ks+1 is read from LDS while step ks's MFMAs run.
+    auto load_frags = [&](const char* sb, int ks, u32x4 (&fa)[MB][FC], u32x4 (&fb)[NB][FC],
+                          u32x4 (&fs)[SQB][FC]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        u32x4 fa[MB][FC], fb[NB][FC];
+      for (int f = 0; f < FC; ++f) {
+        const int ch = ks * 2 * FC + lgrp * FC + f;
 #pragma unroll
         for (int a = 0; a < MB; ++a) {
           const int row = wmi * MB * 32 + a * 32 + lrow;
-#pragma unroll
-          for (int f = 0; f < FC; ++f) {
-            const int ch = ks * 2 * FC + lgrp * FC + f;
-            fa[a][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
-          }
+          fa[a][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const int row = MT + wni * NB * 32 + b * 32 + lrow;
-#pragma unroll
-          for (int f = 0; f < FC; ++f) {
-            const int ch = ks * 2 * FC + lgrp * FC + f;
-            fb[b][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
-          }
+          fb[b][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
         }
+#pragma unroll
+        for (int i = 0; i < SQB; ++i) {
+          const int row = wmi * MB * 32 + ((wni % MB) + i * WN) * 32 + lrow;
+          fs[i][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
+        }
+      }
+    };
+    auto compute = [&](const char* sb) __attribute__((always_inline)) {
+      u32x4 fa[2][MB][FC], fb[2][NB][FC], fs[2][SQB][FC];
+      load_frags(sb, 0, fa[0], fb[0], fs[0]);
+#pragma unroll
+      for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        const int c = ks & 1;
+        if (ks + 1 < C::KSTEPS) load_frags(sb, ks + 1, fa[c ^ 1], fb[c ^ 1], fs[c ^ 1]);
 #pragma unroll
         for (int a = 0; a < MB; ++a)
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(fa[a], fb[b], acc[a][b]);
-        if (do_sq) {
+          for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(fa[c][a], fb[c][b], acc[a][b]);
 #pragma unroll
-          for (int a = 0; a < MB; ++a)
-            if (a % WN == wni) {
-              float q = 0.f;
+        for (int i = 0; i < SQB; ++i) {
+          float q = 0.f;
 #pragma unroll
-              for (int f = 0; f < FC; ++f) q += chunk_sumsq(fa[a][f], T());
-              sq[a] += q;
-            }
+          for (int f = 0; f < FC; ++f) q += chunk_sumsq(fs[c][i][f], T());
+          sq[i] += q;
         }
       }
     };
@@ -292,66 +299,73 @@ __global__ __launch_bounds__(kThreads, 1) void norm_main_kernel(NormPlan p, cons
       float* red_b = red_c + MT;                     // [MT] base row sums
       // Base term: the two k-halves of each row live in lanes l and l+32.
 #pragma unroll
-      for (int a = 0; a < MB; ++a)
-        if (do_sq && (a % WN) == wni) {
-          const float q = sq[a] + __shfl_xor(sq[a], 32, 64);
-          if (lgrp == 0) red_b[wmi * MB * 32 + a * 32 + lrow] = q;
-        }
-      // Cross term, one 32-row block per wave row at a time: U goes to LDS
-      // straight from the accumulators, then each row is dotted with B. The
-      // B chunks of the next round are loaded while this round is reduced.
+      for (int i = 0; i < SQB; ++i) {
+        const float q = sq[i] + __shfl_xor(sq[i], 32, 64);
+        if (do_sq && wni < MB && lgrp == 0) red_b[wmi * MB * 32 + ((wni % MB) + i * WN) * 32 + lrow] = q;
+      }
+      // Cross term, one 32-row block of U at a time: the owning waves write
+      // it to LDS straight from their accumulators, then every row is dotted
+      // with B. The B chunks of the next round are loaded during this one.
       const int ur = tid / C::TPR, part = tid % C::TPR;   // row in the round, column part
-      const int uwm = ur / 32, ua = ur % 32;
       const int64_t gc0 = n0 + (int64_t)part * C::CPTH;
       constexpr int NBC = C::CPTH / EPC;                  // B chunks per thread per round
       u32x4 bcur[NBC], bnxt[NBC];
-      auto load_b = [&](int a, u32x4 (&dst)[NBC]) __attribute__((always_inline)) {
-        const int lr = uwm * MB * 32 + a * 32 + ua;
+      auto load_b = [&](int lr, u32x4 (&dst)[NBC]) __attribute__((always_inline)) {
         const T* brow = B + (mrow0 + lr) * p.r;
         const bool row_ok = lr < m_lim;
 #pragma unroll
         for (int c = 0; c < NBC; ++c) dst[c] = load_chunk(brow, gc0 + c * EPC, p.r, row_ok, VEC);
       };
-      load_b(0, bcur);
+      load_b(ur, bcur);
 #pragma unroll
       for (int a = 0; a < MB; ++a) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int wr = 0; wr < WM; ++wr) {
+          const int lr = wr * MB * 32 + a * 32 + ur;         // tile row of this thread this round
+          if (wmi == wr) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int rr = wmi * 32 + acc_row(v, lgrp);
-            const int cc = wni * NB * 32 + b * 32 + lrow;
-            *reinterpret_cast<float*>(s0 + rr * C::UPITCH + cc * 4) = acc[a][b][v];
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int cc = wni * NB * 32 + b * 32 + lrow;
+                *reinterpret_cast<float*>(s0 + acc_row(v, lgrp) * C::UPITCH + cc * 4) = acc[a][b][v];
+              }
           }
-        __syncthreads();
-        if (a + 1 < MB) load_b(a + 1, bnxt);
-        const int lr = uwm * MB * 32 + a * 32 + ua;       // tile row of this thread
-        float dsum = 0.f;
+          __syncthreads();
+          const bool last = (a + 1 == MB) && (wr + 1 == WM);
+          if (!last) {
+            const int nlr = (wr + 1 < WM) ? (wr + 1) * MB * 32 + a * 32 + ur : (a + 1) * 32 + ur;
+            load_b(nlr, bnxt);
+          }
+          float dsum = 0.f;
 #pragma unroll
-        for (int c = 0; c < NBC; ++c) {
-          const float* up = reinterpret_cast<const float*>(s0 + ur * C::UPITCH + (part * C::CPTH + c * EPC) * 4);
-          float bf[EPC];
-          if constexpr (sizeof(T) == 2) {
+          for (int c = 0; c < NBC; ++c) {
+            const float* up = reinterpret_cast<const float*>(s0 + ur * C::UPITCH + (part * C::CPTH + c * EPC) * 4);
+            float bf[EPC];
+            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              bf[2 * e] = __uint_as_float(bcur[c][e] << 16);
-              bf[2 * e + 1] = __uint_as_float(bcur[c][e] & 0xffff0000u);
+              for (int e = 0; e < 4; ++e) {
+                bf[2 * e] = __uint_as_float(bcur[c][e] << 16);
+                bf[2 * e + 1] = __uint_as_float(bcur[c][e] & 0xffff0000u);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bf[e] = __uint_as_float(bcur[c][e]);
             }
-          } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bf[e] = __uint_as_float(bcur[c][e]);
+            for (int e = 0; e < EPC; ++e) dsum = fmaf(up[e], bf[e], dsum);
           }
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) dsum = fmaf(up[e], bf[e], dsum);
+          for (int off = C::TPR / 2; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
+          if (part == 0) red_c[lr] = dsum;
+          __syncthreads();
+          if (!last) {
+#pragma unroll
+            for (int c = 0; c < NBC; ++c) bcur[c] = bnxt[c];
+          }
         }
-#pragma unroll
-        for (int off = C::TPR / 2; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
-        if (part == 0) red_c[lr] = dsum;
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < NBC; ++c) bcur[c] = bnxt[c];
       }
-      for (int R = tid; R < MT; R += kThreads) {
+      for (int R = tid; R < MT; R += NT) {
         const int64_t grow = mrow0 + R;
         part_cross[(pslot * p.n_nt + n) * p.ld_w + grow] = red_c[R];
         if (do_sq) part_base[pslot * p.ld_w + grow] = red_b[R];
@@ -625,11 +639,12 @@ __global__ __launch_bounds__(kThreads) void magnitude_kernel(const float* m, con
 template <typename T, int WM, int WN, int MB, int NB, int KT>
 hipError_t launch_main(const NormPlan& p, const void* W, const void* A, const void* B, char* ws,
                        hipStream_t st) {
+  constexpr int NT = WM * WN * 64;
   if (p.vec_in && p.vec_b)
-    hipLaunchKernelGGL((norm_main_kernel<T, WM, WN, MB, NB, KT, true>), dim3(p.X * p.P), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((norm_main_kernel<T, WM, WN, MB, NB, KT, true>), dim3(p.X * p.P), dim3(NT), 0, st,
                        p, static_cast<const T*>(W), static_cast<const T*>(A), static_cast<const T*>(B), ws);
   else
-    hipLaunchKernelGGL((norm_main_kernel<T, WM, WN, MB, NB, KT, false>), dim3(p.X * p.P), dim3(kThreads), 0,
+    hipLaunchKernelGGL((norm_main_kernel<T, WM, WN, MB, NB, KT, false>), dim3(p.X * p.P), dim3(NT), 0,
                        st, p, static_cast<const T*>(W), static_cast<const T*>(A), static_cast<const T*>(B), ws);
   return hipGetLastError();
 }
@@ -662,7 +677,7 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
     case kBf16R64: e = launch_main<bf16_t, 2, 2, 4, 1, 64>(p, W, A, B, ws, st); break;
     case kBf16R128: e = launch_main<bf16_t, 1, 4, 4, 1, 64>(p, W, A, B, ws, st); break;
     case kBf16R256: e = launch_main<bf16_t, 1, 4, 4, 2, 64>(p, W, A, B, ws, st); break;
-    case kBf16R384: e = launch_main<bf16_t, 1, 4, 4, 3, 64>(p, W, A, B, ws, st); break;
+    case kBf16R384: e = launch_main<bf16_t, 2, 4, 2, 3, 64>(p, W, A, B, ws, st); break;
     case kBf16R512: e = launch_main<bf16_t, 1, 4, 2, 4, 64>(p, W, A, B, ws, st); break;
     case kBf16R768: e = launch_main<bf16_t, 1, 4, 2, 6, 32>(p, W, A, B, ws, st); break;
     case kF32R32: e = launch_main<float, 4, 1, 1, 1, 32>(p, W, A, B, ws, st); break;
@@ -696,7 +711,7 @@ size_t main_kernel_lds_bytes(int cfg) {
     case kBf16R64: return MainCfg<bf16_t, 2, 2, 4, 1, 64>::L0 + MainCfg<bf16_t, 2, 2, 4, 1, 64>::L1;
     case kBf16R128: return MainCfg<bf16_t, 1, 4, 4, 1, 64>::L0 + MainCfg<bf16_t, 1, 4, 4, 1, 64>::L1;
     case kBf16R256: return MainCfg<bf16_t, 1, 4, 4, 2, 64>::L0 + MainCfg<bf16_t, 1, 4, 4, 2, 64>::L1;
-    case kBf16R384: return MainCfg<bf16_t, 1, 4, 4, 3, 64>::L0 + MainCfg<bf16_t, 1, 4, 4, 3, 64>::L1;
+    case kBf16R384: return MainCfg<bf16_t, 2, 4, 2, 3, 64>::L0 + MainCfg<bf16_t, 2, 4, 2, 3, 64>::L1;
     case kBf16R512: return MainCfg<bf16_t, 1, 4, 2, 4, 64>::L0 + MainCfg<bf16_t, 1, 4, 2, 4, 64>::L1;
     case kBf16R768: return MainCfg<bf16_t, 1, 4, 2, 6, 32>::L0 + MainCfg<bf16_t, 1, 4, 2, 6, 32>::L1;
     case kF32R32: return MainCfg<float, 4, 1, 1, 1, 32>::L0 + MainCfg<float, 4, 1, 1, 1, 32>::L1;
