@@ -40,9 +40,9 @@ DORA_F32 = 1
 DEFAULT_BUDGET = 256 << 20
 
 PLAN_FIELDS = (
-    "mode", "tile_cfg", "tile_rows", "tile_cols", "stage_depth", "row_tiles_w",
-    "row_tiles_a", "col_tiles", "stages", "ranges", "workgroups_per_range",
-    "max_segments", "workspace_bytes", "grid", "lds_bytes",
+    "mode", "tile_cols", "col_tiles", "gram_tile_cols", "gram_col_tiles", "fast_cfg", "gen_cfg",
+    "gram_fast_cfg", "gram_gen_cfg", "granule", "granules", "w_ranges", "gram_ranges", "workspace_bytes",
+    "w_grid", "gram_grid", "lds_bytes",
 )
 
 _lib = None

@@ -37,45 +37,57 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxRank = (int64_t)1 << 16;
 
-int choose_cfg(int dtype, int64_t r) {
-  if (dtype == DORA_F32) return r <= 32 ? dora::kF32R32 : dora::kF32R128;
-  if (r <= 64) return dora::kBf16R64;
-  if (r <= 128) return dora::kBf16R128;
-  if (r <= 256) return dora::kBf16R256;
-  if (r <= 384) return dora::kBf16R384;
-  if (r <= 512) return dora::kBf16R512;
-  return dora::kBf16R768;
-}
-
-int compute_maxseg(const NormPlan& p) {
-  const int64_t T = dora::n_tiles(p);
-  int maxseg = 1;
-  for (int x = 0; x < p.X; ++x) {
-    const int64_t nk = dora::range_lo(p.n_kt, p.X, x + 1) - dora::range_lo(p.n_kt, p.X, x);
-    const int64_t U = T * nk;
-    for (int64_t t = 0; t < T; ++t) {
-      const int sa = dora::slot_of(U, p.P, t * nk), sb = dora::slot_of(U, p.P, t * nk + nk - 1);
-      if (sb - sa + 1 > maxseg) maxseg = sb - sa + 1;
+// Column tiling over r and the kernel configurations of both passes. The
+// W pass covers as many columns per tile as the streaming kernel holds in
+// its accumulators (so W is read once when r <= 512); the Gram pass uses
+// narrower tiles so that its few rows still spread over many workgroups.
+void choose_tiles(NormPlan& p) {
+  const int64_t r = p.r;
+  if (p.dtype == DORA_F32) {
+    if (r <= 32) {
+      p.ntc = 32, p.fcfg = dora::kFastF32, p.gcfg = dora::kGenF32;
+    } else {
+      p.ntc = 128, p.fcfg = dora::kFastF128, p.gcfg = dora::kGenF128;
     }
+    p.ntc_g = p.ntc, p.fcfg_g = p.fcfg, p.gcfg_g = p.gcfg;
+    p.gran = 32;
+  } else {
+    if (r <= 64) {
+      p.ntc = 64, p.fcfg = dora::kFastB64, p.gcfg = dora::kGenB64;
+    } else if (r <= 128) {
+      p.ntc = 128, p.fcfg = dora::kFastB128, p.gcfg = dora::kGenB128;
+    } else if (r <= 256) {
+      p.ntc = 256, p.fcfg = dora::kFastB256, p.gcfg = dora::kGenB256;
+    } else if (r <= 384 || ceil_div(r, 384) * 384 <= ceil_div(r, 512) * 512) {
+      p.ntc = 384, p.fcfg = dora::kFastB384, p.gcfg = dora::kGenB384;
+    } else {
+      p.ntc = 512, p.fcfg = dora::kFastB512, p.gcfg = dora::kGenB512;
+    }
+    if (p.ntc == 64) {
+      p.ntc_g = 64, p.fcfg_g = dora::kFastB64, p.gcfg_g = dora::kGenB64;
+    } else {
+      p.ntc_g = 128, p.fcfg_g = dora::kFastB128, p.gcfg_g = dora::kGenB128;
+    }
+    p.gran = 64;
   }
-  return maxseg;
+  p.n_nt = (int)ceil_div(r, p.ntc);
+  p.n_nt_g = (int)ceil_div(r, p.ntc_g);
 }
 
 void layout(NormPlan& p) {
-  const int64_t xs = (int64_t)p.X * p.maxseg;
   size_t off = 0;
   p.off_base = off;
-  off = align_up(off + (size_t)(xs * p.ld_w) * 4, kAlign);
+  off = align_up(off + (size_t)((int64_t)p.xw * p.ld_w) * 4, kAlign);
   p.off_cross = off;
-  off = align_up(off + (size_t)(xs * p.n_nt * p.ld_w) * 4, kAlign);
+  off = align_up(off + (size_t)((int64_t)p.xw * p.n_nt * p.ld_w) * 4, kAlign);
+  p.off_ba = off;
+  off = align_up(off + (size_t)(ceil_div(p.r32, 64) * p.ld_w) * 4, kAlign);
   p.off_g = off;
-  off = align_up(off + (size_t)(xs * p.ga_rows * p.ga_cols) * 4, kAlign);
+  off = align_up(off + (size_t)((int64_t)p.xg * p.ga_rows * p.ga_cols) * 4, kAlign);
   p.off_ghi = off;
   off = align_up(off + (size_t)(p.r32 * p.r32) * (p.dtype == DORA_BF16 ? 2 : 4), kAlign);
   p.off_glo = off;
   if (p.dtype == DORA_BF16) off = align_up(off + (size_t)(p.r32 * p.r32) * 2, kAlign);
-  p.off_ba = off;
-  off = align_up(off + (size_t)((int64_t)p.n_cb * p.ld_w) * 4, kAlign);
   p.ws_bytes = off;
 }
 
@@ -83,6 +95,35 @@ dora_status check_sizes(int64_t d_out, int64_t d_in, int64_t r) {
   if (d_out < 0 || d_in < 0 || r < 0) return DORA_ERR_INVALID_ARG;
   if (d_out >= kMaxDim || d_in >= kMaxDim || r >= kMaxRank) return DORA_ERR_INVALID_ARG;
   return DORA_OK;
+}
+
+// d_in ranges of the W pass: the power of two (<= 32 and <= the granule
+// count) whose grid fills whole rounds of kGrid workgroups best; ties go to
+// fewer ranges (fewer partials).
+int choose_w_ranges(int64_t tiles, int64_t n_gran) {
+  int best = 1;
+  double best_eff = -1.0;
+  for (int X = 1; X <= 32 && X <= n_gran; X *= 2) {
+    const int64_t wg = tiles * X;
+    const int64_t rounds = (wg + dora::kGrid - 1) / dora::kGrid;
+    const double eff = (double)wg / (double)(rounds * dora::kGrid);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = X;
+    }
+  }
+  return best;
+}
+
+// d_in ranges of the Gram pass: the largest power of two (<= 64 and <= the
+// granule count) that keeps the grid within kGrid workgroups and the partial
+// Gram matrices within kGramPartialCap bytes.
+constexpr int64_t kGramPartialCap = (int64_t)16 << 20;
+int choose_g_ranges(int64_t tiles, int64_t n_gran, int64_t plane_bytes) {
+  int X = 1;
+  while (X * 2 <= 64 && X * 2 <= n_gran && tiles * X * 2 <= dora::kGrid && plane_bytes * X * 2 <= kGramPartialCap)
+    X *= 2;
+  return X;
 }
 
 dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s, size_t budget,
@@ -107,84 +148,61 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
     return DORA_OK;
   }
   p.mode = dora::kModeFactored;
-  p.cfg = choose_cfg(dtype, r);
-  const dora::TileShape ts = dora::tile_shape(p.cfg);
-  p.mt = ts.wm * ts.mb * 32;
-  p.ntc = ts.wn * ts.nb * 32;
-  p.kt = ts.kt;
-  p.n_mt_w = (int)ceil_div(d_out, p.mt);
-  p.n_mt_a = (int)ceil_div(r, p.mt);
-  p.n_nt = (int)ceil_div(r, p.ntc);
-  p.n_kt = ceil_div(d_in, p.kt);
-  p.ld_w = (int64_t)p.n_mt_w * p.mt;
-  p.ga_rows = (int64_t)p.n_mt_a * p.mt;
-  p.ga_cols = (int64_t)p.n_nt * p.ntc;
+  choose_tiles(p);
+  p.n_gran = ceil_div(d_in, p.gran);
+  p.ld_w = ceil_div(d_out, dora::kRowPad) * dora::kRowPad;
+  p.ga_rows = ceil_div(r, dora::kRowPad) * dora::kRowPad;
+  p.ga_cols = (int64_t)p.n_nt_g * p.ntc_g;
   p.r32 = ceil_div(r, 32) * 32;
-  p.n_cb = (int)ceil_div(p.r32, dora::kGramCB);
 
-  // Most parallel split first: one d_in range per die, every compute unit
-  // busy. Then fewer workgroups, which shrink the partials.
-  const int X0 = (int)(p.n_kt < dora::kDies ? p.n_kt : dora::kDies);
-  const int cand[][2] = {{X0, dora::kGrid / X0}, {1, 64}, {1, 16}, {1, 4}, {1, 1}};
-  for (const auto& c : cand) {
-    p.X = c[0];
-    p.P = c[1];
-    // Never more workgroups per range than work units in its smallest range:
-    // then no workgroup is empty, and the partials of a tile are exactly
-    // those of workgroups slot_of(first unit) .. slot_of(last unit).
-    const int64_t u_min = dora::n_tiles(p) * (p.n_kt / p.X);
-    if (u_min < p.P) p.P = (int)u_min;
-    p.maxseg = compute_maxseg(p);
+  const int64_t tiles_w = ceil_div(d_out, dora::kFastRows) * p.n_nt;
+  const int64_t tiles_g = ceil_div(r, dora::kFastRows) * p.n_nt_g;
+  int xw = choose_w_ranges(tiles_w, p.n_gran);
+  int xg = choose_g_ranges(tiles_g, p.n_gran, p.ga_rows * p.ga_cols * 4);
+  // Fit the budget: fewer Gram ranges first, then fewer W ranges.
+  for (;;) {
+    p.xw = xw;
+    p.xg = xg;
     layout(p);
     if (p.ws_bytes <= budget) {
       *out = p;
       return DORA_OK;
     }
+    if (xg > 1) {
+      xg /= 2;
+    } else if (xw > 1) {
+      xw /= 2;
+    } else {
+      return DORA_ERR_BUDGET;
+    }
   }
-  return DORA_ERR_BUDGET;
 }
 
-// Host replay of the kernels' work split: every (range, tile, stage) unit is
-// owned by exactly one workgroup, segment indices stay below maxseg, and the
-// reduction's enumeration of a tile's segments matches the producers.
+// Host replay of the plan: the ranges tile d_in exactly and are non-empty,
+// every grid fits, and every partial the kernels write lies inside its
+// workspace region.
 bool plan_self_check(const NormPlan& p) {
   if (p.mode != dora::kModeFactored) return true;
-  const int64_t T = dora::n_tiles(p);
-  for (int x = 0; x < p.X; ++x) {
-    const int64_t nk = dora::range_lo(p.n_kt, p.X, x + 1) - dora::range_lo(p.n_kt, p.X, x);
-    if (nk <= 0) return false;
-    const int64_t U = T * nk;
-    std::vector<int> cover((size_t)U, 0);
-    std::vector<int> seg_of((size_t)(T * p.maxseg), -1);  // producer slot per (tile, seg)
-    for (int slot = 0; slot < p.P; ++slot) {
-      int64_t u = dora::unit_lo(U, p.P, slot);
-      const int64_t ue = dora::unit_lo(U, p.P, slot + 1);
-      while (u < ue) {
-        const int64_t t = u / nk, i0 = u - t * nk;
-        const int64_t i1 = (ue - u < nk - i0) ? i0 + (ue - u) : nk;
-        const int seg = slot - dora::slot_of(U, p.P, t * nk);
-        if (seg < 0 || seg >= p.maxseg) return false;
-        int& prod = seg_of[(size_t)(t * p.maxseg + seg)];
-        if (prod != -1) return false;
-        prod = slot;
-        for (int64_t i = i0; i < i1; ++i) cover[(size_t)(t * nk + i)] += 1;
-        u += i1 - i0;
-      }
-    }
-    for (int64_t w = 0; w < U; ++w)
-      if (cover[(size_t)w] != 1) return false;
-    for (int64_t t = 0; t < T; ++t) {
-      const int sa = dora::slot_of(U, p.P, t * nk), sb = dora::slot_of(U, p.P, t * nk + nk - 1);
-      for (int sl = sa; sl <= sb; ++sl) {
-        const int k = sl - sa;
-        if (k >= p.maxseg) return false;
-        if (seg_of[(size_t)(t * p.maxseg + k)] != sl) return false;   // every slot in range produced
-      }
-      for (int k = sb - sa + 1; k < p.maxseg; ++k)
-        if (seg_of[(size_t)(t * p.maxseg + k)] != -1) return false;
-    }
+  for (int pass = 0; pass < 2; ++pass) {
+    const int X = pass ? p.xg : p.xw;
+    if (X < 1 || X > p.n_gran) return false;
+    if (dora::range_k0(p, X, 0) != 0 || dora::range_k0(p, X, X) != p.d_in) return false;
+    for (int x = 0; x < X; ++x)
+      if (dora::range_k0(p, X, x + 1) <= dora::range_k0(p, X, x)) return false;
   }
-  return true;
+  // Row tiles of every kernel (the general 512-column tile has 64 rows).
+  const int64_t rows_w = ceil_div(p.d_out, 64) * 64, rows_g = ceil_div(p.r, 64) * 64;
+  if (ceil_div(p.d_out, dora::kFastRows) * dora::kFastRows > p.ld_w || rows_w > p.ld_w) return false;
+  if (ceil_div(p.r, dora::kFastRows) * dora::kFastRows > p.ga_rows || rows_g > p.ga_rows) return false;
+  if ((int64_t)p.n_nt * p.ntc < p.r || p.ga_cols < p.r || p.r32 > p.ga_cols) return false;
+  const int64_t grid_w = p.xw * ceil_div(p.d_out, 64) * p.n_nt;
+  const int64_t grid_g = p.xg * ceil_div(p.r, 64) * p.n_nt_g;
+  if (grid_w >= ((int64_t)1 << 31) || grid_g >= ((int64_t)1 << 31)) return false;
+  if (p.off_cross < p.off_base + (size_t)(p.xw * p.ld_w) * 4) return false;
+  if (p.off_ba < p.off_cross + (size_t)(p.xw * p.n_nt * p.ld_w) * 4) return false;
+  if (p.off_g < p.off_ba + (size_t)(ceil_div(p.r32, 64) * p.ld_w) * 4) return false;
+  if (p.off_ghi < p.off_g + (size_t)(p.xg * p.ga_rows * p.ga_cols) * 4) return false;
+  return p.ws_bytes >= p.off_glo;
 }
 
 dora_status hip_status(hipError_t e) { return e == hipSuccess ? DORA_OK : DORA_ERR_HIP; }
@@ -237,10 +255,12 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   const dora_status st = make_plan(d_out, d_in, r, dtype, s, budget_bytes, &p);
   if (st != DORA_OK) return st;
   if (!plan_self_check(p)) return DORA_ERR_INVALID_ARG;
-  const int64_t vals[] = {p.mode, p.cfg, p.mt, p.ntc, p.kt, p.n_mt_w, p.n_mt_a, p.n_nt, p.n_kt,
-                          p.X, p.P, p.maxseg, (int64_t)p.ws_bytes,
-                          p.mode == dora::kModeFactored ? (int64_t)p.X * p.P : 0,
-                          p.mode == dora::kModeFactored ? (int64_t)dora::main_kernel_lds_bytes(p.cfg) : 0};
+  const bool f = p.mode == dora::kModeFactored;
+  const int64_t grid_w = f ? p.xw * ceil_div(p.d_out, dora::kFastRows) * p.n_nt : 0;
+  const int64_t grid_g = f ? p.xg * ceil_div(p.r, dora::kFastRows) * p.n_nt_g : 0;
+  const int64_t vals[] = {p.mode, p.ntc, p.n_nt, p.ntc_g, p.n_nt_g, p.fcfg, p.gcfg, p.fcfg_g, p.gcfg_g, p.gran,
+                          p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
+                          f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;
@@ -292,10 +312,13 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
   }
   if (workspace_bytes < p.ws_bytes) return DORA_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && (workspace == nullptr || !aligned(workspace, kAlign))) return DORA_ERR_WORKSPACE;
-  // The fast main kernel addresses a tile's rows with 32-bit byte offsets.
-  const uint64_t tile_span = (uint64_t)(p.mt > p.ntc ? p.mt : p.ntc) * (uint64_t)d_in * (uint64_t)es;
-  p.vec_in = aligned(W, 16) && aligned(A, 16) && (d_in % epc(dtype)) == 0 && tile_span < (1ull << 32);
+  // The streaming kernel addresses a tile's rows with 32-bit byte offsets.
+  const int64_t span_rows = p.ntc > 128 ? p.ntc : 128;
+  const uint64_t tile_span = (uint64_t)span_rows * (uint64_t)d_in * (uint64_t)es;
+  const uint64_t b_span = 32ull * (uint64_t)r * (uint64_t)es;
   p.vec_b = aligned(B, 16) && (r % epc(dtype)) == 0;
+  p.fast = aligned(W, 16) && aligned(A, 16) && (d_in % epc(dtype)) == 0 && p.vec_b &&
+           tile_span < (1ull << 31) && b_span < (1ull << 31);
   return hip_status(dora::launch_norm_factored(p, W, A, B, workspace, s, m, eps, wnorm, g, hs));
 }
 

@@ -91,6 +91,11 @@ __device__ __forceinline__ void lds_load16(const void* base, int nbytes, void* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
+// Wait until every direct-to-LDS load this wave issued has landed (vmcnt 0;
+// the export and LDS counters are left alone). Called before the barrier
+// that hands the loaded data to the other waves.
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // XOR swizzle of 16-byte chunks inside LDS rows of CPR chunks, so that the
 // 32 rows one MFMA fragment read touches spread over all LDS banks.
 template <int CPR>

@@ -16,6 +16,7 @@ hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t 
 hipError_t launch_magnitude(const float* m, const float* wnorm, float eps, int64_t n, float* g, hipStream_t st);
 hipError_t launch_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
                           int64_t d_out, void* out, bool vec, hipStream_t st);
-size_t main_kernel_lds_bytes(int cfg);
+size_t fast_kernel_lds_bytes(int cfg);
+size_t gen_kernel_lds_bytes(int cfg);
 
 }  // namespace dora

@@ -1,7 +1,7 @@
-// Work plan of the factored row norm: tile shapes, the split of d_in across
-// the MI355X dies, the even split of each die's work across its compute
-// units, and the workspace layout. Shared by the host planner and the
-// kernels so both derive segment indices from the same integer formulas.
+// Work plan of the factored row norm: column tiling over r, the split of
+// d_in into ranges (one set of partial sums per range), the kernel
+// configurations and the workspace layout. Shared by the host planner and
+// the kernels so both derive ranges from the same integer formulas.
 #pragma once
 
 #include <stddef.h>
@@ -18,39 +18,63 @@ namespace dora {
 // MI355X: 256 compute units in 8 dies (XCDs) of 32. Workgroup b of a launch
 // is placed on die b % 8, so workgroups b, b+8, b+16, ... share one die's L2.
 constexpr int kDies = 8;
-constexpr int kGrid = 256;           // one norm workgroup per compute unit
+constexpr int kGrid = 256;           // compute units
 constexpr int kThreads = 256;        // 4 waves of 64
-constexpr int kGramCB = 64;          // columns of G per Gram-term workgroup
-constexpr int kGramRows = 256;       // rows of B per Gram-term workgroup (32 per wave, 8 waves)
+constexpr int kRowPad = 128;         // partial-sum rows are padded to a multiple of this
 
-// Tile shapes of the norm's main kernel. The workgroup is WM x WN waves (4 or 8);
-// each wave owns MB x NB blocks of 32x32 fp32 accumulators. KT is the d_in
-// depth of one LDS stage, in elements.
+// Streaming kernel: 4 waves, each owning 32 rows of the tile (128 rows) and
+// all of its nb 32-column blocks; W (or A, in the Gram pass) is read
+// straight into registers, the column operand A goes through a ring of ns
+// LDS slots of kt-deep stages.
+struct FastShape {
+  int nb, kt, ns;
+};
+enum FastCfg : int {
+  kFastB64 = 0,    // bf16, 64 columns
+  kFastB128 = 1,   // bf16, 128 columns
+  kFastB256 = 2,   // bf16, 256 columns
+  kFastB384 = 3,   // bf16, 384 columns
+  kFastB512 = 4,   // bf16, 512 columns
+  kFastF32 = 5,    // fp32, 32 columns
+  kFastF128 = 6,   // fp32, 128 columns
+  kNumFastCfg = 7
+};
+DORA_HD FastShape fast_shape(int cfg) {
+  switch (cfg) {
+    case kFastB64: return FastShape{2, 64, 4};
+    case kFastB128: return FastShape{4, 64, 4};
+    case kFastB256: return FastShape{8, 64, 4};
+    case kFastB384: return FastShape{12, 64, 3};
+    case kFastB512: return FastShape{16, 32, 4};
+    case kFastF32: return FastShape{1, 32, 4};
+    default: return FastShape{4, 32, 4};
+  }
+}
+constexpr int kFastRows = 128;
+
+// General kernel (any alignment): WM x WN waves, each owning MB x NB blocks
+// of 32x32 accumulators; KT is the d_in depth of one LDS stage.
 struct TileShape {
   int wm, wn, mb, nb, kt;
 };
-
 enum TileCfg : int {
-  kBf16R64 = 0,   // r <= 64  : 256 x 64 tiles
-  kBf16R128 = 1,  // r <= 128 : 128 x 128
-  kBf16R256 = 2,  // r <= 256 : 128 x 256
-  kBf16R384 = 3,  // r <= 384 : 128 x 384
-  kBf16R512 = 4,  // r <= 512 : 64 x 512
-  kBf16R768 = 5,  // r >  512 : 64 x 768 (several column tiles beyond 768)
-  kF32R32 = 6,    // fp32, r <= 32 : 128 x 32
-  kF32R128 = 7,   // fp32, r > 32  : 128 x 128 (several column tiles beyond 128)
-  kNumTileCfg = 8
+  kGenB64 = 0,    // bf16, 128 x 64 tiles
+  kGenB128 = 1,   // bf16, 128 x 128
+  kGenB256 = 2,   // bf16, 128 x 256
+  kGenB384 = 3,   // bf16, 128 x 384
+  kGenB512 = 4,   // bf16, 64 x 512
+  kGenF32 = 5,    // fp32, 128 x 32
+  kGenF128 = 6,   // fp32, 128 x 128
+  kNumGenCfg = 7
 };
-
 DORA_HD TileShape tile_shape(int cfg) {
   switch (cfg) {
-    case kBf16R64: return TileShape{2, 2, 4, 1, 64};
-    case kBf16R128: return TileShape{1, 4, 4, 1, 64};
-    case kBf16R256: return TileShape{1, 4, 4, 2, 64};
-    case kBf16R384: return TileShape{2, 4, 2, 3, 64};
-    case kBf16R512: return TileShape{1, 4, 2, 4, 64};
-    case kBf16R768: return TileShape{1, 4, 2, 6, 32};
-    case kF32R32: return TileShape{4, 1, 1, 1, 32};
+    case kGenB64: return TileShape{2, 2, 2, 1, 64};
+    case kGenB128: return TileShape{1, 4, 4, 1, 64};
+    case kGenB256: return TileShape{1, 4, 4, 2, 64};
+    case kGenB384: return TileShape{2, 4, 2, 3, 64};
+    case kGenB512: return TileShape{1, 4, 2, 4, 64};
+    case kGenF32: return TileShape{4, 1, 1, 1, 32};
     default: return TileShape{1, 4, 4, 1, 32};
   }
 }
@@ -61,44 +85,41 @@ struct NormPlan {
   int64_t d_out, d_in, r;
   int dtype;            // 0 = bf16, 1 = fp32
   int mode;             // NormMode
-  int cfg;              // TileCfg
-  int vec_in;           // W and A rows allow aligned 16-byte loads
-  int vec_b;            // B rows allow aligned 16-byte loads
-  int mt, ntc, kt;      // tile rows, tile columns, stage depth
-  int n_mt_w;           // row tiles over W
-  int n_mt_a;           // row tiles over A (they produce G = A A^T)
-  int n_nt;             // column tiles over r
-  int64_t n_kt;         // stages over d_in
-  int X;                // d_in ranges (one per die when X == 8)
-  int P;                // workgroups per range; grid = X * P
-  int maxseg;           // most workgroups that share one (range, tile)
-  int64_t ld_w;         // n_mt_w * mt: padded row count of the W partials
-  int64_t ga_rows;      // n_mt_a * mt
-  int64_t ga_cols;      // n_nt * ntc
+  int ntc;              // W pass: columns of one column tile (a multiple of 32)
+  int n_nt;             // W pass: column tiles over r
+  int fcfg;             // W pass: FastCfg used when the inputs allow 16-byte loads
+  int gcfg;             // W pass: TileCfg used otherwise
+  int ntc_g, n_nt_g;    // Gram pass: column tile width and count
+  int fcfg_g, gcfg_g;   // Gram pass: kernel configurations
+  int fast;             // set per call: 1 = streaming kernel, 0 = general kernel
+  int vec_b;            // set per call: B rows allow aligned 16-byte loads
+  int gran;             // d_in granule in elements: range boundaries are multiples of it
+  int64_t n_gran;       // granules over d_in
+  int xw;               // d_in ranges of the W pass
+  int xg;               // d_in ranges of the Gram pass
+  int64_t ld_w;         // padded W rows of the base / cross partials
+  int64_t ga_rows;      // padded A rows of the Gram partials
+  int64_t ga_cols;      // padded Gram columns: n_nt * ntc
   int64_t r32;          // r rounded up to 32: side of the reduced Gram matrix
-  int n_cb;             // 64-column blocks of G in the Gram-term kernel
-  size_t off_base, off_cross, off_g, off_ghi, off_glo, off_ba;
+  size_t off_base, off_cross, off_ba, off_g, off_ghi, off_glo;
   size_t ws_bytes;
 };
 
-// The split below is integer arithmetic on counts that fit 32 bits for any
-// realistic shape; the 64-bit forms are kept for the rest (the division is
-// done in 32 bits whenever both operands fit, which is much cheaper on the GPU).
+// Division done in 32 bits whenever both operands fit, which is much
+// cheaper on the GPU, and in 64 bits otherwise.
 DORA_HD int64_t div_u(int64_t a, int64_t b) {
   if (((uint64_t)a | (uint64_t)b) < (1ull << 32)) return (int64_t)((uint32_t)a / (uint32_t)b);
   return a / b;
 }
 
-// First stage of d_in range x (ranges split n_kt stages as evenly as integers allow).
-DORA_HD int64_t range_lo(int64_t n_kt, int X, int x) { return div_u(n_kt * x, X); }
+// First granule of d_in range x of X (ranges split the granules as evenly
+// as integers allow; every range is non-empty when X <= n_gran).
+DORA_HD int64_t range_lo(int64_t n_gran, int X, int x) { return div_u(n_gran * x, X); }
 
-// Work units of one range are (tile, stage) pairs, tile-major. Workgroup s
-// of P takes units [unit_lo(s), unit_lo(s+1)).
-DORA_HD int64_t unit_lo(int64_t U, int P, int s) { return div_u(U * s, P); }
-
-// The workgroup whose unit range holds unit w (0 <= w < U).
-DORA_HD int slot_of(int64_t U, int P, int64_t w) { return (int)div_u((w + 1) * P - 1, U); }
-
-DORA_HD int64_t n_tiles(const NormPlan& p) { return (int64_t)(p.n_mt_w + p.n_mt_a) * p.n_nt; }
+// First and one-past-last element of d_in range x.
+DORA_HD int64_t range_k0(const NormPlan& p, int X, int x) {
+  const int64_t k = range_lo(p.n_gran, X, x) * p.gran;
+  return k < p.d_in ? k : p.d_in;
+}
 
 }  // namespace dora

@@ -4,24 +4,25 @@
 // ("DoRA优化技术解析：从内存瓶颈到高效实现", cyqw.cn, §1.2 and §1.2.1;
 // "Scaling DoRA", alanhou.org, "Factored Norm").
 //
-// Four launches:
-//   norm_main    one pass over W and A on the matrix cores. Rows of W and
-//                rows of A are stacked as one M dimension and contracted
-//                against A over d_in. W rows give U = W A^T, which is dotted
-//                with B row by row in the epilogue (cross term) and never
-//                stored; the same W fragments are squared (base term). A
-//                rows give G = A A^T partials.
-//                d_in is split into one range per die so each die's L2 holds
-//                the slice of A its 32 workgroups share; inside a range the
-//                (tile, stage) work units are cut evenly across workgroups.
-//   gram_reduce  sums the G partials in a fixed order; for bf16 it stores G
-//                as an unevaluated sum of two bf16 matrices, G ~ Ghi + Glo.
-//   gram_term    (B G) on the matrix cores (B Ghi + B Glo), dotted with B,
-//                per 64-column block of G (Gram term partials).
-//   assemble     fixed-order sums of all partials;
-//                wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and
-//                g = m / max(wnorm, eps) without contraction, with correctly
-//                rounded sqrt and division (same page, §1.2.2, §5.2, §6.2).
+// Launches, in stream order:
+//   Gram pass     G = A A^T: rows of A against rows of A, d_in cut into
+//                 ranges; one partial G tile per (tile, range).
+//   gram_reduce   sums the partials in a fixed order; for bf16 it stores G
+//                 as an unevaluated sum of two bf16 matrices Ghi + Glo.
+//   W pass        one workgroup per (row tile of W, column tile over r,
+//                 d_in range): U = W A^T on the matrix cores, dotted with B
+//                 row by row at the end (cross term; U is never stored), and
+//                 the W fragments squared on the way (base term).
+//   gram_term     (B G) on the matrix cores (B Ghi + B Glo), dotted with B,
+//                 per 64-column block of G (Gram-term partials).
+//   assemble      fixed-order sums of all partials;
+//                 wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and
+//                 g = m / max(wnorm, eps) without contraction, with
+//                 correctly rounded sqrt and division (same page, §1.2.2,
+//                 §5.2, §6.2).
+// The two passes run the streaming kernel when W, A and B allow aligned
+// 16-byte loads, and the general kernel otherwise; both write the same
+// partials.
 //
 // When s == 0 or r == 0 the cross and Gram terms vanish and only a row
 // sum-of-squares kernel runs (same page, §5.1, notes of Algorithm 1).
@@ -33,74 +34,374 @@ namespace dora {
 
 namespace {
 
+constexpr int kGramCB = 64;     // columns of G per Gram-term workgroup
+constexpr int kGramRows = 256;  // rows of B per Gram-term workgroup (32 per wave, 8 waves)
+
+// s_waitcnt with vmcnt(N) and lgkmcnt(0), expcnt left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier that orders memory only through the explicit waits
+// before it: unlike __syncthreads it does not wait for every outstanding
+// load, so direct-to-LDS loads of later stages stay in flight across it.
+// The memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
+// Out-of-range buffer offset: a buffer load at it returns zeros.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming kernel (inputs allow aligned 16-byte loads).
+//
+// Workgroup = WM x WN waves = one (row tile, column tile, d_in range) of MT
+// rows (W, or A in the Gram pass) and NTC columns (rows of A). Wave
+// (wm, wn) owns MB x NB blocks of 32x32 accumulators. Each KT-deep stage of
+// both operands (MT + NTC rows) arrives in one of NS LDS ring slots by
+// direct-to-LDS loads (64 lanes x 16 B = 1 KiB per instruction) issued NS-1
+// stages ahead, so several stages of loads are in flight while the matrix
+// cores work; one barrier per stage publishes a slot and retires the one
+// reused next. The waits before the barrier leave the younger stages'
+// loads outstanding (an ordinary __syncthreads would drain them all).
+// Inside a stage, the fragments of K16 step s+1 are read while step s's
+// MFMAs run.
+// ---------------------------------------------------------------------------
+template <typename T, int WM, int WN, int MB, int NB, int KT, int NS>
+struct FastK {
+  static constexpr int ESZ = Elem<T>::esz;
+  static constexpr int EPC = Elem<T>::epc;
+  static constexpr int FC = Elem<T>::frag_chunks;
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = NW * 64;
+  static constexpr int MT = WM * MB * 32;
+  static constexpr int NTC = WN * NB * 32;
+  static constexpr int RB = KT * ESZ;            // bytes of one LDS row
+  static constexpr int CPR = RB / 16;            // 16-byte chunks per LDS row
+  static constexpr int RPB = 1024 / RB;          // LDS rows per 1 KiB direct-load block
+  static constexpr int KSTEPS = KT / 16;
+  static constexpr int SLOT = (MT + NTC) * RB;   // bytes of one ring slot
+  static constexpr int MBLK = MT * RB / 1024;    // blocks holding row-operand rows
+  static constexpr int BPW = SLOT / 1024 / NW;   // direct-load blocks per wave per stage
+  static constexpr int BPW_M = MBLK / NW;        // of which row-operand blocks
+  // Epilogue: each wave stages B for its rows and columns.
+  static constexpr int RBB = NB * 32 * ESZ;      // bytes of one staged B row segment
+  static constexpr int CPRB = RBB / 16;
+  // XOR mask of the staged-B swizzle: the largest power of two below 8 that
+  // divides the row's chunk count, so a swizzled chunk stays in its row.
+  static constexpr int BSW = CPRB % 8 == 0 ? 7 : (CPRB % 4 == 0 ? 3 : (CPRB % 2 == 0 ? 1 : 0));
+  static constexpr int WB = MB * 32 * RBB;       // bytes staged per wave
+  static constexpr int WPS = SLOT / WB;          // waves staging B in one ring slot
+  static constexpr int WX = NW > WPS * NS ? NW - WPS * NS : 0;   // waves staging B past the ring
+  static_assert(MT == kFastRows, "row tiles match the plan's padding");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(CPR == 8 || CPR == 4, "LDS rows are 64 or 128 bytes");
+  static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
+  static_assert(SLOT % (1024 * NW) == 0 && MBLK % NW == 0, "a stage splits evenly over the waves");
+  static_assert(WB % 1024 == 0 && RBB % 16 == 0, "B stages in whole 1 KiB blocks");
+  static_assert(WPS >= 1, "a wave's B fits one ring slot");
+  static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + WN * MT * 4 <= 160 * 1024, "gfx950 has 160 KiB of LDS");
+  static_assert(BPW * (NS - 1) < 64, "outstanding loads fit vmcnt");
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row `row`: an XOR swizzle
+// under which the 16 lanes that one LDS cycle serves (64 banks of 4 bytes)
+// hit distinct banks for both the fragment reads and the direct loads.
+template <int CPR>
+__device__ __forceinline__ int fswz(int row, int c) {
+  if constexpr (CPR == 8) {
+    return c ^ ((row >> 1) & 7);
+  } else {
+    return c ^ ((row >> 2) & 3);
+  }
+}
+
+template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, bool GRAM>
+__global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, const T* __restrict__ Msrc,
+                                                                    const T* __restrict__ A,
+                                                                    const T* __restrict__ B,
+                                                                    char* __restrict__ ws) {
+  using C = FastK<T, WM, WN, MB, NB, KT, NS>;
+  constexpr int NW = C::NW, MT = C::MT, NTC = C::NTC, RB = C::RB, CPR = C::CPR, RPB = C::RPB;
+  constexpr int FC = C::FC, EPC = C::EPC, ESZ = C::ESZ, KSTEPS = C::KSTEPS, BPW = C::BPW;
+  __shared__ __attribute__((aligned(1024))) char r0[C::SLOT];
+  __shared__ __attribute__((aligned(1024))) char r1[C::SLOT];
+  __shared__ __attribute__((aligned(1024))) char r2[NS > 2 ? C::SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) char r3[NS > 3 ? C::SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) char bx[(!GRAM && C::WX > 0) ? C::WX * C::WB : 16];
+  __shared__ float red[GRAM ? 1 : WN * MT];
+  auto ring = [&](int j) __attribute__((always_inline)) -> char* {
+    return j == 0 ? r0 : (j == 1 ? r1 : (j == 2 ? r2 : r3));
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int lrow = lane & 31, lgrp = lane >> 5;
+
+  const int X = GRAM ? p.xg : p.xw;
+  const int n_nt = GRAM ? (int)(p.ga_cols / NTC) : p.n_nt;
+  const int64_t m_rows = GRAM ? p.r : p.d_out;
+  const int x = blockIdx.x % X;
+  const int t = blockIdx.x / X;
+  const int m = t / n_nt, n = t - m * n_nt;
+  const int64_t mrow0 = (int64_t)m * MT;
+  const int64_t n0 = (int64_t)n * NTC;
+  const int64_t d_in = p.d_in;
+  const uint32_t row_bytes = (uint32_t)(d_in * ESZ);
+  const int64_t k0 = range_k0(p, X, x), k1 = range_k0(p, X, x + 1);
+  const int n_st = (int)((k1 - k0 + KT - 1) / KT);   // stages of this range (>= 1)
+
+  // Both operands through buffer descriptors spanning the tile's valid rows:
+  // rows past the matrix read as zeros.
+  const int64_t m_left = m_rows - mrow0;
+  const int m_lim = m_left < MT ? (int)m_left : MT;
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(Msrc + mrow0 * d_in, (uint32_t)m_lim * row_bytes);
+  const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + n0 * d_in, (uint32_t)n_lim * row_bytes);
+
+  // Direct loads: this wave fills blocks wave, wave + NW, ...; lane l lands at
+  // byte 16*l of its block, which is LDS row blk*RPB + l/CPR, physical chunk
+  // l % CPR. The logical chunk (and so the global k offset) does not depend
+  // on the block, because blocks start on swizzle-period boundaries.
+  const int l_row = lane / CPR;
+  const int a_chunk = fswz<CPR>(wave * RPB + l_row, lane % CPR);
+  // Blocks b < BPW_M of every wave hold row-operand rows, the rest rows of A.
+  uint32_t doff[BPW];
+#pragma unroll
+  for (int b = 0; b < BPW; ++b) {
+    const int row = (b * NW + wave) * RPB + l_row;
+    doff[b] = (uint32_t)(b < C::BPW_M ? row : row - MT) * row_bytes + (uint32_t)(a_chunk * 16);
+  }
+
+  // Stage i of the range into a ring slot. Stages past the range (the loop
+  // runs a whole number of unrolled groups) and chunks past d_in in the
+  // ragged last stage read as zeros, so every step issues the same loads.
+  auto issue = [&](int i, char* slot) __attribute__((always_inline)) {
+    const int64_t ks = k0 + (int64_t)i * KT;
+    const uint32_t kbyte = (uint32_t)((i < n_st ? ks : k0) * ESZ);
+    const bool ok = i < n_st && (ks + KT <= d_in || ks + (int64_t)a_chunk * EPC < d_in);
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      void* dst = slot + (b * NW + wave) * 1024;
+      const uint32_t off = ok ? doff[b] : kOob;
+      if (b < C::BPW_M)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, (__attribute__((address_space(3))) void*)dst, 16, off,
+                                                 (int)kbyte, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (__attribute__((address_space(3))) void*)dst, 16, off,
+                                                 (int)kbyte, 0, 0);
+    }
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+  float sq[MB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a) sq[a] = 0.f;
+
+  // All fragments of one stage: F[s][a] row-operand, F[s][MB + b] column
+  // operand, for K16 step s.
+  typedef u32x4 Frags[KSTEPS][MB + NB][FC];
+  auto read_stage = [&](const char* slot, Frags& F) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int f = 0; f < FC; ++f) {
+        const int c = s * 2 * FC + lgrp * FC + f;
+        const int co = fswz<CPR>(lrow, c) * 16;
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+          F[s][a][f] = *reinterpret_cast<const u32x4*>(slot + ((wm * MB + a) * 32 + lrow) * RB + co);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          F[s][MB + b][f] = *reinterpret_cast<const u32x4*>(slot + (MT + (wn * NB + b) * 32 + lrow) * RB + co);
+      }
+  };
+  auto mfma_stage = [&](const Frags& F) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(F[s][a], F[s][MB + b], acc[a][b]);
+      if constexpr (!GRAM) {
+        // Every wave squares its row fragments (straight-line code); only the
+        // waves of column group 0 store the sums.
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+#pragma unroll
+          for (int f = 0; f < FC; ++f) sq[a] += chunk_sumsq(F[s][a][f], T());
+      }
+    }
+  };
+  // Pipeline. Stage j lives in ring slot j % NS. Iteration i: wait for this
+  // wave's fragment reads of stage i and its loads of stage i+1 (the NS-2
+  // younger stages stay in flight), barrier (stage i is in registers in every
+  // wave and stage i+1 has landed everywhere), load stage i+NS into the slot
+  // stage i vacated, read stage i+1's fragments, then run stage i's MFMAs,
+  // which overlap the next iteration's wait and barrier. The stage count is
+  // rounded up to whole unrolled groups (the extra stages are zeros), so the
+  // loop body is straight-line code with fixed load counts.
+  constexpr int UNR = NS % 2 == 0 ? NS : 2 * NS;   // slots and register sets repeat after UNR stages
+  const int n_pad = (n_st + UNR - 1) / UNR * UNR;
+  Frags F[2];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) issue(j, ring(j));
+  wait_vm_lgkm0<(NS - 1) * BPW>();   // stage 0 complete; stages 1 .. NS-1 in flight
+  barrier_keep_loads();
+  read_stage(ring(0), F[0]);
+  for (int i0 = 0; i0 < n_pad; i0 += UNR) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int i = i0 + j;
+      wait_vm_lgkm0<(NS - 2) * BPW>();
+      barrier_keep_loads();
+      issue(i + NS, ring(j % NS));
+      read_stage(ring((j + 1) % NS), F[(j + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_stage(F[j & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // The ring is reused below: drain the trailing (zero) loads everywhere.
+  wait_vm_lgkm0<0>();
+  barrier_keep_loads();
+
+  if constexpr (GRAM) {
+    float* gdst = reinterpret_cast<float*>(ws + p.off_g) +
+                  ((int64_t)x * p.ga_rows + mrow0 + wm * MB * 32) * p.ga_cols + n0 + wn * NB * 32;
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          gdst[(int64_t)(a * 32 + acc_row(v, lgrp)) * p.ga_cols + b * 32 + lrow] = acc[a][b][v];
+  } else {
+    float* part_base = reinterpret_cast<float*>(ws + p.off_base);
+    float* part_cross = reinterpret_cast<float*>(ws + p.off_cross);
+    const int64_t wrow0 = mrow0 + wm * MB * 32;   // first row of this wave
+    // Base term (waves of column group 0): the two k-halves of each row
+    // live in lanes l and l+32.
+#pragma unroll
+    for (int a = 0; a < MB; ++a) {
+      const float qs = sq[a] + __shfl_xor(sq[a], 32, 64);
+      if (n == 0 && wn == 0 && lgrp == 0) part_base[(int64_t)x * p.ld_w + wrow0 + a * 32 + lrow] = qs;
+    }
+    // Cross term: stage B for this wave's rows and columns in its own part of
+    // the ring (free after the last barrier), dot each accumulator row with
+    // its B row over the wave's columns, then add the column groups in order.
+    char* bb = wave < C::WPS * NS ? ring(wave / C::WPS) + (wave % C::WPS) * C::WB
+                                  : bx + (wave - C::WPS * NS) * C::WB;
+    const int64_t w_left = p.d_out - wrow0;
+    const int w_lim = w_left <= 0 ? 0 : (w_left < MB * 32 ? (int)w_left : MB * 32);
+    const uint32_t brow_bytes = (uint32_t)(p.r * ESZ);
+    const int64_t c0 = n0 + wn * NB * 32;       // first column of this wave
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(B + wrow0 * p.r + c0, (uint32_t)w_lim * brow_bytes);
+#pragma unroll
+    for (int q = 0; q < C::WB / 1024; ++q) {
+      const int slot16 = q * 64 + lane;
+      const int row = slot16 / C::CPRB, c = (slot16 % C::CPRB) ^ (row & C::BSW);
+      const uint32_t off = (c0 + (int64_t)c * EPC < p.r) ? (uint32_t)row * brow_bytes + (uint32_t)(c * 16) : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void*)(bb + q * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+    wait_vm_lgkm0<0>();
+#pragma unroll
+    for (int a = 0; a < MB; ++a) {
+      float pa[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) pa[v] = 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int col = b * 32 + lrow;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = a * 32 + acc_row(v, lgrp);
+          const T bv = *reinterpret_cast<const T*>(bb + row * C::RBB + (((col / EPC) ^ (row & C::BSW)) * 16) +
+                                                   (col % EPC) * ESZ);
+          pa[v] = fmaf(acc[a][b][v], to_f32(bv), pa[v]);
+        }
+      }
+      const float tot = sum32_transpose(pa, lane);
+      if ((lane & 1) == 0) red[wn * MT + wm * MB * 32 + a * 32 + acc_row((lane & 31) >> 1, lgrp)] = tot;
+    }
+    __syncthreads();
+    if (tid < MT) {
+      float cs = 0.f;
+#pragma unroll
+      for (int g = 0; g < WN; ++g) cs += red[g * MT + tid];
+      part_cross[((int64_t)x * p.n_nt + n) * p.ld_w + mrow0 + tid] = cs;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// General kernel (any alignment): one workgroup per (row tile, column tile,
+// d_in range); both operands are staged through two LDS buffers by
+// element-wise register loads with explicit zero fill, one stage ahead.
+// ---------------------------------------------------------------------------
 template <int A_, int B_>
 struct CMax {
   static constexpr int v = A_ > B_ ? A_ : B_;
 };
 
-// ---------------------------------------------------------------------------
-// norm_main
-// ---------------------------------------------------------------------------
 template <typename T, int WM, int WN, int MB, int NB, int KT>
-struct MainCfg {
+struct GenK {
   static constexpr int ESZ = Elem<T>::esz;
   static constexpr int EPC = Elem<T>::epc;
   static constexpr int FC = Elem<T>::frag_chunks;
+  static constexpr int NW = WM * WN;            // waves per workgroup
+  static constexpr int NT = NW * 64;            // threads per workgroup
   static constexpr int MT = WM * MB * 32;
   static constexpr int NTC = WN * NB * 32;
   static constexpr int RB = KT * ESZ;           // bytes of one LDS row
   static constexpr int CPR = RB / 16;           // 16-byte chunks per LDS row
   static constexpr int KSTEPS = KT / 16;
-  static constexpr int NW = WM * WN;            // waves per workgroup
-  static constexpr int NT = NW * 64;            // threads per workgroup
   static constexpr int ROWS = MT + NTC;
   static constexpr int STAGE = ROWS * RB;
   static constexpr int NCH = ROWS * CPR;
-  static constexpr int CPT = NCH / NT;          // chunks per thread (register path)
+  static constexpr int CPT = NCH / NT;          // chunks per thread
   static constexpr int RSTEP = NT / CPR;        // row step between a thread's chunks
-  static constexpr int RPB = 1024 / RB;         // LDS rows per 1 KiB direct-load block
-  static constexpr int MBLK = MT * RB / 1024;   // direct-load blocks of the M rows
-  static constexpr int NBLKS = NTC * RB / 1024; // direct-load blocks of the N rows
-  static constexpr int BPW_M = MBLK / NW, BPW_N = NBLKS / NW, BPW = BPW_M + BPW_N;
-  // Epilogue: one 32-row block of U at a time, in fp32.
-  static constexpr int UR = 32;                 // rows handled per epilogue round
-  static constexpr int UPITCH = NTC * 4 + 16;   // bytes per U row in LDS
-  static constexpr int TPR = NT / UR;           // threads per row in the dot product
-  static constexpr int CPTH = NTC / TPR;        // columns per thread in the dot product
-  static constexpr int UBUF = UR * UPITCH;
-  static constexpr int RED = 2 * MT * 4;        // cross and base row sums
-  static constexpr int L0 = CMax<STAGE, UBUF>::v;
-  static constexpr int L1 = CMax<STAGE, RED>::v;
+  // Epilogue: B rows of one 32-row block of the tile, the tile's NTC columns.
+  static constexpr int RBB = NTC * ESZ;         // bytes of one staged B row
+  static constexpr int CPRB = RBB / 16;         // 16-byte chunks per staged B row
+  static constexpr int BROUND = 32 * RBB;       // bytes of one staged 32-row B block
+  static constexpr int ROUNDS = WM * MB;        // 32-row blocks per tile
+  static constexpr int L0 = CMax<STAGE, BROUND>::v;
+  static constexpr int RED = (WN + 1) * MT * 4; // per-wave cross sums and base sums
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(NCH % NT == 0, "stage must split evenly over the threads");
   static_assert(MT % RSTEP == 0, "M rows end on a thread-row boundary");
   static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
-  static_assert(MBLK % NW == 0 && NBLKS % NW == 0, "direct-load blocks split evenly over the waves");
-  static_assert(CPTH % EPC == 0 && (TPR & (TPR - 1)) == 0, "dot-product split");
-  static_assert(L0 + L1 <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+  static_assert(CPRB % 8 == 0, "staged B rows hold whole swizzle groups");
+  static_assert(2 * L0 + RED <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 };
 
-// Main kernel. Work unit = (tile, d_in stage). A tile is MT rows (of W, or
-// of A for the Gram matrix) by NTC columns of U (rows of A); a stage is KT
-// elements of d_in. The stages of one tile stream through two LDS buffers:
-// a full stage arrives by direct global->LDS loads (global_load_lds_dwordx4,
-// 64 lanes x 16 B into 1 KiB of LDS per instruction) issued before the
-// previous stage's matrix work, so the copy overlaps the MFMAs and needs no
-// staging registers. Each lane picks the global chunk that lands on its LDS
-// slot under the XOR swizzle; rows past the matrix edge load a clamped real
-// row, and those accumulator rows and columns are never used. A ragged last
-// stage, or inputs that do not allow aligned 16-byte loads (VEC == false),
-// go through registers with explicit zero fill.
-template <typename T, int WM, int WN, int MB, int NB, int KT, bool VEC>
-__global__ __launch_bounds__(WM * WN * 64, 1) void norm_main_kernel(NormPlan p, const T* __restrict__ W,
-                                                                 const T* __restrict__ A,
-                                                                 const T* __restrict__ B,
-                                                                 char* __restrict__ ws) {
-  using C = MainCfg<T, WM, WN, MB, NB, KT>;
+template <typename T, int WM, int WN, int MB, int NB, int KT, bool GRAM>
+__global__ __launch_bounds__(WM * WN * 64, 1) void norm_gen_kernel(NormPlan p, const T* __restrict__ Msrc,
+                                                                   const T* __restrict__ A,
+                                                                   const T* __restrict__ B,
+                                                                   char* __restrict__ ws) {
+  using C = GenK<T, WM, WN, MB, NB, KT>;
   constexpr int MT = C::MT, NTC = C::NTC, RB = C::RB, CPR = C::CPR, FC = C::FC, EPC = C::EPC;
-  constexpr int ESZ = C::ESZ, NW = C::NW, NT = C::NT;
+  constexpr int ESZ = C::ESZ, NT = C::NT;
   __shared__ __attribute__((aligned(1024))) char s0[C::L0];
-  __shared__ __attribute__((aligned(1024))) char s1[C::L1];
+  __shared__ __attribute__((aligned(1024))) char s1[C::L0];
+  __shared__ __attribute__((aligned(16))) float sred[C::RED / 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,317 +409,216 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_main_kernel(NormPlan p, 
   const int wmi = wave / WN, wni = wave % WN;
   const int lrow = lane & 31, lgrp = lane >> 5;
 
-  const int X = p.X, P = p.P;
+  const int X = GRAM ? p.xg : p.xw;
+  const int n_nt = GRAM ? (int)(p.ga_cols / NTC) : p.n_nt;
+  const int64_t m_rows = GRAM ? p.r : p.d_out;
   const int x = blockIdx.x % X;
-  const int slot = blockIdx.x / X;
-  const int64_t kb = range_lo(p.n_kt, X, x);
-  const int64_t nk = range_lo(p.n_kt, X, x + 1) - kb;
-  const int64_t U = n_tiles(p) * nk;
-  int64_t u = unit_lo(U, P, slot);
-  const int64_t u_end = unit_lo(U, P, slot + 1);
-
-  float* part_base = reinterpret_cast<float*>(ws + p.off_base);
-  float* part_cross = reinterpret_cast<float*>(ws + p.off_cross);
-  float* part_g = reinterpret_cast<float*>(ws + p.off_g);
+  const int t = blockIdx.x / X;
+  const int m = t / n_nt, n = t - m * n_nt;
   const int64_t d_in = p.d_in;
-  const int64_t row_bytes = d_in * ESZ;
+  const int64_t k0 = range_k0(p, X, x), k1 = range_k0(p, X, x + 1);
+  const int n_st = (int)((k1 - k0 + KT - 1) / KT);
 
-  while (u < u_end) {
-    const int64_t t = u / nk;
-    const int64_t i0 = u - t * nk;
-    const int64_t i1 = (u_end - u < nk - i0) ? i0 + (u_end - u) : nk;
-    const int seg = slot - slot_of(U, P, t * nk);
-    const int m = (int)(t / p.n_nt);
-    const int n = (int)(t % p.n_nt);
-    const bool is_w = m < p.n_mt_w;
-    const int64_t mrow0 = is_w ? (int64_t)m * MT : (int64_t)(m - p.n_mt_w) * MT;
-    const T* msrc = (is_w ? W : A) + mrow0 * d_in;
-    const int64_t m_left = (is_w ? p.d_out : p.r) - mrow0;
-    const int m_lim = m_left < MT ? (int)m_left : MT;   // valid rows of this tile
-    const int64_t n0 = (int64_t)n * NTC;
-    const T* nsrc = A + n0 * d_in;
-    const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
-    const bool do_sq = is_w && n == 0;
+  const int64_t mrow0 = (int64_t)m * MT;
+  const T* msrc = Msrc + mrow0 * d_in;
+  const int64_t m_left = m_rows - mrow0;
+  const int m_lim = m_left < MT ? (int)m_left : MT;   // valid rows of this tile
+  const int64_t n0 = (int64_t)n * NTC;
+  const T* nsrc = A + n0 * d_in;
+  const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
 
-    // Direct loads go through one buffer descriptor per operand, spanning
-    // exactly the tile's valid rows: a lane whose row lies past the matrix
-    // edge is out of range and reads zeros. doff holds each lane's byte
-    // offset (at k = 0) for every 1 KiB LDS block this wave loads.
-    const int m_bytes = (int)((uint32_t)m_lim * (uint32_t)row_bytes);
-    const int n_bytes = (int)((uint32_t)n_lim * (uint32_t)row_bytes);
-    uint32_t doff[C::BPW];
-    {
-      const int sub = lane / CPR, phys = lane % CPR;
+  f32x16 acc[MB][NB];
 #pragma unroll
-      for (int i = 0; i < C::BPW; ++i) {
-        const bool mrow = i < C::BPW_M;
-        const int blk = mrow ? i * NW + wave : C::MBLK + (i - C::BPW_M) * NW + wave;
-        const int row = blk * C::RPB + sub;
-        const int lr = mrow ? row : row - MT;
-        doff[i] = (uint32_t)lr * (uint32_t)row_bytes + (uint32_t)(swz<CPR>(row, phys) * 16);
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+  // Base term: wave wni squares blocks a = (wni % MB) + i*WN of its rows
+  // (every block exactly once when MB >= WN; waves past MB repeat a block
+  // and their sums are dropped).
+  constexpr int SQB = MB >= WN ? MB / WN : 1;
+  float sq[SQB];
+#pragma unroll
+  for (int i = 0; i < SQB; ++i) sq[i] = 0.f;
+
+  // Stage i of the range (elements k0 + i*KT ..), zero past d_in and past
+  // the valid rows.
+  auto reg_stage = [&](int i, char* sb) __attribute__((always_inline)) {
+    const int cch = tid % CPR, row0 = tid / CPR;
+    const int64_t k = k0 + (int64_t)i * KT + (int64_t)cch * EPC;
+    u32x4 st[C::CPT];
+#pragma unroll
+    for (int j = 0; j < C::CPT; ++j) {
+      const int row = row0 + j * C::RSTEP;
+      if (j < MT / C::RSTEP) {
+        st[j] = load_chunk(msrc + (int64_t)row * d_in, k, d_in, row < m_lim, false);
+      } else {
+        const int nr = row - MT;
+        st[j] = load_chunk(nsrc + (int64_t)nr * d_in, k, d_in, nr < n_lim, false);
       }
     }
+#pragma unroll
+    for (int j = 0; j < C::CPT; ++j) {
+      const int row = row0 + j * C::RSTEP;
+      *reinterpret_cast<u32x4*>(sb + row * RB + swz<CPR>(row, cch) * 16) = st[j];
+    }
+  };
 
-    f32x16 acc[MB][NB];
+  auto load_frags = [&](const char* sb, int ks, u32x4 (&fa)[MB][FC], u32x4 (&fb)[NB][FC],
+                        u32x4 (&fs)[SQB][FC]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < FC; ++f) {
+      const int ch = ks * 2 * FC + lgrp * FC + f;
+#pragma unroll
+      for (int a = 0; a < MB; ++a) {
+        const int row = wmi * MB * 32 + a * 32 + lrow;
+        fa[a][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int row = MT + wni * NB * 32 + b * 32 + lrow;
+        fb[b][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < SQB; ++i) {
+        const int row = wmi * MB * 32 + ((wni % MB) + i * WN) * 32 + lrow;
+        fs[i][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
+      }
+    }
+  };
+  auto compute = [&](const char* sb) __attribute__((always_inline)) {
+    u32x4 fa[2][MB][FC], fb[2][NB][FC], fs[2][SQB][FC];
+    load_frags(sb, 0, fa[0], fb[0], fs[0]);
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < C::KSTEPS) load_frags(sb, ks + 1, fa[c ^ 1], fb[c ^ 1], fs[c ^ 1]);
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(fa[c][a], fb[c][b], acc[a][b]);
+      if constexpr (!GRAM) {
+#pragma unroll
+        for (int i = 0; i < SQB; ++i) {
+          float qs = 0.f;
+#pragma unroll
+          for (int f = 0; f < FC; ++f) qs += chunk_sumsq(fs[c][i][f], T());
+          sq[i] += qs;
+        }
+      }
+    }
+  };
+
+  reg_stage(0, s0);
+  __syncthreads();
+  int i = 0;
+  for (; i + 1 < n_st; i += 2) {
+    compute(s0);
+    reg_stage(i + 1, s1);
+    __syncthreads();
+    compute(s1);
+    if (i + 2 < n_st) reg_stage(i + 2, s0);
+    __syncthreads();
+  }
+  if (i < n_st) {
+    compute(s0);
+    __syncthreads();
+  }
+
+  if constexpr (!GRAM) {
+    float* part_base = reinterpret_cast<float*>(ws + p.off_base);
+    float* part_cross = reinterpret_cast<float*>(ws + p.off_cross);
+    float* red_c = sred;              // [WN][MT] cross sums of each wave's columns
+    float* red_b = sred + WN * MT;    // [MT] base sums
+    // Base term: the two k-halves of each row live in lanes l and l+32.
+#pragma unroll
+    for (int i2 = 0; i2 < SQB; ++i2) {
+      const float qs = sq[i2] + __shfl_xor(sq[i2], 32, 64);
+      if (wni < MB && lgrp == 0) red_b[wmi * MB * 32 + ((wni % MB) + i2 * WN) * 32 + lrow] = qs;
+    }
+    // Cross term, one 32-row block of the tile per round: its B rows (the
+    // tile's NTC columns) are staged in LDS; the owning waves multiply
+    // their accumulators by B and sum over their columns with a lane
+    // transpose-reduction.
+    for (int rho = 0; rho < C::ROUNDS; ++rho) {
+      const int wr = rho / MB, a = rho % MB;
+      const int rbase = rho * 32;
+      const int rows = m_lim - rbase < 32 ? (m_lim - rbase > 0 ? m_lim - rbase : 0) : 32;
+      const T* bsrc = B + (mrow0 + rbase) * p.r + n0;
+      for (int qq = tid; qq < 32 * C::CPRB; qq += NT) {
+        const int row = qq / C::CPRB, ch = qq % C::CPRB;
+        const u32x4 v = load_chunk(bsrc + (int64_t)row * p.r, (int64_t)ch * EPC, p.r - n0, row < rows, false);
+        *reinterpret_cast<u32x4*>(s0 + row * C::RBB + ((ch ^ (row & 7)) * 16)) = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int wr2 = 0; wr2 < WM; ++wr2)
+#pragma unroll
+        for (int a2 = 0; a2 < MB; ++a2) {
+          if (wr2 == wr && a2 == a && wmi == wr) {
+            float pa[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pa[v] = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const int col = wni * NB * 32 + b * 32 + lrow;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int row = acc_row(v, lgrp);
+                const T bv = *reinterpret_cast<const T*>(s0 + row * C::RBB + (((col / EPC) ^ (row & 7)) * 16) +
+                                                         (col % EPC) * ESZ);
+                pa[v] = fmaf(acc[a2][b][v], to_f32(bv), pa[v]);
+              }
+            }
+            const float tot = sum32_transpose(pa, lane);
+            if ((lane & 1) == 0) red_c[wni * MT + rbase + acc_row((lane & 31) >> 1, lgrp)] = tot;
+          }
+        }
+      __syncthreads();
+    }
+    for (int R = tid; R < MT; R += NT) {
+      const int64_t grow = mrow0 + R;
+      float cs = 0.f;
+#pragma unroll
+      for (int wn = 0; wn < WN; ++wn) cs += red_c[wn * MT + R];
+      part_cross[((int64_t)x * p.n_nt + n) * p.ld_w + grow] = cs;
+      if (n == 0) part_base[(int64_t)x * p.ld_w + grow] = red_b[R];
+    }
+  } else {
+    // G = A A^T partial for rows mrow0.. of A and columns n0.. .
+    float* gdst = reinterpret_cast<float*>(ws + p.off_g) + (int64_t)x * p.ga_rows * p.ga_cols;
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
-    // Base term: wave wni squares blocks a = (wni % MB) + i*WN of its rows
-    // (every block exactly once when MB >= WN; waves past MB repeat a block
-    // and their sums are dropped).
-    constexpr int SQB = MB >= WN ? MB / WN : 1;
-    float sq[SQB];
-#pragma unroll
-    for (int i = 0; i < SQB; ++i) sq[i] = 0.f;
-
-    auto dma_stage = [&](int64_t kt, char* sb) __attribute__((always_inline)) {
-      const uint32_t koff = (uint32_t)(kt * (KT * ESZ));
-      const bool full = (kt + 1) * KT <= d_in;
-      if (full) {
-#pragma unroll
-        for (int i = 0; i < C::BPW; ++i) {
-          const bool mrow = i < C::BPW_M;
-          const int blk = mrow ? i * NW + wave : C::MBLK + (i - C::BPW_M) * NW + wave;
-          lds_load16(mrow ? (const void*)msrc : (const void*)nsrc, mrow ? m_bytes : n_bytes, sb + blk * 1024, doff[i],
-                     koff);
+        for (int v = 0; v < 16; ++v) {
+          const int64_t gi = mrow0 + wmi * MB * 32 + a * 32 + acc_row(v, lgrp);
+          const int64_t gj = n0 + wni * NB * 32 + b * 32 + lrow;
+          gdst[gi * p.ga_cols + gj] = acc[a][b][v];
         }
-      } else {
-        const int sub = lane / CPR, phys = lane % CPR;
-#pragma unroll
-        for (int i = 0; i < C::BPW; ++i) {
-          const bool mrow = i < C::BPW_M;
-          const int blk = mrow ? i * NW + wave : C::MBLK + (i - C::BPW_M) * NW + wave;
-          char* dst = sb + blk * 1024;
-          const int row = blk * C::RPB + sub;
-          const int64_t k = kt * KT + (int64_t)swz<CPR>(row, phys) * EPC;
-          if (k < d_in) {
-            lds_load16(mrow ? (const void*)msrc : (const void*)nsrc, mrow ? m_bytes : n_bytes, dst, doff[i], koff);
-          } else {
-            *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      }
-    };
-
-    auto reg_stage = [&](int64_t kt, char* sb) __attribute__((always_inline)) {
-      const int cch = tid % CPR, row0 = tid / CPR;   // NT threads cover RSTEP rows per pass
-      const int64_t k = kt * KT + (int64_t)cch * EPC;
-      u32x4 st[C::CPT];
-#pragma unroll
-      for (int i = 0; i < C::CPT; ++i) {
-        const int row = row0 + i * C::RSTEP;
-        if (i < MT / C::RSTEP) {
-          st[i] = load_chunk(msrc + (int64_t)row * d_in, k, d_in, row < m_lim, VEC);
-        } else {
-          const int nr = row - MT;
-          st[i] = load_chunk(nsrc + (int64_t)nr * d_in, k, d_in, nr < n_lim, VEC);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < C::CPT; ++i) {
-        const int row = row0 + i * C::RSTEP;
-        *reinterpret_cast<u32x4*>(sb + row * RB + swz<CPR>(row, cch) * 16) = st[i];
-      }
-    };
-
-    // One stage on the matrix cores. Fragments are double-buffered across
-    // the K16 steps: step ks+1 is read from LDS while step ks's MFMAs run.
-    auto load_frags = [&](const char* sb, int ks, u32x4 (&fa)[MB][FC], u32x4 (&fb)[NB][FC],
-                          u32x4 (&fs)[SQB][FC]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int f = 0; f < FC; ++f) {
-        const int ch = ks * 2 * FC + lgrp * FC + f;
-#pragma unroll
-        for (int a = 0; a < MB; ++a) {
-          const int row = wmi * MB * 32 + a * 32 + lrow;
-          fa[a][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int row = MT + wni * NB * 32 + b * 32 + lrow;
-          fb[b][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < SQB; ++i) {
-          const int row = wmi * MB * 32 + ((wni % MB) + i * WN) * 32 + lrow;
-          fs[i][f] = *reinterpret_cast<const u32x4*>(sb + row * RB + swz<CPR>(row, ch) * 16);
-        }
-      }
-    };
-    auto compute = [&](const char* sb) __attribute__((always_inline)) {
-      u32x4 fa[2][MB][FC], fb[2][NB][FC], fs[2][SQB][FC];
-      load_frags(sb, 0, fa[0], fb[0], fs[0]);
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        const int c = ks & 1;
-        if (ks + 1 < C::KSTEPS) load_frags(sb, ks + 1, fa[c ^ 1], fb[c ^ 1], fs[c ^ 1]);
-#pragma unroll
-        for (int a = 0; a < MB; ++a)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(fa[c][a], fb[c][b], acc[a][b]);
-#pragma unroll
-        for (int i = 0; i < SQB; ++i) {
-          float q = 0.f;
-#pragma unroll
-          for (int f = 0; f < FC; ++f) q += chunk_sumsq(fs[c][i][f], T());
-          sq[i] += q;
-        }
-      }
-    };
-
-    // Prefetch stage `nxt` into `dst` (direct loads before the matrix work,
-    // or registers after it), consume `src`, then barrier.
-    auto step = [&](const char* src, char* dst, int64_t nxt, bool more) __attribute__((always_inline)) {
-      if constexpr (VEC) {
-        if (more) dma_stage(nxt, dst);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(src);
-      } else {
-        compute(src);
-        if (more) reg_stage(nxt, dst);
-      }
-      __syncthreads();
-    };
-
-    if constexpr (VEC) dma_stage(kb + i0, s0);
-    else reg_stage(kb + i0, s0);
-    __syncthreads();
-    int64_t it = i0;
-    for (; it + 1 < i1; it += 2) {
-      step(s0, s1, kb + it + 1, true);
-      step(s1, s0, kb + it + 2, it + 2 < i1);
-    }
-    if (it < i1) step(s0, s1, 0, false);
-
-    const int64_t pslot = (int64_t)x * p.maxseg + seg;
-    if (is_w) {
-      float* red_c = reinterpret_cast<float*>(s1);   // [MT] cross row sums
-      float* red_b = red_c + MT;                     // [MT] base row sums
-      // Base term: the two k-halves of each row live in lanes l and l+32.
-#pragma unroll
-      for (int i = 0; i < SQB; ++i) {
-        const float q = sq[i] + __shfl_xor(sq[i], 32, 64);
-        if (do_sq && wni < MB && lgrp == 0) red_b[wmi * MB * 32 + ((wni % MB) + i * WN) * 32 + lrow] = q;
-      }
-      // Cross term, one 32-row block of U at a time: the owning waves write
-      // it to LDS straight from their accumulators, then every row is dotted
-      // with B. The B chunks of the next round are loaded during this one.
-      const int ur = tid / C::TPR, part = tid % C::TPR;   // row in the round, column part
-      const int64_t gc0 = n0 + (int64_t)part * C::CPTH;
-      constexpr int NBC = C::CPTH / EPC;                  // B chunks per thread per round
-      u32x4 bcur[NBC], bnxt[NBC];
-      auto load_b = [&](int lr, u32x4 (&dst)[NBC]) __attribute__((always_inline)) {
-        const T* brow = B + (mrow0 + lr) * p.r;
-        const bool row_ok = lr < m_lim;
-#pragma unroll
-        for (int c = 0; c < NBC; ++c) dst[c] = load_chunk(brow, gc0 + c * EPC, p.r, row_ok, VEC);
-      };
-      load_b(ur, bcur);
-#pragma unroll
-      for (int a = 0; a < MB; ++a) {
-#pragma unroll
-        for (int wr = 0; wr < WM; ++wr) {
-          const int lr = wr * MB * 32 + a * 32 + ur;         // tile row of this thread this round
-          if (wmi == wr) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int cc = wni * NB * 32 + b * 32 + lrow;
-                *reinterpret_cast<float*>(s0 + acc_row(v, lgrp) * C::UPITCH + cc * 4) = acc[a][b][v];
-              }
-          }
-          __syncthreads();
-          const bool last = (a + 1 == MB) && (wr + 1 == WM);
-          if (!last) {
-            const int nlr = (wr + 1 < WM) ? (wr + 1) * MB * 32 + a * 32 + ur : (a + 1) * 32 + ur;
-            load_b(nlr, bnxt);
-          }
-          float dsum = 0.f;
-#pragma unroll
-          for (int c = 0; c < NBC; ++c) {
-            const float* up = reinterpret_cast<const float*>(s0 + ur * C::UPITCH + (part * C::CPTH + c * EPC) * 4);
-            float bf[EPC];
-            if constexpr (sizeof(T) == 2) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                bf[2 * e] = __uint_as_float(bcur[c][e] << 16);
-                bf[2 * e + 1] = __uint_as_float(bcur[c][e] & 0xffff0000u);
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) bf[e] = __uint_as_float(bcur[c][e]);
-            }
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) dsum = fmaf(up[e], bf[e], dsum);
-          }
-#pragma unroll
-          for (int off = C::TPR / 2; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
-          if (part == 0) red_c[lr] = dsum;
-          __syncthreads();
-          if (!last) {
-#pragma unroll
-            for (int c = 0; c < NBC; ++c) bcur[c] = bnxt[c];
-          }
-        }
-      }
-      for (int R = tid; R < MT; R += NT) {
-        const int64_t grow = mrow0 + R;
-        part_cross[(pslot * p.n_nt + n) * p.ld_w + grow] = red_c[R];
-        if (do_sq) part_base[pslot * p.ld_w + grow] = red_b[R];
-      }
-      __syncthreads();
-    } else {
-      // G = A A^T partial for rows mrow0.. of A and columns n0.. .
-      float* gdst = part_g + pslot * p.ga_rows * p.ga_cols;
-#pragma unroll
-      for (int a = 0; a < MB; ++a)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t gi = mrow0 + wmi * MB * 32 + a * 32 + acc_row(v, lgrp);
-            const int64_t gj = n0 + wni * NB * 32 + b * 32 + lrow;
-            gdst[gi * p.ga_cols + gj] = acc[a][b][v];
-          }
-    }
-    u += i1 - i0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// gram_reduce: G[i][j] = sum over d_in ranges and segments, fixed order.
-// Eight lanes per element, lane x summing range x's segments; the eight
-// range sums are then combined by a fixed xor tree.
+// gram_reduce: G[i][j] = sum over the Gram pass's ranges, in range order.
+// One thread per element, consecutive j in consecutive lanes.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t idx = gid >> 3;
-  const int x = (int)(gid & 7);
   const int64_t r32 = p.r32;
-  const bool live = idx < r32 * r32;
-  const int64_t i = live ? idx / r32 : 0, j = live ? idx % r32 : 0;
+  const int64_t i = blockIdx.y;
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= r32) return;
   const float* part_g = reinterpret_cast<const float*>(ws + p.off_g);
   float acc = 0.f;
-  if (live && x < p.X && i < p.r && j < p.r) {
-    const int ma = (int)(i / p.mt), n = (int)(j / p.ntc);
-    const int64_t t = (int64_t)(p.n_mt_w + ma) * p.n_nt + n;
-    const int64_t nk = range_lo(p.n_kt, p.X, x + 1) - range_lo(p.n_kt, p.X, x);
-    const int64_t U = n_tiles(p) * nk;
-    const int sa = slot_of(U, p.P, t * nk), sb = slot_of(U, p.P, t * nk + nk - 1);
-    for (int s = sa; s <= sb; ++s) {
-      const int64_t ps = (int64_t)x * p.maxseg + (s - sa);
-      acc += part_g[(ps * p.ga_rows + i) * p.ga_cols + j];
-    }
+  if (i < p.r && j < p.r) {
+    const int64_t plane = p.ga_rows * p.ga_cols;
+    const float* src = part_g + i * p.ga_cols + j;
+    for (int x = 0; x < p.xg; ++x) acc += src[(int64_t)x * plane];
   }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
-  acc += __shfl_xor(acc, 4, 64);
-  if (!live || x != 0) return;
+  const int64_t idx = i * r32 + j;
   if constexpr (sizeof(T) == 2) {
     bf16_t* ghi = reinterpret_cast<bf16_t*>(ws + p.off_ghi);
     bf16_t* glo = reinterpret_cast<bf16_t*>(ws + p.off_glo);
@@ -514,6 +714,7 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(sg + blk * 1024), 16, 0, 0);
     }
+    wait_lds_loads();
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
@@ -548,42 +749,22 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
 // assemble: per row, fixed-order sums of the partials, then
 // wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and g = m / max(wnorm, eps),
 // every operation separately rounded (no contraction), sqrt and division
-// correctly rounded.
+// correctly rounded. One thread per row; reads are coalesced.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void assemble_kernel(NormPlan p, const char* __restrict__ ws, float s,
                                                             const float* m, float eps, float* wnorm, float* g) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t j = gid >> 3;
-  const int x = (int)(gid & 7);
-  const bool live = j < p.d_out;
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= p.d_out) return;
   const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
   const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
   const float* part_ba = reinterpret_cast<const float*>(ws + p.off_ba);
-  // Lane x: range x's base and cross partials.
-  float base = 0.f, cross = 0.f;
-  if (live && x < p.X) {
-    const int mt_idx = (int)(j / p.mt);
-    const int64_t nk = range_lo(p.n_kt, p.X, x + 1) - range_lo(p.n_kt, p.X, x);
-    const int64_t U = n_tiles(p) * nk;
-    for (int n = 0; n < p.n_nt; ++n) {
-      const int64_t t = (int64_t)mt_idx * p.n_nt + n;
-      const int sa = slot_of(U, p.P, t * nk), sb = slot_of(U, p.P, t * nk + nk - 1);
-      for (int sl = sa; sl <= sb; ++sl) {
-        const int64_t ps = (int64_t)x * p.maxseg + (sl - sa);
-        cross += part_cross[(ps * p.n_nt + n) * p.ld_w + j];
-        if (n == 0) base += part_base[ps * p.ld_w + j];
-      }
-    }
+  float base = 0.f, cross = 0.f, ba = 0.f;
+  for (int x = 0; x < p.xw; ++x) {
+    base += part_base[(int64_t)x * p.ld_w + j];
+    for (int n = 0; n < p.n_nt; ++n) cross += part_cross[((int64_t)x * p.n_nt + n) * p.ld_w + j];
   }
-  base += __shfl_xor(base, 1, 64);
-  base += __shfl_xor(base, 2, 64);
-  base += __shfl_xor(base, 4, 64);
-  cross += __shfl_xor(cross, 1, 64);
-  cross += __shfl_xor(cross, 2, 64);
-  cross += __shfl_xor(cross, 4, 64);
-  if (!live || x != 0) return;
-  float ba = 0.f;
-  for (int cb = 0; cb < p.n_cb; ++cb) ba += part_ba[(int64_t)cb * p.ld_w + j];
+  const int n_cb = (int)((p.r32 + kGramCB - 1) / kGramCB);
+  for (int cb = 0; cb < n_cb; ++cb) ba += part_ba[(int64_t)cb * p.ld_w + j];
   const float two_s = s + s;
   const float s2 = __fmul_rn(s, s);
   float val = __fadd_rn(__fadd_rn(base, __fmul_rn(two_s, cross)), __fmul_rn(s2, ba));
@@ -636,32 +817,66 @@ __global__ __launch_bounds__(kThreads) void magnitude_kernel(const float* m, con
   g[j] = m[j] / d;
 }
 
-template <typename T, int WM, int WN, int MB, int NB, int KT>
-hipError_t launch_main(const NormPlan& p, const void* W, const void* A, const void* B, char* ws,
-                       hipStream_t st) {
-  constexpr int NT = WM * WN * 64;
-  if (p.vec_in && p.vec_b)
-    hipLaunchKernelGGL((norm_main_kernel<T, WM, WN, MB, NB, KT, true>), dim3(p.X * p.P), dim3(NT), 0, st,
-                       p, static_cast<const T*>(W), static_cast<const T*>(A), static_cast<const T*>(B), ws);
-  else
-    hipLaunchKernelGGL((norm_main_kernel<T, WM, WN, MB, NB, KT, false>), dim3(p.X * p.P), dim3(NT), 0,
-                       st, p, static_cast<const T*>(W), static_cast<const T*>(A), static_cast<const T*>(B), ws);
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, bool GRAM>
+hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const void* B, char* ws, hipStream_t st) {
+  using C = FastK<T, WM, WN, MB, NB, KT, NS>;
+  const int64_t rows = GRAM ? p.r : p.d_out;
+  const int64_t cols = GRAM ? p.ga_cols : (int64_t)p.n_nt * p.ntc;
+  const int64_t grid = (GRAM ? p.xg : p.xw) * ceil_div64(rows, C::MT) * (cols / C::NTC);
+  hipLaunchKernelGGL((norm_fast_kernel<T, WM, WN, MB, NB, KT, NS, GRAM>), dim3((unsigned)grid), dim3(C::NT), 0, st,
+                     p, static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws);
   return hipGetLastError();
+}
+
+template <typename T, int WM, int WN, int MB, int NB, int KT, bool GRAM>
+hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const void* B, char* ws, hipStream_t st) {
+  using C = GenK<T, WM, WN, MB, NB, KT>;
+  const int64_t rows = GRAM ? p.r : p.d_out;
+  const int64_t cols = GRAM ? p.ga_cols : (int64_t)p.n_nt * p.ntc;
+  const int64_t grid = (GRAM ? p.xg : p.xw) * ceil_div64(rows, C::MT) * (cols / C::NTC);
+  hipLaunchKernelGGL((norm_gen_kernel<T, WM, WN, MB, NB, KT, GRAM>), dim3((unsigned)grid), dim3(C::NT), 0, st, p,
+                     static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws);
+  return hipGetLastError();
+}
+
+template <bool GRAM>
+hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
+                       char* ws, hipStream_t st) {
+  if (p.fast) {
+    switch (fcfg) {
+      case kFastB64: return launch_fast<bf16_t, 4, 2, 1, 1, 64, 4, GRAM>(p, M, A, B, ws, st);
+      case kFastB128: return launch_fast<bf16_t, 2, 4, 2, 1, 64, 4, GRAM>(p, M, A, B, ws, st);
+      case kFastB256: return launch_fast<bf16_t, 2, 4, 2, 2, 32, 4, GRAM>(p, M, A, B, ws, st);
+      case kFastB384: return launch_fast<bf16_t, 2, 4, 2, 3, 32, 4, GRAM>(p, M, A, B, ws, st);
+      case kFastB512: return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, GRAM>(p, M, A, B, ws, st);
+      case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, GRAM>(p, M, A, B, ws, st);
+      case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, GRAM>(p, M, A, B, ws, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (gcfg) {
+    case kGenB64: return launch_gen<bf16_t, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
+    case kGenB128: return launch_gen<bf16_t, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
+    case kGenB256: return launch_gen<bf16_t, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
+    case kGenB384: return launch_gen<bf16_t, 2, 4, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
+    case kGenB512: return launch_gen<bf16_t, 1, 4, 2, 4, 64, GRAM>(p, M, A, B, ws, st);
+    case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st);
+    case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T>
 hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, const float* m, float eps,
                        float* wnorm, float* g, hipStream_t st) {
-  const int64_t n_g = p.r32 * p.r32;
-  hipLaunchKernelGGL((gram_reduce_kernel<T>), dim3((unsigned)((8 * n_g + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, p, ws);
+  const int n_cb = (int)((p.r32 + kGramCB - 1) / kGramCB);
+  hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)n_cb),
+                     dim3(kGramRows * 2), 0, st, p, static_cast<const T*>(B), ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)p.n_cb),
-                     dim3(kGramRows * 2), 0, st, p, static_cast<const T*>(B), ws);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((8 * p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
                      p, ws, s, m, eps, wnorm, g);
   return hipGetLastError();
 }
@@ -672,18 +887,14 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
                                 float s, const float* m, float eps, float* wnorm, float* g,
                                 hipStream_t st) {
   char* ws = static_cast<char*>(ws_);
-  hipError_t e = hipErrorInvalidValue;
-  switch (p.cfg) {
-    case kBf16R64: e = launch_main<bf16_t, 2, 2, 4, 1, 64>(p, W, A, B, ws, st); break;
-    case kBf16R128: e = launch_main<bf16_t, 1, 4, 4, 1, 64>(p, W, A, B, ws, st); break;
-    case kBf16R256: e = launch_main<bf16_t, 1, 4, 4, 2, 64>(p, W, A, B, ws, st); break;
-    case kBf16R384: e = launch_main<bf16_t, 2, 4, 2, 3, 64>(p, W, A, B, ws, st); break;
-    case kBf16R512: e = launch_main<bf16_t, 1, 4, 2, 4, 64>(p, W, A, B, ws, st); break;
-    case kBf16R768: e = launch_main<bf16_t, 1, 4, 2, 6, 32>(p, W, A, B, ws, st); break;
-    case kF32R32: e = launch_main<float, 4, 1, 1, 1, 32>(p, W, A, B, ws, st); break;
-    case kF32R128: e = launch_main<float, 1, 4, 4, 1, 32>(p, W, A, B, ws, st); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipError_t e = launch_pass<true>(p, p.fcfg_g, p.gcfg_g, A, A, B, ws, st);   // Gram pass
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
+                     dim3((unsigned)((p.r32 + kThreads - 1) / kThreads), (unsigned)p.r32), dim3(kThreads), 0, st,
+                     p, ws);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_pass<false>(p, p.fcfg, p.gcfg, W, A, B, ws, st);                // W pass
   if (e != hipSuccess) return e;
   if (p.dtype == 0) return launch_tail<bf16_t>(p, B, ws, s, m, eps, wnorm, g, st);
   return launch_tail<float>(p, B, ws, s, m, eps, wnorm, g, st);
@@ -706,18 +917,34 @@ hipError_t launch_magnitude(const float* m, const float* wnorm, float eps, int64
   return hipGetLastError();
 }
 
-size_t main_kernel_lds_bytes(int cfg) {
+size_t fast_kernel_lds_bytes(int cfg) {
+#define DORA_LDS(NS, ...) (size_t)(FastK<__VA_ARGS__, NS>::SLOT * NS + FastK<__VA_ARGS__, NS>::WX * FastK<__VA_ARGS__, NS>::WB)
   switch (cfg) {
-    case kBf16R64: return MainCfg<bf16_t, 2, 2, 4, 1, 64>::L0 + MainCfg<bf16_t, 2, 2, 4, 1, 64>::L1;
-    case kBf16R128: return MainCfg<bf16_t, 1, 4, 4, 1, 64>::L0 + MainCfg<bf16_t, 1, 4, 4, 1, 64>::L1;
-    case kBf16R256: return MainCfg<bf16_t, 1, 4, 4, 2, 64>::L0 + MainCfg<bf16_t, 1, 4, 4, 2, 64>::L1;
-    case kBf16R384: return MainCfg<bf16_t, 2, 4, 2, 3, 64>::L0 + MainCfg<bf16_t, 2, 4, 2, 3, 64>::L1;
-    case kBf16R512: return MainCfg<bf16_t, 1, 4, 2, 4, 64>::L0 + MainCfg<bf16_t, 1, 4, 2, 4, 64>::L1;
-    case kBf16R768: return MainCfg<bf16_t, 1, 4, 2, 6, 32>::L0 + MainCfg<bf16_t, 1, 4, 2, 6, 32>::L1;
-    case kF32R32: return MainCfg<float, 4, 1, 1, 1, 32>::L0 + MainCfg<float, 4, 1, 1, 1, 32>::L1;
-    case kF32R128: return MainCfg<float, 1, 4, 4, 1, 32>::L0 + MainCfg<float, 1, 4, 4, 1, 32>::L1;
+    case kFastB64: return DORA_LDS(4, bf16_t, 4, 2, 1, 1, 64);
+    case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
+    case kFastB256: return DORA_LDS(4, bf16_t, 2, 4, 2, 2, 32);
+    case kFastB384: return DORA_LDS(4, bf16_t, 2, 4, 2, 3, 32);
+    case kFastB512: return DORA_LDS(3, bf16_t, 2, 4, 2, 4, 32);
+    case kFastF32: return DORA_LDS(4, float, 4, 1, 1, 1, 32);
+    case kFastF128: return DORA_LDS(4, float, 2, 4, 2, 1, 32);
     default: return 0;
   }
+#undef DORA_LDS
+}
+
+size_t gen_kernel_lds_bytes(int cfg) {
+#define DORA_LDS(...) (size_t)(2 * GenK<__VA_ARGS__>::L0 + GenK<__VA_ARGS__>::RED)
+  switch (cfg) {
+    case kGenB64: return DORA_LDS(bf16_t, 2, 2, 2, 1, 64);
+    case kGenB128: return DORA_LDS(bf16_t, 1, 4, 4, 1, 64);
+    case kGenB256: return DORA_LDS(bf16_t, 1, 4, 4, 2, 64);
+    case kGenB384: return DORA_LDS(bf16_t, 2, 4, 2, 3, 64);
+    case kGenB512: return DORA_LDS(bf16_t, 1, 4, 2, 4, 64);
+    case kGenF32: return DORA_LDS(float, 4, 1, 1, 1, 32);
+    case kGenF128: return DORA_LDS(float, 1, 4, 4, 1, 32);
+    default: return 0;
+  }
+#undef DORA_LDS
 }
 
 }  // namespace dora

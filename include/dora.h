@@ -90,15 +90,17 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
 /*
  * The plan dora_factored_norm would use, for diagnostics and benchmarks.
  * Fills info[0 .. n_info-1] with, in order: mode (0 nothing to do, 1 row
- * sum of squares only, 2 factored), tile configuration, tile rows, tile
- * columns, stage depth along d_in, row tiles over W, row tiles over A,
- * column tiles, stages, d_in ranges, workgroups per range, most workgroups
- * sharing one (range, tile), workspace bytes, main-kernel grid, main-kernel
- * LDS bytes; entries past the last field are set to -1.
- * Before returning it replays the work split on the host and checks that
- * every (range, tile, stage) unit has exactly one owner and that the
- * reduction enumerates exactly the partials the producers write;
- * DORA_ERR_INVALID_ARG if not. Host only; never touches the GPU.
+ * sum of squares only, 2 factored), W-pass column tile width, W-pass column
+ * tiles, Gram-pass column tile width, Gram-pass column tiles, streaming and
+ * general kernel configuration of the W pass, the same of the Gram pass,
+ * d_in granule (elements), granules over d_in, d_in ranges of the W pass,
+ * d_in ranges of the Gram pass, workspace bytes, W-pass grid and Gram-pass
+ * grid of the streaming kernel, its LDS bytes in the W pass; entries past
+ * the last field are set to -1.
+ * Before returning it replays the plan on the host and checks that the
+ * d_in ranges tile d_in exactly, every grid fits and every partial sum the
+ * kernels write lies inside its workspace region; DORA_ERR_INVALID_ARG if
+ * not. Host only; never touches the GPU.
  */
 dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s,
                                 size_t budget_bytes, int64_t* info, int n_info);

@@ -57,7 +57,10 @@ def test_plans_of_the_workloads(name):
     assert info["mode"] == 2
     assert info["workspace_bytes"] <= w.budget
     assert info["workspace_bytes"] == bnd.dora_norm_workspace_size(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
-    assert info["grid"] <= 256 and info["lds_bytes"] <= 160 * 1024
+    assert info["gram_grid"] <= 256 and info["lds_bytes"] <= 160 * 1024
+    # the W pass: one workgroup per (row tile, d_in range)
+    assert info["w_grid"] == -(-w.d_out // 128) * info["col_tiles"] * info["w_ranges"]
+    assert info["gram_grid"] == -(-w.r // 128) * info["gram_col_tiles"] * info["gram_ranges"]
     assert info["tile_cols"] * info["col_tiles"] >= w.r
 
 
@@ -85,7 +88,7 @@ def test_budget_fallback_and_error():
     full = bnd.dora_norm_plan_info(8192, 8192, 384, "bf16", 0.5, 256 * MiB)
     small = bnd.dora_norm_plan_info(8192, 8192, 384, "bf16", 0.5, 2 * MiB)
     assert small["workspace_bytes"] <= 2 * MiB < full["workspace_bytes"]
-    assert small["grid"] < full["grid"]
+    assert small["gram_ranges"] < full["gram_ranges"]
     with pytest.raises(bnd.DoraError) as e:
         bnd.dora_norm_workspace_size(8192, 8192, 384, "bf16", 0.5, 1024)
     assert e.value.status == 3
@@ -140,3 +143,12 @@ def test_magnitude_argument_errors():
     assert lib.dora_magnitude_scale(P(0x1000), P(0x2000), 1e-6, -1, P(0x3000), None) == 1
     assert lib.dora_magnitude_scale(None, None, 1e-6, 0, None, None) == 0
     assert lib.dora_magnitude_scale(P(0x1000), P(0x1004), 1e-6, 4, P(0x1004), None) == 1   # g overlaps m
+
+
+def test_library_resolves_every_kernel_stub():
+    """The host pass of hipcc can drop a kernel's launch stub without an error;
+    the library then fails to load. Every kernel stub must be defined."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", bnd.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "device_stub" not in out, [ln for ln in out.splitlines() if "device_stub" in ln][:5]

@@ -131,7 +131,7 @@ def test_deterministic_and_budget_invariant():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     small = bnd.dora_norm_plan_info(1500, 4096, 384, "bf16", 0.5, 2 << 20)
     big = bnd.dora_norm_plan_info(1500, 4096, 384, "bf16", 0.5, 256 << 20)
-    assert small["grid"] != big["grid"]
+    assert (small["gram_ranges"], small["w_ranges"]) != (big["gram_ranges"], big["w_ranges"])
     c, _ = _run(W, A, B, "bf16", 0.5, budget=2 << 20)
     assert np.max(np.abs(c.astype(np.float64) - a) / a) <= 1e-6
     check_norm(c, O.dense_row_norm(W, A, B, 0.5))
