@@ -81,13 +81,11 @@ void layout(NormPlan& p) {
   p.off_cross = off;
   off = align_up(off + (size_t)((int64_t)p.xw * p.n_nt * p.ld_w) * 4, kAlign);
   p.off_ba = off;
-  off = align_up(off + (size_t)(ceil_div(p.r32, 64) * p.ld_w) * 4, kAlign);
+  off = align_up(off + (size_t)((int64_t)(p.n_bt > p.n_cb ? p.n_bt : p.n_cb) * p.ld_w) * 4, kAlign);
   p.off_g = off;
   off = align_up(off + (size_t)((int64_t)p.xg * p.ga_rows * p.ga_cols) * 4, kAlign);
-  p.off_ghi = off;
-  off = align_up(off + (size_t)(p.r32 * p.r32) * (p.dtype == DORA_BF16 ? 2 : 4), kAlign);
-  p.off_glo = off;
-  if (p.dtype == DORA_BF16) off = align_up(off + (size_t)(p.r32 * p.r32) * 2, kAlign);
+  p.off_gg = off;
+  off = align_up(off + (size_t)(p.r32 * p.r32) * 4, kAlign);   // bf16 hi and lo, or fp32
   p.ws_bytes = off;
 }
 
@@ -154,6 +152,16 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.ga_rows = ceil_div(r, dora::kRowPad) * dora::kRowPad;
   p.ga_cols = (int64_t)p.n_nt_g * p.ntc_g;
   p.r32 = ceil_div(r, 32) * 32;
+  // Gram-term tiles: the streaming kernel covers up to 384 columns of G in
+  // one tile (bf16; 128 for fp32) and uses 256-column tiles beyond; the
+  // general kernel uses kGramCols.
+  if (dtype == DORA_BF16) {
+    p.bcfg = p.r32 <= 384 ? (int)ceil_div(p.r32, 128) : 2;
+  } else {
+    p.bcfg = 1;
+  }
+  p.n_bt = (int)ceil_div(p.r32, 128 * (int64_t)p.bcfg);
+  p.n_cb = (int)ceil_div(p.r32, dora::kGramCols);
 
   const int64_t tiles_w = ceil_div(d_out, dora::kFastRows) * p.n_nt;
   const int64_t tiles_g = ceil_div(r, dora::kFastRows) * p.n_nt_g;
@@ -200,9 +208,9 @@ bool plan_self_check(const NormPlan& p) {
   if (grid_w >= ((int64_t)1 << 31) || grid_g >= ((int64_t)1 << 31)) return false;
   if (p.off_cross < p.off_base + (size_t)(p.xw * p.ld_w) * 4) return false;
   if (p.off_ba < p.off_cross + (size_t)(p.xw * p.n_nt * p.ld_w) * 4) return false;
-  if (p.off_g < p.off_ba + (size_t)(ceil_div(p.r32, 64) * p.ld_w) * 4) return false;
-  if (p.off_ghi < p.off_g + (size_t)(p.xg * p.ga_rows * p.ga_cols) * 4) return false;
-  return p.ws_bytes >= p.off_glo;
+  if (p.off_g < p.off_ba + (size_t)((int64_t)(p.n_bt > p.n_cb ? p.n_bt : p.n_cb) * p.ld_w) * 4) return false;
+  if (p.off_gg < p.off_g + (size_t)(p.xg * p.ga_rows * p.ga_cols) * 4) return false;
+  return p.ws_bytes >= p.off_gg + (size_t)(p.r32 * p.r32) * 4;
 }
 
 dora_status hip_status(hipError_t e) { return e == hipSuccess ? DORA_OK : DORA_ERR_HIP; }

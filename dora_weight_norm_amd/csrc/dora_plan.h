@@ -51,6 +51,7 @@ DORA_HD FastShape fast_shape(int cfg) {
   }
 }
 constexpr int kFastRows = 128;
+constexpr int kGramCols = 64;      // columns of G per Gram-term tile
 
 // General kernel (any alignment): WM x WN waves, each owning MB x NB blocks
 // of 32x32 accumulators; KT is the d_in depth of one LDS stage.
@@ -101,7 +102,14 @@ struct NormPlan {
   int64_t ga_rows;      // padded A rows of the Gram partials
   int64_t ga_cols;      // padded Gram columns: n_nt * ntc
   int64_t r32;          // r rounded up to 32: side of the reduced Gram matrix
-  size_t off_base, off_cross, off_ba, off_g, off_ghi, off_glo;
+  int bcfg;             // Gram-term pass (streaming kernel): 128-column blocks per tile (bf16)
+  int n_bt;             // Gram-term column tiles of the streaming kernel
+  int n_cb;             // Gram-term column tiles of the general kernel (kGramCols columns each)
+  size_t off_base;      // [xw][ld_w] fp32 base partials
+  size_t off_cross;     // [xw][n_nt][ld_w] fp32 cross partials
+  size_t off_ba;        // [max(n_bt, n_cb)][ld_w] fp32 Gram-term partials
+  size_t off_g;         // [xg][ga_rows][ga_cols] fp32 Gram partials
+  size_t off_gg;        // reduced Gram matrix: bf16 [r32][Ghi | Glo], fp32 [r32][r32]
   size_t ws_bytes;
 };
 

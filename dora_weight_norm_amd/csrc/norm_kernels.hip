@@ -34,7 +34,7 @@ namespace dora {
 
 namespace {
 
-constexpr int kGramCB = 64;     // columns of G per Gram-term workgroup
+constexpr int kGramCB = kGramCols;   // columns of G per Gram-term workgroup
 constexpr int kGramRows = 256;  // rows of B per Gram-term workgroup (32 per wave, 8 waves)
 
 // s_waitcnt with vmcnt(N) and lgkmcnt(0), expcnt left alone (gfx9 encoding:
@@ -99,7 +99,7 @@ struct FastK {
   static constexpr int WB = MB * 32 * RBB;       // bytes staged per wave
   static constexpr int WPS = SLOT / WB;          // waves staging B in one ring slot
   static constexpr int WX = NW > WPS * NS ? NW - WPS * NS : 0;   // waves staging B past the ring
-  static_assert(MT == kFastRows, "row tiles match the plan's padding");
+  static_assert(kRowPad % MT == 0, "row tiles divide the plan's row padding");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(CPR == 8 || CPR == 4, "LDS rows are 64 or 128 bytes");
   static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
@@ -122,14 +122,61 @@ __device__ __forceinline__ int fswz(int row, int c) {
   }
 }
 
-template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, bool GRAM>
+// What one launch of the streaming kernel computes.
+//   kPassW     U = W A^T per (row tile, column tile, d_in range); epilogue:
+//              base and cross partials.
+//   kPassGram  G = A A^T partial tiles per d_in range.
+//   kPassBG    (B G) over the virtual depth [B | B] . [Ghi ; Glo] (bf16) or
+//              B . G (fp32) per (row tile, column tile of G); epilogue: dot
+//              with B. With a single column tile the Gram term of each row is
+//              complete in its workgroup, which then assembles wnorm and g;
+//              otherwise it stores per-tile partials for the assembly kernel.
+enum PassKind : int { kPassW = 0, kPassGram = 1, kPassBG = 2 };
+
+// Scalars and outputs of the final assembly (used by kPassBG only).
+struct AssembleArgs {
+  float s, eps;
+  const float* m;
+  float* wnorm;
+  float* g;
+};
+
+// wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and g = m / max(wnorm, eps),
+// every operation separately rounded (no contraction), sqrt and division
+// correctly rounded ("DoRA优化技术解析", cyqw.cn, §1.2.2, §5.2, §6.2). base and
+// cross are summed from their partials in a fixed order.
+__device__ __forceinline__ void assemble_row(const NormPlan& p, const char* ws, float s, float eps, const float* m,
+                                             float* wnorm, float* g, int64_t j, float ba) {
+  const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
+  const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
+  float base = 0.f, cross = 0.f;
+  for (int x = 0; x < p.xw; ++x) {
+    base += part_base[(int64_t)x * p.ld_w + j];
+    for (int n = 0; n < p.n_nt; ++n) cross += part_cross[((int64_t)x * p.n_nt + n) * p.ld_w + j];
+  }
+  const float two_s = s + s;
+  const float s2 = __fmul_rn(s, s);
+  float val = __fadd_rn(__fadd_rn(base, __fmul_rn(two_s, cross)), __fmul_rn(s2, ba));
+  val = (val < 0.f) ? 0.f : val;
+  const float wn = sqrtf(val);
+  wnorm[j] = wn;
+  if (m != nullptr) {
+    const float d = (wn < eps) ? eps : wn;
+    g[j] = m[j] / d;
+  }
+}
+
+template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, int MODE>
 __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, const T* __restrict__ Msrc,
                                                                     const T* __restrict__ A,
                                                                     const T* __restrict__ B,
-                                                                    char* __restrict__ ws) {
+                                                                    char* __restrict__ ws, AssembleArgs aa) {
   using C = FastK<T, WM, WN, MB, NB, KT, NS>;
   constexpr int NW = C::NW, MT = C::MT, NTC = C::NTC, RB = C::RB, CPR = C::CPR, RPB = C::RPB;
   constexpr int FC = C::FC, EPC = C::EPC, ESZ = C::ESZ, KSTEPS = C::KSTEPS, BPW = C::BPW;
+  constexpr bool GRAM = MODE == kPassGram;
+  constexpr bool BG = MODE == kPassBG;
+  constexpr int NG = sizeof(T) == 2 ? 2 : 1;   // parts of the stored Gram matrix (hi, lo)
   __shared__ __attribute__((aligned(1024))) char r0[C::SLOT];
   __shared__ __attribute__((aligned(1024))) char r1[C::SLOT];
   __shared__ __attribute__((aligned(1024))) char r2[NS > 2 ? C::SLOT : 16];
@@ -146,8 +193,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane & 31, lgrp = lane >> 5;
 
-  const int X = GRAM ? p.xg : p.xw;
-  const int n_nt = GRAM ? (int)(p.ga_cols / NTC) : p.n_nt;
+  // Tile of this workgroup and the geometry of both operands.
+  const int X = BG ? 1 : (GRAM ? p.xg : p.xw);
+  const int n_nt = BG ? p.n_bt : (GRAM ? (int)(p.ga_cols / NTC) : p.n_nt);
   const int64_t m_rows = GRAM ? p.r : p.d_out;
   const int x = blockIdx.x % X;
   const int t = blockIdx.x / X;
@@ -155,17 +203,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int64_t mrow0 = (int64_t)m * MT;
   const int64_t n0 = (int64_t)n * NTC;
   const int64_t d_in = p.d_in;
-  const uint32_t row_bytes = (uint32_t)(d_in * ESZ);
-  const int64_t k0 = range_k0(p, X, x), k1 = range_k0(p, X, x + 1);
-  const int n_st = (int)((k1 - k0 + KT - 1) / KT);   // stages of this range (>= 1)
+  // Row operand: W (or A) rows of d_in, or B rows of r read twice (hi, lo).
+  const int64_t m_ld = BG ? p.r : d_in;             // elements per row
+  const int64_t m_kvalid = BG ? p.r : d_in;         // valid k of a row
+  const int64_t m_kwrap = BG ? p.r32 : ((int64_t)1 << 62);
+  // Column operand: A rows of d_in, or rows of the stored Gram matrix.
+  const int64_t n_ld = BG ? (int64_t)NG * p.r32 : d_in;
+  const int64_t n_rows = BG ? p.r32 : p.r;
+  const T* Nsrc = BG ? reinterpret_cast<const T*>(ws + p.off_gg) : A;
+  const uint32_t m_rowb = (uint32_t)(m_ld * ESZ), n_rowb = (uint32_t)(n_ld * ESZ);
+  const int64_t k0 = BG ? 0 : range_k0(p, X, x);
+  const int64_t k1 = BG ? (int64_t)NG * p.r32 : range_k0(p, X, x + 1);
+  const int n_st = (int)((k1 - k0 + KT - 1) / KT);   // stages of this tile (>= 1)
 
   // Both operands through buffer descriptors spanning the tile's valid rows:
   // rows past the matrix read as zeros.
   const int64_t m_left = m_rows - mrow0;
   const int m_lim = m_left < MT ? (int)m_left : MT;
-  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(Msrc + mrow0 * d_in, (uint32_t)m_lim * row_bytes);
-  const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + n0 * d_in, (uint32_t)n_lim * row_bytes);
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(Msrc + mrow0 * m_ld, (uint32_t)m_lim * m_rowb);
+  const int n_lim = n_rows - n0 < NTC ? (int)(n_rows - n0) : NTC;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(Nsrc + n0 * n_ld, (uint32_t)n_lim * n_rowb);
 
   // Direct loads: this wave fills blocks wave, wave + NW, ...; lane l lands at
   // byte 16*l of its block, which is LDS row blk*RPB + l/CPR, physical chunk
@@ -173,31 +230,38 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // on the block, because blocks start on swizzle-period boundaries.
   const int l_row = lane / CPR;
   const int a_chunk = fswz<CPR>(wave * RPB + l_row, lane % CPR);
-  // Blocks b < BPW_M of every wave hold row-operand rows, the rest rows of A.
+  // Blocks b < BPW_M of every wave hold row-operand rows, the rest the
+  // column operand's rows.
   uint32_t doff[BPW];
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {
     const int row = (b * NW + wave) * RPB + l_row;
-    doff[b] = (uint32_t)(b < C::BPW_M ? row : row - MT) * row_bytes + (uint32_t)(a_chunk * 16);
+    doff[b] = b < C::BPW_M ? (uint32_t)row * m_rowb + (uint32_t)(a_chunk * 16)
+                           : (uint32_t)(row - MT) * n_rowb + (uint32_t)(a_chunk * 16);
   }
 
-  // Stage i of the range into a ring slot. Stages past the range (the loop
-  // runs a whole number of unrolled groups) and chunks past d_in in the
-  // ragged last stage read as zeros, so every step issues the same loads.
+  // Stage i of the tile into a ring slot. Stages past the tile (the loop
+  // runs a whole number of unrolled groups) and chunks past the valid depth
+  // read as zeros, so every step issues the same loads.
   auto issue = [&](int i, char* slot) __attribute__((always_inline)) {
     const int64_t ks = k0 + (int64_t)i * KT;
-    const uint32_t kbyte = (uint32_t)((i < n_st ? ks : k0) * ESZ);
-    const bool ok = i < n_st && (ks + KT <= d_in || ks + (int64_t)a_chunk * EPC < d_in);
+    const int64_t km = ks < m_kwrap ? ks : ks - m_kwrap;    // row-operand depth index
+    const bool in = i < n_st;
+    const uint32_t kb_m = (uint32_t)((in ? km : 0) * ESZ), kb_n = (uint32_t)((in ? ks : 0) * ESZ);
+    const bool ok_m = in && km + (int64_t)a_chunk * EPC < m_kvalid;
+    const bool ok_n = in && ks + (int64_t)a_chunk * EPC < (BG ? k1 : d_in);
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
+      // (Offsets are computed before the builtin call: a conditional
+      // expression inside its argument list made hipcc's host pass drop the
+      // kernel's launch stub.)
       void* dst = slot + (b * NW + wave) * 1024;
-      const uint32_t off = ok ? doff[b] : kOob;
+      const uint32_t off = (b < C::BPW_M ? ok_m : ok_n) ? doff[b] : kOob;
+      const int kb = (int)(b < C::BPW_M ? kb_m : kb_n);
       if (b < C::BPW_M)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, (__attribute__((address_space(3))) void*)dst, 16, off,
-                                                 (int)kbyte, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (__attribute__((address_space(3))) void*)dst, 16, off,
-                                                 (int)kbyte, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0, 0);
     }
   };
 
@@ -237,7 +301,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       for (int a = 0; a < MB; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(F[s][a], F[s][MB + b], acc[a][b]);
-      if constexpr (!GRAM) {
+      if constexpr (MODE == kPassW) {
         // Every wave squares its row fragments (straight-line code); only the
         // waves of column group 0 store the sums.
 #pragma unroll
@@ -291,26 +355,27 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
         for (int v = 0; v < 16; ++v)
           gdst[(int64_t)(a * 32 + acc_row(v, lgrp)) * p.ga_cols + b * 32 + lrow] = acc[a][b][v];
   } else {
-    float* part_base = reinterpret_cast<float*>(ws + p.off_base);
-    float* part_cross = reinterpret_cast<float*>(ws + p.off_cross);
     const int64_t wrow0 = mrow0 + wm * MB * 32;   // first row of this wave
-    // Base term (waves of column group 0): the two k-halves of each row
-    // live in lanes l and l+32.
+    if constexpr (MODE == kPassW) {
+      // Base term (waves of column group 0): the two k-halves of each row
+      // live in lanes l and l+32.
+      float* part_base = reinterpret_cast<float*>(ws + p.off_base);
 #pragma unroll
-    for (int a = 0; a < MB; ++a) {
-      const float qs = sq[a] + __shfl_xor(sq[a], 32, 64);
-      if (n == 0 && wn == 0 && lgrp == 0) part_base[(int64_t)x * p.ld_w + wrow0 + a * 32 + lrow] = qs;
+      for (int a = 0; a < MB; ++a) {
+        const float qs = sq[a] + __shfl_xor(sq[a], 32, 64);
+        if (n == 0 && wn == 0 && lgrp == 0) part_base[(int64_t)x * p.ld_w + wrow0 + a * 32 + lrow] = qs;
+      }
     }
-    // Cross term: stage B for this wave's rows and columns in its own part of
-    // the ring (free after the last barrier), dot each accumulator row with
-    // its B row over the wave's columns, then add the column groups in order.
+    // Dot each accumulator row with its B row over this wave's columns: stage
+    // B for the wave's rows and columns in its own part of the ring (free
+    // after the last barrier), then add the column groups in order.
     char* bb = wave < C::WPS * NS ? ring(wave / C::WPS) + (wave % C::WPS) * C::WB
                                   : bx + (wave - C::WPS * NS) * C::WB;
     const int64_t w_left = p.d_out - wrow0;
     const int w_lim = w_left <= 0 ? 0 : (w_left < MB * 32 ? (int)w_left : MB * 32);
     const uint32_t brow_bytes = (uint32_t)(p.r * ESZ);
     const int64_t c0 = n0 + wn * NB * 32;       // first column of this wave
-    const __amdgpu_buffer_rsrc_t brs = make_rsrc(B + wrow0 * p.r + c0, (uint32_t)w_lim * brow_bytes);
+    const __amdgpu_buffer_rsrc_t brs = make_rsrc(B + wrow0 * p.r + (c0 < p.r ? c0 : 0), (uint32_t)w_lim * brow_bytes);
 #pragma unroll
     for (int q = 0; q < C::WB / 1024; ++q) {
       const int slot16 = q * 64 + lane;
@@ -340,11 +405,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       if ((lane & 1) == 0) red[wn * MT + wm * MB * 32 + a * 32 + acc_row((lane & 31) >> 1, lgrp)] = tot;
     }
     __syncthreads();
-    if (tid < MT) {
-      float cs = 0.f;
+    if (BG && n_nt == 1) {
+      // The whole Gram term of each row is here: assemble the tile's rows.
+      if (tid < MT && mrow0 + tid < p.d_out) {
+        float ba = 0.f;
 #pragma unroll
-      for (int g = 0; g < WN; ++g) cs += red[g * MT + tid];
-      part_cross[((int64_t)x * p.n_nt + n) * p.ld_w + mrow0 + tid] = cs;
+        for (int gi = 0; gi < WN; ++gi) ba += red[gi * MT + tid];
+        assemble_row(p, ws, aa.s, aa.eps, aa.m, aa.wnorm, aa.g, mrow0 + tid, ba);
+      }
+    } else {
+      float* part = reinterpret_cast<float*>(ws + (BG ? p.off_ba : p.off_cross));
+      const int64_t plane = BG ? (int64_t)n : (int64_t)x * p.n_nt + n;
+      if (tid < MT) {
+        float cs = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < WN; ++gi) cs += red[gi * MT + tid];
+        part[plane * p.ld_w + mrow0 + tid] = cs;
+      }
     }
   }
 }
@@ -618,16 +695,15 @@ __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(NormPlan p, char*
     const float* src = part_g + i * p.ga_cols + j;
     for (int x = 0; x < p.xg; ++x) acc += src[(int64_t)x * plane];
   }
-  const int64_t idx = i * r32 + j;
   if constexpr (sizeof(T) == 2) {
-    bf16_t* ghi = reinterpret_cast<bf16_t*>(ws + p.off_ghi);
-    bf16_t* glo = reinterpret_cast<bf16_t*>(ws + p.off_glo);
+    // Row i of the stored matrix: [hi(G[i][0..r32)), lo(G[i][0..r32))].
+    bf16_t* gg = reinterpret_cast<bf16_t*>(ws + p.off_gg) + i * 2 * r32;
     const bf16_t h = f32_to_bf16_rne(acc);
     const float rem = acc - bf16_bits_to_f32(h);
-    ghi[idx] = h;
-    glo[idx] = f32_to_bf16_rne(rem);
+    gg[j] = h;
+    gg[r32 + j] = f32_to_bf16_rne(rem);
   } else {
-    reinterpret_cast<float*>(ws + p.off_ghi)[idx] = acc;
+    reinterpret_cast<float*>(ws + p.off_gg)[i * r32 + j] = acc;
   }
 }
 
@@ -710,7 +786,7 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
       int64_t grow = c0 + row, gk = k0 + (int64_t)ch * EPC;
       grow = grow < r32 ? grow : r32 - 1;          // past the matrix: a real row, never used
       gk = gk < r32 ? gk : r32 - EPC;
-      const char* src = ws + (part == 0 ? p.off_ghi : p.off_glo) + (grow * r32 + gk) * (int64_t)sizeof(T);
+      const char* src = ws + p.off_gg + (grow * C::NG * r32 + part * r32 + gk) * (int64_t)sizeof(T);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(sg + blk * 1024), 16, 0, 0);
     }
@@ -751,30 +827,14 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
 // every operation separately rounded (no contraction), sqrt and division
 // correctly rounded. One thread per row; reads are coalesced.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void assemble_kernel(NormPlan p, const char* __restrict__ ws, float s,
+__global__ __launch_bounds__(kThreads) void assemble_kernel(NormPlan p, const char* __restrict__ ws, int n_ba, float s,
                                                             const float* m, float eps, float* wnorm, float* g) {
   const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (j >= p.d_out) return;
-  const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
-  const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
   const float* part_ba = reinterpret_cast<const float*>(ws + p.off_ba);
-  float base = 0.f, cross = 0.f, ba = 0.f;
-  for (int x = 0; x < p.xw; ++x) {
-    base += part_base[(int64_t)x * p.ld_w + j];
-    for (int n = 0; n < p.n_nt; ++n) cross += part_cross[((int64_t)x * p.n_nt + n) * p.ld_w + j];
-  }
-  const int n_cb = (int)((p.r32 + kGramCB - 1) / kGramCB);
-  for (int cb = 0; cb < n_cb; ++cb) ba += part_ba[(int64_t)cb * p.ld_w + j];
-  const float two_s = s + s;
-  const float s2 = __fmul_rn(s, s);
-  float val = __fadd_rn(__fadd_rn(base, __fmul_rn(two_s, cross)), __fmul_rn(s2, ba));
-  val = (val < 0.f) ? 0.f : val;
-  const float wn = sqrtf(val);
-  wnorm[j] = wn;
-  if (m != nullptr) {
-    const float d = (wn < eps) ? eps : wn;
-    g[j] = m[j] / d;
-  }
+  float ba = 0.f;
+  for (int c = 0; c < n_ba; ++c) ba += part_ba[(int64_t)c * p.ld_w + j];
+  assemble_row(p, ws, s, eps, m, wnorm, g, j, ba);
 }
 
 // ---------------------------------------------------------------------------
@@ -819,14 +879,21 @@ __global__ __launch_bounds__(kThreads) void magnitude_kernel(const float* m, con
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, bool GRAM>
-hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const void* B, char* ws, hipStream_t st) {
+template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, int MODE>
+hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const void* B, char* ws,
+                       const AssembleArgs& aa, hipStream_t st) {
   using C = FastK<T, WM, WN, MB, NB, KT, NS>;
-  const int64_t rows = GRAM ? p.r : p.d_out;
-  const int64_t cols = GRAM ? p.ga_cols : (int64_t)p.n_nt * p.ntc;
-  const int64_t grid = (GRAM ? p.xg : p.xw) * ceil_div64(rows, C::MT) * (cols / C::NTC);
-  hipLaunchKernelGGL((norm_fast_kernel<T, WM, WN, MB, NB, KT, NS, GRAM>), dim3((unsigned)grid), dim3(C::NT), 0, st,
-                     p, static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws);
+  int64_t grid;
+  if (MODE == kPassBG) {
+    grid = ceil_div64(p.d_out, C::MT) * p.n_bt;   // n_bt * NTC covers r32
+  } else {
+    const bool gram = MODE == kPassGram;
+    const int64_t rows = gram ? p.r : p.d_out;
+    const int64_t cols = gram ? p.ga_cols : (int64_t)p.n_nt * p.ntc;
+    grid = (gram ? p.xg : p.xw) * ceil_div64(rows, C::MT) * (cols / C::NTC);
+  }
+  hipLaunchKernelGGL((norm_fast_kernel<T, WM, WN, MB, NB, KT, NS, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, st,
+                     p, static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws, aa);
   return hipGetLastError();
 }
 
@@ -844,15 +911,17 @@ hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const voi
 template <bool GRAM>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
                        char* ws, hipStream_t st) {
+  constexpr int MODE = GRAM ? kPassGram : kPassW;
+  const AssembleArgs aa{};
   if (p.fast) {
     switch (fcfg) {
-      case kFastB64: return launch_fast<bf16_t, 4, 2, 1, 1, 64, 4, GRAM>(p, M, A, B, ws, st);
-      case kFastB128: return launch_fast<bf16_t, 2, 4, 2, 1, 64, 4, GRAM>(p, M, A, B, ws, st);
-      case kFastB256: return launch_fast<bf16_t, 2, 4, 2, 2, 32, 4, GRAM>(p, M, A, B, ws, st);
-      case kFastB384: return launch_fast<bf16_t, 2, 4, 2, 3, 32, 4, GRAM>(p, M, A, B, ws, st);
-      case kFastB512: return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, GRAM>(p, M, A, B, ws, st);
-      case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, GRAM>(p, M, A, B, ws, st);
-      case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, GRAM>(p, M, A, B, ws, st);
+      case kFastB64: return launch_fast<bf16_t, 4, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastB128: return launch_fast<bf16_t, 2, 4, 2, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastB256: return launch_fast<bf16_t, 2, 4, 2, 2, 32, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastB384: return launch_fast<bf16_t, 2, 4, 2, 3, 32, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastB512: return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
+      case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
       default: return hipErrorInvalidValue;
     }
   }
@@ -871,13 +940,32 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
 template <typename T>
 hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, const float* m, float eps,
                        float* wnorm, float* g, hipStream_t st) {
-  const int n_cb = (int)((p.r32 + kGramCB - 1) / kGramCB);
-  hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)n_cb),
+  if (p.fast) {
+    // Gram term on the matrix cores; with one column tile the assembly is
+    // fused in, otherwise a small kernel adds the column-tile partials.
+    const AssembleArgs aa{s, eps, m, wnorm, g};
+    hipError_t e;
+    if constexpr (sizeof(T) == 2) {
+      switch (p.bcfg) {
+        case 1: e = launch_fast<bf16_t, 2, 4, 1, 1, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st); break;
+        case 2: e = launch_fast<bf16_t, 2, 4, 1, 2, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st); break;
+        case 3: e = launch_fast<bf16_t, 2, 4, 1, 3, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      e = launch_fast<float, 2, 4, 1, 1, 32, 2, kPassBG>(p, B, nullptr, B, ws, aa, st);
+    }
+    if (e != hipSuccess || p.n_bt == 1) return e;
+    hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       st, p, ws, p.n_bt, s, m, eps, wnorm, g);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)p.n_cb),
                      dim3(kGramRows * 2), 0, st, p, static_cast<const T*>(B), ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
-                     p, ws, s, m, eps, wnorm, g);
+                     p, ws, p.n_cb, s, m, eps, wnorm, g);
   return hipGetLastError();
 }
 
