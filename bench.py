@@ -49,7 +49,11 @@ def compose_bytes(T, d_out, esize):
 
 
 def cpu_baseline(w, W, A, B, base, lora, g_host):
-    """The fp64 CPU oracle, as it stands, on the whole workload once."""
+    """The fp64 CPU oracle, as it stands, on a bounded sample of the workload.
+
+    The whole norm once (dense W + sBA in fp64 through BLAS), and the compose
+    on the first rows only, scaled to all rows.
+    """
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -57,12 +61,13 @@ def cpu_baseline(w, W, A, B, base, lora, g_host):
 
     blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    affinity = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     O.dense_row_norm(W, A, B, w.s)
     t_norm = time.perf_counter() - t0
     rows = min(w.T, 2048)
     t0 = time.perf_counter()
-    O.bf16_round(O.compose(base[:rows], lora[:rows], g_host, w.s))
+    O.round_to_dtype(O.compose(base[:rows], lora[:rows], g_host, w.s), w.dtype)
     t_comp = (time.perf_counter() - t0) * (w.T / rows)
     esize = 2 if w.dtype == "bf16" else 4
     del np
@@ -73,7 +78,7 @@ def cpu_baseline(w, W, A, B, base, lora, g_host):
         "kind": "oracle",
         "sample": (f"whole norm once ({w.d_out}x{w.d_in}, r={w.r}) in {t_norm:.2f} s; compose on "
                    f"{rows} of {w.T} rows scaled to all rows ({t_comp:.2f} s); fp64 numpy, BLAS threads="
-                   f"{threads}, elementwise single-threaded"),
+                   f"{threads} of {affinity} cores in the affinity mask, elementwise single-threaded"),
         "norm_ms": t_norm * 1e3,
         "compose_ms": t_comp * 1e3,
         "compose_gbs": compose_bytes(w.T, w.d_out, esize) / t_comp / 1e9,
@@ -89,7 +94,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling profiler byte counters)")
-    ap.add_argument("--traffic", default=None, help="JSON of measured HBM bytes per launch, by kernel")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON of measured HBM bytes per call (default: profiles/traffic_<workload>.json)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -183,18 +189,30 @@ def main() -> int:
     comp_gbs = cb / (comp_ms * 1e-3) / 1e9
     mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else F32_MFMA_PEAK_TFLOPS
 
-    traffic = {}
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f)
+    # Measured HBM bytes per call, from rocprofv3 FETCH_SIZE/WRITE_SIZE runs of
+    # this same command (see profiles/); null when the kernels changed since.
+    from dora_weight_norm_amd import profiling as prof
+
+    tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    traffic, traffic_note = {}, "no counter run for this workload"
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tj = json.load(f)
+        if tj.get("source_hash") == prof.source_hash():
+            traffic = {"norm": tj["norm_bytes_per_call"], "compose": tj["compose_bytes_per_call"]}
+            traffic_note = os.path.relpath(tpath, ROOT)
+        else:
+            traffic_note = "kernels changed since the counters in " + os.path.relpath(tpath, ROOT)
 
     roof_compose = {"bound": "hbm", "achieved": comp_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": comp_gbs / HBM_PEAK_GBS, "traffic": traffic.get("compose"),
-                    "kernel": "compose_kernel", "algorithmic_bytes": cb}
+                    "kernel": "compose_kernel", "algorithmic_bytes": cb, "traffic_source": traffic_note}
     roof_norm = {"bound": "mfma", "achieved": norm_tflops, "peak": mfma_peak, "unit": "TFLOP/s",
                  "frac": norm_tflops / mfma_peak, "traffic": traffic.get("norm"),
-                 "kernel": "dora_factored_norm (norm_main + gram_reduce + norm_finish)",
-                 "algorithmic_flops": F, "hbm_gbs": norm_gbs, "hbm_frac": norm_gbs / HBM_PEAK_GBS}
+                 "kernel": "dora_factored_norm: Gram pass, gram_reduce, W pass, Gram term + assembly "
+                           "(one C-ABI call, timed as a unit)",
+                 "algorithmic_flops": F, "algorithmic_bytes": nb, "hbm_gbs": norm_gbs,
+                 "hbm_frac": norm_gbs / HBM_PEAK_GBS, "traffic_source": traffic_note}
     dominant = roof_compose if comp_ms >= norm_ms else roof_norm
 
     res = {

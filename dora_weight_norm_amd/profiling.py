@@ -1,0 +1,167 @@
+"""Summaries of rocprofv3 runs of bench.py, for the profiles/ folder.
+
+Turns the CSV output of three rocprofv3 runs of the same bench command
+(kernel trace with --stats, then --pmc FETCH_SIZE, then --pmc WRITE_SIZE)
+into
+
+  profiles/<kernel-set>_<workload>.md   per-kernel durations, counters and
+                                        the commands that produced them;
+  profiles/traffic_<workload>.json      measured HBM bytes per norm call and
+                                        per compose call, read by bench.py.
+
+FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch. Each is scaled by
+what the same counter reads for a plain device copy of known size (bench.py
+--copy-calibration runs one of 1 GiB), so that the figures are bytes.
+
+    python -m dora_weight_norm_amd.profiling --workload NAME --kt DIR --fetch DIR --write DIR \
+        --cmd-kt "..." --cmd-fetch "..." --cmd-write "..." [--out profiles]
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CALIB_BYTES = 1 << 30   # bench.py --copy-calibration copies this many bytes
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources: measured traffic is only valid for these."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_role(name: str) -> str | None:
+    """Which part of the hot path a kernel belongs to (None: not ours)."""
+    if "dora::" not in name:
+        return None
+    if "compose_kernel" in name:
+        return "compose"
+    return "norm"
+
+
+def short_name(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("unsigned short", "bf16")
+    n = re.sub(r"\(dora::NormPlan.*$|\(.*$", "", n)
+    n = n.replace("void dora::", "").replace("dora::", "")
+    m = re.match(r"norm_fast_kernel<(.*)>", n)
+    if m:
+        args = [a.strip() for a in m.group(1).split(",")]
+        mode = {"0": "W pass", "1": "Gram pass", "2": "Gram term + assembly"}.get(args[-1], args[-1])
+        n = f"norm_fast_kernel<{', '.join(args)}> ({mode})"
+    return n
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern))
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def read_stats(kt_dir: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(kt_dir, "*kernel_stats.csv")))))
+    out = []
+    for r in rows:
+        out.append({"name": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                    "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+                    "total_us": float(r["TotalDurationNs"]) / 1e3})
+    return out
+
+
+def read_counter(pmc_dir: str, counter: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(pmc_dir, "*counter_collection.csv")))))
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def calibration(per: dict) -> float:
+    """KiB the counter reports for the 1 GiB copy: the largest copy dispatch."""
+    best = 0.0
+    for name, vals in per.items():
+        if "copy" in name and "dora::" not in name:
+            best = max(best, max(vals))
+    if best <= 0:
+        raise RuntimeError("no copy dispatch found for the calibration")
+    return (CALIB_BYTES / 1024.0) / best
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--kt", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--cmd-kt", required=True)
+    ap.add_argument("--cmd-fetch", required=True)
+    ap.add_argument("--cmd-write", required=True)
+    ap.add_argument("--out", default=os.path.join(os.path.dirname(HERE), "profiles"))
+    args = ap.parse_args()
+
+    stats = read_stats(args.kt)
+    fetch = read_counter(args.fetch, "FETCH_SIZE")
+    write = read_counter(args.write, "WRITE_SIZE")
+    f_scale, w_scale = calibration(fetch), calibration(write)
+
+    ours = [s for s in stats if kernel_role(s["name"])]
+    steps = max(s["calls"] for s in ours if kernel_role(s["name"]) == "compose")
+    traffic = {"norm": 0.0, "compose": 0.0}
+    lines = []
+    for s in sorted(ours, key=lambda s: -s["total_us"]):
+        role = kernel_role(s["name"])
+        fk = fetch.get(s["name"], [])
+        wk = write.get(s["name"], [])
+        fb = (sum(fk) / len(fk)) * 1024 * f_scale if fk else float("nan")
+        wb = (sum(wk) / len(wk)) * 1024 * w_scale if wk else float("nan")
+        per_step = s["calls"] / steps
+        if fk and wk:
+            traffic[role] += (fb + wb) * per_step
+        lines.append(f"| {short_name(s['name'])} | {role} | {s['calls']} | {s['avg_us']:.2f} | {s['min_us']:.2f} | "
+                     f"{s['max_us']:.2f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+    norm_us = sum(s["avg_us"] * s["calls"] / steps for s in ours if kernel_role(s["name"]) == "norm")
+    comp_us = sum(s["avg_us"] * s["calls"] / steps for s in ours if kernel_role(s["name"]) == "compose")
+
+    os.makedirs(args.out, exist_ok=True)
+    tj = {"workload": args.workload, "source_hash": source_hash(),
+          "norm_bytes_per_call": traffic["norm"], "compose_bytes_per_call": traffic["compose"],
+          "fetch_scale": f_scale, "write_scale": w_scale,
+          "norm_us_per_call": norm_us, "compose_us_per_call": comp_us,
+          "commands": {"fetch": args.cmd_fetch, "write": args.cmd_write}}
+    with open(os.path.join(args.out, f"traffic_{args.workload}.json"), "w") as f:
+        json.dump(tj, f, indent=1)
+        f.write("\n")
+    md = [f"# Norm and compose kernels, workload {args.workload}", "",
+          "rocprofv3 kernel trace (durations) and two counter passes (HBM bytes) of the same bench.py",
+          "command. Bytes are per dispatch, scaled by the copy calibration below.", "",
+          "| kernel | part | calls | avg µs | min µs | max µs | FETCH MB | WRITE MB |",
+          "|---|---|---|---|---|---|---|---|"] + lines + [
+          "",
+          f"- steps in the trace: {steps}; norm call = sum of its kernels = {norm_us:.2f} µs; "
+          f"compose call = {comp_us:.2f} µs",
+          f"- HBM traffic per norm call: {traffic['norm'] / 1e6:.1f} MB; per compose call: "
+          f"{traffic['compose'] / 1e6:.1f} MB",
+          f"- copy calibration (1 GiB device copy): FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}",
+          f"- HIP sources hash: {tj['source_hash']}", "",
+          "Commands:", "", "```", args.cmd_kt, args.cmd_fetch, args.cmd_write, "```", ""]
+    with open(os.path.join(args.out, f"norm_compose_{args.workload}.md"), "w") as f:
+        f.write("\n".join(md))
+    print("\n".join(md))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
