@@ -58,6 +58,7 @@ __all__ = [
     "compose_naive",
     "compose_f32_stable",
     "compose_f32_naive",
+    "compose_backward",
     "round_to_dtype",
     "table1_memory",
 ]
@@ -228,6 +229,36 @@ def compose(base, lora, g, s):
     lora = _f64(lora)
     g = _f64(g)[None, :]
     return (g - 1.0) * base + g * (s * lora)
+
+
+def compose_backward(dy, base, lora, g, s, wnorm=None, eps=None):
+    """Gradients of the compose delta with respect to base, lora, g (and m).
+
+    The pages describe a fused backward of the compose and report its speed
+    [P1 §4.2, §5.2, §6.1 Table 9] but print no formulas. Reading: the
+    plainest derivative of delta = (g - 1) * base + g * (s * lora), with g a
+    per-column constant for base and lora and the row norm detached (it is
+    not differentiated through), so for L = sum(dy * delta):
+
+        d_base[t,j] = (g[j] - 1) * dy[t,j]
+        d_lora[t,j] = g[j] * s * dy[t,j]
+        dg[j]       = sum_t dy[t,j] * (base[t,j] + s * lora[t,j])
+        dm[j]       = dg[j] / max(wnorm[j], eps)      (g = m / max(wnorm, eps))
+
+    All in fp64. Returns (d_base, d_lora, dg) or, with wnorm, (d_base,
+    d_lora, dg, dm).
+    """
+    dy = _f64(dy)
+    base = _f64(base)
+    lora = _f64(lora)
+    g = _f64(g)
+    gc = g[None, :]
+    d_base = (gc - 1.0) * dy
+    d_lora = gc * (s * dy)
+    dg = np.sum(dy * (base + s * lora), axis=0)
+    if wnorm is None:
+        return d_base, d_lora, dg
+    return d_base, d_lora, dg, dg / np.where(_f64(wnorm) < eps, eps, _f64(wnorm))
 
 
 def compose_naive(base, lora, g, s):

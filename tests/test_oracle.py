@@ -293,6 +293,68 @@ def test_stable_compose_beats_naive_near_one():
     assert e_st < e_nv / 2
 
 
+# ----------------------------------------------------- compose backward ----
+
+def test_compose_backward_matches_finite_differences():
+    """The delta is linear in base, lora and g separately, so central
+    differences of L = sum(dy * delta) are exact up to fp64 rounding."""
+    rng = np.random.default_rng(21)
+    T, d, s = 5, 7, 0.75
+    dy, base, lora = (rng.standard_normal((T, d)) for _ in range(3))
+    g = 1.0 + 0.1 * rng.standard_normal(d)
+    d_base, d_lora, dg = O.compose_backward(dy, base, lora, g, s)
+
+    def loss(b, l, gg):
+        return float(np.sum(dy * O.compose(b, l, gg, s)))
+
+    h = 1e-3
+    for (t, j) in [(0, 0), (2, 3), (4, 6)]:
+        e = np.zeros((T, d))
+        e[t, j] = h
+        fd_b = (loss(base + e, lora, g) - loss(base - e, lora, g)) / (2 * h)
+        fd_l = (loss(base, lora + e, g) - loss(base, lora - e, g)) / (2 * h)
+        assert abs(fd_b - d_base[t, j]) <= 1e-9 and abs(fd_l - d_lora[t, j]) <= 1e-9
+    for j in range(d):
+        e = np.zeros(d)
+        e[j] = h
+        fd_g = (loss(base, lora, g + e) - loss(base, lora, g - e)) / (2 * h)
+        assert abs(fd_g - dg[j]) <= 1e-9 * max(1.0, abs(dg[j]))
+
+
+def test_compose_backward_exact_and_special_cases():
+    rng = np.random.default_rng(22)
+    T, d = 6, 5
+    dy = O.bf16_round(rng.standard_normal((T, d)))
+    base = O.bf16_round(rng.standard_normal((T, d)))
+    lora = O.bf16_round(0.1 * rng.standard_normal((T, d)))
+    g = O.f32_round(1.0 + 0.0015 * rng.standard_normal(d))
+    s = 0.5
+    d_base, d_lora, dg = O.compose_backward(dy, base, lora, g, s)
+    # exact rational arithmetic on the storage values
+    for j in range(d):
+        gj = Fraction(float(g[j]))
+        acc = Fraction(0)
+        for t in range(T):
+            y = Fraction(float(dy[t, j]))
+            assert Fraction(float(d_base[t, j])) == (gj - 1) * y
+            assert Fraction(float(d_lora[t, j])) == gj * Fraction(s) * y
+            acc += y * (Fraction(float(base[t, j])) + Fraction(s) * Fraction(float(lora[t, j])))
+        assert abs(float(acc) - dg[j]) <= 4 * np.finfo(np.float64).eps * float(sum(
+            abs(Fraction(float(dy[t, j]))) * (abs(Fraction(float(base[t, j]))) + abs(Fraction(float(lora[t, j]))))
+            for t in range(T)))
+    # g = 1: no base gradient, lora gradient s * dy
+    d_base1, d_lora1, _ = O.compose_backward(dy, base, lora, np.ones(d), s)
+    assert np.all(d_base1 == 0) and np.array_equal(d_lora1, s * dy)
+    # s = 0: no lora gradient, dg = sum dy * base
+    _, d_lora0, dg0 = O.compose_backward(dy, base, lora, g, 0.0)
+    assert np.all(d_lora0 == 0)
+    np.testing.assert_allclose(dg0, np.sum(dy * base, axis=0), rtol=1e-15)
+    # dm = dg / max(wnorm, eps), and the eps floor
+    wn = np.array([2.0, 0.5, 0.0, 1e-9, 4.0])
+    *_, dm = O.compose_backward(dy, base, lora, g, s, wnorm=wn, eps=1e-6)
+    np.testing.assert_array_equal(dm, dg / np.array([2.0, 0.5, 1e-6, 1e-6, 4.0]))
+
+
 # ------------------------------------------------------ planted mistakes ----
 
 def test_pins_reject_planted_mistakes():
@@ -339,3 +401,42 @@ def test_pins_reject_planted_mistakes():
     assert compose_ok(O.compose)
     for name, fn in compose_mutants.items():
         assert not compose_ok(fn), name
+
+    # The compose backward: finite differences of the forward oracle catch
+    # each planted mistake.
+    dy = rng.standard_normal((3, 4))
+    b3, l3 = rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
+    g3 = 1.0 + 0.1 * rng.standard_normal(4)
+
+    def backward_ok(fn):
+        d_base, d_lora, dg = fn(dy, b3, l3, g3, 0.75)
+        h = 1e-3
+
+        def loss(b, l, g):
+            return float(np.sum(dy * O.compose(b, l, g, 0.75)))
+        e = np.zeros((3, 4))
+        e[1, 2] = h
+        ok = abs((loss(b3 + e, l3, g3) - loss(b3 - e, l3, g3)) / (2 * h) - d_base[1, 2]) < 1e-9
+        ok &= abs((loss(b3, l3 + e, g3) - loss(b3, l3 - e, g3)) / (2 * h) - d_lora[1, 2]) < 1e-9
+        eg = np.zeros(4)
+        eg[3] = h
+        ok &= abs((loss(b3, l3, g3 + eg) - loss(b3, l3, g3 - eg)) / (2 * h) - dg[3]) < 1e-9
+        return bool(ok)
+
+    def mut(kind):
+        def fn(dy, b, l, g, s):
+            d_base, d_lora, dg = O.compose_backward(dy, b, l, g, s)
+            if kind == "g instead of g-1":
+                d_base = g[None] * dy
+            elif kind == "dropped s on lora":
+                d_lora = g[None] * dy
+            elif kind == "dg without lora":
+                dg = np.sum(dy * b, axis=0)
+            elif kind == "dg over the wrong axis":
+                dg = np.sum(dy * (b + s * l), axis=1)[: len(g)]
+            return d_base, d_lora, dg
+        return fn
+
+    assert backward_ok(O.compose_backward)
+    for kind in ("g instead of g-1", "dropped s on lora", "dg without lora", "dg over the wrong axis"):
+        assert not backward_ok(mut(kind)), kind
