@@ -432,11 +432,11 @@ def test_pins_reject_planted_mistakes():
                 d_lora = g[None] * dy
             elif kind == "dg without lora":
                 dg = np.sum(dy * b, axis=0)
-            elif kind == "dg over the wrong axis":
-                dg = np.sum(dy * (b + s * l), axis=1)[: len(g)]
+            elif kind == "s on base in dg":
+                dg = np.sum(dy * (l + s * b), axis=0)
             return d_base, d_lora, dg
         return fn
 
     assert backward_ok(O.compose_backward)
-    for kind in ("g instead of g-1", "dropped s on lora", "dg without lora", "dg over the wrong axis"):
+    for kind in ("g instead of g-1", "dropped s on lora", "dg without lora", "s on base in dg"):
         assert not backward_ok(mut(kind)), kind
