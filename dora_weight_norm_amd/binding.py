@@ -31,6 +31,8 @@ __all__ = [
     "DORA_BF16",
     "DORA_F32",
     "PLAN_FIELDS",
+    "dora_compose_backward",
+    "dora_compose_backward_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdora.so")
@@ -82,6 +84,9 @@ def load():
                                       _c_p, _c_p, _c_f, _c_p, _c_p]),
         "dora_magnitude_scale": (_c_i, [_c_p, _c_p, _c_f, _c_i64, _c_p, _c_p]),
         "dora_compose": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
+        "dora_compose_backward_workspace_size": (_c_i, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+        "dora_compose_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p, _c_p,
+                                         _c_p, _c_f, _c_p, _c_p, _c_sz, _c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -218,3 +223,50 @@ def dora_compose(base, lora, g, s: float, out=None, stream=None):
             raise ValueError("out must match base")
     _call("dora_compose", _ptr(base), _ptr(lora), _ptr(g), s, dt, T, d_out, _ptr(out), _stream(stream))
     return out
+
+
+def dora_compose_backward_workspace_size(T: int, d_out: int) -> int:
+    ws = _c_sz()
+    _call("dora_compose_backward_workspace_size", T, d_out, ctypes.byref(ws))
+    return ws.value
+
+
+def dora_compose_backward(dy, base, lora, g, s: float, need_dg: bool = True, wnorm=None, eps: float = 1e-6,
+                          d_base=None, d_lora=None, workspace=None, stream=None):
+    """Gradients of delta = (g - 1) * base + g * (s * lora), the row norm detached.
+
+    Returns (d_base, d_lora, dg, dm): d_base and d_lora like dy; dg fp32
+    [d_out] (None when need_dg is False: the magnitude is frozen, base and
+    lora are then not read and may be None); dm = dg / max(wnorm, eps) when
+    wnorm is given.
+    """
+    _dev(dy, "dy")
+    _dev(g, "g")
+    if dy.dim() != 2:
+        raise ValueError("dy must be [T, d_out]")
+    T, d_out = dy.shape
+    if g.dtype != torch.float32 or g.shape != (d_out,):
+        raise ValueError("g must be float32 [d_out]")
+    if need_dg:
+        for t, nm in ((base, "base"), (lora, "lora")):
+            _dev(t, nm)
+            if t.shape != dy.shape or t.dtype != dy.dtype:
+                raise ValueError(f"{nm} must match dy")
+    if wnorm is not None:
+        if not need_dg:
+            raise ValueError("dm needs dg")
+        _dev(wnorm, "wnorm")
+        if wnorm.dtype != torch.float32 or wnorm.shape != (d_out,):
+            raise ValueError("wnorm must be float32 [d_out]")
+    dt = _dtype_code(dy.dtype)
+    d_base = torch.empty_like(dy) if d_base is None else d_base
+    d_lora = torch.empty_like(dy) if d_lora is None else d_lora
+    dg = torch.empty(d_out, dtype=torch.float32, device=dy.device) if need_dg else None
+    dm = torch.empty(d_out, dtype=torch.float32, device=dy.device) if wnorm is not None else None
+    ws_bytes = dora_compose_backward_workspace_size(T, d_out) if need_dg else 0
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dy.device)
+    _call("dora_compose_backward", _ptr(dy), _ptr(base if need_dg else None), _ptr(lora if need_dg else None),
+          _ptr(g), s, dt, T, d_out, _ptr(d_base), _ptr(d_lora), _ptr(dg), _ptr(wnorm), eps, _ptr(dm),
+          _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream))
+    return d_base, d_lora, dg, dm

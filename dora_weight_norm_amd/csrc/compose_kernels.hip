@@ -3,6 +3,10 @@
 //   out[t,j] = (g[j] - 1) * base[t,j] + g[j] * (s * lora[t,j])
 //
 // ("DoRA优化技术解析：从内存瓶颈到高效实现", cyqw.cn, §2.1, §2.1.1, §5.2.)
+// The backward of the same map (the row norm detached) is below: d_base,
+// d_lora and, unless the magnitude is frozen, dg by a deterministic
+// two-stage column reduction.
+//
 // One HBM pass: base and lora are streamed once, out written once, g read
 // once per thread into registers. Each thread owns one 16-byte column strip
 // (8 bf16 or 4 fp32 columns) and walks rows with a stride of the grid's
@@ -130,6 +134,143 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Compose backward. For L = sum(dy * delta) with delta as above and the row
+// norm detached ("DoRA优化技术解析", cyqw.cn, §4.2, §5.2, §6.1 Table 9 report
+// this fused backward; its formulas are the plain derivative):
+//   d_base[t,j] = (g[j] - 1) * dy[t,j]
+//   d_lora[t,j] = g[j] * (s * dy[t,j])
+//   dg[j]       = sum_t dy[t,j] * (base[t,j] + s * lora[t,j])
+// Each thread owns one 16-byte column strip and a fixed set of rows, as in
+// the forward; with DG it also accumulates its rows' dg terms in fp32
+// (fma(dy, fma(s, lora, base), acc), rows in increasing order) and stores
+// one partial per (row block, column). A second kernel adds the row-block
+// partials in increasing order, so dg is reproducible; no float atomics.
+// With the magnitude frozen (no dg), base and lora are not read at all.
+// ---------------------------------------------------------------------------
+constexpr int kBwdMaxRowBlocks = 256;
+
+template <typename T, int VEC, bool DG>
+__global__ __launch_bounds__(256) void compose_bwd_kernel(const T* dy, const T* base, const T* lora,
+                                                          const float* __restrict__ g, float s, int64_t T_rows,
+                                                          int64_t d_out, T* d_base, T* d_lora, float* part) {
+  using V = typename Strip<T, VEC>::V;
+  const int64_t cg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (cg >= d_out / VEC) return;
+  const int64_t c0 = cg * VEC;
+  float gv[VEC], gm1[VEC], acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    gv[e] = g[c0 + e];
+    gm1[e] = gv[e] - 1.0f;
+    acc[e] = 0.f;
+  }
+  const int64_t step = (int64_t)gridDim.y * kUnroll;
+  for (int64_t t0 = (int64_t)blockIdx.y * kUnroll; t0 < T_rows; t0 += step) {
+    V yv[kUnroll], bv[kUnroll], lv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t0 + u < T_rows) {
+        const int64_t off = (t0 + u) * d_out + c0;
+        yv[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(dy + off));
+        if constexpr (DG) {
+          bv[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(base + off));
+          lv[u] = __builtin_nontemporal_load(reinterpret_cast<const V*>(lora + off));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (t0 + u < T_rows) {
+        float y[VEC], ob[VEC], ol[VEC];
+        unpack<T, VEC>(yv[u], y);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          ob[e] = gm1[e] * y[e];
+          ol[e] = gv[e] * (s * y[e]);
+        }
+        if constexpr (DG) {
+          float b[VEC], l[VEC];
+          unpack<T, VEC>(bv[u], b);
+          unpack<T, VEC>(lv[u], l);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] = fmaf(y[e], fmaf(s, l[e], b[e]), acc[e]);
+        }
+        const int64_t off = (t0 + u) * d_out + c0;
+        if (d_base != nullptr) __builtin_nontemporal_store(pack<T, VEC>(ob), reinterpret_cast<V*>(d_base + off));
+        if (d_lora != nullptr) __builtin_nontemporal_store(pack<T, VEC>(ol), reinterpret_cast<V*>(d_lora + off));
+      }
+    }
+  }
+  if constexpr (DG) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) part[(int64_t)blockIdx.y * d_out + c0 + e] = acc[e];
+  }
+}
+
+// dg[j] = sum of the row-block partials in increasing order; optionally
+// dm[j] = dg[j] / max(wnorm[j], eps) (correctly rounded division).
+__global__ __launch_bounds__(256) void compose_bwd_reduce_kernel(const float* part, int n_part, int64_t d_out,
+                                                                 float* dg, const float* wnorm, float eps,
+                                                                 float* dm) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= d_out) return;
+  float acc = 0.f;
+  for (int y = 0; y < n_part; ++y) acc += part[(int64_t)y * d_out + j];
+  dg[j] = acc;
+  if (dm != nullptr) {
+    const float wn = wnorm[j];
+    const float d = (wn < eps) ? eps : wn;
+    dm[j] = acc / d;
+  }
+}
+
+// Launch shape shared by the compose kernels: one thread per 16-byte strip,
+// about 8 resident workgroups per compute unit, at most max_by row blocks.
+struct Grid2 {
+  int64_t tpb, bx, by;
+};
+Grid2 strip_grid(int64_t T_rows, int64_t d_out, int vec, int64_t max_by) {
+  const int64_t ncg = d_out / vec;
+  int64_t tpb = ((ncg + 63) / 64) * 64;
+  if (tpb > 256) tpb = 256;
+  if (tpb < 64) tpb = 64;
+  const int64_t bx = (ncg + tpb - 1) / tpb;
+  int64_t by = 2048 / (bx > 0 ? bx : 1);
+  if (by < 1) by = 1;
+  const int64_t row_iters = (T_rows + kUnroll - 1) / kUnroll;
+  if (by > row_iters) by = row_iters;
+  if (by > max_by) by = max_by;
+  return Grid2{tpb, bx, by};
+}
+
+template <typename T, int VEC>
+hipError_t launch_bwd(const void* dy, const void* base, const void* lora, const float* g, float s, int64_t T_rows,
+                      int64_t d_out, void* d_base, void* d_lora, float* dg, const float* wnorm, float eps, float* dm,
+                      float* part, hipStream_t st) {
+  const Grid2 q = strip_grid(T_rows, d_out, VEC, kBwdMaxRowBlocks);
+  if (q.by > 0 && q.bx > 0) {
+    if (dg != nullptr)
+      hipLaunchKernelGGL((compose_bwd_kernel<T, VEC, true>), dim3((unsigned)q.bx, (unsigned)q.by),
+                         dim3((unsigned)q.tpb), 0, st, static_cast<const T*>(dy), static_cast<const T*>(base),
+                         static_cast<const T*>(lora), g, s, T_rows, d_out, static_cast<T*>(d_base),
+                         static_cast<T*>(d_lora), part);
+    else
+      hipLaunchKernelGGL((compose_bwd_kernel<T, VEC, false>), dim3((unsigned)q.bx, (unsigned)q.by),
+                         dim3((unsigned)q.tpb), 0, st, static_cast<const T*>(dy), static_cast<const T*>(base),
+                         static_cast<const T*>(lora), g, s, T_rows, d_out, static_cast<T*>(d_base),
+                         static_cast<T*>(d_lora), part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dg != nullptr) {
+    hipLaunchKernelGGL(compose_bwd_reduce_kernel, dim3((unsigned)((d_out + 255) / 256)), dim3(256), 0, st, part,
+                       (int)q.by, d_out, dg, wnorm, eps, dm);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
@@ -140,6 +281,25 @@ hipError_t launch_compose(const void* base, const void* lora, const float* g, fl
   }
   return vec ? launch<float, 4>(base, lora, g, s, T, d_out, out, st)
              : launch<float, 1>(base, lora, g, s, T, d_out, out, st);
+}
+
+size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out) {
+  // Row blocks never exceed this for any strip width (see strip_grid).
+  int64_t by = (T + kUnroll - 1) / kUnroll;
+  if (by > kBwdMaxRowBlocks) by = kBwdMaxRowBlocks;
+  return (size_t)(by * d_out) * 4;
+}
+
+hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora, const float* g, float s, int dtype,
+                              int64_t T, int64_t d_out, void* d_base, void* d_lora, float* dg, const float* wnorm,
+                              float eps, float* dm, void* ws, bool vec, hipStream_t st) {
+  float* part = static_cast<float*>(ws);
+  if (dtype == 0) {
+    return vec ? launch_bwd<bf16_t, 8>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st)
+               : launch_bwd<bf16_t, 1>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st);
+  }
+  return vec ? launch_bwd<float, 4>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st)
+             : launch_bwd<float, 1>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st);
 }
 
 }  // namespace dora

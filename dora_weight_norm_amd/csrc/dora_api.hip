@@ -360,4 +360,57 @@ dora_status dora_compose(const void* base, const void* lora, const float* g, flo
       dora::launch_compose(base, lora, g, s, dtype, T, d_out, out, vec, static_cast<hipStream_t>(stream)));
 }
 
+dora_status dora_compose_backward_workspace_size(int64_t T, int64_t d_out, size_t* ws_bytes) {
+  if (ws_bytes == nullptr || T < 0 || d_out < 0 || T >= kMaxDim * 64 || d_out >= kMaxDim) return DORA_ERR_INVALID_ARG;
+  *ws_bytes = dora::compose_bwd_workspace_bytes(T, d_out);
+  return DORA_OK;
+}
+
+dora_status dora_compose_backward(const void* dy, const void* base, const void* lora, const float* g, float s,
+                                  int dtype, int64_t T, int64_t d_out, void* d_base, void* d_lora, float* dg,
+                                  const float* wnorm, float eps, float* dm, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;
+  if (T < 0 || d_out < 0 || T >= kMaxDim * 64 || d_out >= kMaxDim || !isfinite(s)) return DORA_ERR_INVALID_ARG;
+  if (dm != nullptr && (dg == nullptr || wnorm == nullptr || !isfinite(eps) || !(eps > 0.0f)))
+    return DORA_ERR_INVALID_ARG;
+  if (d_out == 0) return DORA_OK;
+  const bool need_rows = T > 0 && (d_base != nullptr || d_lora != nullptr || dg != nullptr);
+  if (g == nullptr || !aligned(g, 4)) return DORA_ERR_INVALID_ARG;
+  if (need_rows && dy == nullptr) return DORA_ERR_INVALID_ARG;
+  if (dg != nullptr && T > 0 && (base == nullptr || lora == nullptr)) return DORA_ERR_INVALID_ARG;
+  const int64_t es = esize(dtype);
+  const void* elems[] = {dy, dg ? base : nullptr, dg ? lora : nullptr, d_base, d_lora};
+  for (const void* p : elems)
+    if (p != nullptr && !aligned(p, (size_t)es)) return DORA_ERR_INVALID_ARG;
+  if (!aligned(dg, 4) || !aligned(dm, 4) || !aligned(wnorm, 4)) return DORA_ERR_INVALID_ARG;
+  // Outputs overlap no input and no other output.
+  const int64_t nE = T * d_out * es, nV = d_out * 4;
+  const void* ins[] = {dy, dg ? base : nullptr, dg ? lora : nullptr, g, wnorm};
+  const int64_t nin[] = {nE, nE, nE, nV, nV};
+  const void* outs[] = {d_base, d_lora, dg, dm};
+  const int64_t nout[] = {nE, nE, nV, nV};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlap(outs[o], nout[o], ins[i], nin[i])) return DORA_ERR_INVALID_ARG;
+    for (int o2 = o + 1; o2 < 4; ++o2)
+      if (overlap(outs[o], nout[o], outs[o2], nout[o2])) return DORA_ERR_INVALID_ARG;
+  }
+  const size_t need = dora::compose_bwd_workspace_bytes(T, d_out);
+  if (dg != nullptr && need > 0) {
+    if (workspace_bytes < need) return DORA_ERR_WORKSPACE;
+    if (workspace == nullptr || !aligned(workspace, kAlign)) return DORA_ERR_WORKSPACE;
+    for (int o = 0; o < 4; ++o)
+      if (overlap(workspace, (int64_t)need, outs[o], nout[o])) return DORA_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i)
+      if (overlap(workspace, (int64_t)need, ins[i], nin[i])) return DORA_ERR_INVALID_ARG;
+  }
+  if (!need_rows && dg == nullptr) return DORA_OK;
+  bool vec = (d_out % epc(dtype)) == 0;
+  for (const void* p : elems)
+    if (p != nullptr && !aligned(p, 16)) vec = false;
+  return hip_status(dora::launch_compose_bwd(dy, base, lora, g, s, dtype, T, d_out, d_base, d_lora, dg, wnorm, eps,
+                                             dm, workspace, vec, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -18,6 +18,7 @@ write-ups: d_in = 8192 at r = 384, the 8192 x 28672 MLP shape, KV d_out =
     base  ~ N(0, 1)             lora ~ N(0, 0.1^2)
     m_noise ~ N(0, 1)   (the magnitude is m = wnorm * (1 + 0.0015 m_noise);
                          the product with wnorm is left to the caller)
+    dy    ~ N(0, 1)             an upstream gradient for the compose backward
     g     = fp32(1 + 0.0015 N(0, 1))  for compose-only runs
 """
 
@@ -37,12 +38,13 @@ __all__ = [
     "norm_inputs",
     "compose_inputs",
     "m_noise",
+    "grad_inputs",
 ]
 
 MiB = 1 << 20
 
 # Stream ids, one per tensor.
-STREAMS = {"W": 0, "A": 1, "B": 2, "m_noise": 3, "base": 4, "lora": 5, "g": 6}
+STREAMS = {"W": 0, "A": 1, "B": 2, "m_noise": 3, "base": 4, "lora": 5, "g": 6, "dy": 7, "wnorm": 8}
 
 G_SPREAD = 0.0015      # std of the magnitude scale g around 1
 B_STD = 0.02
@@ -130,3 +132,11 @@ def compose_inputs(T: int, d_out: int, dtype: str, seed: int):
     lora = to_storage(normal(seed, "lora", (T, d_out), LORA_STD), dtype)
     g = normal(seed, "g", (d_out,), G_SPREAD, 1.0).astype(np.float32)
     return base, lora, g
+
+
+def grad_inputs(T: int, d_out: int, dtype: str, seed: int):
+    """dy [T, d_out] (storage values) for the compose backward, plus a
+    positive fp32 stand-in row norm wnorm = 1 + |N(0,1)| for dm."""
+    dy = to_storage(normal(seed, "dy", (T, d_out)), dtype)
+    wnorm = (1.0 + np.abs(normal(seed, "wnorm", (d_out,)))).astype(np.float32)
+    return dy, wnorm

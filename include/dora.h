@@ -14,7 +14,11 @@
  *                       §1.2.2);
  *   dora_compose        the stable magnitude compose
  *                       (g - 1) * base + g * (s * lora) in one pass
- *                       (same page, §2.1, §2.1.1, §5.2).
+ *                       (same page, §2.1, §2.1.1, §5.2);
+ *   dora_compose_backward
+ *                       its gradients d_base, d_lora and dg (dm) in one
+ *                       pass plus a deterministic column reduction (same
+ *                       page, §4.2, §5.2, §6.1 Table 9).
  *
  * Conventions shared by every entry point:
  *   - Matrices are dense, row-major and contiguous. Layouts follow LoRA:
@@ -169,6 +173,43 @@ dora_status dora_magnitude_scale(const float* m, const float* wnorm, float eps,
  */
 dora_status dora_compose(const void* base, const void* lora, const float* g, float s,
                          int dtype, int64_t T, int64_t d_out, void* out, void* stream);
+
+/*
+ * Workspace bytes dora_compose_backward needs to produce dg for a [T, d_out]
+ * problem (at most 256 * d_out * 4). Host only. DORA_ERR_INVALID_ARG for
+ * negative sizes or ws_bytes == NULL.
+ */
+dora_status dora_compose_backward_workspace_size(int64_t T, int64_t d_out, size_t* ws_bytes);
+
+/*
+ * Backward of the stable compose (cyqw.cn §4.2, §5.2, §6.1 Table 9 report
+ * this fused backward; its formulas are the plain derivative of
+ * delta = (g - 1) * base + g * (s * lora) with the row norm detached):
+ *
+ *   d_base[t,j] = (g[j] - 1) * dy[t,j]               (fp32, RNE to dtype)
+ *   d_lora[t,j] = g[j] * (s * dy[t,j])               (fp32, RNE to dtype)
+ *   dg[j]       = sum_t dy[t,j] * (base[t,j] + s * lora[t,j])     (fp32)
+ *   dm[j]       = dg[j] / max(wnorm[j], eps)   (g = m / max(wnorm, eps))
+ *
+ * dy, base, lora, d_base, d_lora: device [T, d_out] row-major of `dtype`.
+ * g, wnorm, dg, dm: fp32 [d_out] device arrays. Any of d_base, d_lora, dg
+ * may be NULL to skip that output; with dg == NULL (magnitude frozen) base
+ * and lora are not read and may be NULL. dm requires dg, wnorm and eps > 0.
+ * dg is summed in fp32 in a fixed order (each thread's rows in increasing
+ * order, then row blocks in increasing order): reproducible for a fixed
+ * shape, no atomics. Outputs overlap no input and no other output.
+ * `workspace` (256-byte aligned, dora_compose_backward_workspace_size bytes)
+ * is needed only when dg != NULL; its contents on entry are ignored.
+ * Asynchronous on `stream`.
+ *
+ * Errors: DORA_ERR_INVALID_ARG (negative size, non-finite s, bad eps,
+ * missing or misaligned pointer, overlapping buffers),
+ * DORA_ERR_UNSUPPORTED_DTYPE, DORA_ERR_WORKSPACE, DORA_ERR_HIP.
+ */
+dora_status dora_compose_backward(const void* dy, const void* base, const void* lora, const float* g,
+                                  float s, int dtype, int64_t T, int64_t d_out, void* d_base,
+                                  void* d_lora, float* dg, const float* wnorm, float eps, float* dm,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }
