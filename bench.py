@@ -6,12 +6,15 @@ compose, over one batch of synthetic inputs already resident in HBM.
 Default workload: d_out = d_in = 8192, r = 384, s = 0.5, bf16, compose over
 T = 8192 rows (batch 2 x seq 4096).
 
+The fused compose backward (d_base, d_lora, dg, dm) is timed after the
+steps, on its own, and reported under "compose_backward".
+
 Prints one JSON line. `value` is the factored norm's algorithmic TFLOP/s;
 the compose's GB/s and fraction of HBM peak, per-call times and the
 roofline objects ride in the same line. Kernel times come from HIP events
 recorded on the stream the kernels run on.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-backward]
 """
 
 from __future__ import annotations
@@ -46,6 +49,12 @@ def norm_bytes(d_out, d_in, r, esize):
 def compose_bytes(T, d_out, esize):
     """base and lora read, out written; g read once (fp32)."""
     return 3 * T * d_out * esize + 4 * d_out
+
+
+def compose_bwd_bytes(T, d_out, esize, dm=True):
+    """dy, base and lora read, d_base and d_lora written; g read and dg
+    written (fp32); with the magnitude trained also wnorm read, dm written."""
+    return 5 * T * d_out * esize + (16 if dm else 8) * d_out
 
 
 def cpu_baseline(w, W, A, B, base, lora, g_host):
@@ -85,6 +94,53 @@ def cpu_baseline(w, W, A, B, base, lora, g_host):
     }
 
 
+def time_compose_backward(args, w, lib, bnd, I, based, lorad, g, wnorm, stream, tdt, esize):
+    """The fused compose backward, timed on its own after the forward steps
+    (it is not part of a forward step): d_base, d_lora, dg and dm over the
+    same T x d_out batch, with dy drawn like the other inputs."""
+    import numpy as np
+    import torch
+
+    P = ctypes.c_void_p
+    dy_h, _ = I.grad_inputs(w.T, w.d_out, w.dtype, w.seed)
+    dy = torch.from_numpy(dy_h).cuda().to(tdt)
+    del dy_h
+    d_base, d_lora = torch.empty_like(dy), torch.empty_like(dy)
+    dg = torch.empty(w.d_out, dtype=torch.float32, device="cuda")
+    dm = torch.empty_like(dg)
+    ws_bytes = bnd.dora_compose_backward_workspace_size(w.T, w.d_out)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    dt = bnd._dtype_code(w.dtype)
+    a = (P(dy.data_ptr()), P(based.data_ptr()), P(lorad.data_ptr()), P(g.data_ptr()), w.s, dt, w.T, w.d_out,
+         P(d_base.data_ptr()), P(d_lora.data_ptr()), P(dg.data_ptr()), P(wnorm.data_ptr()), w.eps,
+         P(dm.data_ptr()), P(ws.data_ptr()), ws_bytes, P(stream.cuda_stream))
+
+    def run():
+        st = lib.dora_compose_backward(*a)
+        if st:
+            raise bnd.DoraError("dora_compose_backward", st)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    print(f"# timing {K} compose backward calls", file=sys.stderr, flush=True)
+    for k in range(K):
+        ev[k][0].record(stream)
+        run()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    times = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms = float(np.mean(times))
+    nb = compose_bwd_bytes(w.T, w.d_out, esize)
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"ms": ms, "median_ms": float(np.median(times)), "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": nb, "workspace_bytes": ws_bytes,
+            "note": "d_base, d_lora, dg and dm in one C-ABI call (row-strip kernel + fixed-order column "
+                    "reduction); timed separately, not part of the forward step"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +148,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline_8192x8192_r384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the separately timed compose backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling profiler byte counters)")
     ap.add_argument("--traffic", default=None,
@@ -178,6 +236,8 @@ def main() -> int:
     wall = time.perf_counter() - t0
     norm_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
     comp_ms = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]))
+    norm_med = float(np.median([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
+    comp_med = float(np.median([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]))
     span_ms = ev[0][0].elapsed_time(ev[K - 1][2])
     ms_per_step = span_ms / K
 
@@ -199,7 +259,8 @@ def main() -> int:
         with open(tpath) as f:
             tj = json.load(f)
         if tj.get("source_hash") == prof.source_hash():
-            traffic = {"norm": tj["norm_bytes_per_call"], "compose": tj["compose_bytes_per_call"]}
+            traffic = {"norm": tj["norm_bytes_per_call"], "compose": tj["compose_bytes_per_call"],
+                       "compose_bwd": tj.get("compose_bwd_bytes_per_call") or None}
             traffic_note = os.path.relpath(tpath, ROOT)
         else:
             traffic_note = "kernels changed since the counters in " + os.path.relpath(tpath, ROOT)
@@ -231,9 +292,11 @@ def main() -> int:
         "config": {"workload": w.name, "d_out": w.d_out, "d_in": w.d_in, "r": w.r, "s": w.s, "T": w.T,
                    "budget_MiB": w.budget >> 20, "parallelism": "single-gpu"},
         "norm_ms": norm_ms,
+        "norm_median_ms": norm_med,
         "norm_tflops": norm_tflops,
         "norm_gbs": norm_gbs,
         "compose_ms": comp_ms,
+        "compose_median_ms": comp_med,
         "compose_gbs": comp_gbs,
         "compose_hbm_frac": comp_gbs / HBM_PEAK_GBS,
         "wall_ms_per_step": wall / K * 1e3,
@@ -242,6 +305,10 @@ def main() -> int:
         "roofline_compose": roof_compose,
         "plan": bnd.dora_norm_plan_info(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget),
     }
+    if not args.no_backward:
+        res["compose_backward"] = time_compose_backward(args, w, lib, bnd, I, based, lorad, g, wnorm, stream,
+                                                        tdt, esize)
+        res["compose_backward"]["traffic"] = traffic.get("compose_bwd")
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, W, A, B, base, lora, g.cpu().numpy())

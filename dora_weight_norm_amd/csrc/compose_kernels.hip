@@ -145,7 +145,7 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
 // the forward; with DG it also accumulates its rows' dg terms in fp32
 // (fma(dy, fma(s, lora, base), acc), rows in increasing order) and stores
 // one partial per (row block, column). A second kernel adds the row-block
-// partials in increasing order, so dg is reproducible; no float atomics.
+// partials in a fixed order, so dg is reproducible; no float atomics.
 // With the magnitude frozen (no dg), base and lora are not read at all.
 // ---------------------------------------------------------------------------
 constexpr int kBwdMaxRowBlocks = 256;
@@ -208,20 +208,50 @@ __global__ __launch_bounds__(256) void compose_bwd_kernel(const T* dy, const T* 
   }
 }
 
-// dg[j] = sum of the row-block partials in increasing order; optionally
-// dm[j] = dg[j] / max(wnorm[j], eps) (correctly rounded division).
+// dg[j] = sum of the row-block partials; optionally dm[j] = dg[j] /
+// max(wnorm[j], eps) (correctly rounded division). One workgroup owns 64
+// columns; its four waves each sum a contiguous quarter of the row blocks in
+// increasing order (loads issued kBwdBatch at a time, added in order), then
+// wave 0 adds the four quarter sums in order. The order is fixed by n_part
+// alone, so dg is reproducible.
+constexpr int kBwdCols = 64;
+constexpr int kBwdSplit = 4;
+constexpr int kBwdBatch = 8;
+
 __global__ __launch_bounds__(256) void compose_bwd_reduce_kernel(const float* part, int n_part, int64_t d_out,
                                                                  float* dg, const float* wnorm, float eps,
                                                                  float* dm) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= d_out) return;
+  __shared__ float red[kBwdSplit][kBwdCols];
+  const int c = threadIdx.x % kBwdCols;
+  const int q = threadIdx.x / kBwdCols;
+  const int64_t j = (int64_t)blockIdx.x * kBwdCols + c;
+  const bool live = j < d_out;
+  const int y0 = (int)(((int64_t)n_part * q) / kBwdSplit);
+  const int y1 = (int)(((int64_t)n_part * (q + 1)) / kBwdSplit);
   float acc = 0.f;
-  for (int y = 0; y < n_part; ++y) acc += part[(int64_t)y * d_out + j];
-  dg[j] = acc;
+  if (live) {
+    const float* col = part + j;
+    int y = y0;
+    for (; y + kBwdBatch <= y1; y += kBwdBatch) {
+      float v[kBwdBatch];
+#pragma unroll
+      for (int u = 0; u < kBwdBatch; ++u) v[u] = col[(int64_t)(y + u) * d_out];
+#pragma unroll
+      for (int u = 0; u < kBwdBatch; ++u) acc += v[u];
+    }
+    for (; y < y1; ++y) acc += col[(int64_t)y * d_out];
+  }
+  red[q][c] = acc;
+  __syncthreads();
+  if (q != 0 || !live) return;
+  float tot = red[0][c];
+#pragma unroll
+  for (int k = 1; k < kBwdSplit; ++k) tot += red[k][c];
+  dg[j] = tot;
   if (dm != nullptr) {
     const float wn = wnorm[j];
     const float d = (wn < eps) ? eps : wn;
-    dm[j] = acc / d;
+    dm[j] = tot / d;
   }
 }
 
@@ -264,7 +294,8 @@ hipError_t launch_bwd(const void* dy, const void* base, const void* lora, const 
     if (e != hipSuccess) return e;
   }
   if (dg != nullptr) {
-    hipLaunchKernelGGL(compose_bwd_reduce_kernel, dim3((unsigned)((d_out + 255) / 256)), dim3(256), 0, st, part,
+    hipLaunchKernelGGL(compose_bwd_reduce_kernel, dim3((unsigned)((d_out + kBwdCols - 1) / kBwdCols)),
+                       dim3(kBwdCols * kBwdSplit), 0, st, part,
                        (int)q.by, d_out, dg, wnorm, eps, dm);
     return hipGetLastError();
   }

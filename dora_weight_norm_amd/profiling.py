@@ -6,8 +6,9 @@ into
 
   profiles/<kernel-set>_<workload>.md   per-kernel durations, counters and
                                         the commands that produced them;
-  profiles/traffic_<workload>.json      measured HBM bytes per norm call and
-                                        per compose call, read by bench.py.
+  profiles/traffic_<workload>.json      measured HBM bytes per norm call, per
+                                        compose call and per compose backward
+                                        call, read by bench.py.
 
 FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch. Each is scaled by
 what the same counter reads for a plain device copy of known size (bench.py
@@ -45,6 +46,8 @@ def kernel_role(name: str) -> str | None:
     """Which part of the hot path a kernel belongs to (None: not ours)."""
     if "dora::" not in name:
         return None
+    if "compose_bwd" in name:
+        return "compose_bwd"
     if "compose_kernel" in name:
         return "compose"
     return "norm"
@@ -118,8 +121,14 @@ def main() -> int:
     f_scale, w_scale = calibration(fetch), calibration(write)
 
     ours = [s for s in stats if kernel_role(s["name"])]
-    steps = max(s["calls"] for s in ours if kernel_role(s["name"]) == "compose")
-    traffic = {"norm": 0.0, "compose": 0.0}
+    # Calls of each part: every kernel of a part runs at least once per call,
+    # so the least-called kernel of the part counts its calls.
+    part_calls = {}
+    for s in ours:
+        role = kernel_role(s["name"])
+        part_calls[role] = min(part_calls.get(role, s["calls"]), s["calls"])
+    steps = part_calls["compose"]
+    traffic = {"norm": 0.0, "compose": 0.0, "compose_bwd": 0.0}
     lines = []
     for s in sorted(ours, key=lambda s: -s["total_us"]):
         role = kernel_role(s["name"])
@@ -127,19 +136,23 @@ def main() -> int:
         wk = write.get(s["name"], [])
         fb = (sum(fk) / len(fk)) * 1024 * f_scale if fk else float("nan")
         wb = (sum(wk) / len(wk)) * 1024 * w_scale if wk else float("nan")
-        per_step = s["calls"] / steps
+        per_step = s["calls"] / part_calls[role]
         if fk and wk:
             traffic[role] += (fb + wb) * per_step
         lines.append(f"| {short_name(s['name'])} | {role} | {s['calls']} | {s['avg_us']:.2f} | {s['min_us']:.2f} | "
                      f"{s['max_us']:.2f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
-    norm_us = sum(s["avg_us"] * s["calls"] / steps for s in ours if kernel_role(s["name"]) == "norm")
-    comp_us = sum(s["avg_us"] * s["calls"] / steps for s in ours if kernel_role(s["name"]) == "compose")
+    def part_us(role):
+        return sum(s["avg_us"] * s["calls"] / part_calls[role] for s in ours if kernel_role(s["name"]) == role)
+
+    norm_us, comp_us = part_us("norm"), part_us("compose")
+    bwd_us = part_us("compose_bwd") if "compose_bwd" in part_calls else 0.0
 
     os.makedirs(args.out, exist_ok=True)
     tj = {"workload": args.workload, "source_hash": source_hash(),
           "norm_bytes_per_call": traffic["norm"], "compose_bytes_per_call": traffic["compose"],
           "fetch_scale": f_scale, "write_scale": w_scale,
-          "norm_us_per_call": norm_us, "compose_us_per_call": comp_us,
+          "compose_bwd_bytes_per_call": traffic["compose_bwd"],
+          "norm_us_per_call": norm_us, "compose_us_per_call": comp_us, "compose_bwd_us_per_call": bwd_us,
           "commands": {"fetch": args.cmd_fetch, "write": args.cmd_write}}
     with open(os.path.join(args.out, f"traffic_{args.workload}.json"), "w") as f:
         json.dump(tj, f, indent=1)
@@ -150,10 +163,12 @@ def main() -> int:
           "| kernel | part | calls | avg µs | min µs | max µs | FETCH MB | WRITE MB |",
           "|---|---|---|---|---|---|---|---|"] + lines + [
           "",
-          f"- steps in the trace: {steps}; norm call = sum of its kernels = {norm_us:.2f} µs; "
+          f"- compose calls in the trace: {steps}; norm call = sum of its kernels = {norm_us:.2f} µs; "
           f"compose call = {comp_us:.2f} µs",
           f"- HBM traffic per norm call: {traffic['norm'] / 1e6:.1f} MB; per compose call: "
           f"{traffic['compose'] / 1e6:.1f} MB",
+          f"- compose backward call (timed on its own after the steps) = {bwd_us:.2f} µs; HBM traffic "
+          f"{traffic['compose_bwd'] / 1e6:.1f} MB",
           f"- copy calibration (1 GiB device copy): FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}",
           f"- HIP sources hash: {tj['source_hash']}", "",
           "Commands:", "", "```", args.cmd_kt, args.cmd_fetch, args.cmd_write, "```", ""]
