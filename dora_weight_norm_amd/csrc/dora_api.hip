@@ -148,8 +148,8 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.mode = dora::kModeFactored;
   choose_tiles(p);
   p.n_gran = ceil_div(d_in, p.gran);
-  p.ld_w = ceil_div(d_out, dora::kRowPad) * dora::kRowPad;
-  p.ga_rows = ceil_div(r, dora::kRowPad) * dora::kRowPad;
+  p.ld_w = ceil_div(d_out, dora::kRowPadW) * dora::kRowPadW;
+  p.ga_rows = ceil_div(r, dora::kRowPadG) * dora::kRowPadG;
   p.ga_cols = (int64_t)p.n_nt_g * p.ntc_g;
   p.r32 = ceil_div(r, 32) * 32;
   // Gram-term tiles: the streaming kernel covers up to 384 columns of G in
@@ -163,8 +163,8 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.n_bt = (int)ceil_div(p.r32, 128 * (int64_t)p.bcfg);
   p.n_cb = (int)ceil_div(p.r32, dora::kGramCols);
 
-  const int64_t tiles_w = ceil_div(d_out, dora::kFastRows) * p.n_nt;
-  const int64_t tiles_g = ceil_div(r, dora::kFastRows) * p.n_nt_g;
+  const int64_t tiles_w = ceil_div(d_out, dora::fast_rows(p.fcfg)) * p.n_nt;
+  const int64_t tiles_g = ceil_div(r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g;
   int xw = choose_w_ranges(tiles_w, p.n_gran);
   int xg = choose_g_ranges(tiles_g, p.n_gran, p.ga_rows * p.ga_cols * 4);
   // Fit the budget: fewer Gram ranges first, then fewer W ranges.
@@ -200,8 +200,9 @@ bool plan_self_check(const NormPlan& p) {
   }
   // Row tiles of every kernel (the general 512-column tile has 64 rows).
   const int64_t rows_w = ceil_div(p.d_out, 64) * 64, rows_g = ceil_div(p.r, 64) * 64;
-  if (ceil_div(p.d_out, dora::kFastRows) * dora::kFastRows > p.ld_w || rows_w > p.ld_w) return false;
-  if (ceil_div(p.r, dora::kFastRows) * dora::kFastRows > p.ga_rows || rows_g > p.ga_rows) return false;
+  const int fw = dora::fast_rows(p.fcfg), fg = dora::fast_rows(p.fcfg_g);
+  if (ceil_div(p.d_out, fw) * fw > p.ld_w || rows_w > p.ld_w) return false;
+  if (ceil_div(p.r, fg) * fg > p.ga_rows || rows_g > p.ga_rows) return false;
   if ((int64_t)p.n_nt * p.ntc < p.r || p.ga_cols < p.r || p.r32 > p.ga_cols) return false;
   const int64_t grid_w = p.xw * ceil_div(p.d_out, 64) * p.n_nt;
   const int64_t grid_g = p.xg * ceil_div(p.r, 64) * p.n_nt_g;
@@ -264,11 +265,11 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   if (st != DORA_OK) return st;
   if (!plan_self_check(p)) return DORA_ERR_INVALID_ARG;
   const bool f = p.mode == dora::kModeFactored;
-  const int64_t grid_w = f ? p.xw * ceil_div(p.d_out, dora::kFastRows) * p.n_nt : 0;
-  const int64_t grid_g = f ? p.xg * ceil_div(p.r, dora::kFastRows) * p.n_nt_g : 0;
+  const int64_t grid_w = f ? p.xw * ceil_div(p.d_out, dora::fast_rows(p.fcfg)) * p.n_nt : 0;
+  const int64_t grid_g = f ? p.xg * ceil_div(p.r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g : 0;
   const int64_t vals[] = {p.mode, p.ntc, p.n_nt, p.ntc_g, p.n_nt_g, p.fcfg, p.gcfg, p.fcfg_g, p.gcfg_g, p.gran,
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
-                          f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0};
+                          f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;

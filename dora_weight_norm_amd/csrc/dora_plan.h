@@ -20,38 +20,25 @@ namespace dora {
 constexpr int kDies = 8;
 constexpr int kGrid = 256;           // compute units
 constexpr int kThreads = 256;        // 4 waves of 64
-constexpr int kRowPad = 128;         // partial-sum rows are padded to a multiple of this
+constexpr int kRowPadW = 128;        // W-pass partial rows (ld_w) are padded to a multiple of this
+constexpr int kRowPadG = 128;        // Gram partial rows (ga_rows) are padded to a multiple of this
 
-// Streaming kernel: 4 waves, each owning 32 rows of the tile (128 rows) and
-// all of its nb 32-column blocks; W (or A, in the Gram pass) is read
-// straight into registers, the column operand A goes through a ring of ns
-// LDS slots of kt-deep stages.
-struct FastShape {
-  int nb, kt, ns;
-};
+// Streaming kernel configurations. Each holds MT rows (of W, or of A in the
+// Gram pass) by NTC columns (rows of A) per workgroup; the column operand
+// and the row operand go through a ring of LDS slots by direct loads.
 enum FastCfg : int {
-  kFastB64 = 0,    // bf16, 64 columns
-  kFastB128 = 1,   // bf16, 128 columns
-  kFastB256 = 2,   // bf16, 256 columns
-  kFastB384 = 3,   // bf16, 384 columns
-  kFastB512 = 4,   // bf16, 512 columns
-  kFastF32 = 5,    // fp32, 32 columns
-  kFastF128 = 6,   // fp32, 128 columns
+  kFastB64 = 0,    // bf16, 128 x 64, 8 waves
+  kFastB128 = 1,   // bf16, 128 x 128, 8 waves
+  kFastB256 = 2,   // bf16, 128 x 256, 8 waves
+  kFastB384 = 3,   // bf16, 128 x 384, 8 waves
+  kFastB512 = 4,   // bf16, 128 x 512, 8 waves
+  kFastF32 = 5,    // fp32, 128 x 32, 4 waves
+  kFastF128 = 6,   // fp32, 128 x 128, 8 waves
   kNumFastCfg = 7
 };
-DORA_HD FastShape fast_shape(int cfg) {
-  switch (cfg) {
-    case kFastB64: return FastShape{2, 64, 4};
-    case kFastB128: return FastShape{4, 64, 4};
-    case kFastB256: return FastShape{8, 64, 4};
-    case kFastB384: return FastShape{12, 64, 3};
-    case kFastB512: return FastShape{16, 32, 4};
-    case kFastF32: return FastShape{1, 32, 4};
-    default: return FastShape{4, 32, 4};
-  }
-}
-constexpr int kFastRows = 128;
-constexpr int kGramCols = 64;      // columns of G per Gram-term tile
+// Rows per workgroup tile of a streaming configuration.
+DORA_HD int fast_rows(int) { return 128; }
+constexpr int kGramCols = 64;      // columns of G per Gram-term tile (general kernel)
 
 // General kernel (any alignment): WM x WN waves, each owning MB x NB blocks
 // of 32x32 accumulators; KT is the d_in depth of one LDS stage.

@@ -70,8 +70,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // cores work; one barrier per stage publishes a slot and retires the one
 // reused next. The waits before the barrier leave the younger stages'
 // loads outstanding (an ordinary __syncthreads would drain them all).
-// Inside a stage, the fragments of K16 step s+1 are read while step s's
-// MFMAs run.
+// The fragments of the next K16 step are read into one of two register
+// sets while the current step's MFMAs run.
 // ---------------------------------------------------------------------------
 template <typename T, int WM, int WN, int MB, int NB, int KT, int NS>
 struct FastK {
@@ -90,24 +90,28 @@ struct FastK {
   static constexpr int MBLK = MT * RB / 1024;    // blocks holding row-operand rows
   static constexpr int BPW = SLOT / 1024 / NW;   // direct-load blocks per wave per stage
   static constexpr int BPW_M = MBLK / NW;        // of which row-operand blocks
-  // Epilogue: each wave stages B for its rows and columns.
+  // Epilogue: each wave stages B for its rows and columns, one 32-row block
+  // (round) at a time, in a private region of one or two round buffers.
   static constexpr int RBB = NB * 32 * ESZ;      // bytes of one staged B row segment
   static constexpr int CPRB = RBB / 16;
   // XOR mask of the staged-B swizzle: the largest power of two below 8 that
   // divides the row's chunk count, so a swizzled chunk stays in its row.
   static constexpr int BSW = CPRB % 8 == 0 ? 7 : (CPRB % 4 == 0 ? 3 : (CPRB % 2 == 0 ? 1 : 0));
-  static constexpr int WB = MB * 32 * RBB;       // bytes staged per wave
+  static constexpr int RW = 32 * RBB;            // bytes of one round
+  static constexpr int LPR = RW / 1024;          // direct loads per round
+  static constexpr int NBUF = MB > 1 ? 2 : 1;    // round buffers per wave
+  static constexpr int WB = NBUF * RW;           // bytes of a wave's region
   static constexpr int WPS = SLOT / WB;          // waves staging B in one ring slot
   static constexpr int WX = NW > WPS * NS ? NW - WPS * NS : 0;   // waves staging B past the ring
-  static_assert(kRowPad % MT == 0, "row tiles divide the plan's row padding");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(CPR == 8 || CPR == 4, "LDS rows are 64 or 128 bytes");
   static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
   static_assert(SLOT % (1024 * NW) == 0 && MBLK % NW == 0, "a stage splits evenly over the waves");
-  static_assert(WB % 1024 == 0 && RBB % 16 == 0, "B stages in whole 1 KiB blocks");
+  static_assert(RW % 1024 == 0 && RBB % 16 == 0, "B stages in whole 1 KiB blocks");
   static_assert(WPS >= 1, "a wave's B fits one ring slot");
   static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + WN * MT * 4 <= 160 * 1024, "gfx950 has 160 KiB of LDS");
-  static_assert(BPW * (NS - 1) < 64, "outstanding loads fit vmcnt");
+  static_assert(BPW * (NS - 1) < 64 && LPR < 64, "outstanding loads fit vmcnt");
+  static_assert(KSTEPS % 2 == 0, "fragment buffers alternate within a stage");
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row `row`: an XOR swizzle
@@ -141,6 +145,32 @@ struct AssembleArgs {
   float* g;
 };
 
+// sum_{i < n} p[i * stride], added in increasing i. The loads are issued
+// kSumBatch at a time (they do not depend on the running sum), so a long sum
+// costs n / kSumBatch memory round trips instead of n; the order of the
+// additions, and so the result, is that of the plain loop.
+constexpr int kSumBatch = 16;
+__device__ __forceinline__ float ordered_sum(const float* p, int64_t stride, int n) {
+  float acc = 0.f;
+  int i = 0;
+  for (; i + kSumBatch <= n; i += kSumBatch) {
+    float v[kSumBatch];
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u) v[u] = p[(int64_t)(i + u) * stride];
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u) acc += v[u];
+  }
+  if (i < n) {
+    float v[kSumBatch];
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u) v[u] = (i + u < n) ? p[(int64_t)(i + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u)
+      if (i + u < n) acc += v[u];
+  }
+  return acc;
+}
+
 // wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and g = m / max(wnorm, eps),
 // every operation separately rounded (no contraction), sqrt and division
 // correctly rounded ("DoRA优化技术解析", cyqw.cn, §1.2.2, §5.2, §6.2). base and
@@ -149,11 +179,9 @@ __device__ __forceinline__ void assemble_row(const NormPlan& p, const char* ws, 
                                              float* wnorm, float* g, int64_t j, float ba) {
   const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
   const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
-  float base = 0.f, cross = 0.f;
-  for (int x = 0; x < p.xw; ++x) {
-    base += part_base[(int64_t)x * p.ld_w + j];
-    for (int n = 0; n < p.n_nt; ++n) cross += part_cross[((int64_t)x * p.n_nt + n) * p.ld_w + j];
-  }
+  // Cross partials are planes (x, n) in the order x * n_nt + n.
+  const float base = ordered_sum(part_base + j, p.ld_w, p.xw);
+  const float cross = ordered_sum(part_cross + j, p.ld_w, p.xw * p.n_nt);
   const float two_s = s + s;
   const float s2 = __fmul_rn(s, s);
   float val = __fadd_rn(__fadd_rn(base, __fmul_rn(two_s, cross)), __fmul_rn(s2, ba));
@@ -176,6 +204,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   constexpr int FC = C::FC, EPC = C::EPC, ESZ = C::ESZ, KSTEPS = C::KSTEPS, BPW = C::BPW;
   constexpr bool GRAM = MODE == kPassGram;
   constexpr bool BG = MODE == kPassBG;
+  static_assert((GRAM ? kRowPadG : kRowPadW) % MT == 0, "row tiles divide the plan's row padding");
   constexpr int NG = sizeof(T) == 2 ? 2 : 1;   // parts of the stored Gram matrix (hi, lo)
   __shared__ __attribute__((aligned(1024))) char r0[C::SLOT];
   __shared__ __attribute__((aligned(1024))) char r1[C::SLOT];
@@ -276,68 +305,68 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
 #pragma unroll
   for (int a = 0; a < MB; ++a) sq[a] = 0.f;
 
-  // All fragments of one stage: F[s][a] row-operand, F[s][MB + b] column
-  // operand, for K16 step s.
-  typedef u32x4 Frags[KSTEPS][MB + NB][FC];
-  auto read_stage = [&](const char* slot, Frags& F) __attribute__((always_inline)) {
+  // Fragments of one K16 step: F[a] row operand, F[MB + b] column operand.
+  typedef u32x4 Frag[MB + NB][FC];
+  auto read_step = [&](const char* slot, int s, Frag& F) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
+    for (int f = 0; f < FC; ++f) {
+      const int c = s * 2 * FC + lgrp * FC + f;
+      const int co = fswz<CPR>(lrow, c) * 16;
 #pragma unroll
-      for (int f = 0; f < FC; ++f) {
-        const int c = s * 2 * FC + lgrp * FC + f;
-        const int co = fswz<CPR>(lrow, c) * 16;
+      for (int a = 0; a < MB; ++a)
+        F[a][f] = *reinterpret_cast<const u32x4*>(slot + ((wm * MB + a) * 32 + lrow) * RB + co);
 #pragma unroll
-        for (int a = 0; a < MB; ++a)
-          F[s][a][f] = *reinterpret_cast<const u32x4*>(slot + ((wm * MB + a) * 32 + lrow) * RB + co);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          F[s][MB + b][f] = *reinterpret_cast<const u32x4*>(slot + (MT + (wn * NB + b) * 32 + lrow) * RB + co);
-      }
+      for (int b = 0; b < NB; ++b)
+        F[MB + b][f] = *reinterpret_cast<const u32x4*>(slot + (MT + (wn * NB + b) * 32 + lrow) * RB + co);
+    }
   };
-  auto mfma_stage = [&](const Frags& F) __attribute__((always_inline)) {
+  auto mfma_step = [&](const Frag& F) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(F[a], F[MB + b], acc[a][b]);
+    if constexpr (MODE == kPassW) {
+      // Every wave squares its row fragments (straight-line code); only the
+      // waves of column group 0 store the sums.
 #pragma unroll
       for (int a = 0; a < MB; ++a)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(F[s][a], F[s][MB + b], acc[a][b]);
-      if constexpr (MODE == kPassW) {
-        // Every wave squares its row fragments (straight-line code); only the
-        // waves of column group 0 store the sums.
-#pragma unroll
-        for (int a = 0; a < MB; ++a)
-#pragma unroll
-          for (int f = 0; f < FC; ++f) sq[a] += chunk_sumsq(F[s][a][f], T());
-      }
+        for (int f = 0; f < FC; ++f) sq[a] += chunk_sumsq(F[a][f], T());
     }
   };
-  // Pipeline. Stage j lives in ring slot j % NS. Iteration i: wait for this
-  // wave's fragment reads of stage i and its loads of stage i+1 (the NS-2
-  // younger stages stay in flight), barrier (stage i is in registers in every
-  // wave and stage i+1 has landed everywhere), load stage i+NS into the slot
-  // stage i vacated, read stage i+1's fragments, then run stage i's MFMAs,
-  // which overlap the next iteration's wait and barrier. The stage count is
-  // rounded up to whole unrolled groups (the extra stages are zeros), so the
-  // loop body is straight-line code with fixed load counts.
-  constexpr int UNR = NS % 2 == 0 ? NS : 2 * NS;   // slots and register sets repeat after UNR stages
-  const int n_pad = (n_st + UNR - 1) / UNR * UNR;
-  Frags F[2];
+  // Pipeline. Stage j lives in ring slot j % NS. In stage i, K16 step s+1's
+  // fragments are read while step s's MFMAs run. Before the last step: wait
+  // for this wave's fragment reads of stage i and its loads of stage i+1
+  // (the NS-2 younger stages stay in flight), barrier (stage i is in
+  // registers in every wave and stage i+1 has landed everywhere), load stage
+  // i+NS into the slot stage i vacated and read stage i+1's first step. The
+  // stage count is rounded up to whole unrolled groups (the extra stages are
+  // zeros), so the loop body is straight-line code with fixed load counts.
+  const int n_pad = (n_st + NS - 1) / NS * NS;
+  Frag H[2];
 #pragma unroll
   for (int j = 0; j < NS; ++j) issue(j, ring(j));
   wait_vm_lgkm0<(NS - 1) * BPW>();   // stage 0 complete; stages 1 .. NS-1 in flight
   barrier_keep_loads();
-  read_stage(ring(0), F[0]);
-  for (int i0 = 0; i0 < n_pad; i0 += UNR) {
+  read_step(ring(0), 0, H[0]);
+  for (int i0 = 0; i0 < n_pad; i0 += NS) {
 #pragma unroll
-    for (int j = 0; j < UNR; ++j) {
+    for (int j = 0; j < NS; ++j) {
       const int i = i0 + j;
-      wait_vm_lgkm0<(NS - 2) * BPW>();
-      barrier_keep_loads();
-      issue(i + NS, ring(j % NS));
-      read_stage(ring((j + 1) % NS), F[(j + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_stage(F[j & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        if (s + 1 < KSTEPS) {
+          read_step(ring(j), s + 1, H[(s + 1) & 1]);
+        } else {
+          wait_vm_lgkm0<(NS - 2) * BPW>();
+          barrier_keep_loads();
+          issue(i + NS, ring(j));
+          read_step(ring((j + 1) % NS), 0, H[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(H[s & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   // The ring is reused below: drain the trailing (zero) loads everywhere.
@@ -366,9 +395,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
         if (n == 0 && wn == 0 && lgrp == 0) part_base[(int64_t)x * p.ld_w + wrow0 + a * 32 + lrow] = qs;
       }
     }
-    // Dot each accumulator row with its B row over this wave's columns: stage
-    // B for the wave's rows and columns in its own part of the ring (free
-    // after the last barrier), then add the column groups in order.
+    // Dot each accumulator row with its B row over this wave's columns. B
+    // is staged per 32-row block (round) in the wave's own LDS region (the
+    // ring is free after the last barrier), the next round's loads in flight
+    // while this round is used; then the column groups are added in order.
     char* bb = wave < C::WPS * NS ? ring(wave / C::WPS) + (wave % C::WPS) * C::WB
                                   : bx + (wave - C::WPS * NS) * C::WB;
     const int64_t w_left = p.d_out - wrow0;
@@ -376,17 +406,27 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     const uint32_t brow_bytes = (uint32_t)(p.r * ESZ);
     const int64_t c0 = n0 + wn * NB * 32;       // first column of this wave
     const __amdgpu_buffer_rsrc_t brs = make_rsrc(B + wrow0 * p.r + (c0 < p.r ? c0 : 0), (uint32_t)w_lim * brow_bytes);
+    auto issue_b = [&](int a, char* buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < C::WB / 1024; ++q) {
-      const int slot16 = q * 64 + lane;
-      const int row = slot16 / C::CPRB, c = (slot16 % C::CPRB) ^ (row & C::BSW);
-      const uint32_t off = (c0 + (int64_t)c * EPC < p.r) ? (uint32_t)row * brow_bytes + (uint32_t)(c * 16) : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void*)(bb + q * 1024), 16,
-                                               off, 0, 0, 0);
-    }
-    wait_vm_lgkm0<0>();
+      for (int q = 0; q < C::LPR; ++q) {
+        const int slot16 = q * 64 + lane;
+        const int row = slot16 / C::CPRB, c = (slot16 % C::CPRB) ^ (row & C::BSW);
+        const uint32_t off = (c0 + (int64_t)c * EPC < p.r)
+                                 ? (uint32_t)(a * 32 + row) * brow_bytes + (uint32_t)(c * 16) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void*)(buf + q * 1024), 16,
+                                                 off, 0, 0, 0);
+      }
+    };
+    issue_b(0, bb);
+    if constexpr (MB > 1) issue_b(1, bb + C::RW);
 #pragma unroll
     for (int a = 0; a < MB; ++a) {
+      const char* buf = bb + (a & 1) * C::RW;
+      if (a + 1 < MB) {
+        wait_vm_lgkm0<C::LPR>();   // round a landed; round a+1 in flight
+      } else {
+        wait_vm_lgkm0<0>();
+      }
       float pa[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) pa[v] = 0.f;
@@ -395,14 +435,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
         const int col = b * 32 + lrow;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = a * 32 + acc_row(v, lgrp);
-          const T bv = *reinterpret_cast<const T*>(bb + row * C::RBB + (((col / EPC) ^ (row & C::BSW)) * 16) +
+          const int row = acc_row(v, lgrp);
+          const T bv = *reinterpret_cast<const T*>(buf + row * C::RBB + (((col / EPC) ^ (row & C::BSW)) * 16) +
                                                    (col % EPC) * ESZ);
           pa[v] = fmaf(acc[a][b][v], to_f32(bv), pa[v]);
         }
       }
       const float tot = sum32_transpose(pa, lane);
       if ((lane & 1) == 0) red[wn * MT + wm * MB * 32 + a * 32 + acc_row((lane & 31) >> 1, lgrp)] = tot;
+      if (a + 2 < MB) {
+        wait_vm_lgkm0<C::LPR>();   // this round's LDS reads are done before its buffer is refilled
+        issue_b(a + 2, bb + (a & 1) * C::RW);
+      }
     }
     __syncthreads();
     if (BG && n_nt == 1) {
@@ -691,9 +735,7 @@ __global__ __launch_bounds__(kThreads) void gram_reduce_kernel(NormPlan p, char*
   const float* part_g = reinterpret_cast<const float*>(ws + p.off_g);
   float acc = 0.f;
   if (i < p.r && j < p.r) {
-    const int64_t plane = p.ga_rows * p.ga_cols;
-    const float* src = part_g + i * p.ga_cols + j;
-    for (int x = 0; x < p.xg; ++x) acc += src[(int64_t)x * plane];
+    acc = ordered_sum(part_g + i * p.ga_cols + j, p.ga_rows * p.ga_cols, p.xg);
   }
   if constexpr (sizeof(T) == 2) {
     // Row i of the stored matrix: [hi(G[i][0..r32)), lo(G[i][0..r32))].
@@ -832,8 +874,7 @@ __global__ __launch_bounds__(kThreads) void assemble_kernel(NormPlan p, const ch
   const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (j >= p.d_out) return;
   const float* part_ba = reinterpret_cast<const float*>(ws + p.off_ba);
-  float ba = 0.f;
-  for (int c = 0; c < n_ba; ++c) ba += part_ba[(int64_t)c * p.ld_w + j];
+  const float ba = ordered_sum(part_ba + j, p.ld_w, n_ba);
   assemble_row(p, ws, s, eps, m, wnorm, g, j, ba);
 }
 
@@ -914,16 +955,23 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
   constexpr int MODE = GRAM ? kPassGram : kPassW;
   const AssembleArgs aa{};
   if (p.fast) {
+    // The Gram pass only uses the 64- and 128-column configurations.
     switch (fcfg) {
       case kFastB64: return launch_fast<bf16_t, 4, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
       case kFastB128: return launch_fast<bf16_t, 2, 4, 2, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
-      case kFastB256: return launch_fast<bf16_t, 2, 4, 2, 2, 32, 4, MODE>(p, M, A, B, ws, aa, st);
-      case kFastB384: return launch_fast<bf16_t, 2, 4, 2, 3, 32, 4, MODE>(p, M, A, B, ws, aa, st);
-      case kFastB512: return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
       case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
       case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
-      default: return hipErrorInvalidValue;
+      default: break;
     }
+    if constexpr (!GRAM) {
+      switch (fcfg) {
+        case kFastB256: return launch_fast<bf16_t, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
+        case kFastB384: return launch_fast<bf16_t, 2, 4, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
+        case kFastB512: return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
+        default: break;
+      }
+    }
+    return hipErrorInvalidValue;
   }
   switch (gcfg) {
     case kGenB64: return launch_gen<bf16_t, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
@@ -1010,8 +1058,8 @@ size_t fast_kernel_lds_bytes(int cfg) {
   switch (cfg) {
     case kFastB64: return DORA_LDS(4, bf16_t, 4, 2, 1, 1, 64);
     case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
-    case kFastB256: return DORA_LDS(4, bf16_t, 2, 4, 2, 2, 32);
-    case kFastB384: return DORA_LDS(4, bf16_t, 2, 4, 2, 3, 32);
+    case kFastB256: return DORA_LDS(3, bf16_t, 2, 4, 2, 2, 64);
+    case kFastB384: return DORA_LDS(2, bf16_t, 2, 4, 2, 3, 64);
     case kFastB512: return DORA_LDS(3, bf16_t, 2, 4, 2, 4, 32);
     case kFastF32: return DORA_LDS(4, float, 4, 1, 1, 1, 32);
     case kFastF128: return DORA_LDS(4, float, 2, 4, 2, 1, 32);

@@ -59,7 +59,7 @@ def test_plans_of_the_workloads(name):
     assert info["workspace_bytes"] == bnd.dora_norm_workspace_size(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
     assert info["gram_grid"] <= 256 and info["lds_bytes"] <= 160 * 1024
     # the W pass: one workgroup per (row tile, d_in range)
-    assert info["w_grid"] == -(-w.d_out // 128) * info["col_tiles"] * info["w_ranges"]
+    assert info["w_grid"] == -(-w.d_out // info["tile_rows"]) * info["col_tiles"] * info["w_ranges"]
     assert info["gram_grid"] == -(-w.r // 128) * info["gram_col_tiles"] * info["gram_ranges"]
     assert info["tile_cols"] * info["col_tiles"] >= w.r
 
