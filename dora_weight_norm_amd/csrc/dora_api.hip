@@ -74,6 +74,10 @@ void choose_tiles(NormPlan& p) {
   p.n_nt_g = (int)ceil_div(r, p.ntc_g);
 }
 
+// Gram partial planes the workspace holds: the Gram pass writes xg, the W
+// pass with the Gram blocks folded in writes xw.
+int gram_planes(const NormPlan& p) { return p.gfold && p.xw > p.xg ? p.xw : p.xg; }
+
 void layout(NormPlan& p) {
   size_t off = 0;
   p.off_base = off;
@@ -83,7 +87,7 @@ void layout(NormPlan& p) {
   p.off_ba = off;
   off = align_up(off + (size_t)((int64_t)(p.n_bt > p.n_cb ? p.n_bt : p.n_cb) * p.ld_w) * 4, kAlign);
   p.off_g = off;
-  off = align_up(off + (size_t)((int64_t)p.xg * p.ga_rows * p.ga_cols) * 4, kAlign);
+  off = align_up(off + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4, kAlign);
   p.off_gg = off;
   off = align_up(off + (size_t)(p.r32 * p.r32) * 4, kAlign);   // bf16 hi and lo, or fp32
   p.ws_bytes = off;
@@ -164,6 +168,14 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.n_cb = (int)ceil_div(p.r32, dora::kGramCols);
 
   const int64_t tiles_w = ceil_div(d_out, dora::fast_rows(p.fcfg)) * p.n_nt;
+  // G = A A^T folds into the streaming W pass when one column tile of at
+  // most 128 columns holds all of A's rows and every 32x32 block of G finds
+  // a wave (one per wave). Every wave then reads two more fragments and runs
+  // one more MFMA per K16 step; on wider tiles those LDS reads cost the W
+  // pass as much as the separate Gram pass takes.
+  const int64_t nbc = p.r32 / 32;
+  p.gfold = p.n_nt == 1 && p.ntc <= 128 &&
+            nbc * nbc <= (int64_t)dora::fast_waves(p.fcfg) * ceil_div(d_out, dora::fast_rows(p.fcfg));
   const int64_t tiles_g = ceil_div(r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g;
   int xw = choose_w_ranges(tiles_w, p.n_gran);
   int xg = choose_g_ranges(tiles_g, p.n_gran, p.ga_rows * p.ga_cols * 4);
@@ -210,7 +222,7 @@ bool plan_self_check(const NormPlan& p) {
   if (p.off_cross < p.off_base + (size_t)(p.xw * p.ld_w) * 4) return false;
   if (p.off_ba < p.off_cross + (size_t)(p.xw * p.n_nt * p.ld_w) * 4) return false;
   if (p.off_g < p.off_ba + (size_t)((int64_t)(p.n_bt > p.n_cb ? p.n_bt : p.n_cb) * p.ld_w) * 4) return false;
-  if (p.off_gg < p.off_g + (size_t)(p.xg * p.ga_rows * p.ga_cols) * 4) return false;
+  if (p.off_gg < p.off_g + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4) return false;
   return p.ws_bytes >= p.off_gg + (size_t)(p.r32 * p.r32) * 4;
 }
 
@@ -269,7 +281,8 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   const int64_t grid_g = f ? p.xg * ceil_div(p.r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g : 0;
   const int64_t vals[] = {p.mode, p.ntc, p.n_nt, p.ntc_g, p.n_nt_g, p.fcfg, p.gcfg, p.fcfg_g, p.gcfg_g, p.gran,
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
-                          f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0};
+                          f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0,
+                          f ? p.gfold : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;

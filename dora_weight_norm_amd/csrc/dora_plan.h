@@ -36,8 +36,10 @@ enum FastCfg : int {
   kFastF128 = 6,   // fp32, 128 x 128, 8 waves
   kNumFastCfg = 7
 };
-// Rows per workgroup tile of a streaming configuration.
+// Rows per workgroup tile, and waves per workgroup, of a streaming
+// configuration.
 DORA_HD int fast_rows(int) { return 128; }
+DORA_HD int fast_waves(int cfg) { return cfg == kFastF32 ? 4 : 8; }
 constexpr int kGramCols = 64;      // columns of G per Gram-term tile (general kernel)
 
 // General kernel (any alignment): WM x WN waves, each owning MB x NB blocks
@@ -85,6 +87,8 @@ struct NormPlan {
   int64_t n_gran;       // granules over d_in
   int xw;               // d_in ranges of the W pass
   int xg;               // d_in ranges of the Gram pass
+  int gfold;            // the streaming W pass also computes G (no Gram pass); its
+                        // Gram partials are then per W-pass range (xw planes)
   int64_t ld_w;         // padded W rows of the base / cross partials
   int64_t ga_rows;      // padded A rows of the Gram partials
   int64_t ga_cols;      // padded Gram columns: n_nt * ntc
@@ -95,7 +99,7 @@ struct NormPlan {
   size_t off_base;      // [xw][ld_w] fp32 base partials
   size_t off_cross;     // [xw][n_nt][ld_w] fp32 cross partials
   size_t off_ba;        // [max(n_bt, n_cb)][ld_w] fp32 Gram-term partials
-  size_t off_g;         // [xg][ga_rows][ga_cols] fp32 Gram partials
+  size_t off_g;         // [max(xg, xw if gfold)][ga_rows][ga_cols] fp32 Gram partials
   size_t off_gg;        // reduced Gram matrix: bf16 [r32][Ghi | Glo], fp32 [r32][r32]
   size_t ws_bytes;
 };

@@ -13,16 +13,20 @@
 //                 d_in range): U = W A^T on the matrix cores, dotted with B
 //                 row by row at the end (cross term; U is never stored), and
 //                 the W fragments squared on the way (base term).
-//   gram_term     (B G) on the matrix cores (B Ghi + B Glo), dotted with B,
-//                 per 64-column block of G (Gram-term partials).
+//   Gram term     (B G) on the matrix cores (B Ghi + B Glo), dotted with B
+//                 (Gram-term partials), with the assembly fused in when one
+//                 tile covers all of G's columns; otherwise
 //   assemble      fixed-order sums of all partials;
 //                 wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and
 //                 g = m / max(wnorm, eps) without contraction, with
 //                 correctly rounded sqrt and division (same page, §1.2.2,
 //                 §5.2, §6.2).
-// The two passes run the streaming kernel when W, A and B allow aligned
-// 16-byte loads, and the general kernel otherwise; both write the same
-// partials.
+// When the streaming W pass has a single column tile (all of A's rows in
+// each stage) it also computes the blocks of G, and the order becomes
+// W pass, gram_reduce, Gram term: the separate Gram pass, and its second
+// read of A, are skipped.
+// The passes run the streaming kernel when W, A and B allow aligned 16-byte
+// loads, and the general kernels otherwise; both write the same partials.
 //
 // When s == 0 or r == 0 the cross and Gram terms vanish and only a row
 // sum-of-squares kernel runs (same page, §5.1, notes of Algorithm 1).
@@ -130,12 +134,18 @@ __device__ __forceinline__ int fswz(int row, int c) {
 //   kPassW     U = W A^T per (row tile, column tile, d_in range); epilogue:
 //              base and cross partials.
 //   kPassGram  G = A A^T partial tiles per d_in range.
+//   kPassWG    kPassW, and in the same pass the blocks of G = A A^T for the
+//              d_in range: the column operand is all of A's rows (one column
+//              tile), so its stages in LDS are exactly what G needs. Wave q of
+//              row tile m computes the 32x32 block m + n_mt * q of G (if it
+//              exists) with one more MFMA per K16 step and stores it as that
+//              range's Gram partial; no separate Gram pass runs.
 //   kPassBG    (B G) over the virtual depth [B | B] . [Ghi ; Glo] (bf16) or
 //              B . G (fp32) per (row tile, column tile of G); epilogue: dot
 //              with B. With a single column tile the Gram term of each row is
 //              complete in its workgroup, which then assembles wnorm and g;
 //              otherwise it stores per-tile partials for the assembly kernel.
-enum PassKind : int { kPassW = 0, kPassGram = 1, kPassBG = 2 };
+enum PassKind : int { kPassW = 0, kPassGram = 1, kPassBG = 2, kPassWG = 3 };
 
 // Scalars and outputs of the final assembly (used by kPassBG only).
 struct AssembleArgs {
@@ -204,6 +214,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   constexpr int FC = C::FC, EPC = C::EPC, ESZ = C::ESZ, KSTEPS = C::KSTEPS, BPW = C::BPW;
   constexpr bool GRAM = MODE == kPassGram;
   constexpr bool BG = MODE == kPassBG;
+  constexpr bool GF = MODE == kPassWG;               // Gram blocks folded into the W pass
+  constexpr bool WP = MODE == kPassW || GF;          // W pass
   static_assert((GRAM ? kRowPadG : kRowPadW) % MT == 0, "row tiles divide the plan's row padding");
   constexpr int NG = sizeof(T) == 2 ? 2 : 1;   // parts of the stored Gram matrix (hi, lo)
   __shared__ __attribute__((aligned(1024))) char r0[C::SLOT];
@@ -304,9 +316,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   float sq[MB];
 #pragma unroll
   for (int a = 0; a < MB; ++a) sq[a] = 0.f;
+  // Folded Gram block of this wave: rows gI, columns gJ (32-blocks of G).
+  int gI = 0, gJ = 0;
+  bool has_g = false;
+  f32x16 gacc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) gacc[v] = 0.f;
+  if constexpr (GF) {
+    const int nbc = (int)(p.r32 / 32);
+    const int n_mt = (int)((p.d_out + MT - 1) / MT);
+    const int gb = m + n_mt * wave;
+    has_g = gb < nbc * nbc;
+    gI = has_g ? gb / nbc : 0;
+    gJ = has_g ? gb - gI * nbc : 0;
+  }
 
-  // Fragments of one K16 step: F[a] row operand, F[MB + b] column operand.
-  typedef u32x4 Frag[MB + NB][FC];
+  // Fragments of one K16 step: F[a] row operand, F[MB + b] column operand,
+  // F[MB + NB] and F[MB + NB + 1] the folded Gram block's row and column
+  // blocks of A.
+  constexpr int NGF = GF ? 2 : 0;
+  typedef u32x4 Frag[MB + NB + NGF][FC];
   auto read_step = [&](const char* slot, int s, Frag& F) __attribute__((always_inline)) {
 #pragma unroll
     for (int f = 0; f < FC; ++f) {
@@ -318,6 +347,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
 #pragma unroll
       for (int b = 0; b < NB; ++b)
         F[MB + b][f] = *reinterpret_cast<const u32x4*>(slot + (MT + (wn * NB + b) * 32 + lrow) * RB + co);
+      if constexpr (GF) {
+        F[MB + NB][f] = *reinterpret_cast<const u32x4*>(slot + (MT + gI * 32 + lrow) * RB + co);
+        F[MB + NB + 1][f] = *reinterpret_cast<const u32x4*>(slot + (MT + gJ * 32 + lrow) * RB + co);
+      }
     }
   };
   auto mfma_step = [&](const Frag& F) __attribute__((always_inline)) {
@@ -325,7 +358,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     for (int a = 0; a < MB; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(F[a], F[MB + b], acc[a][b]);
-    if constexpr (MODE == kPassW) {
+    if constexpr (GF) gacc = Mfma<T>::run(F[MB + NB], F[MB + NB + 1], gacc);
+    if constexpr (WP) {
       // Every wave squares its row fragments (straight-line code); only the
       // waves of column group 0 store the sums.
 #pragma unroll
@@ -385,7 +419,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           gdst[(int64_t)(a * 32 + acc_row(v, lgrp)) * p.ga_cols + b * 32 + lrow] = acc[a][b][v];
   } else {
     const int64_t wrow0 = mrow0 + wm * MB * 32;   // first row of this wave
-    if constexpr (MODE == kPassW) {
+    if constexpr (GF) {
+      if (has_g) {
+        float* gdst = reinterpret_cast<float*>(ws + p.off_g) + ((int64_t)x * p.ga_rows + gI * 32) * p.ga_cols + gJ * 32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) gdst[(int64_t)acc_row(v, lgrp) * p.ga_cols + lrow] = gacc[v];
+      }
+    }
+    if constexpr (WP) {
       // Base term (waves of column group 0): the two k-halves of each row
       // live in lanes l and l+32.
       float* part_base = reinterpret_cast<float*>(ws + p.off_base);
@@ -949,10 +990,10 @@ hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const voi
   return hipGetLastError();
 }
 
-template <bool GRAM>
+template <int MODE>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
                        char* ws, hipStream_t st) {
-  constexpr int MODE = GRAM ? kPassGram : kPassW;
+  constexpr bool GRAM = MODE == kPassGram;
   const AssembleArgs aa{};
   if (p.fast) {
     // The Gram pass only uses the 64- and 128-column configurations.
@@ -967,21 +1008,27 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
       switch (fcfg) {
         case kFastB256: return launch_fast<bf16_t, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
         case kFastB384: return launch_fast<bf16_t, 2, 4, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
-        case kFastB512: return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
+        case kFastB512:
+          if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
+          else return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
         default: break;
       }
     }
     return hipErrorInvalidValue;
   }
-  switch (gcfg) {
-    case kGenB64: return launch_gen<bf16_t, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
-    case kGenB128: return launch_gen<bf16_t, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
-    case kGenB256: return launch_gen<bf16_t, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
-    case kGenB384: return launch_gen<bf16_t, 2, 4, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
-    case kGenB512: return launch_gen<bf16_t, 1, 4, 2, 4, 64, GRAM>(p, M, A, B, ws, st);
-    case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st);
-    case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st);
-    default: return hipErrorInvalidValue;
+  if constexpr (MODE == kPassWG) {
+    return hipErrorInvalidValue;   // the general kernel never folds the Gram blocks in
+  } else {
+    switch (gcfg) {
+      case kGenB64: return launch_gen<bf16_t, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB128: return launch_gen<bf16_t, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB256: return launch_gen<bf16_t, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB384: return launch_gen<bf16_t, 2, 4, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB512: return launch_gen<bf16_t, 1, 4, 2, 4, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st);
+      case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st);
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
@@ -1023,15 +1070,25 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
                                 float s, const float* m, float eps, float* wnorm, float* g,
                                 hipStream_t st) {
   char* ws = static_cast<char*>(ws_);
-  hipError_t e = launch_pass<true>(p, p.fcfg_g, p.gcfg_g, A, A, B, ws, st);   // Gram pass
+  const bool fold = p.fast && p.gfold;
+  hipError_t e;
+  if (fold) {
+    e = launch_pass<kPassWG>(p, p.fcfg, p.gcfg, W, A, B, ws, st);   // W pass with G folded in
+  } else {
+    e = launch_pass<kPassGram>(p, p.fcfg_g, p.gcfg_g, A, A, B, ws, st);   // Gram pass
+  }
   if (e != hipSuccess) return e;
+  NormPlan q = p;
+  if (fold) q.xg = p.xw;   // one Gram partial per W-pass range
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
                      dim3((unsigned)((p.r32 + kThreads - 1) / kThreads), (unsigned)p.r32), dim3(kThreads), 0, st,
-                     p, ws);
+                     q, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_pass<false>(p, p.fcfg, p.gcfg, W, A, B, ws, st);                // W pass
-  if (e != hipSuccess) return e;
+  if (!fold) {
+    e = launch_pass<kPassW>(p, p.fcfg, p.gcfg, W, A, B, ws, st);   // W pass
+    if (e != hipSuccess) return e;
+  }
   if (p.dtype == 0) return launch_tail<bf16_t>(p, B, ws, s, m, eps, wnorm, g, st);
   return launch_tail<float>(p, B, ws, s, m, eps, wnorm, g, st);
 }

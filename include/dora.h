@@ -99,8 +99,10 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
  * general kernel configuration of the W pass, the same of the Gram pass,
  * d_in granule (elements), granules over d_in, d_in ranges of the W pass,
  * d_in ranges of the Gram pass, workspace bytes, W-pass grid and Gram-pass
- * grid of the streaming kernel, its LDS bytes in the W pass, and the rows
- * of its W-pass tile; entries past the last field are set to -1.
+ * grid of the streaming kernel, its LDS bytes in the W pass, the rows of
+ * its W-pass tile, and 1 if the streaming W pass computes G itself (no
+ * separate Gram pass; gram grid and ranges then do not apply), else 0;
+ * entries past the last field are set to -1.
  * Before returning it replays the plan on the host and checks that the
  * d_in ranges tile d_in exactly, every grid fits and every partial sum the
  * kernels write lies inside its workspace region; DORA_ERR_INVALID_ARG if
