@@ -7,7 +7,9 @@ Default workload: d_out = d_in = 8192, r = 384, s = 0.5, bf16, compose over
 T = 8192 rows (batch 2 x seq 4096).
 
 The fused compose backward (d_base, d_lora, dg, dm) is timed after the
-steps, on its own, and reported under "compose_backward".
+steps, on its own, and reported under "compose_backward"; "comparisons"
+holds the eager PyTorch compose and a PEFT-style dense norm (time and peak
+memory) measured the same way.
 
 Prints one JSON line. `value` is the factored norm's algorithmic TFLOP/s;
 the compose's GB/s and fraction of HBM peak, per-call times and the
@@ -15,6 +17,7 @@ roofline objects ride in the same line. Kernel times come from HIP events
 recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-backward]
+                    [--no-comparisons]
 """
 
 from __future__ import annotations
@@ -141,6 +144,86 @@ def time_compose_backward(args, w, lib, bnd, I, based, lorad, g, wnorm, stream, 
                     "reduction); timed separately, not part of the forward step"}
 
 
+def _event_ms(fn, reps, stream):
+    """Mean milliseconds of fn() over reps calls, HIP events on `stream`."""
+    import numpy as np
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for k in range(reps):
+        ev[k][0].record(stream)
+        fn()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def comparisons(args, w, bnd, Wd, Ad, Bd, based, lorad, g, md, comp_ms, norm_ms, stream, tdt):
+    """The pages' own comparisons, measured on this GPU (not part of a step):
+
+    - eager compose: the PyTorch expression (g-1)*base + g*(s*lora) in the
+      storage dtype, four elementwise launches over T x d_out, against the
+      fused compose;
+    - dense norm: the PEFT-style ||W + s*(B @ A)||_row, which materialises
+      the d_out x d_in product, against the factored norm, in time and in
+      peak allocator memory (torch.cuda.max_memory_allocated).
+    """
+    import torch
+
+    reps = max(3, min(args.steps, 20))
+    gb = g.to(tdt)
+    gm1 = gb - 1
+
+    def eager():
+        return gm1 * based + gb * (w.s * lorad)
+
+    for _ in range(2):
+        eager()
+    torch.cuda.synchronize()
+    eager_ms = _event_ms(eager, reps, stream)
+
+    def dense():
+        return torch.linalg.norm(Wd + w.s * (Bd @ Ad), dim=1)
+
+    ws_bytes = bnd.dora_norm_workspace_size(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
+
+    def factored():
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        return bnd.dora_factored_norm(Wd, Ad, Bd, w.s, budget_bytes=w.budget, m=md, eps=w.eps, workspace=ws)
+
+    def peak(fn):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base_mem = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        out = fn()
+        torch.cuda.synchronize()
+        extra = torch.cuda.max_memory_allocated() - base_mem
+        del out
+        return extra
+
+    dense()
+    torch.cuda.synchronize()
+    dense_ms = _event_ms(dense, reps, stream)
+    dense_peak = peak(dense)
+    fact_peak = peak(factored)
+    return {
+        "eager_compose_ms": eager_ms,
+        "fused_compose_ms": comp_ms,
+        "compose_speedup_vs_eager": eager_ms / comp_ms,
+        "dense_norm_ms": dense_ms,
+        "factored_norm_ms": norm_ms,
+        "norm_speedup_vs_dense": dense_ms / norm_ms,
+        "dense_norm_peak_bytes": dense_peak,
+        "factored_norm_peak_bytes": fact_peak,
+        "norm_memory_ratio": dense_peak / max(fact_peak, 1),
+        "note": "eager compose: 4 elementwise torch launches in the storage dtype; dense norm: "
+                "torch.linalg.norm(W + s*(B @ A), dim=1) as PEFT forms it; peaks are "
+                "torch.cuda.max_memory_allocated above the resident inputs, the factored one "
+                "including its workspace and wnorm/g outputs",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +233,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separately timed compose backward")
+    ap.add_argument("--no-comparisons", action="store_true",
+                    help="skip the eager-compose and dense-norm comparisons")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling profiler byte counters)")
     ap.add_argument("--traffic", default=None,
@@ -309,6 +394,9 @@ def main() -> int:
         res["compose_backward"] = time_compose_backward(args, w, lib, bnd, I, based, lorad, g, wnorm, stream,
                                                         tdt, esize)
         res["compose_backward"]["traffic"] = traffic.get("compose_bwd")
+    if not args.no_comparisons:
+        print("# comparisons: eager compose, dense norm", file=sys.stderr, flush=True)
+        res["comparisons"] = comparisons(args, w, bnd, Wd, Ad, Bd, based, lorad, g, md, comp_ms, norm_ms, stream, tdt)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, W, A, B, base, lora, g.cpu().numpy())

@@ -27,6 +27,7 @@ __all__ = [
     "dora_norm_plan_info",
     "dora_factored_norm",
     "dora_magnitude_scale",
+    "dora_norm_to_dtype",
     "dora_compose",
     "DORA_BF16",
     "DORA_F32",
@@ -83,6 +84,7 @@ def load():
         "dora_factored_norm": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i64, _c_i64, _c_i64, _c_f, _c_sz, _c_p, _c_sz,
                                       _c_p, _c_p, _c_f, _c_p, _c_p]),
         "dora_magnitude_scale": (_c_i, [_c_p, _c_p, _c_f, _c_i64, _c_p, _c_p]),
+        "dora_norm_to_dtype": (_c_i, [_c_p, _c_i64, _c_i, _c_p, _c_p]),
         "dora_compose": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
         "dora_compose_backward_workspace_size": (_c_i, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
         "dora_compose_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p, _c_p,
@@ -201,6 +203,18 @@ def dora_magnitude_scale(m, wnorm, eps: float = 1e-6, g=None, stream=None):
         g = torch.empty_like(m)
     _call("dora_magnitude_scale", _ptr(m), _ptr(wnorm), eps, m.numel(), _ptr(g), _stream(stream))
     return g
+
+
+def dora_norm_to_dtype(wnorm, dtype, out=None, stream=None):
+    """wnorm (fp32 [n]) rounded to `dtype` (bfloat16 or float32), nearest even."""
+    _dev(wnorm, "wnorm")
+    if wnorm.dtype != torch.float32 or wnorm.dim() != 1:
+        raise ValueError("wnorm must be float32 [n]")
+    tdt = {DORA_BF16: torch.bfloat16, DORA_F32: torch.float32}[_dtype_code(dtype)]
+    if out is None:
+        out = torch.empty(wnorm.shape, dtype=tdt, device=wnorm.device)
+    _call("dora_norm_to_dtype", _ptr(wnorm), wnorm.numel(), _dtype_code(dtype), _ptr(out), _stream(stream))
+    return out
 
 
 def dora_compose(base, lora, g, s: float, out=None, stream=None):

@@ -356,6 +356,17 @@ dora_status dora_magnitude_scale(const float* m, const float* wnorm, float eps, 
   return hip_status(dora::launch_magnitude(m, wnorm, eps, d_out, g, static_cast<hipStream_t>(stream)));
 }
 
+dora_status dora_norm_to_dtype(const float* wnorm, int64_t n, int dtype, void* out, void* stream) {
+  if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;
+  if (n < 0 || n >= kMaxDim) return DORA_ERR_INVALID_ARG;
+  if (n == 0) return DORA_OK;
+  const int64_t es = esize(dtype);
+  if (wnorm == nullptr || out == nullptr || !aligned(wnorm, 4) || !aligned(out, (size_t)es))
+    return DORA_ERR_INVALID_ARG;
+  if (overlap(out, n * es, wnorm, n * 4)) return DORA_ERR_INVALID_ARG;
+  return hip_status(dora::launch_cast(wnorm, n, dtype, out, static_cast<hipStream_t>(stream)));
+}
+
 dora_status dora_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
                          int64_t d_out, void* out, void* stream) {
   if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;

@@ -959,6 +959,14 @@ __global__ __launch_bounds__(kThreads) void magnitude_kernel(const float* m, con
   g[j] = m[j] / d;
 }
 
+// out[j] = wnorm[j] rounded to the storage type (round to nearest even),
+// the cast that ends Algorithm 1 ("DoRA优化技术解析", cyqw.cn, §5.1, step 7).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void cast_kernel(const float* wnorm, int64_t n, T* out) {
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j < n) out[j] = from_f32<T>(wnorm[j]);
+}
+
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, int MODE>
@@ -1107,6 +1115,15 @@ hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t 
 hipError_t launch_magnitude(const float* m, const float* wnorm, float eps, int64_t n, float* g, hipStream_t st) {
   hipLaunchKernelGGL(magnitude_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, m,
                      wnorm, eps, n, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const float* wnorm, int64_t n, int dtype, void* out, hipStream_t st) {
+  const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+  if (dtype == 0)
+    hipLaunchKernelGGL(cast_kernel<bf16_t>, grid, dim3(kThreads), 0, st, wnorm, n, static_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL(cast_kernel<float>, grid, dim3(kThreads), 0, st, wnorm, n, static_cast<float*>(out));
   return hipGetLastError();
 }
 

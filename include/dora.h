@@ -156,6 +156,19 @@ dora_status dora_magnitude_scale(const float* m, const float* wnorm, float eps,
                                  int64_t d_out, float* g, void* stream);
 
 /*
+ * out[j] = wnorm[j] rounded to the storage type `dtype` (round to nearest
+ * even; DORA_F32 copies): the cast with which Algorithm 1 returns the norm
+ * (cyqw.cn §5.1, step 7). dora_factored_norm keeps wnorm and g in fp32;
+ * callers that want the pages' input-dtype norm apply this to its wnorm.
+ * wnorm: fp32 [n] device array; out: [n] device array of `dtype`, owned by
+ * the caller, not overlapping wnorm. Asynchronous on `stream`.
+ * Errors: DORA_ERR_INVALID_ARG (negative n, NULL pointer with n > 0,
+ * misaligned or overlapping pointers), DORA_ERR_UNSUPPORTED_DTYPE,
+ * DORA_ERR_HIP.
+ */
+dora_status dora_norm_to_dtype(const float* wnorm, int64_t n, int dtype, void* out, void* stream);
+
+/*
  * Stable magnitude compose (cyqw.cn §2.1, §2.1.1, §5.2):
  *
  *   out[t,j] = (g[j] - 1) * base[t,j] + g[j] * (s * lora[t,j])

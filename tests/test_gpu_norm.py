@@ -36,6 +36,9 @@ CASES = [
     ("one_row", 1, 64, 1, "bf16", 2.0, 15),
     ("kv_512x3584_r768", 512, 3584, 768, "bf16", 0.25, 40),   # workload, whole
     ("qproj_4096x4096_r64", 4096, 4096, 64, "bf16", 2.0, 1),  # workload, whole
+    # rsLoRA scale alpha / sqrt(r) (alpha = 16): s is no power of two
+    ("rslora_r384", 1000, 2048, 384, "bf16", 16.0 / 384 ** 0.5, 16),
+    ("rslora_r64_f32", 300, 640, 64, "f32", 16.0 / 64 ** 0.5 * 0.7, 17),
 ]
 
 
@@ -165,3 +168,24 @@ def test_budget_too_small_raises():
     with pytest.raises(bnd.DoraError) as e:
         bnd.dora_factored_norm(dev(W, "bf16"), dev(A, "bf16"), dev(B, "bf16"), 0.5, budget_bytes=4096)
     assert e.value.status == 3
+
+
+def test_norm_cast_to_input_dtype():
+    """The pages' Algorithm 1 returns wnorm in the input dtype (§5.1, step 7):
+    the cast is round-to-nearest-even of the fp32 wnorm, so the bf16 norm is
+    within half a bf16 ulp of the oracle plus the fp32 bound."""
+    d_out, d_in, r, s = 777, 1024, 96, 0.5
+    W, A, B = I.norm_inputs(d_out, d_in, r, "bf16", 18)
+    ref = O.dense_row_norm(W, A, B, s)
+    wn, _ = bnd.dora_factored_norm(dev(W, "bf16"), dev(A, "bf16"), dev(B, "bf16"), s)
+    out = bnd.dora_norm_to_dtype(wn, "bf16")
+    same = bnd.dora_norm_to_dtype(wn, "f32")
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16 and torch.equal(same, wn)
+    got = out.float().cpu().numpy().astype(np.float64)
+    # exactly the nearest-even bf16 of the fp32 wnorm the library returned
+    np.testing.assert_array_equal(got, O.round_to_dtype(wn.cpu().numpy().astype(np.float64), "bf16"))
+    from gpu_helpers import bf16_ulp
+    assert np.all(np.abs(got - ref) <= 0.5 * bf16_ulp(ref) + 1e-5 * ref)
+    with pytest.raises(bnd.DoraError):
+        bnd.dora_norm_to_dtype(wn, "bf16", out=wn.view(torch.bfloat16)[:d_out])   # overlaps wnorm
