@@ -59,6 +59,8 @@ __all__ = [
     "compose_f32_stable",
     "compose_f32_naive",
     "compose_backward",
+    "layer_output",
+    "dora_linear",
     "round_to_dtype",
     "table1_memory",
 ]
@@ -259,6 +261,31 @@ def compose_backward(dy, base, lora, g, s, wnorm=None, eps=None):
     if wnorm is None:
         return d_base, d_lora, dg
     return d_base, d_lora, dg, dg / np.where(_f64(wnorm) < eps, eps, _f64(wnorm))
+
+
+def layer_output(base, lora, g, s):
+    """y = base + delta, the DoRA layer's output from its two projections.
+
+    The compose delta is what the layer adds to the base projection
+    [P1 §2.1.1]; fp64.
+    """
+    return _f64(base) + compose(base, lora, g, s)
+
+
+def dora_linear(x, W, A, B, m, s, eps):
+    """The DoRA linear layer from its definition [P2 "The Problem"].
+
+    The adapted weight is W' = m * V / max(||V||_row, eps) with the
+    direction V = W + s B A, rows scaled by the magnitude m; the layer maps
+    x [T, d_in] to y = x W'^T [T, d_out]. Everything in fp64 with V formed
+    densely (weight space), which is independent of the activation-space
+    route the library takes (x W^T and (x A^T) B^T, then the compose).
+    """
+    x, W, A, B, m = (_f64(v) for v in (x, W, A, B, m))
+    V = W + s * (B @ A)
+    wn = np.sqrt(np.sum(V * V, axis=1))
+    scale = m / np.where(wn < eps, eps, wn)
+    return x @ (scale[:, None] * V).T
 
 
 def compose_naive(base, lora, g, s):

@@ -357,6 +357,59 @@ def test_compose_backward_exact_and_special_cases():
 
 # ------------------------------------------------------ planted mistakes ----
 
+def test_layer_output_and_linear_hand_worked():
+    """Hand-worked: B = 0, W = [3, 4], m = 10: the weight is renormalised to
+    10 * [3, 4] / 5 = [6, 8], so x = [1, 2] gives 1*6 + 2*8 = 22. With
+    W = [3, 0], A = [0, 1], B = [4], s = 1 the direction is [3, 4], its norm
+    5 = m, so g = 1 and x = [1, 1] gives 3 + 4 = 7."""
+    y = O.dora_linear(np.array([[1.0, 2.0]]), np.array([[3.0, 4.0]]), np.array([[1.0, 0.0]]),
+                      np.array([[0.0]]), np.array([10.0]), 1.0, 1e-6)
+    assert y.shape == (1, 1) and y[0, 0] == 22.0
+    y = O.dora_linear(np.array([[1.0, 1.0]]), np.array([[3.0, 0.0]]), np.array([[0.0, 1.0]]),
+                      np.array([[4.0]]), np.array([5.0]), 1.0, 1e-6)
+    assert y[0, 0] == 7.0
+    # layer output: base 2, lora 6, g = 1.5, s = 0.5 -> 2 + (0.5 * 2 + 1.5 * 3) = 7.5
+    assert O.layer_output(np.array([[2.0]]), np.array([[6.0]]), np.array([1.5]), 0.5)[0, 0] == 7.5
+
+
+def test_linear_weight_space_equals_activation_space():
+    """The weight-space definition (dense V, normalised rows) equals the
+    activation-space route base + compose(x W^T, x A^T B^T, g) with g from the
+    row norm; and layer_output = g * (base + s * lora) exactly in algebra."""
+    rng = np.random.default_rng(3)
+    T, d_out, d_in, r, s, eps = 7, 11, 13, 4, 0.75, 1e-6
+    x = rng.standard_normal((T, d_in))
+    W = rng.standard_normal((d_out, d_in)) / 4
+    A = rng.standard_normal((r, d_in)) / 4
+    B = rng.standard_normal((d_out, r)) / 4
+    m = rng.uniform(0.5, 2.0, d_out)
+    y = O.dora_linear(x, W, A, B, m, s, eps)
+    g = O.magnitude_scale(m, O.dense_row_norm(W, A, B, s), eps)
+    base, lora = x @ W.T, (x @ A.T) @ B.T
+    y2 = O.layer_output(base, lora, g, s)
+    np.testing.assert_allclose(y, y2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y2, g[None, :] * (base + s * lora), rtol=1e-13, atol=1e-13)
+    # m = ||V||: g = 1 and the layer is the plain LoRA layer x W^T + s x A^T B^T
+    y1 = O.dora_linear(x, W, A, B, O.dense_row_norm(W, A, B, s), s, eps)
+    np.testing.assert_allclose(y1, base + s * lora, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_without_adapter_is_weight_normalisation():
+    """B = 0 (the LoRA initialisation) leaves weight normalisation: each output
+    row j is m_j * <x, w_j> / ||w_j||, computed here one row at a time."""
+    rng = np.random.default_rng(4)
+    T, d_out, d_in, r = 5, 6, 9, 3
+    x = rng.standard_normal((T, d_in))
+    W = rng.standard_normal((d_out, d_in))
+    m = rng.uniform(0.5, 2.0, d_out)
+    y = O.dora_linear(x, W, rng.standard_normal((r, d_in)), np.zeros((d_out, r)), m, 2.0, 1e-6)
+    for j in range(d_out):
+        wj = W[j]
+        nrm = np.sqrt(sum(v * v for v in wj))
+        for t in range(T):
+            assert abs(y[t, j] - m[j] * sum(a * b for a, b in zip(x[t], wj)) / nrm) <= 1e-12 * (1 + abs(y[t, j]))
+
+
 def test_pins_reject_planted_mistakes():
     """Each mutant of the oracle must fail at least one of the checks above."""
     rng = np.random.default_rng(15)
@@ -440,3 +493,28 @@ def test_pins_reject_planted_mistakes():
     assert backward_ok(O.compose_backward)
     for kind in ("g instead of g-1", "dropped s on lora", "dg without lora", "s on base in dg"):
         assert not backward_ok(mut(kind)), kind
+
+    # The linear layer: the hand-worked example and the weight-space /
+    # activation-space identity catch each planted mistake.
+    xs = rng.standard_normal((3, 5))
+    Ws, As, Bs = rng.standard_normal((4, 5)), rng.standard_normal((2, 5)), rng.standard_normal((4, 2))
+    ms = rng.uniform(0.5, 2.0, 4)
+
+    def linear_ok(fn):
+        hand = fn(np.array([[1.0, 2.0]]), np.array([[3.0, 4.0]]), np.array([[1.0, 0.0]]),
+                  np.array([[0.0]]), np.array([10.0]), 1.0, 1e-6)[0, 0] == 22.0
+        gs = O.magnitude_scale(ms, O.dense_row_norm(Ws, As, Bs, 0.5), 1e-6)
+        ref = O.layer_output(xs @ Ws.T, (xs @ As.T) @ Bs.T, gs, 0.5)
+        return bool(hand and np.allclose(fn(xs, Ws, As, Bs, ms, 0.5, 1e-6), ref, rtol=1e-12, atol=1e-12))
+
+    def lin_mut(kind):
+        def fn(x, W, A, B, m, s, eps):
+            V = W + (1.0 if kind == "dropped s" else s) * (B @ A)
+            wn = np.sqrt(np.sum((W if kind == "norm of W" else V) ** 2, axis=1))
+            scale = (np.ones_like(m) if kind == "dropped magnitude" else m) / wn
+            return x @ (scale[:, None] * (W if kind == "product with W" else V)).T
+        return fn
+
+    assert linear_ok(O.dora_linear)
+    for kind in ("dropped s", "norm of W", "dropped magnitude", "product with W"):
+        assert not linear_ok(lin_mut(kind)), kind
