@@ -9,7 +9,9 @@ T = 8192 rows (batch 2 x seq 4096).
 The fused compose backward (d_base, d_lora, dg, dm) is timed after the
 steps, on its own, and reported under "compose_backward"; "comparisons"
 holds the eager PyTorch compose and a PEFT-style dense norm (time and peak
-memory) measured the same way.
+memory) measured the same way; "linear_forward" times the whole DoRA
+linear layer (projections by hipBLASLt, norm and output by libdora) at the
+workload's T beside a plain LoRA layer.
 
 Prints one JSON line. `value` is the factored norm's algorithmic TFLOP/s;
 the compose's GB/s and fraction of HBM peak, per-call times and the
@@ -17,7 +19,7 @@ roofline objects ride in the same line. Kernel times come from HIP events
 recorded on the stream the kernels run on.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-backward]
-                    [--no-comparisons]
+                    [--no-comparisons] [--no-linear]
 """
 
 from __future__ import annotations
@@ -224,6 +226,42 @@ def comparisons(args, w, bnd, Wd, Ad, Bd, based, lorad, g, md, comp_ms, norm_ms,
     }
 
 
+def linear_forward(args, w, I, Wd, Ad, Bd, md, stream, tdt):
+    """The whole DoRA linear layer at this workload's T (not part of a step):
+    x W^T and (x A^T) B^T by hipBLASLt, the factored norm and the single-pass
+    layer output by libdora; beside it the plain LoRA layer (the same two
+    products, then base + s * lora) to show what DoRA's magnitude costs."""
+    import torch
+
+    from dora_weight_norm_amd.layer import dora_linear
+
+    x = torch.from_numpy(I.activations(w.T, w.d_in, w.dtype, w.seed)).cuda().to(tdt)
+    reps = max(3, min(args.steps, 20))
+
+    def dora():
+        return dora_linear(x, Wd, Ad, Bd, md, w.s, eps=w.eps, budget_bytes=w.budget)
+
+    def lora():
+        return torch.mm(x, Wd.t()) + w.s * torch.mm(torch.mm(x, Ad.t()), Bd.t())
+
+    for fn in (dora, lora):
+        fn()
+    torch.cuda.synchronize()
+    dora_ms = _event_ms(dora, reps, stream)
+    lora_ms = _event_ms(lora, reps, stream)
+    flops = 2 * w.T * w.d_out * w.d_in + 2 * w.T * w.r * (w.d_in + w.d_out)
+    return {
+        "T": w.T,
+        "dora_linear_ms": dora_ms,
+        "tokens_per_s": w.T / (dora_ms * 1e-3),
+        "gemm_tflops": flops / (dora_ms * 1e-3) / 1e12,
+        "lora_linear_ms": lora_ms,
+        "dora_overhead_vs_lora": dora_ms / lora_ms,
+        "note": "y = x (m V/||V||)^T with V = W + sBA; projections by torch.mm (hipBLASLt), norm and "
+                "output by libdora; lora_linear is torch.mm(x, W^T) + s * (x A^T) B^T",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +273,8 @@ def main() -> int:
                     help="skip the separately timed compose backward")
     ap.add_argument("--no-comparisons", action="store_true",
                     help="skip the eager-compose and dense-norm comparisons")
+    ap.add_argument("--no-linear", action="store_true",
+                    help="skip the whole DoRA linear layer forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling profiler byte counters)")
     ap.add_argument("--traffic", default=None,
@@ -397,6 +437,9 @@ def main() -> int:
     if not args.no_comparisons:
         print("# comparisons: eager compose, dense norm", file=sys.stderr, flush=True)
         res["comparisons"] = comparisons(args, w, bnd, Wd, Ad, Bd, based, lorad, g, md, comp_ms, norm_ms, stream, tdt)
+    if not args.no_linear:
+        print("# whole DoRA linear layer", file=sys.stderr, flush=True)
+        res["linear_forward"] = linear_forward(args, w, I, Wd, Ad, Bd, md, stream, tdt)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, W, A, B, base, lora, g.cpu().numpy())

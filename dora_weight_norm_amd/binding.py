@@ -28,6 +28,7 @@ __all__ = [
     "dora_factored_norm",
     "dora_magnitude_scale",
     "dora_norm_to_dtype",
+    "dora_layer_output",
     "dora_compose",
     "DORA_BF16",
     "DORA_F32",
@@ -86,6 +87,7 @@ def load():
         "dora_magnitude_scale": (_c_i, [_c_p, _c_p, _c_f, _c_i64, _c_p, _c_p]),
         "dora_norm_to_dtype": (_c_i, [_c_p, _c_i64, _c_i, _c_p, _c_p]),
         "dora_compose": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
+        "dora_layer_output": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
         "dora_compose_backward_workspace_size": (_c_i, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
         "dora_compose_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                                          _c_p, _c_f, _c_p, _c_p, _c_sz, _c_p]),
@@ -217,8 +219,7 @@ def dora_norm_to_dtype(wnorm, dtype, out=None, stream=None):
     return out
 
 
-def dora_compose(base, lora, g, s: float, out=None, stream=None):
-    """out = (g - 1) * base + g * (s * lora), with g [d_out] scaling columns of [T, d_out]."""
+def _compose_call(name, base, lora, g, s, out, stream):
     for t, nm in ((base, "base"), (lora, "lora"), (g, "g")):
         _dev(t, nm)
     if base.shape != lora.shape or base.dtype != lora.dtype:
@@ -235,9 +236,18 @@ def dora_compose(base, lora, g, s: float, out=None, stream=None):
         _dev(out, "out")
         if out.shape != base.shape or out.dtype != base.dtype:
             raise ValueError("out must match base")
-    _call("dora_compose", _ptr(base), _ptr(lora), _ptr(g), s, dt, T, d_out, _ptr(out), _stream(stream))
+    _call(name, _ptr(base), _ptr(lora), _ptr(g), s, dt, T, d_out, _ptr(out), _stream(stream))
     return out
 
+
+def dora_compose(base, lora, g, s: float, out=None, stream=None):
+    """out = (g - 1) * base + g * (s * lora), with g [d_out] scaling columns of [T, d_out]."""
+    return _compose_call("dora_compose", base, lora, g, s, out, stream)
+
+
+def dora_layer_output(base, lora, g, s: float, y=None, stream=None):
+    """y = base + ((g - 1) * base + g * (s * lora)): the DoRA layer output, one rounding."""
+    return _compose_call("dora_layer_output", base, lora, g, s, y, stream)
 
 def dora_compose_backward_workspace_size(T: int, d_out: int) -> int:
     ws = _c_sz()

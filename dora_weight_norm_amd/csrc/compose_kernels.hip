@@ -15,6 +15,13 @@
 // from the L2 or the Infinity Cache. Arithmetic is fp32: s*lora first, then
 // one fused multiply-add g*(s*lora) + (g-1)*base, rounded once (RNE) to the
 // storage type.
+//
+// The same kernel with ADD writes the layer output instead of the delta,
+// y = base + delta (same page, §2.1.1: the compose result is added to the
+// base projection): delta is formed as above in fp32, base is added in
+// fp32, and y is rounded once to the storage type. That saves the separate
+// addition's extra pass (read base and delta, write y) and its second
+// rounding.
 #include "dora_device.h"
 #include "dora_launch.h"
 
@@ -73,7 +80,7 @@ __device__ __forceinline__ typename Strip<T, VEC>::V pack(const float (&f)[VEC])
   }
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool ADD>
 __global__ __launch_bounds__(256) void compose_kernel(const T* base, const T* lora, const float* __restrict__ g,
                                                       float s, int64_t T_rows, int64_t d_out, T* out) {
   using V = typename Strip<T, VEC>::V;
@@ -107,6 +114,7 @@ __global__ __launch_bounds__(256) void compose_kernel(const T* base, const T* lo
         for (int e = 0; e < VEC; ++e) {
           const float sl = s * l[e];
           o[e] = fmaf(gv[e], sl, gm1[e] * b[e]);
+          if constexpr (ADD) o[e] = o[e] + b[e];
         }
         const int64_t off = (t0 + u) * d_out + c0;
         __builtin_nontemporal_store(pack<T, VEC>(o), reinterpret_cast<V*>(out + off));
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(256) void compose_kernel(const T* base, const T* lo
   }
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool ADD>
 hipError_t launch(const void* base, const void* lora, const float* g, float s, int64_t T_rows, int64_t d_out,
                   void* out, hipStream_t st) {
   const int64_t ncg = d_out / VEC;
@@ -128,7 +136,7 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
   const int64_t row_iters = (T_rows + kUnroll - 1) / kUnroll;
   if (by > row_iters) by = row_iters;
   if (by > 65535) by = 65535;
-  hipLaunchKernelGGL((compose_kernel<T, VEC>), dim3((unsigned)bx, (unsigned)by), dim3((unsigned)tpb), 0, st,
+  hipLaunchKernelGGL((compose_kernel<T, VEC, ADD>), dim3((unsigned)bx, (unsigned)by), dim3((unsigned)tpb), 0, st,
                      static_cast<const T*>(base), static_cast<const T*>(lora), g, s, T_rows, d_out,
                      static_cast<T*>(out));
   return hipGetLastError();
@@ -305,13 +313,21 @@ hipError_t launch_bwd(const void* dy, const void* base, const void* lora, const 
 }  // namespace
 
 hipError_t launch_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
-                          int64_t d_out, void* out, bool vec, hipStream_t st) {
-  if (dtype == 0) {
-    return vec ? launch<bf16_t, 8>(base, lora, g, s, T, d_out, out, st)
-               : launch<bf16_t, 1>(base, lora, g, s, T, d_out, out, st);
+                          int64_t d_out, void* out, bool vec, bool add_base, hipStream_t st) {
+  if (add_base) {
+    if (dtype == 0) {
+      return vec ? launch<bf16_t, 8, true>(base, lora, g, s, T, d_out, out, st)
+                 : launch<bf16_t, 1, true>(base, lora, g, s, T, d_out, out, st);
+    }
+    return vec ? launch<float, 4, true>(base, lora, g, s, T, d_out, out, st)
+               : launch<float, 1, true>(base, lora, g, s, T, d_out, out, st);
   }
-  return vec ? launch<float, 4>(base, lora, g, s, T, d_out, out, st)
-             : launch<float, 1>(base, lora, g, s, T, d_out, out, st);
+  if (dtype == 0) {
+    return vec ? launch<bf16_t, 8, false>(base, lora, g, s, T, d_out, out, st)
+               : launch<bf16_t, 1, false>(base, lora, g, s, T, d_out, out, st);
+  }
+  return vec ? launch<float, 4, false>(base, lora, g, s, T, d_out, out, st)
+             : launch<float, 1, false>(base, lora, g, s, T, d_out, out, st);
 }
 
 size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out) {

@@ -228,6 +228,24 @@ bool plan_self_check(const NormPlan& p) {
 
 dora_status hip_status(hipError_t e) { return e == hipSuccess ? DORA_OK : DORA_ERR_HIP; }
 
+dora_status compose_checked(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
+                            int64_t d_out, void* out, bool add_base, void* stream) {
+  if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;
+  if (T < 0 || d_out < 0 || T >= kMaxDim * 64 || d_out >= kMaxDim || !isfinite(s)) return DORA_ERR_INVALID_ARG;
+  if (T == 0 || d_out == 0) return DORA_OK;
+  if (base == nullptr || lora == nullptr || g == nullptr || out == nullptr) return DORA_ERR_INVALID_ARG;
+  const int64_t es = esize(dtype);
+  if (!aligned(base, (size_t)es) || !aligned(lora, (size_t)es) || !aligned(out, (size_t)es) || !aligned(g, 4))
+    return DORA_ERR_INVALID_ARG;
+  const int64_t nE = T * d_out * es;
+  if (out != base && overlap(out, nE, base, nE)) return DORA_ERR_INVALID_ARG;
+  if (out != lora && overlap(out, nE, lora, nE)) return DORA_ERR_INVALID_ARG;
+  if (overlap(out, nE, g, d_out * 4)) return DORA_ERR_INVALID_ARG;
+  const bool vec = (d_out % epc(dtype)) == 0 && aligned(base, 16) && aligned(lora, 16) && aligned(out, 16);
+  return hip_status(dora::launch_compose(base, lora, g, s, dtype, T, d_out, out, vec, add_base,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -369,20 +387,12 @@ dora_status dora_norm_to_dtype(const float* wnorm, int64_t n, int dtype, void* o
 
 dora_status dora_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
                          int64_t d_out, void* out, void* stream) {
-  if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;
-  if (T < 0 || d_out < 0 || T >= kMaxDim * 64 || d_out >= kMaxDim || !isfinite(s)) return DORA_ERR_INVALID_ARG;
-  if (T == 0 || d_out == 0) return DORA_OK;
-  if (base == nullptr || lora == nullptr || g == nullptr || out == nullptr) return DORA_ERR_INVALID_ARG;
-  const int64_t es = esize(dtype);
-  if (!aligned(base, (size_t)es) || !aligned(lora, (size_t)es) || !aligned(out, (size_t)es) || !aligned(g, 4))
-    return DORA_ERR_INVALID_ARG;
-  const int64_t nE = T * d_out * es;
-  if (out != base && overlap(out, nE, base, nE)) return DORA_ERR_INVALID_ARG;
-  if (out != lora && overlap(out, nE, lora, nE)) return DORA_ERR_INVALID_ARG;
-  if (overlap(out, nE, g, d_out * 4)) return DORA_ERR_INVALID_ARG;
-  const bool vec = (d_out % epc(dtype)) == 0 && aligned(base, 16) && aligned(lora, 16) && aligned(out, 16);
-  return hip_status(
-      dora::launch_compose(base, lora, g, s, dtype, T, d_out, out, vec, static_cast<hipStream_t>(stream)));
+  return compose_checked(base, lora, g, s, dtype, T, d_out, out, false, stream);
+}
+
+dora_status dora_layer_output(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
+                              int64_t d_out, void* y, void* stream) {
+  return compose_checked(base, lora, g, s, dtype, T, d_out, y, true, stream);
 }
 
 dora_status dora_compose_backward_workspace_size(int64_t T, int64_t d_out, size_t* ws_bytes) {

@@ -16,7 +16,7 @@ hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t 
 hipError_t launch_magnitude(const float* m, const float* wnorm, float eps, int64_t n, float* g, hipStream_t st);
 hipError_t launch_cast(const float* wnorm, int64_t n, int dtype, void* out, hipStream_t st);
 hipError_t launch_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
-                          int64_t d_out, void* out, bool vec, hipStream_t st);
+                          int64_t d_out, void* out, bool vec, bool add_base, hipStream_t st);
 size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out);
 hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora, const float* g, float s, int dtype,
                               int64_t T, int64_t d_out, void* d_base, void* d_lora, float* dg, const float* wnorm,

@@ -39,12 +39,13 @@ __all__ = [
     "compose_inputs",
     "m_noise",
     "grad_inputs",
+    "activations",
 ]
 
 MiB = 1 << 20
 
 # Stream ids, one per tensor.
-STREAMS = {"W": 0, "A": 1, "B": 2, "m_noise": 3, "base": 4, "lora": 5, "g": 6, "dy": 7, "wnorm": 8}
+STREAMS = {"W": 0, "A": 1, "B": 2, "m_noise": 3, "base": 4, "lora": 5, "g": 6, "dy": 7, "wnorm": 8, "x": 9}
 
 G_SPREAD = 0.0015      # std of the magnitude scale g around 1
 B_STD = 0.02
@@ -140,3 +141,9 @@ def grad_inputs(T: int, d_out: int, dtype: str, seed: int):
     dy = to_storage(normal(seed, "dy", (T, d_out)), dtype)
     wnorm = (1.0 + np.abs(normal(seed, "wnorm", (d_out,)))).astype(np.float32)
     return dy, wnorm
+
+
+def activations(T: int, d_in: int, dtype: str, seed: int):
+    """Layer input x [T, d_in] ~ N(0, 1) (storage values), for the whole
+    DoRA linear layer."""
+    return to_storage(normal(seed, "x", (T, d_in)), dtype)

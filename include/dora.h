@@ -190,6 +190,23 @@ dora_status dora_compose(const void* base, const void* lora, const float* g, flo
                          int dtype, int64_t T, int64_t d_out, void* out, void* stream);
 
 /*
+ * DoRA layer output: the compose delta added to the base projection
+ * (cyqw.cn §2.1.1: the layer returns base + delta; "Scaling DoRA",
+ * alanhou.org, "The Problem": the adapted weight is m * V / ||V||_row with
+ * V = W + sBA, so y = x V'^T = g * (base + s * lora) with base = x W^T,
+ * lora = x A^T B^T):
+ *
+ *   y[t,j] = base[t,j] + ((g[j] - 1) * base[t,j] + g[j] * (s * lora[t,j]))
+ *
+ * Same arguments, layout, ownership and errors as dora_compose, with y in
+ * place of out. The delta is formed in fp32 exactly as dora_compose forms
+ * it, base is added in fp32, and y is rounded once to the storage type, in
+ * the same single pass (base and lora read once, y written once).
+ */
+dora_status dora_layer_output(const void* base, const void* lora, const float* g, float s,
+                              int dtype, int64_t T, int64_t d_out, void* y, void* stream);
+
+/*
  * Workspace bytes dora_compose_backward needs to produce dg for a [T, d_out]
  * problem (at most 256 * d_out * 4). Host only. DORA_ERR_INVALID_ARG for
  * negative sizes or ws_bytes == NULL.
