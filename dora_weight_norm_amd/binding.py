@@ -32,6 +32,7 @@ __all__ = [
     "dora_compose",
     "DORA_BF16",
     "DORA_F32",
+    "DORA_F16",
     "PLAN_FIELDS",
     "dora_compose_backward",
     "dora_compose_backward_workspace_size",
@@ -41,6 +42,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdora.so"
 
 DORA_BF16 = 0
 DORA_F32 = 1
+DORA_F16 = 2
 DEFAULT_BUDGET = 256 << 20
 
 PLAN_FIELDS = (
@@ -119,7 +121,9 @@ def _dtype_code(dtype) -> int:
         return DORA_BF16
     if dtype in (torch.float32, "f32", DORA_F32):
         return DORA_F32
-    raise TypeError(f"unsupported dtype {dtype}; libdora takes bfloat16 or float32")
+    if dtype in (torch.float16, "f16", DORA_F16):
+        return DORA_F16
+    raise TypeError(f"unsupported dtype {dtype}; libdora takes bfloat16, float16 or float32")
 
 
 def _ptr(t):
@@ -165,7 +169,8 @@ def dora_factored_norm(W, A, B, s: float, budget_bytes: int = DEFAULT_BUDGET, m=
                        workspace=None, wnorm=None, g=None, stream=None):
     """wnorm = ||W + s B A||_row (fp32) and, if m is given, g = m / max(wnorm, eps).
 
-    W [d_out, d_in], A [r, d_in], B [d_out, r], all bfloat16 or all float32,
+    W [d_out, d_in], A [r, d_in], B [d_out, r], all of one dtype (bfloat16,
+    float16 or float32),
     on the GPU. Returns (wnorm, g); g is None when m is None.
     """
     for t, nm in ((W, "W"), (A, "A"), (B, "B")):
@@ -208,11 +213,11 @@ def dora_magnitude_scale(m, wnorm, eps: float = 1e-6, g=None, stream=None):
 
 
 def dora_norm_to_dtype(wnorm, dtype, out=None, stream=None):
-    """wnorm (fp32 [n]) rounded to `dtype` (bfloat16 or float32), nearest even."""
+    """wnorm (fp32 [n]) rounded to `dtype` (bfloat16, float16 or float32), nearest even."""
     _dev(wnorm, "wnorm")
     if wnorm.dtype != torch.float32 or wnorm.dim() != 1:
         raise ValueError("wnorm must be float32 [n]")
-    tdt = {DORA_BF16: torch.bfloat16, DORA_F32: torch.float32}[_dtype_code(dtype)]
+    tdt = {DORA_BF16: torch.bfloat16, DORA_F32: torch.float32, DORA_F16: torch.float16}[_dtype_code(dtype)]
     if out is None:
         out = torch.empty(wnorm.shape, dtype=tdt, device=wnorm.device)
     _call("dora_norm_to_dtype", _ptr(wnorm), wnorm.numel(), _dtype_code(dtype), _ptr(out), _stream(stream))

@@ -22,6 +22,8 @@
 // fp32, and y is rounded once to the storage type. That saves the separate
 // addition's extra pass (read base and delta, write y) and its second
 // rounding.
+#include <type_traits>
+
 #include "dora_device.h"
 #include "dora_launch.h"
 
@@ -42,6 +44,10 @@ struct Strip<bf16_t, 8> {
   using V = u32x4;
 };
 template <>
+struct Strip<f16_t, 8> {
+  using V = u32x4;
+};
+template <>
 struct Strip<float, 4> {
   using V = u32x4;
 };
@@ -50,6 +56,10 @@ template <typename T, int VEC>
 __device__ __forceinline__ void unpack(const typename Strip<T, VEC>::V& v, float (&f)[VEC]) {
   if constexpr (VEC == 1) {
     f[0] = to_f32(v);
+  } else if constexpr (std::is_same<T, f16_t>::value) {
+    const f16x8 h = __builtin_bit_cast(f16x8, v);   // the whole vector at once
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
   } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -66,6 +76,11 @@ template <typename T, int VEC>
 __device__ __forceinline__ typename Strip<T, VEC>::V pack(const float (&f)[VEC]) {
   if constexpr (VEC == 1) {
     return from_f32<T>(f[0]);
+  } else if constexpr (std::is_same<T, f16_t>::value) {
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (f16_t)f[i];   // round to nearest even
+    return __builtin_bit_cast(u32x4, h);
   } else if constexpr (sizeof(T) == 2) {
     u32x4 v;
 #pragma unroll
@@ -314,20 +329,23 @@ hipError_t launch_bwd(const void* dy, const void* base, const void* lora, const 
 
 hipError_t launch_compose(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
                           int64_t d_out, void* out, bool vec, bool add_base, hipStream_t st) {
+#define DORA_COMPOSE(ADD)                                                                      \
+  switch (dtype) {                                                                             \
+    case 0:                                                                                    \
+      return vec ? launch<bf16_t, 8, ADD>(base, lora, g, s, T, d_out, out, st)                 \
+                 : launch<bf16_t, 1, ADD>(base, lora, g, s, T, d_out, out, st);                \
+    case 2:                                                                                    \
+      return vec ? launch<f16_t, 8, ADD>(base, lora, g, s, T, d_out, out, st)                  \
+                 : launch<f16_t, 1, ADD>(base, lora, g, s, T, d_out, out, st);                 \
+    default:                                                                                   \
+      return vec ? launch<float, 4, ADD>(base, lora, g, s, T, d_out, out, st)                  \
+                 : launch<float, 1, ADD>(base, lora, g, s, T, d_out, out, st);                 \
+  }
   if (add_base) {
-    if (dtype == 0) {
-      return vec ? launch<bf16_t, 8, true>(base, lora, g, s, T, d_out, out, st)
-                 : launch<bf16_t, 1, true>(base, lora, g, s, T, d_out, out, st);
-    }
-    return vec ? launch<float, 4, true>(base, lora, g, s, T, d_out, out, st)
-               : launch<float, 1, true>(base, lora, g, s, T, d_out, out, st);
+    DORA_COMPOSE(true)
   }
-  if (dtype == 0) {
-    return vec ? launch<bf16_t, 8, false>(base, lora, g, s, T, d_out, out, st)
-               : launch<bf16_t, 1, false>(base, lora, g, s, T, d_out, out, st);
-  }
-  return vec ? launch<float, 4, false>(base, lora, g, s, T, d_out, out, st)
-             : launch<float, 1, false>(base, lora, g, s, T, d_out, out, st);
+  DORA_COMPOSE(false)
+#undef DORA_COMPOSE
 }
 
 size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out) {
@@ -341,12 +359,17 @@ hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora
                               int64_t T, int64_t d_out, void* d_base, void* d_lora, float* dg, const float* wnorm,
                               float eps, float* dm, void* ws, bool vec, hipStream_t st) {
   float* part = static_cast<float*>(ws);
-  if (dtype == 0) {
-    return vec ? launch_bwd<bf16_t, 8>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st)
-               : launch_bwd<bf16_t, 1>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st);
+  switch (dtype) {
+    case 0:
+      return vec ? launch_bwd<bf16_t, 8>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st)
+                 : launch_bwd<bf16_t, 1>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st);
+    case 2:
+      return vec ? launch_bwd<f16_t, 8>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st)
+                 : launch_bwd<f16_t, 1>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st);
+    default:
+      return vec ? launch_bwd<float, 4>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st)
+                 : launch_bwd<float, 1>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st);
   }
-  return vec ? launch_bwd<float, 4>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st)
-             : launch_bwd<float, 1>(dy, base, lora, g, s, T, d_out, d_base, d_lora, dg, wnorm, eps, dm, part, st);
 }
 
 }  // namespace dora

@@ -20,9 +20,9 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool valid_dtype(int dt) { return dt == DORA_BF16 || dt == DORA_F32; }
-int64_t esize(int dt) { return dt == DORA_BF16 ? 2 : 4; }
-int64_t epc(int dt) { return dt == DORA_BF16 ? 8 : 4; }
+bool valid_dtype(int dt) { return dt == DORA_BF16 || dt == DORA_F32 || dt == DORA_F16; }
+int64_t esize(int dt) { return dt == DORA_F32 ? 4 : 2; }
+int64_t epc(int dt) { return dt == DORA_F32 ? 4 : 8; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -90,6 +90,8 @@ void layout(NormPlan& p) {
   off = align_up(off + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4, kAlign);
   p.off_gg = off;
   off = align_up(off + (size_t)(p.r32 * p.r32) * 4, kAlign);   // bf16 hi and lo, or fp32
+  p.off_bf = off;
+  if (p.dtype == DORA_F16) off = align_up(off + (size_t)(p.d_out * p.r) * 4, kAlign);   // B widened to fp32
   p.ws_bytes = off;
 }
 
@@ -157,8 +159,9 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.ga_cols = (int64_t)p.n_nt_g * p.ntc_g;
   p.r32 = ceil_div(r, 32) * 32;
   // Gram-term tiles: the streaming kernel covers up to 384 columns of G in
-  // one tile (bf16; 128 for fp32) and uses 256-column tiles beyond; the
-  // general kernel uses kGramCols.
+  // one tile (bf16; 128 for fp32, and for fp16, whose Gram term runs in
+  // fp32) and uses 256-column tiles beyond; the general kernel uses
+  // kGramCols.
   if (dtype == DORA_BF16) {
     p.bcfg = p.r32 <= 384 ? (int)ceil_div(p.r32, 128) : 2;
   } else {
@@ -223,7 +226,8 @@ bool plan_self_check(const NormPlan& p) {
   if (p.off_ba < p.off_cross + (size_t)(p.xw * p.n_nt * p.ld_w) * 4) return false;
   if (p.off_g < p.off_ba + (size_t)((int64_t)(p.n_bt > p.n_cb ? p.n_bt : p.n_cb) * p.ld_w) * 4) return false;
   if (p.off_gg < p.off_g + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4) return false;
-  return p.ws_bytes >= p.off_gg + (size_t)(p.r32 * p.r32) * 4;
+  if (p.off_bf < p.off_gg + (size_t)(p.r32 * p.r32) * 4) return false;
+  return p.ws_bytes >= p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.r) * 4 : 0);
 }
 
 dora_status hip_status(hipError_t e) { return e == hipSuccess ? DORA_OK : DORA_ERR_HIP; }

@@ -10,8 +10,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Storage types: bf16 is carried as its 16 raw bits.
+// Storage types: bf16 is carried as its 16 raw bits; fp16 is the native
+// half type.
 typedef uint16_t bf16_t;
+typedef _Float16 f16_t;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 template <typename T>
 struct Elem;
@@ -20,6 +23,12 @@ struct Elem<bf16_t> {
   static constexpr int esz = 2;
   static constexpr int epc = 8;         // elements per 16-byte chunk
   static constexpr int frag_chunks = 1; // 16-byte chunks per MFMA operand fragment
+};
+template <>
+struct Elem<f16_t> {
+  static constexpr int esz = 2;
+  static constexpr int epc = 8;
+  static constexpr int frag_chunks = 1;
 };
 template <>
 struct Elem<float> {
@@ -37,12 +46,15 @@ __device__ __forceinline__ bf16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_bits_to_f32(v); }
+__device__ __forceinline__ float to_f32(f16_t v) { return (float)v; }
 __device__ __forceinline__ float to_f32(float v) { return v; }
 
 template <typename T>
 __device__ __forceinline__ T from_f32(float f);
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return f32_to_bf16_rne(f); }
+template <>
+__device__ __forceinline__ f16_t from_f32<f16_t>(float f) { return (f16_t)f; }   // round to nearest even
 template <>
 __device__ __forceinline__ float from_f32<float>(float f) { return f; }
 
@@ -57,6 +69,16 @@ __device__ __forceinline__ float chunk_sumsq(const u32x4& v, bf16_t) {
   q = __builtin_amdgcn_fdot2_f32_bf16(h.s23, h.s23, q, false);
   q = __builtin_amdgcn_fdot2_f32_bf16(h.s45, h.s45, q, false);
   q = __builtin_amdgcn_fdot2_f32_bf16(h.s67, h.s67, q, false);
+  return q;
+}
+// fp16: v_dot2_f32_f16 on pairs (each fp16 square is exact in fp32).
+__device__ __forceinline__ float chunk_sumsq(const u32x4& v, f16_t) {
+  const f16x8 h = __builtin_bit_cast(f16x8, v);
+  float q = 0.f;
+  q = __builtin_amdgcn_fdot2(h.s01, h.s01, q, false);
+  q = __builtin_amdgcn_fdot2(h.s23, h.s23, q, false);
+  q = __builtin_amdgcn_fdot2(h.s45, h.s45, q, false);
+  q = __builtin_amdgcn_fdot2(h.s67, h.s67, q, false);
   return q;
 }
 __device__ __forceinline__ float chunk_sumsq(const u32x4& v, float) {
@@ -109,7 +131,8 @@ __device__ __forceinline__ int swz(int row, int c) {
 }
 
 // acc += A_frag * B_frag over one 16-deep slice of K.
-// bf16: one v_mfma_f32_32x32x16_bf16. fp32: eight v_mfma_f32_32x32x2_f32,
+// bf16: one v_mfma_f32_32x32x16_bf16; fp16: one v_mfma_f32_32x32x16_f16.
+// fp32: eight v_mfma_f32_32x32x2_f32,
 // element e of both fragments forming the e-th pair of K indices.
 template <typename T>
 struct Mfma;
@@ -118,6 +141,13 @@ struct Mfma<bf16_t> {
   static __device__ __forceinline__ f32x16 run(const u32x4* a, const u32x4* b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
                                                    __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<f16_t> {
+  static __device__ __forceinline__ f32x16 run(const u32x4* a, const u32x4* b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]), __builtin_bit_cast(f16x8, b[0]),
+                                                  c, 0, 0, 0);
   }
 };
 template <>

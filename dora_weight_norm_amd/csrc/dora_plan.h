@@ -73,7 +73,7 @@ enum NormMode : int { kModeEmpty = 0, kModeRowOnly = 1, kModeFactored = 2 };
 
 struct NormPlan {
   int64_t d_out, d_in, r;
-  int dtype;            // 0 = bf16, 1 = fp32
+  int dtype;            // 0 = bf16, 1 = fp32, 2 = fp16
   int mode;             // NormMode
   int ntc;              // W pass: columns of one column tile (a multiple of 32)
   int n_nt;             // W pass: column tiles over r
@@ -101,6 +101,7 @@ struct NormPlan {
   size_t off_ba;        // [max(n_bt, n_cb)][ld_w] fp32 Gram-term partials
   size_t off_g;         // [max(xg, xw if gfold)][ga_rows][ga_cols] fp32 Gram partials
   size_t off_gg;        // reduced Gram matrix: bf16 [r32][Ghi | Glo], fp32 [r32][r32]
+  size_t off_bf;        // fp16 inputs only: B widened to fp32 [d_out][r] for the Gram term
   size_t ws_bytes;
 };
 

@@ -967,6 +967,12 @@ __global__ __launch_bounds__(kThreads) void cast_kernel(const float* wnorm, int6
   if (j < n) out[j] = from_f32<T>(wnorm[j]);
 }
 
+// out[i] = in[i] as fp32 (exact).
+__global__ __launch_bounds__(kThreads) void widen_kernel(const f16_t* in, int64_t n, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) out[i] = (float)in[i];
+}
+
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, int MODE>
@@ -998,7 +1004,8 @@ hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const voi
   return hipGetLastError();
 }
 
-template <int MODE>
+// H is the 16-bit storage type (bf16 or fp16); fp32 uses the F* configurations.
+template <int MODE, typename H>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
                        char* ws, hipStream_t st) {
   constexpr bool GRAM = MODE == kPassGram;
@@ -1006,19 +1013,19 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
   if (p.fast) {
     // The Gram pass only uses the 64- and 128-column configurations.
     switch (fcfg) {
-      case kFastB64: return launch_fast<bf16_t, 4, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
-      case kFastB128: return launch_fast<bf16_t, 2, 4, 2, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastB64: return launch_fast<H, 4, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastB128: return launch_fast<H, 2, 4, 2, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
       case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
       case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
       default: break;
     }
     if constexpr (!GRAM) {
       switch (fcfg) {
-        case kFastB256: return launch_fast<bf16_t, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
-        case kFastB384: return launch_fast<bf16_t, 2, 4, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
+        case kFastB256: return launch_fast<H, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
+        case kFastB384: return launch_fast<H, 2, 4, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
         case kFastB512:
           if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
-          else return launch_fast<bf16_t, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
+          else return launch_fast<H, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
         default: break;
       }
     }
@@ -1028,16 +1035,23 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
     return hipErrorInvalidValue;   // the general kernel never folds the Gram blocks in
   } else {
     switch (gcfg) {
-      case kGenB64: return launch_gen<bf16_t, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB128: return launch_gen<bf16_t, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB256: return launch_gen<bf16_t, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB384: return launch_gen<bf16_t, 2, 4, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB512: return launch_gen<bf16_t, 1, 4, 2, 4, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB64: return launch_gen<H, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB128: return launch_gen<H, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB256: return launch_gen<H, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB384: return launch_gen<H, 2, 4, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB512: return launch_gen<H, 1, 4, 2, 4, 64, GRAM>(p, M, A, B, ws, st);
       case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st);
       case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st);
       default: return hipErrorInvalidValue;
     }
   }
+}
+
+template <int MODE>
+hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
+                       char* ws, hipStream_t st) {
+  return p.dtype == 2 ? launch_pass<MODE, f16_t>(p, fcfg, gcfg, M, A, B, ws, st)
+                      : launch_pass<MODE, bf16_t>(p, fcfg, gcfg, M, A, B, ws, st);
 }
 
 template <typename T>
@@ -1088,6 +1102,8 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   if (e != hipSuccess) return e;
   NormPlan q = p;
   if (fold) q.xg = p.xw;   // one Gram partial per W-pass range
+  // bf16 keeps G as bf16 hi + lo for the bf16 Gram term; fp32 and fp16 keep
+  // it in fp32 (fp16's range cannot hold every G) for the fp32 Gram term.
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
                      dim3((unsigned)((p.r32 + kThreads - 1) / kThreads), (unsigned)p.r32), dim3(kThreads), 0, st,
                      q, ws);
@@ -1098,6 +1114,16 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
     if (e != hipSuccess) return e;
   }
   if (p.dtype == 0) return launch_tail<bf16_t>(p, B, ws, s, m, eps, wnorm, g, st);
+  if (p.dtype == 2) {
+    // fp16: the Gram term runs in fp32 on B widened (exactly) into the workspace.
+    float* Bf = reinterpret_cast<float*>(ws + p.off_bf);
+    const int64_t nB = p.d_out * p.r;
+    hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((nB + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                       static_cast<const f16_t*>(B), nB, Bf);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_tail<float>(p, Bf, ws, s, m, eps, wnorm, g, st);
+  }
   return launch_tail<float>(p, B, ws, s, m, eps, wnorm, g, st);
 }
 
@@ -1106,6 +1132,9 @@ hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t 
   if (dtype == 0)
     hipLaunchKernelGGL((norm_rowonly_kernel<bf16_t>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(W), d_out, d_in, vec, m, eps, wnorm, g);
+  else if (dtype == 2)
+    hipLaunchKernelGGL((norm_rowonly_kernel<f16_t>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
+                       static_cast<const f16_t*>(W), d_out, d_in, vec, m, eps, wnorm, g);
   else
     hipLaunchKernelGGL((norm_rowonly_kernel<float>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
                        static_cast<const float*>(W), d_out, d_in, vec, m, eps, wnorm, g);
@@ -1122,6 +1151,8 @@ hipError_t launch_cast(const float* wnorm, int64_t n, int dtype, void* out, hipS
   const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
   if (dtype == 0)
     hipLaunchKernelGGL(cast_kernel<bf16_t>, grid, dim3(kThreads), 0, st, wnorm, n, static_cast<bf16_t*>(out));
+  else if (dtype == 2)
+    hipLaunchKernelGGL(cast_kernel<f16_t>, grid, dim3(kThreads), 0, st, wnorm, n, static_cast<f16_t*>(out));
   else
     hipLaunchKernelGGL(cast_kernel<float>, grid, dim3(kThreads), 0, st, wnorm, n, static_cast<float*>(out));
   return hipGetLastError();

@@ -104,12 +104,14 @@ def _f32_to_bf16_values(x32: np.ndarray) -> np.ndarray:
 
 
 def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
-    """fp64 -> fp32 (RNE) -> bf16 (RNE) if dtype == 'bf16'; float32 result."""
+    """fp64 -> fp32 (RNE) -> bf16 or fp16 (RNE) for those dtypes; float32 result."""
     x32 = np.ascontiguousarray(x64, dtype=np.float32)
     if dtype == "f32":
         return x32
     if dtype == "bf16":
         return _f32_to_bf16_values(x32)
+    if dtype == "f16":
+        return x32.astype(np.float16).astype(np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

@@ -58,7 +58,9 @@ typedef enum dora_status {
 
 typedef enum dora_dtype {
   DORA_BF16 = 0, /* bfloat16 storage, fp32 arithmetic */
-  DORA_F32 = 1   /* binary32 storage and arithmetic   */
+  DORA_F32 = 1,  /* binary32 storage and arithmetic   */
+  DORA_F16 = 2   /* binary16 storage, fp32 arithmetic (accumulation and the
+                    Gram term in fp32: G may exceed binary16's range) */
 } dora_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */

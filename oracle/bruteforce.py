@@ -77,3 +77,32 @@ def round_fraction_bf16(q: Fraction) -> Fraction:
     if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
         fl += 1
     return sign * fl * spacing
+
+
+def round_fraction_f16(q: Fraction):
+    """Round an exact rational to IEEE binary16, ties to even, on integers.
+
+    11 significant bits in the normal range (exponents -14 .. 15), a fixed
+    spacing of 2^-24 below 2^-14 (subnormals), and +-inf at or beyond the
+    midpoint 65520 between the largest finite value 65504 and 2^16.
+    Returns a Fraction, or +-float('inf').
+    """
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = 0
+    while a >= 2 ** (e + 1):
+        e += 1
+    while a < Fraction(2) ** e:
+        e -= 1
+    spacing = Fraction(2) ** (max(e, -14) - 10)
+    n = a / spacing
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * spacing
+    if v > 65504:
+        return sign * float("inf")
+    return sign * v

@@ -49,6 +49,7 @@ import numpy as np
 __all__ = [
     "bf16_round",
     "f32_round",
+    "f16_round",
     "dense_row_norm",
     "chunk_size",
     "algorithm1_row_norm",
@@ -107,10 +108,20 @@ def f32_round(x):
     return _f64(x).astype(np.float32).astype(np.float64)
 
 
+def f16_round(x):
+    """Round fp64 values once to IEEE binary16, nearest even (numpy's
+    float64 -> float16 conversion, a correctly rounded library routine);
+    returned as fp64. Overflow goes to +-inf, as IEEE rounding does."""
+    with np.errstate(over="ignore"):
+        return _f64(x).astype(np.float16).astype(np.float64)
+
+
 def round_to_dtype(x, dtype: str):
-    """Round once from fp64 to the output storage type ('bf16' or 'f32')."""
+    """Round once from fp64 to the output storage type ('bf16', 'f16' or 'f32')."""
     if dtype == "bf16":
         return bf16_round(x)
+    if dtype == "f16":
+        return f16_round(x)
     if dtype == "f32":
         return f32_round(x)
     raise ValueError(f"unknown dtype {dtype!r}")

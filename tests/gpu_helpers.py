@@ -7,7 +7,7 @@ from dora_weight_norm_amd import binding as bnd
 from dora_weight_norm_amd import inputs as I
 from oracle import dora_oracle as O
 
-TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}
 NORM_RTOL = 1e-5          # wnorm vs the fp64 oracle, relative
 
 
@@ -60,19 +60,32 @@ def ulp32(x: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.frexp(ax)[1] - 24)
 
 
-def check_compose(out_gpu: torch.Tensor, base, lora, g, s, dtype):
-    """The bar: within 1 bf16 ulp of the oracle's output, for every storage type.
+def f16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of binary16 numbers at |x| (2^-24 in the subnormal range)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -14)
+    return np.ldexp(1.0, np.frexp(ax)[1] - 11)
 
-    bf16: |out - RNE_bf16(ref)| <= 1 bf16 ulp.
+
+def storage_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The compose bar's unit: a bf16 ulp for bf16 and fp32 storage (fp32 also
+    gets its own tighter bound), an fp16 ulp for fp16 storage."""
+    return f16_ulp(x) if dtype == "f16" else bf16_ulp(x)
+
+
+def check_compose(out_gpu: torch.Tensor, base, lora, g, s, dtype):
+    """The bar: within 1 ulp of the oracle's output (bf16 ulp for bf16 and
+    fp32 storage, fp16 ulp for fp16).
+
+    bf16, f16: |out - RNE(ref)| <= 1 ulp of the storage type.
     f32 : additionally the bound the evaluation order implies,
           fma(g, RN(s*lora), RN((g-1)*base)): half an ulp of each rounded
-          operand plus one ulp of the result. Returns the worst error in bf16 ulps.
+          operand plus one ulp of the result. Returns the worst error in ulps.
     """
     ref = O.compose(base, lora, g, s)
     got = out_gpu.float().cpu().numpy().astype(np.float64)
     err = np.abs(got - O.round_to_dtype(ref, dtype))
-    ub = bf16_ulp(ref)
-    assert np.all(err <= ub), f"max err {np.max(err / ub):.2f} bf16 ulp"
+    ub = storage_ulp(ref, dtype)
+    assert np.all(err <= ub), f"max err {np.max(err / ub):.2f} ulp"
     if dtype == "f32":
         g2 = np.asarray(g, np.float64)[None, :]
         t = np.abs((g2 - 1.0) * base)

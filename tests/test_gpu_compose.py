@@ -46,7 +46,8 @@ def test_compose_workload_sampled_rows(name):
 
 
 @pytest.mark.parametrize("T,d_out,dtype", [(37, 1001, "bf16"), (5, 3, "f32"), (129, 520, "bf16"),
-                                           (64, 250, "f32"), (1, 8, "bf16")])
+                                           (64, 250, "f32"), (1, 8, "bf16"), (37, 1001, "f16"),
+                                           (512, 4096, "f16")])
 def test_compose_ragged_shapes(T, d_out, dtype):
     base, lora, g = I.compose_inputs(T, d_out, dtype, 31)
     out = bnd.dora_compose(dev(base, dtype), dev(lora, dtype), torch.from_numpy(g).cuda(), 0.5)

@@ -17,7 +17,7 @@ from dora_weight_norm_amd import binding as bnd
 from dora_weight_norm_amd import inputs as I
 from oracle import dora_oracle as O
 
-from gpu_helpers import bf16_ulp, dev, say, ulp32
+from gpu_helpers import dev, say, storage_ulp, ulp32
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +33,8 @@ def _inputs(T, d_out, dtype, seed):
 def _check_elem(got_t, ref, dtype, what):
     got = got_t.float().cpu().numpy().astype(np.float64)
     err = np.abs(got - O.round_to_dtype(ref, dtype))
-    ub = bf16_ulp(ref)
-    assert np.all(err <= ub), f"{what}: max err {np.max(err / ub):.2f} bf16 ulp"
+    ub = storage_ulp(ref, dtype)
+    assert np.all(err <= ub), f"{what}: max err {np.max(err / ub):.2f} ulp"
     if dtype == "f32":
         e32 = np.abs(got - ref)
         assert np.all(e32 <= 2 * ulp32(np.abs(ref))), f"{what}: fp32 bound exceeded"
@@ -58,6 +58,8 @@ CASES = [
     ("ragged_bf16", 37, 1001, "bf16", 0.5, 5),
     ("ragged_f32", 129, 250, "f32", 0.75, 6),
     ("one_row", 1, 8, "bf16", 2.0, 7),
+    ("f16", 256, 2048, "f16", 0.5, 8),
+    ("f16_ragged", 37, 1001, "f16", 0.75, 9),
 ]
 
 

@@ -28,7 +28,7 @@ from dora_weight_norm_amd import inputs as I
 from dora_weight_norm_amd.layer import dora_linear
 from oracle import dora_oracle as O
 
-from gpu_helpers import bf16_ulp, dev, magnitude, say, ulp32
+from gpu_helpers import bf16_ulp, dev, f16_ulp, magnitude, say, ulp32
 
 pytestmark = pytest.mark.gpu
 
@@ -37,11 +37,11 @@ EPS = 1e-6
 
 
 def _ulp(x, dtype):
-    return bf16_ulp(x) if dtype == "bf16" else ulp32(x)
+    return {"bf16": bf16_ulp, "f16": f16_ulp, "f32": ulp32}[dtype](x)
 
 
 @pytest.mark.parametrize("T,d_out,dtype,s", [(64, 1000, "bf16", 0.5), (129, 250, "f32", 0.75),
-                                             (33, 520, "bf16", 16.0 / 384 ** 0.5)])
+                                             (33, 520, "bf16", 16.0 / 384 ** 0.5), (64, 1000, "f16", 0.5)])
 def test_layer_output_matches_oracle(T, d_out, dtype, s):
     base, lora, g = I.compose_inputs(T, d_out, dtype, 41)
     y = bnd.dora_layer_output(dev(base, dtype), dev(lora, dtype), torch.from_numpy(g).cuda(), s)
@@ -66,6 +66,7 @@ CASES = [
     ("f32_tiny_workload", 64, 256, 256, 8, "f32", 2.0, 0, None),
     ("bf16_r384_batched", 96, 512, 2048, 384, "bf16", 0.5, 51, (2, 48)),
     ("bf16_rslora", 40, 384, 1536, 64, "bf16", 16.0 / 64 ** 0.5, 52, None),
+    ("f16_r384", 64, 512, 2048, 384, "f16", 0.5, 53, None),
 ]
 
 

@@ -39,6 +39,12 @@ CASES = [
     # rsLoRA scale alpha / sqrt(r) (alpha = 16): s is no power of two
     ("rslora_r384", 1000, 2048, 384, "bf16", 16.0 / 384 ** 0.5, 16),
     ("rslora_r64_f32", 300, 640, 64, "f32", 16.0 / 64 ** 0.5 * 0.7, 17),
+    # fp16 storage: fp16 matrix cores, fp32 Gram term on B widened to fp32
+    ("f16_ragged_vec", 300, 1000, 40, "f16", 0.5, 60),
+    ("f16_r384", 1000, 2048, 384, "f16", 0.5, 61),
+    ("f16_scalar_loads", 257, 1001, 13, "f16", 0.75, 62),
+    ("f16_qproj_folded_gram", 4096, 4096, 64, "f16", 2.0, 63),
+    ("f16_r700_tiles", 300, 1024, 700, "f16", 0.25, 64),
 ]
 
 

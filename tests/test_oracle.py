@@ -279,6 +279,21 @@ def test_bf16_round_matches_torch_and_ties():
         assert O.bf16_round(v) == float(bf.round_fraction_bf16(Fraction(v)))
 
 
+def test_f16_round_matches_exact_rounding():
+    """The oracle's fp16 rounding against exact rational rounding (ties to
+    even, subnormals, overflow to inf)."""
+    rng = np.random.default_rng(14)
+    vals = list(rng.standard_normal(300) * 3.0) + list(rng.standard_normal(50) * 1e-5)
+    vals += [1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, -(1.0 + 2.0 ** -11), 65504.0, 65519.0, 65520.0,
+             -65520.0, 2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -14 + 2.0 ** -25, 0.1, 1.0 / 3.0]
+    for v in vals:
+        want = bf.round_fraction_f16(Fraction(v))
+        got = O.f16_round(v)
+        assert (got == want) if isinstance(want, Fraction) else (got == want), (v, got, want)
+    assert O.f16_round(1.0 + 2.0 ** -11) == 1.0 and O.f16_round(1.0 + 3 * 2.0 ** -11) == 1.0 + 2.0 ** -9
+    assert O.f16_round(65520.0) == np.inf and O.f16_round(3 * 2.0 ** -25) == 2.0 ** -23
+
+
 def test_stable_compose_beats_naive_near_one():
     # Near g = 1 the naive form cancels; the stable form keeps (g-1) explicit.
     rng = np.random.default_rng(14)
