@@ -49,7 +49,10 @@ def kernel_role(name: str) -> str | None:
     if "compose_bwd" in name:
         return "compose_bwd"
     if "compose_kernel" in name:
-        return "compose"
+        # compose_kernel<T, VEC, ADD>: ADD = true is the layer output
+        return "layer_output" if re.search(r"compose_kernel<[^>]*true>", name) else "compose"
+    if "widen_kernel" in name or "cast_kernel" in name:
+        return "norm"
     return "norm"
 
 
@@ -128,7 +131,7 @@ def main() -> int:
         role = kernel_role(s["name"])
         part_calls[role] = min(part_calls.get(role, s["calls"]), s["calls"])
     steps = part_calls["compose"]
-    traffic = {"norm": 0.0, "compose": 0.0, "compose_bwd": 0.0}
+    traffic = {"norm": 0.0, "compose": 0.0, "compose_bwd": 0.0, "layer_output": 0.0}
     lines = []
     for s in sorted(ours, key=lambda s: -s["total_us"]):
         role = kernel_role(s["name"])
