@@ -149,6 +149,10 @@ def main() -> int:
 
     norm_us, comp_us = part_us("norm"), part_us("compose")
     bwd_us = part_us("compose_bwd") if "compose_bwd" in part_calls else 0.0
+    # The longest single launch of a step decides which roofline bench.py
+    # reports as the dominant kernel.
+    step_kernels = [s for s in ours if kernel_role(s["name"]) in ("norm", "compose")]
+    longest = max(step_kernels, key=lambda s: s["avg_us"])
 
     os.makedirs(args.out, exist_ok=True)
     tj = {"workload": args.workload, "source_hash": source_hash(),
@@ -156,6 +160,8 @@ def main() -> int:
           "fetch_scale": f_scale, "write_scale": w_scale,
           "compose_bwd_bytes_per_call": traffic["compose_bwd"],
           "norm_us_per_call": norm_us, "compose_us_per_call": comp_us, "compose_bwd_us_per_call": bwd_us,
+          "longest_step_kernel": {"name": short_name(longest["name"]), "part": kernel_role(longest["name"]),
+                                  "avg_us": longest["avg_us"]},
           "commands": {"fetch": args.cmd_fetch, "write": args.cmd_write}}
     with open(os.path.join(args.out, f"traffic_{args.workload}.json"), "w") as f:
         json.dump(tj, f, indent=1)
@@ -168,6 +174,7 @@ def main() -> int:
           "",
           f"- compose calls in the trace: {steps}; norm call = sum of its kernels = {norm_us:.2f} µs; "
           f"compose call = {comp_us:.2f} µs",
+          f"- longest single launch of a step: {short_name(longest['name'])} ({longest['avg_us']:.2f} µs)",
           f"- HBM traffic per norm call: {traffic['norm'] / 1e6:.1f} MB; per compose call: "
           f"{traffic['compose'] / 1e6:.1f} MB",
           f"- compose backward call (timed on its own after the steps) = {bwd_us:.2f} µs; HBM traffic "
