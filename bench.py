@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 F32_MFMA_PEAK_TFLOPS = 157.3
+NSETS = 3                       # input sets the steps rotate through
 METRIC = "factored-norm ms/TFLOP/s + compose GB/s (%HBM peak), 8192×8192 r=384 bf16"
 
 
@@ -317,25 +318,34 @@ def main() -> int:
     P = ctypes.c_void_p
     sptr = P(stream.cuda_stream)
     dt = bnd._dtype_code(w.dtype)
-    norm_args = (P(Wd.data_ptr()), P(Ad.data_ptr()), P(Bd.data_ptr()), dt, w.d_out, w.d_in, w.r, w.s, w.budget,
-                 P(ws.data_ptr()), ws_bytes, P(wnorm.data_ptr()), P(md.data_ptr()), w.eps, P(g.data_ptr()), sptr)
-    comp_args = (P(based.data_ptr()), P(lorad.data_ptr()), P(g.data_ptr()), w.s, dt, w.T, w.d_out,
-                 P(out.data_ptr()), sptr)
+    # Steps rotate through NSETS copies of the inputs (same values, distinct
+    # buffers): one step's W, A, B, base and lora take about 400 MB, so the
+    # three sets (1.2 GB) exceed the 256 MB Infinity Cache and the L2, and
+    # every step reads its inputs from HBM rather than from what the
+    # previous step left in the caches.
+    sets = [(Wd, Ad, Bd, based, lorad)] + [tuple(t.clone() for t in (Wd, Ad, Bd, based, lorad))
+                                           for _ in range(NSETS - 1)]
+    torch.cuda.synchronize()
+    norm_args = [(P(S[0].data_ptr()), P(S[1].data_ptr()), P(S[2].data_ptr()), dt, w.d_out, w.d_in, w.r, w.s,
+                  w.budget, P(ws.data_ptr()), ws_bytes, P(wnorm.data_ptr()), P(md.data_ptr()), w.eps,
+                  P(g.data_ptr()), sptr) for S in sets]
+    comp_args = [(P(S[3].data_ptr()), P(S[4].data_ptr()), P(g.data_ptr()), w.s, dt, w.T, w.d_out,
+                  P(out.data_ptr()), sptr) for S in sets]
 
-    def run_norm():
-        st = lib.dora_factored_norm(*norm_args)
+    def run_norm(k=0):
+        st = lib.dora_factored_norm(*norm_args[k % NSETS])
         if st:
             raise bnd.DoraError("dora_factored_norm", st)
 
-    def run_compose():
-        st = lib.dora_compose(*comp_args)
+    def run_compose(k=0):
+        st = lib.dora_compose(*comp_args[k % NSETS])
         if st:
             raise bnd.DoraError("dora_compose", st)
 
     print(f"# warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        run_norm()
-        run_compose()
+    for k in range(args.warmup):
+        run_norm(k)
+        run_compose(k)
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -353,9 +363,9 @@ def main() -> int:
     t0 = time.perf_counter()
     for k in range(K):
         ev[k][0].record(stream)
-        run_norm()
+        run_norm(k)
         ev[k][1].record(stream)
-        run_compose()
+        run_compose(k)
         ev[k][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

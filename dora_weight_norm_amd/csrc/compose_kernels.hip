@@ -145,8 +145,9 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
   int64_t tpb = ((ncg + 63) / 64) * 64;
   if (tpb > 256) tpb = 256;
   const int64_t bx = (ncg + tpb - 1) / tpb;
-  // About 8 resident workgroups per compute unit over 256 CUs.
-  int64_t by = 2048 / bx;
+  // About 16 workgroups per compute unit over 256 CUs (8 resident at a
+  // time): more, shorter row strips balance the tail of the grid better.
+  int64_t by = 4096 / bx;
   if (by < 1) by = 1;
   const int64_t row_iters = (T_rows + kUnroll - 1) / kUnroll;
   if (by > row_iters) by = row_iters;

@@ -78,6 +78,10 @@ void choose_tiles(NormPlan& p) {
 // pass with the Gram blocks folded in writes xw.
 int gram_planes(const NormPlan& p) { return p.gfold && p.xw > p.xg ? p.xw : p.xg; }
 
+// Gram-term partial planes: n_bt from the streaming kernel, n_cb from the
+// general one.
+int64_t ba_planes(const NormPlan& p) { return p.n_bt > p.n_cb ? p.n_bt : p.n_cb; }
+
 void layout(NormPlan& p) {
   size_t off = 0;
   p.off_base = off;
@@ -85,7 +89,7 @@ void layout(NormPlan& p) {
   p.off_cross = off;
   off = align_up(off + (size_t)((int64_t)p.xw * p.n_nt * p.ld_w) * 4, kAlign);
   p.off_ba = off;
-  off = align_up(off + (size_t)((int64_t)(p.n_bt > p.n_cb ? p.n_bt : p.n_cb) * p.ld_w) * 4, kAlign);
+  off = align_up(off + (size_t)(ba_planes(p) * p.ld_w) * 4, kAlign);
   p.off_g = off;
   off = align_up(off + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4, kAlign);
   p.off_gg = off;
@@ -224,7 +228,7 @@ bool plan_self_check(const NormPlan& p) {
   if (grid_w >= ((int64_t)1 << 31) || grid_g >= ((int64_t)1 << 31)) return false;
   if (p.off_cross < p.off_base + (size_t)(p.xw * p.ld_w) * 4) return false;
   if (p.off_ba < p.off_cross + (size_t)(p.xw * p.n_nt * p.ld_w) * 4) return false;
-  if (p.off_g < p.off_ba + (size_t)((int64_t)(p.n_bt > p.n_cb ? p.n_bt : p.n_cb) * p.ld_w) * 4) return false;
+  if (p.off_g < p.off_ba + (size_t)(ba_planes(p) * p.ld_w) * 4) return false;
   if (p.off_gg < p.off_g + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4) return false;
   if (p.off_bf < p.off_gg + (size_t)(p.r32 * p.r32) * 4) return false;
   return p.ws_bytes >= p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.r) * 4 : 0);

@@ -185,13 +185,8 @@ __device__ __forceinline__ float ordered_sum(const float* p, int64_t stride, int
 // every operation separately rounded (no contraction), sqrt and division
 // correctly rounded ("DoRA优化技术解析", cyqw.cn, §1.2.2, §5.2, §6.2). base and
 // cross are summed from their partials in a fixed order.
-__device__ __forceinline__ void assemble_row(const NormPlan& p, const char* ws, float s, float eps, const float* m,
-                                             float* wnorm, float* g, int64_t j, float ba) {
-  const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
-  const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
-  // Cross partials are planes (x, n) in the order x * n_nt + n.
-  const float base = ordered_sum(part_base + j, p.ld_w, p.xw);
-  const float cross = ordered_sum(part_cross + j, p.ld_w, p.xw * p.n_nt);
+__device__ __forceinline__ void assemble_sums(float base, float cross, float ba, float s, float eps, const float* m,
+                                              float* wnorm, float* g, int64_t j) {
   const float two_s = s + s;
   const float s2 = __fmul_rn(s, s);
   float val = __fadd_rn(__fadd_rn(base, __fmul_rn(two_s, cross)), __fmul_rn(s2, ba));
@@ -202,6 +197,16 @@ __device__ __forceinline__ void assemble_row(const NormPlan& p, const char* ws, 
     const float d = (wn < eps) ? eps : wn;
     g[j] = m[j] / d;
   }
+}
+
+__device__ __forceinline__ void assemble_row(const NormPlan& p, const char* ws, float s, float eps, const float* m,
+                                             float* wnorm, float* g, int64_t j, float ba) {
+  const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
+  const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
+  // Cross partials are planes (x, n) in the order x * n_nt + n.
+  const float base = ordered_sum(part_base + j, p.ld_w, p.xw);
+  const float cross = ordered_sum(part_cross + j, p.ld_w, p.xw * p.n_nt);
+  assemble_sums(base, cross, ba, s, eps, m, wnorm, g, j);
 }
 
 template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, int MODE>
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       }
     } else {
       float* part = reinterpret_cast<float*>(ws + (BG ? p.off_ba : p.off_cross));
-      const int64_t plane = BG ? (int64_t)n : (int64_t)x * p.n_nt + n;
+      const int64_t plane = (int64_t)x * n_nt + n;
       if (tid < MT) {
         float cs = 0.f;
 #pragma unroll
@@ -914,9 +919,30 @@ __global__ __launch_bounds__(kThreads) void assemble_kernel(NormPlan p, const ch
                                                             const float* m, float eps, float* wnorm, float* g) {
   const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (j >= p.d_out) return;
-  const float* part_ba = reinterpret_cast<const float*>(ws + p.off_ba);
-  const float ba = ordered_sum(part_ba + j, p.ld_w, n_ba);
-  assemble_row(p, ws, s, eps, m, wnorm, g, j, ba);
+  const float* pb = reinterpret_cast<const float*>(ws + p.off_base) + j;
+  const float* pc = reinterpret_cast<const float*>(ws + p.off_cross) + j;
+  const float* pa = reinterpret_cast<const float*>(ws + p.off_ba) + j;
+  const int nb = p.xw, nc = p.xw * p.n_nt, na = n_ba;
+  const int n = nb > nc ? (nb > na ? nb : na) : (nc > na ? nc : na);
+  // The three sums in lock step: each batch issues all its loads before any
+  // addition, and each sum still adds its planes in increasing order.
+  float base = 0.f, cross = 0.f, ba = 0.f;
+  for (int i = 0; i < n; i += kSumBatch) {
+    float vb[kSumBatch], vc[kSumBatch], va[kSumBatch];
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u) {
+      vb[u] = (i + u < nb) ? pb[(int64_t)(i + u) * p.ld_w] : 0.f;
+      vc[u] = (i + u < nc) ? pc[(int64_t)(i + u) * p.ld_w] : 0.f;
+      va[u] = (i + u < na) ? pa[(int64_t)(i + u) * p.ld_w] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u) {
+      if (i + u < nb) base += vb[u];
+      if (i + u < nc) cross += vc[u];
+      if (i + u < na) ba += va[u];
+    }
+  }
+  assemble_sums(base, cross, ba, s, eps, m, wnorm, g, j);
 }
 
 // ---------------------------------------------------------------------------
