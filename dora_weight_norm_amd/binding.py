@@ -48,7 +48,7 @@ DEFAULT_BUDGET = 256 << 20
 PLAN_FIELDS = (
     "mode", "tile_cols", "col_tiles", "gram_tile_cols", "gram_col_tiles", "fast_cfg", "gen_cfg",
     "gram_fast_cfg", "gram_gen_cfg", "granule", "granules", "w_ranges", "gram_ranges", "workspace_bytes",
-    "w_grid", "gram_grid", "lds_bytes", "tile_rows", "gram_folded",
+    "w_grid", "gram_grid", "lds_bytes", "tile_rows", "gram_folded", "gram_symmetric",
 )
 
 _lib = None

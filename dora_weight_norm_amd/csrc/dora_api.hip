@@ -123,13 +123,15 @@ int choose_w_ranges(int64_t tiles, int64_t n_gran) {
   return best;
 }
 
-// d_in ranges of the Gram pass: the largest power of two (<= 64 and <= the
-// granule count) that keeps the grid within kGrid workgroups and the partial
-// Gram matrices within kGramPartialCap bytes.
+// d_in ranges of the Gram pass: the largest power of two (<= max_x and <=
+// the granule count) that keeps the grid within kGrid workgroups and the written
+// partial Gram matrices (what the reduction reads) within kGramPartialCap
+// bytes.
 constexpr int64_t kGramPartialCap = (int64_t)16 << 20;
-int choose_g_ranges(int64_t tiles, int64_t n_gran, int64_t plane_bytes) {
+int choose_g_ranges(int64_t tiles, int64_t n_gran, int64_t plane_bytes, int max_x) {
   int X = 1;
-  while (X * 2 <= 64 && X * 2 <= n_gran && tiles * X * 2 <= dora::kGrid && plane_bytes * X * 2 <= kGramPartialCap)
+  while (X * 2 <= max_x && X * 2 <= n_gran && tiles * X * 2 <= dora::kGrid &&
+         plane_bytes * X * 2 <= kGramPartialCap)
     X *= 2;
   return X;
 }
@@ -183,9 +185,18 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   const int64_t nbc = p.r32 / 32;
   p.gfold = p.n_nt == 1 && p.ntc <= 128 &&
             nbc * nbc <= (int64_t)dora::fast_waves(p.fcfg) * ceil_div(d_out, dora::fast_rows(p.fcfg));
-  const int64_t tiles_g = ceil_div(r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g;
+  // The 128 x 128 Gram tiles are square, so only those on and above the
+  // diagonal are computed (the reduction reads the rest transposed); with a
+  // third less work per range, the Gram pass can split d_in further.
+  p.gsym = p.fcfg_g == dora::kFastB128;
+  const int64_t ntg = ceil_div(r, dora::kGramTile);
+  const int64_t tiles_g = p.gsym ? dora::tri_count(ntg) : ceil_div(r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g;
+  const int64_t plane = p.ga_rows * p.ga_cols * 4;
+  const int64_t written = p.gsym ? plane * dora::tri_count(ntg) / (ntg * ntg) : plane;
   int xw = choose_w_ranges(tiles_w, p.n_gran);
-  int xg = choose_g_ranges(tiles_g, p.n_gran, p.ga_rows * p.ga_cols * 4);
+  // Square tiles: at most 16 ranges, so the reduction sums each element's
+  // partials in one round trip of loads.
+  int xg = choose_g_ranges(tiles_g, p.n_gran, written, p.gsym ? 16 : 64);
   // Fit the budget: fewer Gram ranges first, then fewer W ranges.
   for (;;) {
     p.xw = xw;
@@ -304,11 +315,13 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   if (!plan_self_check(p)) return DORA_ERR_INVALID_ARG;
   const bool f = p.mode == dora::kModeFactored;
   const int64_t grid_w = f ? p.xw * ceil_div(p.d_out, dora::fast_rows(p.fcfg)) * p.n_nt : 0;
-  const int64_t grid_g = f ? p.xg * ceil_div(p.r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g : 0;
+  const int64_t grid_g = !f ? 0
+                             : p.xg * (p.gsym ? dora::tri_count(ceil_div(p.r, dora::kGramTile))
+                                              : ceil_div(p.r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g);
   const int64_t vals[] = {p.mode, p.ntc, p.n_nt, p.ntc_g, p.n_nt_g, p.fcfg, p.gcfg, p.fcfg_g, p.gcfg_g, p.gran,
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
                           f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0,
-                          f ? p.gfold : 0};
+                          f ? p.gfold : 0, f ? p.gsym : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;

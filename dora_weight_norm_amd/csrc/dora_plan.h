@@ -41,6 +41,20 @@ enum FastCfg : int {
 DORA_HD int fast_rows(int) { return 128; }
 DORA_HD int fast_waves(int cfg) { return cfg == kFastF32 ? 4 : 8; }
 constexpr int kGramCols = 64;      // columns of G per Gram-term tile (general kernel)
+constexpr int kGramTile = 128;     // side of the square streaming Gram-pass tile
+
+// Number of tiles on and above the diagonal of an nt x nt tile grid, and
+// the (row, column) tile of upper-triangle tile t in row-major order.
+DORA_HD int64_t tri_count(int64_t nt) { return nt * (nt + 1) / 2; }
+DORA_HD void tri_tile(int t, int nt, int* m, int* n) {
+  int row = 0;
+  while (t >= nt - row) {
+    t -= nt - row;
+    ++row;
+  }
+  *m = row;
+  *n = row + t;
+}
 
 // General kernel (any alignment): WM x WN waves, each owning MB x NB blocks
 // of 32x32 accumulators; KT is the d_in depth of one LDS stage.
@@ -87,6 +101,8 @@ struct NormPlan {
   int64_t n_gran;       // granules over d_in
   int xw;               // d_in ranges of the W pass
   int xg;               // d_in ranges of the Gram pass
+  int gsym;             // the streaming Gram pass computes only the tiles on and above
+                        // the diagonal (square kGramTile tiles; G is symmetric)
   int gfold;            // the streaming W pass also computes G (no Gram pass); its
                         // Gram partials are then per W-pass range (xw planes)
   int64_t ld_w;         // padded W rows of the base / cross partials

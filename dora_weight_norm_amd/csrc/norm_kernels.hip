@@ -245,7 +245,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int64_t m_rows = GRAM ? p.r : p.d_out;
   const int x = blockIdx.x % X;
   const int t = blockIdx.x / X;
-  const int m = t / n_nt, n = t - m * n_nt;
+  int m = t / n_nt, n = t - m * n_nt;
+  if constexpr (GRAM) {
+    if (MT == NTC && p.gsym) tri_tile(t, n_nt, &m, &n);   // upper-triangle tiles only
+  }
   const int64_t mrow0 = (int64_t)m * MT;
   const int64_t n0 = (int64_t)n * NTC;
   const int64_t d_in = p.d_in;
@@ -773,25 +776,73 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_gen_kernel(NormPlan p, c
 // One thread per element, consecutive j in consecutive lanes.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws) {
+__device__ __forceinline__ void store_gram(char* ws, const NormPlan& p, int64_t i, int64_t j, float v) {
   const int64_t r32 = p.r32;
-  const int64_t i = blockIdx.y;
-  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (j >= r32) return;
-  const float* part_g = reinterpret_cast<const float*>(ws + p.off_g);
-  float acc = 0.f;
-  if (i < p.r && j < p.r) {
-    acc = ordered_sum(part_g + i * p.ga_cols + j, p.ga_rows * p.ga_cols, p.xg);
-  }
   if constexpr (sizeof(T) == 2) {
     // Row i of the stored matrix: [hi(G[i][0..r32)), lo(G[i][0..r32))].
     bf16_t* gg = reinterpret_cast<bf16_t*>(ws + p.off_gg) + i * 2 * r32;
-    const bf16_t h = f32_to_bf16_rne(acc);
-    const float rem = acc - bf16_bits_to_f32(h);
+    const bf16_t h = f32_to_bf16_rne(v);
     gg[j] = h;
-    gg[r32 + j] = f32_to_bf16_rne(rem);
+    gg[r32 + j] = f32_to_bf16_rne(v - bf16_bits_to_f32(h));
   } else {
-    reinterpret_cast<float*>(ws + p.off_gg)[i * r32 + j] = acc;
+    reinterpret_cast<float*>(ws + p.off_gg)[i * r32 + j] = v;
+  }
+}
+
+// One workgroup of 1024 threads per 32 x 32 block (bi, bj) of G on or above
+// the diagonal, one element per thread: each element sums its x partials in
+// increasing x (kSumBatch planes per round trip), reading only blocks on or
+// above the diagonal, which every Gram pass computes. The block is written
+// as G[bi][bj] and, off the diagonal, transposed through LDS as G[bj][bi],
+// so every global access is along a row.
+constexpr int kReduceThreads = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws) {
+  constexpr int RG = kReduceThreads / 32;   // row groups; each thread owns 32 / RG rows
+  constexpr int RPT = 32 / RG;
+  __shared__ float tile[32][33];
+  int bi, bj;
+  tri_tile(blockIdx.x, (int)(p.r32 / 32), &bi, &bj);
+  const int c = threadIdx.x % 32, rg = threadIdx.x / 32;
+  const float* part_g = reinterpret_cast<const float*>(ws + p.off_g);
+  const int64_t plane = p.ga_rows * p.ga_cols;
+  const int64_t j = (int64_t)bj * 32 + c;
+  float acc[RPT];
+  const float* src[RPT];
+  bool live[RPT];
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const int64_t i = (int64_t)bi * 32 + rg + RG * q;
+    acc[q] = 0.f;
+    live[q] = i < p.r && j < p.r;
+    src[q] = part_g + i * p.ga_cols + j;
+  }
+  for (int x0 = 0; x0 < p.xg; x0 += kSumBatch) {
+    float v[RPT][kSumBatch];
+#pragma unroll
+    for (int q = 0; q < RPT; ++q)
+#pragma unroll
+      for (int u = 0; u < kSumBatch; ++u)
+        v[q][u] = (live[q] && x0 + u < p.xg) ? src[q][(int64_t)(x0 + u) * plane] : 0.f;
+#pragma unroll
+    for (int q = 0; q < RPT; ++q)
+#pragma unroll
+      for (int u = 0; u < kSumBatch; ++u)
+        if (x0 + u < p.xg) acc[q] += v[q][u];
+  }
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const int row = rg + RG * q;
+    store_gram<T>(ws, p, (int64_t)bi * 32 + row, j, acc[q]);
+    tile[row][c] = acc[q];
+  }
+  if (bi == bj) return;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < RPT; ++q) {
+    const int row = rg + RG * q;   // row of the transposed block: column `row` of the tile
+    store_gram<T>(ws, p, (int64_t)bj * 32 + row, (int64_t)bi * 32 + c, tile[c][row]);
   }
 }
 
@@ -1012,7 +1063,9 @@ hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const vo
     const bool gram = MODE == kPassGram;
     const int64_t rows = gram ? p.r : p.d_out;
     const int64_t cols = gram ? p.ga_cols : (int64_t)p.n_nt * p.ntc;
-    grid = (gram ? p.xg : p.xw) * ceil_div64(rows, C::MT) * (cols / C::NTC);
+    const int64_t tiles = (gram && C::MT == C::NTC && p.gsym) ? tri_count(cols / C::NTC)
+                                                               : ceil_div64(rows, C::MT) * (cols / C::NTC);
+    grid = (gram ? p.xg : p.xw) * tiles;
   }
   hipLaunchKernelGGL((norm_fast_kernel<T, WM, WN, MB, NB, KT, NS, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, st,
                      p, static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws, aa);
@@ -1131,8 +1184,7 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   // bf16 keeps G as bf16 hi + lo for the bf16 Gram term; fp32 and fp16 keep
   // it in fp32 (fp16's range cannot hold every G) for the fp32 Gram term.
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
-                     dim3((unsigned)((p.r32 + kThreads - 1) / kThreads), (unsigned)p.r32), dim3(kThreads), 0, st,
-                     q, ws);
+                     dim3((unsigned)tri_count(p.r32 / 32)), dim3(kReduceThreads), 0, st, q, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!fold) {

@@ -103,8 +103,9 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
  * d_in ranges of the Gram pass, workspace bytes, W-pass grid and Gram-pass
  * grid of the streaming kernel, its LDS bytes in the W pass, the rows of
  * its W-pass tile, and 1 if the streaming W pass computes G itself (no
- * separate Gram pass; gram grid and ranges then do not apply), else 0;
- * entries past the last field are set to -1.
+ * separate Gram pass; gram grid and ranges then do not apply), else 0,
+ * and 1 if the streaming Gram pass computes only the tiles on and above the
+ * diagonal of G, else 0; entries past the last field are set to -1.
  * Before returning it replays the plan on the host and checks that the
  * d_in ranges tile d_in exactly, every grid fits and every partial sum the
  * kernels write lies inside its workspace region; DORA_ERR_INVALID_ARG if

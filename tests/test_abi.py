@@ -60,7 +60,11 @@ def test_plans_of_the_workloads(name):
     assert info["gram_grid"] <= 256 and info["lds_bytes"] <= 160 * 1024
     # the W pass: one workgroup per (row tile, d_in range)
     assert info["w_grid"] == -(-w.d_out // info["tile_rows"]) * info["col_tiles"] * info["w_ranges"]
-    assert info["gram_grid"] == -(-w.r // 128) * info["gram_col_tiles"] * info["gram_ranges"]
+    nt = -(-w.r // 128)
+    tiles_g = nt * (nt + 1) // 2 if info["gram_symmetric"] else nt * info["gram_col_tiles"]
+    assert info["gram_grid"] == tiles_g * info["gram_ranges"]
+    # square 128-column Gram tiles are the symmetric ones
+    assert info["gram_symmetric"] == (info["gram_tile_cols"] == 128 and w.dtype != "f32")
     assert info["tile_cols"] * info["col_tiles"] >= w.r
 
 

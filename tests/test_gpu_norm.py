@@ -45,6 +45,9 @@ CASES = [
     ("f16_scalar_loads", 257, 1001, 13, "f16", 0.75, 62),
     ("f16_qproj_folded_gram", 4096, 4096, 64, "f16", 2.0, 63),
     ("f16_r700_tiles", 300, 1024, 700, "f16", 0.25, 64),
+    # element loads (d_in % 8 != 0) under a plan with square Gram tiles: the
+    # general kernel computes every tile, the reduction reads the upper ones
+    ("gen_path_symmetric_gram", 300, 1001, 200, "bf16", 0.5, 19),
 ]
 
 
