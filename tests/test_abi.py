@@ -156,3 +156,58 @@ def test_library_resolves_every_kernel_stub():
     out = subprocess.run(["nm", "-D", "--undefined-only", bnd.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     assert "device_stub" not in out, [ln for ln in out.splitlines() if "device_stub" in ln][:5]
+
+
+def test_layer_output_argument_errors_return_before_launch():
+    lib = bnd.load()
+    P = ctypes.c_void_p
+
+    def call(base=0x100000, lora=0x200000, g=0x300000, s=0.5, dtype=0, T=4, d_out=8, y=0x400000):
+        return lib.dora_layer_output(P(base), P(lora), P(g), s, dtype, T, d_out, P(y), None)
+
+    assert call(dtype=3) == 2                # 0 bf16, 1 fp32, 2 fp16; nothing else
+    assert call(T=-1) == 1
+    assert call(s=float("nan")) == 1
+    assert call(lora=None) == 1
+    assert call(y=0x200002) == 1             # partial overlap with lora
+    assert call(y=0x100001) == 1             # misaligned element
+    assert call(T=0) == 0 and call(d_out=0) == 0
+
+
+def test_norm_to_dtype_argument_errors():
+    lib = bnd.load()
+    P = ctypes.c_void_p
+    assert lib.dora_norm_to_dtype(P(0x1000), 8, 5, P(0x2000), None) == 2
+    assert lib.dora_norm_to_dtype(P(0x1000), -1, 0, P(0x2000), None) == 1
+    assert lib.dora_norm_to_dtype(None, 8, 0, P(0x2000), None) == 1
+    assert lib.dora_norm_to_dtype(P(0x1002), 8, 0, P(0x2000), None) == 1     # wnorm misaligned
+    assert lib.dora_norm_to_dtype(P(0x1000), 8, 0, P(0x2001), None) == 1     # bf16 out misaligned
+    assert lib.dora_norm_to_dtype(P(0x1000), 8, 0, P(0x1010), None) == 1     # out overlaps wnorm
+    assert lib.dora_norm_to_dtype(None, 0, 0, None, None) == 0               # nothing to do
+
+
+def test_compose_backward_argument_errors_return_before_launch():
+    lib = bnd.load()
+    P = ctypes.c_void_p
+    sz = ctypes.c_size_t()
+    assert lib.dora_compose_backward_workspace_size(4, 8, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert lib.dora_compose_backward_workspace_size(-1, 8, ctypes.byref(sz)) == 1
+    assert lib.dora_compose_backward_workspace_size(4, 8, None) == 1
+
+    def call(dy=0x100000, base=0x200000, lora=0x300000, g=0x400000, s=0.5, dtype=0, T=4, d_out=8,
+             d_base=0x500000, d_lora=0x600000, dg=0x700000, wnorm=None, eps=1e-6, dm=None, ws=0x800000,
+             ws_bytes=1 << 20):
+        return lib.dora_compose_backward(P(dy), P(base), P(lora), P(g), s, dtype, T, d_out, P(d_base), P(d_lora),
+                                         P(dg), P(wnorm), eps, P(dm), P(ws), ws_bytes, None)
+
+    assert call(dtype=4) == 2
+    assert call(T=-1) == 1
+    assert call(s=float("inf")) == 1
+    assert call(dy=None) == 1
+    assert call(base=None) == 1                        # dg needs base and lora
+    assert call(dm=0x900000) == 1                      # dm needs wnorm
+    assert call(dm=0x900000, wnorm=0xA00000, eps=0.0) == 1
+    assert call(d_lora=0x500010) == 1                  # outputs overlap
+    assert call(d_base=0x100000) == 1                  # output is an input
+    assert call(ws_bytes=16) == 4                      # workspace too small
+    assert call(d_out=0) == 0
