@@ -173,6 +173,7 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
 // With the magnitude frozen (no dg), base and lora are not read at all.
 // ---------------------------------------------------------------------------
 constexpr int kBwdMaxRowBlocks = 256;
+constexpr int kBwdTargetBlocks = 256;   // about one workgroup per compute unit
 
 template <typename T, int VEC, bool DG>
 __global__ __launch_bounds__(256) void compose_bwd_kernel(const T* dy, const T* base, const T* lora,
@@ -279,8 +280,9 @@ __global__ __launch_bounds__(256) void compose_bwd_reduce_kernel(const float* pa
   }
 }
 
-// Launch shape shared by the compose kernels: one thread per 16-byte strip,
-// about 8 resident workgroups per compute unit, at most max_by row blocks.
+// Launch shape of the backward: one thread per 16-byte strip, and about
+// kBwdTargetBlocks workgroups in all (at most max_by row blocks). Fewer,
+// longer row strips stream as fast and leave fewer dg partials to reduce.
 struct Grid2 {
   int64_t tpb, bx, by;
 };
@@ -290,7 +292,7 @@ Grid2 strip_grid(int64_t T_rows, int64_t d_out, int vec, int64_t max_by) {
   if (tpb > 256) tpb = 256;
   if (tpb < 64) tpb = 64;
   const int64_t bx = (ncg + tpb - 1) / tpb;
-  int64_t by = 2048 / (bx > 0 ? bx : 1);
+  int64_t by = kBwdTargetBlocks / (bx > 0 ? bx : 1);
   if (by < 1) by = 1;
   const int64_t row_iters = (T_rows + kUnroll - 1) / kUnroll;
   if (by > row_iters) by = row_iters;
@@ -350,9 +352,13 @@ hipError_t launch_compose(const void* base, const void* lora, const float* g, fl
 }
 
 size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out) {
-  // Row blocks never exceed this for any strip width (see strip_grid).
-  int64_t by = (T + kUnroll - 1) / kUnroll;
-  if (by > kBwdMaxRowBlocks) by = kBwdMaxRowBlocks;
+  // The most row blocks any strip width (element, fp32 or 16-bit vectors)
+  // can take (see strip_grid).
+  int64_t by = 0;
+  for (int vec : {1, 4, 8}) {
+    const int64_t b = strip_grid(T, d_out, vec, kBwdMaxRowBlocks).by;
+    by = b > by ? b : by;
+  }
   return (size_t)(by * d_out) * 4;
 }
 
