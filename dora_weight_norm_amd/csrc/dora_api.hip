@@ -93,7 +93,7 @@ void layout(NormPlan& p) {
   p.off_g = off;
   off = align_up(off + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4, kAlign);
   p.off_gg = off;
-  off = align_up(off + (size_t)(p.r32 * p.r32) * 4, kAlign);   // bf16 hi and lo, or fp32
+  off = align_up(off + (size_t)(p.rg * p.rg) * 4, kAlign);   // bf16 hi and lo, or fp32
   p.off_bf = off;
   if (p.dtype == DORA_F16) off = align_up(off + (size_t)(p.d_out * p.r) * 4, kAlign);   // B widened to fp32
   p.ws_bytes = off;
@@ -163,18 +163,19 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.ld_w = ceil_div(d_out, dora::kRowPadW) * dora::kRowPadW;
   p.ga_rows = ceil_div(r, dora::kRowPadG) * dora::kRowPadG;
   p.ga_cols = (int64_t)p.n_nt_g * p.ntc_g;
-  p.r32 = ceil_div(r, 32) * 32;
+  const int64_t rq = dtype == DORA_BF16 ? 64 : 32;
+  p.rg = ceil_div(r, rq) * rq;
   // Gram-term tiles: the streaming kernel covers up to 384 columns of G in
   // one tile (bf16; 128 for fp32, and for fp16, whose Gram term runs in
   // fp32) and uses 256-column tiles beyond; the general kernel uses
   // kGramCols.
   if (dtype == DORA_BF16) {
-    p.bcfg = p.r32 <= 384 ? (int)ceil_div(p.r32, 128) : 2;
+    p.bcfg = p.rg <= 384 ? (int)ceil_div(p.rg, 128) : 2;
   } else {
     p.bcfg = 1;
   }
-  p.n_bt = (int)ceil_div(p.r32, 128 * (int64_t)p.bcfg);
-  p.n_cb = (int)ceil_div(p.r32, dora::kGramCols);
+  p.n_bt = (int)ceil_div(p.rg, 128 * (int64_t)p.bcfg);
+  p.n_cb = (int)ceil_div(p.rg, dora::kGramCols);
 
   const int64_t tiles_w = ceil_div(d_out, dora::fast_rows(p.fcfg)) * p.n_nt;
   // G = A A^T folds into the streaming W pass when one column tile of at
@@ -182,7 +183,7 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   // a wave (one per wave). Every wave then reads two more fragments and runs
   // one more MFMA per K16 step; on wider tiles those LDS reads cost the W
   // pass as much as the separate Gram pass takes.
-  const int64_t nbc = p.r32 / 32;
+  const int64_t nbc = p.rg / 32;
   p.gfold = p.n_nt == 1 && p.ntc <= 128 &&
             nbc * nbc <= (int64_t)dora::fast_waves(p.fcfg) * ceil_div(d_out, dora::fast_rows(p.fcfg));
   // The 128 x 128 Gram tiles are square, so only those on and above the
@@ -233,7 +234,7 @@ bool plan_self_check(const NormPlan& p) {
   const int fw = dora::fast_rows(p.fcfg), fg = dora::fast_rows(p.fcfg_g);
   if (ceil_div(p.d_out, fw) * fw > p.ld_w || rows_w > p.ld_w) return false;
   if (ceil_div(p.r, fg) * fg > p.ga_rows || rows_g > p.ga_rows) return false;
-  if ((int64_t)p.n_nt * p.ntc < p.r || p.ga_cols < p.r || p.r32 > p.ga_cols) return false;
+  if ((int64_t)p.n_nt * p.ntc < p.r || p.ga_cols < p.r || p.rg > p.ga_cols) return false;
   const int64_t grid_w = p.xw * ceil_div(p.d_out, 64) * p.n_nt;
   const int64_t grid_g = p.xg * ceil_div(p.r, 64) * p.n_nt_g;
   if (grid_w >= ((int64_t)1 << 31) || grid_g >= ((int64_t)1 << 31)) return false;
@@ -241,7 +242,7 @@ bool plan_self_check(const NormPlan& p) {
   if (p.off_ba < p.off_cross + (size_t)(p.xw * p.n_nt * p.ld_w) * 4) return false;
   if (p.off_g < p.off_ba + (size_t)(ba_planes(p) * p.ld_w) * 4) return false;
   if (p.off_gg < p.off_g + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4) return false;
-  if (p.off_bf < p.off_gg + (size_t)(p.r32 * p.r32) * 4) return false;
+  if (p.off_bf < p.off_gg + (size_t)(p.rg * p.rg) * 4) return false;
   return p.ws_bytes >= p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.r) * 4 : 0);
 }
 

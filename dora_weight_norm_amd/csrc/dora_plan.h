@@ -108,7 +108,10 @@ struct NormPlan {
   int64_t ld_w;         // padded W rows of the base / cross partials
   int64_t ga_rows;      // padded A rows of the Gram partials
   int64_t ga_cols;      // padded Gram columns: n_nt * ntc
-  int64_t r32;          // r rounded up to 32: side of the reduced Gram matrix
+  int64_t rg;           // side of the reduced Gram matrix: r rounded up to 64 for bf16
+                        // (its Gram term runs over the depth [hi | lo] in 64-deep stages,
+                        // so the seam between the parts must fall on a stage boundary),
+                        // to 32 otherwise
   int bcfg;             // Gram-term pass (streaming kernel): 128-column blocks per tile (bf16)
   int n_bt;             // Gram-term column tiles of the streaming kernel
   int n_cb;             // Gram-term column tiles of the general kernel (kGramCols columns each)
@@ -116,7 +119,7 @@ struct NormPlan {
   size_t off_cross;     // [xw][n_nt][ld_w] fp32 cross partials
   size_t off_ba;        // [max(n_bt, n_cb)][ld_w] fp32 Gram-term partials
   size_t off_g;         // [max(xg, xw if gfold)][ga_rows][ga_cols] fp32 Gram partials
-  size_t off_gg;        // reduced Gram matrix: bf16 [r32][Ghi | Glo], fp32 [r32][r32]
+  size_t off_gg;        // reduced Gram matrix: bf16 [rg][Ghi | Glo], fp32 [rg][rg]
   size_t off_bf;        // fp16 inputs only: B widened to fp32 [d_out][r] for the Gram term
   size_t ws_bytes;
 };

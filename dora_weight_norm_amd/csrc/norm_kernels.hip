@@ -255,14 +255,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // Row operand: W (or A) rows of d_in, or B rows of r read twice (hi, lo).
   const int64_t m_ld = BG ? p.r : d_in;             // elements per row
   const int64_t m_kvalid = BG ? p.r : d_in;         // valid k of a row
-  const int64_t m_kwrap = BG ? p.r32 : ((int64_t)1 << 62);
+  const int64_t m_kwrap = BG ? p.rg : ((int64_t)1 << 62);
   // Column operand: A rows of d_in, or rows of the stored Gram matrix.
-  const int64_t n_ld = BG ? (int64_t)NG * p.r32 : d_in;
-  const int64_t n_rows = BG ? p.r32 : p.r;
+  const int64_t n_ld = BG ? (int64_t)NG * p.rg : d_in;
+  const int64_t n_rows = BG ? p.rg : p.r;
   const T* Nsrc = BG ? reinterpret_cast<const T*>(ws + p.off_gg) : A;
   const uint32_t m_rowb = (uint32_t)(m_ld * ESZ), n_rowb = (uint32_t)(n_ld * ESZ);
   const int64_t k0 = BG ? 0 : range_k0(p, X, x);
-  const int64_t k1 = BG ? (int64_t)NG * p.r32 : range_k0(p, X, x + 1);
+  const int64_t k1 = BG ? (int64_t)NG * p.rg : range_k0(p, X, x + 1);
   const int n_st = (int)((k1 - k0 + KT - 1) / KT);   // stages of this tile (>= 1)
 
   // Both operands through buffer descriptors spanning the tile's valid rows:
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
 #pragma unroll
   for (int v = 0; v < 16; ++v) gacc[v] = 0.f;
   if constexpr (GF) {
-    const int nbc = (int)(p.r32 / 32);
+    const int nbc = (int)(p.rg / 32);
     const int n_mt = (int)((p.d_out + MT - 1) / MT);
     const int gb = m + n_mt * wave;
     has_g = gb < nbc * nbc;
@@ -777,15 +777,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_gen_kernel(NormPlan p, c
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void store_gram(char* ws, const NormPlan& p, int64_t i, int64_t j, float v) {
-  const int64_t r32 = p.r32;
+  const int64_t rg = p.rg;
   if constexpr (sizeof(T) == 2) {
-    // Row i of the stored matrix: [hi(G[i][0..r32)), lo(G[i][0..r32))].
-    bf16_t* gg = reinterpret_cast<bf16_t*>(ws + p.off_gg) + i * 2 * r32;
+    // Row i of the stored matrix: [hi(G[i][0..rg)), lo(G[i][0..rg))].
+    bf16_t* gg = reinterpret_cast<bf16_t*>(ws + p.off_gg) + i * 2 * rg;
     const bf16_t h = f32_to_bf16_rne(v);
     gg[j] = h;
-    gg[r32 + j] = f32_to_bf16_rne(v - bf16_bits_to_f32(h));
+    gg[rg + j] = f32_to_bf16_rne(v - bf16_bits_to_f32(h));
   } else {
-    reinterpret_cast<float*>(ws + p.off_gg)[i * r32 + j] = v;
+    reinterpret_cast<float*>(ws + p.off_gg)[i * rg + j] = v;
   }
 }
 
@@ -803,7 +803,7 @@ __global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p,
   constexpr int RPT = 32 / RG;
   __shared__ float tile[32][33];
   int bi, bj;
-  tri_tile(blockIdx.x, (int)(p.r32 / 32), &bi, &bj);
+  tri_tile(blockIdx.x, (int)(p.rg / 32), &bi, &bj);
   const int c = threadIdx.x % 32, rg = threadIdx.x / 32;
   const float* part_g = reinterpret_cast<const float*>(ws + p.off_g);
   const int64_t plane = p.ga_rows * p.ga_cols;
@@ -880,7 +880,7 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, lgrp = lane >> 5;
-  const int64_t r = p.r, r32 = p.r32;
+  const int64_t r = p.r, rg = p.rg;
   const int64_t c0 = (int64_t)blockIdx.y * kGramCB;
   const int64_t j0 = (int64_t)blockIdx.x * kGramRows + wave * 32;
   const int64_t arow = j0 + lrow;
@@ -906,7 +906,7 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[q][v] = 0.f;
 
-  for (int64_t k0 = 0; k0 < r32; k0 += C::KC) {
+  for (int64_t k0 = 0; k0 < rg; k0 += C::KC) {
     u32x4 fa[C::NKS][FC];   // this lane's B fragments for the chunk
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks)
@@ -923,9 +923,9 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
       const int slot16 = (blk % (C::PART / 1024)) * 64 + lane;
       const int row = slot16 / C::CPRG, ch = (slot16 % C::CPRG) ^ (row & 7);
       int64_t grow = c0 + row, gk = k0 + (int64_t)ch * EPC;
-      grow = grow < r32 ? grow : r32 - 1;          // past the matrix: a real row, never used
-      gk = gk < r32 ? gk : r32 - EPC;
-      const char* src = ws + p.off_gg + (grow * C::NG * r32 + part * r32 + gk) * (int64_t)sizeof(T);
+      grow = grow < rg ? grow : rg - 1;          // past the matrix: a real row, never used
+      gk = gk < rg ? gk : rg - EPC;
+      const char* src = ws + p.off_gg + (grow * C::NG * rg + part * rg + gk) * (int64_t)sizeof(T);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(sg + blk * 1024), 16, 0, 0);
     }
@@ -1058,7 +1058,7 @@ hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const vo
   using C = FastK<T, WM, WN, MB, NB, KT, NS>;
   int64_t grid;
   if (MODE == kPassBG) {
-    grid = ceil_div64(p.d_out, C::MT) * p.n_bt;   // n_bt * NTC covers r32
+    grid = ceil_div64(p.d_out, C::MT) * p.n_bt;   // n_bt * NTC covers rg
   } else {
     const bool gram = MODE == kPassGram;
     const int64_t rows = gram ? p.r : p.d_out;
@@ -1184,7 +1184,7 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   // bf16 keeps G as bf16 hi + lo for the bf16 Gram term; fp32 and fp16 keep
   // it in fp32 (fp16's range cannot hold every G) for the fp32 Gram term.
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
-                     dim3((unsigned)tri_count(p.r32 / 32)), dim3(kReduceThreads), 0, st, q, ws);
+                     dim3((unsigned)tri_count(p.rg / 32)), dim3(kReduceThreads), 0, st, q, ws);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!fold) {

@@ -92,6 +92,35 @@ def test_norm_full_size_sampled_rows(name):
     say(f"    {len(rows)} rows, worst rel err {worst:.2e}")
 
 
+# W = 0 leaves only the Gram term: wnorm = |s| ||(BA)_j||, so an error in the
+# Gram term (B G) . B shows at full size rather than diluted by ||W||^2. The
+# ranks put the end of r on both sides of a 64-column boundary, with and
+# without the Gram blocks folded into the W pass, on every path.
+GRAM_ALONE = [
+    ("r8_folded", 300, 512, 8, "bf16", 0.5),
+    ("r32_folded", 300, 512, 32, "bf16", 2.0),
+    ("r72_folded", 300, 512, 72, "bf16", 0.5),
+    ("r160", 300, 512, 160, "bf16", 0.5),
+    ("r384", 300, 512, 384, "bf16", 0.25),
+    ("r160_general", 300, 1001, 160, "bf16", 0.5),
+    ("r160_f16", 300, 512, 160, "f16", 0.5),
+    ("r40_f32", 300, 512, 40, "f32", 0.5),
+]
+
+
+@pytest.mark.parametrize("case", GRAM_ALONE, ids=[c[0] for c in GRAM_ALONE])
+def test_gram_term_alone(case):
+    name, d_out, d_in, r, dtype, s = case
+    say(f"[norm-gram-alone] {name} d_out={d_out} d_in={d_in} r={r} {dtype} s={s}")
+    _, A, B = I.norm_inputs(d_out, d_in, r, dtype, 24)
+    W = np.zeros((d_out, d_in), np.float32)
+    ref = O.dense_row_norm(W, A, B, s)
+    assert np.all(ref > 0)
+    wn, _ = _run(W, A, B, dtype, s)
+    worst = check_norm(wn, ref)
+    say(f"    worst rel err {worst:.2e}")
+
+
 def test_s_zero_and_zero_sizes():
     W, A, B = I.norm_inputs(130, 300, 12, "bf16", 20)
     wn, _ = _run(W, A, B, "bf16", 0.0)
