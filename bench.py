@@ -16,7 +16,8 @@ workload's T beside a plain LoRA layer.
 Prints one JSON line. `value` is the factored norm's algorithmic TFLOP/s;
 the compose's GB/s and fraction of HBM peak, per-call times and the
 roofline objects ride in the same line. Kernel times come from HIP events
-recorded on the stream the kernels run on.
+recorded on the stream the kernels run on; the W-pass kernel inside the
+norm call is timed by events the library records around its launches.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-backward]
                     [--no-comparisons] [--no-linear]
@@ -45,6 +46,18 @@ METRIC = "factored-norm ms/TFLOP/s + compose GB/s (%HBM peak), 8192×8192 r=384 
 def norm_flops(d_out, d_in, r):
     """U = W A^T, G = A A^T, B G, the base squares, and the two row dots."""
     return 2 * d_out * d_in * r + 2 * r * r * d_in + 2 * d_out * r * r + 2 * d_out * d_in + 4 * d_out * r
+
+
+def w_pass_flops(d_out, d_in, r, plan):
+    """Algorithmic work of the W-pass kernel alone: U = W A^T, the base
+    squares and the row dot with B; with the Gram term inside it also B G,
+    with G folded into it also G = A A^T."""
+    f = 2 * d_out * d_in * r + 2 * d_out * d_in + 2 * d_out * r
+    if plan["gram_term_fused"]:
+        f += 2 * d_out * r * r
+    if plan["gram_folded"]:
+        f += 2 * r * r * d_in
+    return f
 
 
 def norm_bytes(d_out, d_in, r, esize):
@@ -266,8 +279,8 @@ def linear_forward(args, w, I, Wd, Ad, Bd, md, stream, tdt):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="headline_8192x8192_r384")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
@@ -369,6 +382,29 @@ def main() -> int:
         ev[k][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # The W-pass kernel inside the norm call: the same K steps again, with
+    # the library recording one event on the stream before that launch and
+    # one after it (its launch-event hook; launch w_launch lies between
+    # marks w_launch and w_launch + 1). Each recorded event adds about 3 us
+    # between launches, so the steps above, which give the per-call times,
+    # run without them.
+    plan = bnd.dora_norm_plan_info(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
+    wl = plan["w_launch"]
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for pair in marks:
+        for e in pair:
+            e.record(stream)          # creates the HIP event behind each
+    torch.cuda.synchronize()
+    mark_arrays = [(P * (wl + 2))(*([None] * wl + [a.cuda_event, b.cuda_event])) for a, b in marks]
+    print(f"# timing the W-pass launch over {K} more steps", file=sys.stderr, flush=True)
+    for k in range(K):
+        lib.dora_set_launch_events(mark_arrays[k], wl + 2)
+        run_norm(k)
+        run_compose(k)
+    torch.cuda.synchronize()
+    lib.dora_set_launch_events(None, 0)
+    w_ms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
     norm_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
     comp_ms = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]))
     norm_med = float(np.median([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
@@ -397,7 +433,8 @@ def main() -> int:
         longest = tj.get("longest_step_kernel")
         if tj.get("source_hash") == prof.source_hash():
             traffic = {"norm": tj["norm_bytes_per_call"], "compose": tj["compose_bytes_per_call"],
-                       "compose_bwd": tj.get("compose_bwd_bytes_per_call") or None}
+                       "compose_bwd": tj.get("compose_bwd_bytes_per_call") or None,
+                       "w_pass": tj.get("w_pass_bytes_per_launch")}
             traffic_note = os.path.relpath(tpath, ROOT)
         else:
             traffic_note = "kernels changed since the counters in " + os.path.relpath(tpath, ROOT)
@@ -405,21 +442,33 @@ def main() -> int:
     roof_compose = {"bound": "hbm", "achieved": comp_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": comp_gbs / HBM_PEAK_GBS, "traffic": traffic.get("compose"),
                     "kernel": "compose_kernel", "algorithmic_bytes": cb, "traffic_source": traffic_note}
+    if plan["gram_folded"]:
+        launches = "W pass with the G blocks, gram_reduce, Gram term + assembly"
+    elif plan["gram_term_fused"]:
+        launches = "Gram pass, gram_reduce, W pass with the Gram term, assembly"
+    else:
+        launches = "Gram pass, gram_reduce, W pass, Gram term + assembly"
     roof_norm = {"bound": "mfma", "achieved": norm_tflops, "peak": mfma_peak, "unit": "TFLOP/s",
                  "frac": norm_tflops / mfma_peak, "traffic": traffic.get("norm"),
-                 "kernel": "dora_factored_norm: Gram pass, gram_reduce, W pass, Gram term + assembly "
-                           "(one C-ABI call, timed as a unit)",
+                 "kernel": f"dora_factored_norm: {launches} (one C-ABI call, timed as a unit)",
                  "algorithmic_flops": F, "algorithmic_bytes": nb, "hbm_gbs": norm_gbs,
                  "hbm_frac": norm_gbs / HBM_PEAK_GBS, "traffic_source": traffic_note}
+    Fw = w_pass_flops(w.d_out, w.d_in, w.r, plan)
+    w_tflops = Fw / (w_ms * 1e-3) / 1e12
+    w_name = ("W pass with the Gram term" if plan["gram_term_fused"]
+              else "W pass with the G blocks" if plan["gram_folded"] else "W pass")
+    roof_w = {"bound": "mfma", "achieved": w_tflops, "peak": mfma_peak, "unit": "TFLOP/s",
+              "frac": w_tflops / mfma_peak, "traffic": traffic.get("w_pass"),
+              "kernel": f"norm_fast_kernel ({w_name}; launch {wl} of the norm call)",
+              "algorithmic_flops": Fw, "launch_ms": w_ms, "traffic_source": traffic_note}
     # The dominant kernel is the longest single launch of a step, as the
-    # committed kernel trace of this workload lists it; the norm call (four
-    # launches) stands in for its W-pass kernel, which cannot be timed on
-    # its own from outside the library. Without a trace the longer of the
-    # two calls decides.
+    # committed kernel trace of this workload lists it: the compose kernel,
+    # or the norm's W pass. Without a trace, the longer of the compose
+    # launch and the W-pass launch decides.
     if longest is not None:
-        dominant = roof_compose if longest.get("part") == "compose" else roof_norm
+        dominant = roof_compose if longest.get("part") == "compose" else roof_w
     else:
-        dominant = roof_compose if comp_ms >= norm_ms else roof_norm
+        dominant = roof_compose if comp_ms >= w_ms else roof_w
 
     res = {
         "metric": METRIC,
@@ -446,9 +495,10 @@ def main() -> int:
         "compose_hbm_frac": comp_gbs / HBM_PEAK_GBS,
         "wall_ms_per_step": wall / K * 1e3,
         "roofline": dominant,
+        "roofline_w_pass": roof_w,
         "roofline_norm": roof_norm,
         "roofline_compose": roof_compose,
-        "plan": bnd.dora_norm_plan_info(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget),
+        "plan": plan,
     }
     if not args.no_backward:
         res["compose_backward"] = time_compose_backward(args, w, lib, bnd, I, based, lorad, g, wnorm, stream,

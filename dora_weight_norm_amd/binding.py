@@ -36,6 +36,7 @@ __all__ = [
     "PLAN_FIELDS",
     "dora_compose_backward",
     "dora_compose_backward_workspace_size",
+    "dora_set_launch_events",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdora.so")
@@ -48,7 +49,8 @@ DEFAULT_BUDGET = 256 << 20
 PLAN_FIELDS = (
     "mode", "tile_cols", "col_tiles", "gram_tile_cols", "gram_col_tiles", "fast_cfg", "gen_cfg",
     "gram_fast_cfg", "gram_gen_cfg", "granule", "granules", "w_ranges", "gram_ranges", "workspace_bytes",
-    "w_grid", "gram_grid", "lds_bytes", "tile_rows", "gram_folded", "gram_symmetric",
+    "w_grid", "gram_grid", "lds_bytes", "tile_rows", "gram_folded", "gram_symmetric", "gram_term_fused",
+    "w_launch",
 )
 
 _lib = None
@@ -86,6 +88,7 @@ def load():
         "dora_norm_plan_info": (_c_i, [_c_i64, _c_i64, _c_i64, _c_i, _c_f, _c_sz, ctypes.POINTER(_c_i64), _c_i]),
         "dora_factored_norm": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i64, _c_i64, _c_i64, _c_f, _c_sz, _c_p, _c_sz,
                                       _c_p, _c_p, _c_f, _c_p, _c_p]),
+        "dora_set_launch_events": (_c_i, [ctypes.POINTER(_c_p), _c_i]),
         "dora_magnitude_scale": (_c_i, [_c_p, _c_p, _c_f, _c_i64, _c_p, _c_p]),
         "dora_norm_to_dtype": (_c_i, [_c_p, _c_i64, _c_i, _c_p, _c_p]),
         "dora_compose": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
@@ -200,6 +203,22 @@ def dora_factored_norm(W, A, B, s: float, budget_bytes: int = DEFAULT_BUDGET, m=
           _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
           _ptr(wnorm), _ptr(m), eps, _ptr(g) if m is not None else None, _stream(stream))
     return wnorm, (g if m is not None else None)
+
+
+def dora_set_launch_events(events) -> None:
+    """Events recorded around the launches of later dora_factored_norm calls.
+
+    `events`: a sequence of created torch.cuda.Event objects (record each
+    once before passing it, so that it exists), raw hipEvent_t handles, or
+    None entries (marks that are skipped); an empty sequence or None clears
+    the hook. The caller keeps the events alive while they are set.
+    """
+    events = list(events or [])
+    handles = [None if e is None else int(getattr(e, "cuda_event", e)) for e in events]
+    if any(h == 0 for h in handles):
+        raise ValueError("an event has no HIP handle yet (record it once first)")
+    arr = (_c_p * max(len(handles), 1))(*handles)
+    _call("dora_set_launch_events", arr, len(handles))
 
 
 def dora_magnitude_scale(m, wnorm, eps: float = 1e-6, g=None, stream=None):

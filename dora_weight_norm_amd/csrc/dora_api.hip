@@ -322,7 +322,8 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   const int64_t vals[] = {p.mode, p.ntc, p.n_nt, p.ntc_g, p.n_nt_g, p.fcfg, p.gcfg, p.fcfg_g, p.gcfg_g, p.gran,
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
                           f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0,
-                          f ? p.gfold : 0, f ? p.gsym : 0};
+                          f ? p.gfold : 0, f ? p.gsym : 0, f ? (int64_t)(!p.gfold && p.dtype != DORA_F16) : 0,
+                          f ? (p.gfold ? 0 : 2) : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;
@@ -382,6 +383,12 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
   p.fast = aligned(W, 16) && aligned(A, 16) && (d_in % epc(dtype)) == 0 && p.vec_b &&
            tile_span < (1ull << 31) && b_span < (1ull << 31);
   return hip_status(dora::launch_norm_factored(p, W, A, B, workspace, s, m, eps, wnorm, g, hs));
+}
+
+dora_status dora_set_launch_events(void* const* events, int n_events) {
+  if (n_events < 0 || (n_events > 0 && events == nullptr)) return DORA_ERR_INVALID_ARG;
+  dora::set_launch_events(reinterpret_cast<const hipEvent_t*>(events), n_events);
+  return DORA_OK;
 }
 
 dora_status dora_magnitude_scale(const float* m, const float* wnorm, float eps, int64_t d_out, float* g,

@@ -21,6 +21,9 @@ size_t compose_bwd_workspace_bytes(int64_t T, int64_t d_out);
 hipError_t launch_compose_bwd(const void* dy, const void* base, const void* lora, const float* g, float s, int dtype,
                               int64_t T, int64_t d_out, void* d_base, void* d_lora, float* dg, const float* wnorm,
                               float eps, float* dm, void* ws, bool vec, hipStream_t st);
+// Benchmark hook: events recorded around the launches of each norm call.
+constexpr int kMaxLaunchEvents = 8;
+void set_launch_events(const hipEvent_t* events, int n);
 size_t fast_kernel_lds_bytes(int cfg);
 size_t gen_kernel_lds_bytes(int cfg);
 

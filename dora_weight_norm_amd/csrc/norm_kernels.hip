@@ -12,19 +12,25 @@
 //   W pass        one workgroup per (row tile of W, column tile over r,
 //                 d_in range): U = W A^T on the matrix cores, dotted with B
 //                 row by row at the end (cross term; U is never stored), and
-//                 the W fragments squared on the way (base term).
-//   Gram term     (B G) on the matrix cores (B Ghi + B Glo), dotted with B
-//                 (Gram-term partials), with the assembly fused in when one
-//                 tile covers all of G's columns; otherwise
+//                 the W fragments squared on the way (base term). On the
+//                 streaming path (bf16, fp32) each workgroup then runs its
+//                 share of the Gram term's depth, B against (s/2) G, in the
+//                 same accumulators: the dot with B at the end is then
+//                 cross + (s/2) ba, since the Gram term (B G) . B is linear
+//                 in B G.
 //   assemble      fixed-order sums of all partials;
 //                 wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and
 //                 g = m / max(wnorm, eps) without contraction, with
 //                 correctly rounded sqrt and division (same page, §1.2.2,
 //                 §5.2, §6.2).
-// When the streaming W pass has a single column tile (all of A's rows in
-// each stage) it also computes the blocks of G, and the order becomes
-// W pass, gram_reduce, Gram term: the separate Gram pass, and its second
-// read of A, are skipped.
+// Otherwise (fp16, the general kernels, and G folded into the W pass) the
+// Gram term is a pass of its own after the W pass: (B G) on the matrix cores
+// (B Ghi + B Glo for bf16), dotted with B, with the assembly fused in when
+// one tile covers all of G's columns.
+// When the streaming W pass has a single column tile of at most 128 columns
+// (all of A's rows in each stage) it also computes the blocks of G, and the
+// order becomes W pass, gram_reduce, Gram term: the separate Gram pass, and
+// its second read of A, are skipped.
 // The passes run the streaming kernel when W, A and B allow aligned 16-byte
 // loads, and the general kernels otherwise; both write the same partials.
 //
@@ -145,7 +151,13 @@ __device__ __forceinline__ int fswz(int row, int c) {
 //              with B. With a single column tile the Gram term of each row is
 //              complete in its workgroup, which then assembles wnorm and g;
 //              otherwise it stores per-tile partials for the assembly kernel.
-enum PassKind : int { kPassW = 0, kPassGram = 1, kPassBG = 2, kPassWG = 3 };
+//   kPassWB    kPassW, then, in the same accumulators, the workgroup's share
+//              (d_in range x of X takes part x of X of the virtual depth) of
+//              the kPassBG product against the reduced Gram matrix scaled by
+//              s/2. Since rowsum(B . (U + (s/2) B G)) = cross + (s/2) ba, the
+//              epilogue's dot with B then yields cross + (s/2) ba per (range,
+//              column tile), and no separate Gram-term pass runs.
+enum PassKind : int { kPassW = 0, kPassGram = 1, kPassBG = 2, kPassWG = 3, kPassWB = 4 };
 
 // Scalars and outputs of the final assembly (used by kPassBG only).
 struct AssembleArgs {
@@ -220,7 +232,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   constexpr bool GRAM = MODE == kPassGram;
   constexpr bool BG = MODE == kPassBG;
   constexpr bool GF = MODE == kPassWG;               // Gram blocks folded into the W pass
-  constexpr bool WP = MODE == kPassW || GF;          // W pass
+  constexpr bool WB = MODE == kPassWB;               // Gram-term stages after the W stages
+  constexpr bool WP = MODE == kPassW || GF || WB;    // W pass
   static_assert((GRAM ? kRowPadG : kRowPadW) % MT == 0, "row tiles divide the plan's row padding");
   constexpr int NG = sizeof(T) == 2 ? 2 : 1;   // parts of the stored Gram matrix (hi, lo)
   __shared__ __attribute__((aligned(1024))) char r0[C::SLOT];
@@ -239,7 +252,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int wm = wave / WN, wn = wave % WN;
   const int lrow = lane & 31, lgrp = lane >> 5;
 
-  // Tile of this workgroup and the geometry of both operands.
+  // Tile of this workgroup.
   const int X = BG ? 1 : (GRAM ? p.xg : p.xw);
   const int n_nt = BG ? p.n_bt : (GRAM ? (int)(p.ga_cols / NTC) : p.n_nt);
   const int64_t m_rows = GRAM ? p.r : p.d_out;
@@ -252,26 +265,40 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int64_t mrow0 = (int64_t)m * MT;
   const int64_t n0 = (int64_t)n * NTC;
   const int64_t d_in = p.d_in;
-  // Row operand: W (or A) rows of d_in, or B rows of r read twice (hi, lo).
-  const int64_t m_ld = BG ? p.r : d_in;             // elements per row
-  const int64_t m_kvalid = BG ? p.r : d_in;         // valid k of a row
-  const int64_t m_kwrap = BG ? p.rg : ((int64_t)1 << 62);
-  // Column operand: A rows of d_in, or rows of the stored Gram matrix.
-  const int64_t n_ld = BG ? (int64_t)NG * p.rg : d_in;
-  const int64_t n_rows = BG ? p.rg : p.r;
-  const T* Nsrc = BG ? reinterpret_cast<const T*>(ws + p.off_gg) : A;
-  const uint32_t m_rowb = (uint32_t)(m_ld * ESZ), n_rowb = (uint32_t)(n_ld * ESZ);
-  const int64_t k0 = BG ? 0 : range_k0(p, X, x);
-  const int64_t k1 = BG ? (int64_t)NG * p.rg : range_k0(p, X, x + 1);
-  const int n_st = (int)((k1 - k0 + KT - 1) / KT);   // stages of this tile (>= 1)
-
-  // Both operands through buffer descriptors spanning the tile's valid rows:
-  // rows past the matrix read as zeros.
   const int64_t m_left = m_rows - mrow0;
-  const int m_lim = m_left < MT ? (int)m_left : MT;
-  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(Msrc + mrow0 * m_ld, (uint32_t)m_lim * m_rowb);
-  const int n_lim = n_rows - n0 < NTC ? (int)(n_rows - n0) : NTC;
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(Nsrc + n0 * n_ld, (uint32_t)n_lim * n_rowb);
+  const int m_lim = m_left < MT ? (int)m_left : MT;   // valid rows of the tile
+
+  // Stages of the tile, in two phases.
+  //  1. (every mode but kPassBG) Msrc rows (W, or A in the Gram pass)
+  //     against A's rows over this workgroup's d_in range [k0, k1).
+  //  2. (kPassBG; kPassWB after phase 1) B's rows against rows of the
+  //     stored Gram matrix over the virtual depth [v0, v0 + n_bs KT) of
+  //     [0, NG rg): B's columns against Ghi, then again against Glo. rg is
+  //     a whole number of stages, so no stage straddles the seam.
+  const int64_t k0 = BG ? 0 : range_k0(p, X, x);
+  const int64_t k1 = BG ? 0 : range_k0(p, X, x + 1);
+  const int n_st = (int)((k1 - k0 + KT - 1) / KT);   // phase-1 stages (>= 1 unless kPassBG)
+  int n_bs = 0;
+  int64_t v0 = 0;
+  if constexpr (BG || WB) {
+    const int64_t vg = (int64_t)NG * p.rg / KT;     // stages of the whole virtual depth
+    const int64_t g0 = div_u(vg * x, X);
+    n_bs = (int)(div_u(vg * (x + 1), X) - g0);
+    v0 = g0 * KT;
+  }
+  const int n_tot = n_st + n_bs;
+
+  // Every operand goes through a buffer descriptor spanning the tile's valid
+  // rows: rows past the matrix read as zeros.
+  const uint32_t m_rowb = (uint32_t)(d_in * ESZ), n_rowb = m_rowb;
+  const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(Msrc + mrow0 * d_in, (uint32_t)m_lim * m_rowb);
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + n0 * d_in, (uint32_t)n_lim * n_rowb);
+  const uint32_t b_rowb = (uint32_t)(p.r * ESZ), g_rowb = (uint32_t)((int64_t)NG * p.rg * ESZ);
+  const int g_lim = p.rg - n0 < NTC ? (int)(p.rg - n0) : NTC;
+  const T* Gs = reinterpret_cast<const T*>(ws + p.off_gg);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(B + mrow0 * p.r, (uint32_t)m_lim * b_rowb);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(Gs + n0 * NG * p.rg, (uint32_t)g_lim * g_rowb);
 
   // Direct loads: this wave fills blocks wave, wave + NW, ...; lane l lands at
   // byte 16*l of its block, which is LDS row blk*RPB + l/CPR, physical chunk
@@ -280,37 +307,45 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int l_row = lane / CPR;
   const int a_chunk = fswz<CPR>(wave * RPB + l_row, lane % CPR);
   // Blocks b < BPW_M of every wave hold row-operand rows, the rest the
-  // column operand's rows.
-  uint32_t doff[BPW];
+  // column operand's rows; doff for phase 1, eoff for phase 2.
+  uint32_t doff[BPW], eoff[BPW];
 #pragma unroll
   for (int b = 0; b < BPW; ++b) {
     const int row = (b * NW + wave) * RPB + l_row;
     doff[b] = b < C::BPW_M ? (uint32_t)row * m_rowb + (uint32_t)(a_chunk * 16)
                            : (uint32_t)(row - MT) * n_rowb + (uint32_t)(a_chunk * 16);
+    eoff[b] = b < C::BPW_M ? (uint32_t)row * b_rowb + (uint32_t)(a_chunk * 16)
+                           : (uint32_t)(row - MT) * g_rowb + (uint32_t)(a_chunk * 16);
   }
 
   // Stage i of the tile into a ring slot. Stages past the tile (the loop
   // runs a whole number of unrolled groups) and chunks past the valid depth
   // read as zeros, so every step issues the same loads.
   auto issue = [&](int i, char* slot) __attribute__((always_inline)) {
-    const int64_t ks = k0 + (int64_t)i * KT;
-    const int64_t km = ks < m_kwrap ? ks : ks - m_kwrap;    // row-operand depth index
-    const bool in = i < n_st;
+    const bool ph2 = BG || (WB && i >= n_st);       // uniform
+    const int j = i - n_st;
+    const bool in = ph2 ? j < n_bs : i < n_st;
+    const int64_t ks = ph2 ? v0 + (int64_t)j * KT : k0 + (int64_t)i * KT;   // column-operand depth
+    const int64_t km = (ph2 && ks >= p.rg) ? ks - p.rg : ks;              // row-operand depth
     const uint32_t kb_m = (uint32_t)((in ? km : 0) * ESZ), kb_n = (uint32_t)((in ? ks : 0) * ESZ);
-    const bool ok_m = in && km + (int64_t)a_chunk * EPC < m_kvalid;
-    const bool ok_n = in && ks + (int64_t)a_chunk * EPC < (BG ? k1 : d_in);
+    const bool ok_m = in && km + (int64_t)a_chunk * EPC < (ph2 ? p.r : d_in);
+    const bool ok_n = in && (ph2 || ks + (int64_t)a_chunk * EPC < d_in);
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
       // (Offsets are computed before the builtin call: a conditional
       // expression inside its argument list made hipcc's host pass drop the
       // kernel's launch stub.)
       void* dst = slot + (b * NW + wave) * 1024;
-      const uint32_t off = (b < C::BPW_M ? ok_m : ok_n) ? doff[b] : kOob;
+      const uint32_t o = ph2 ? eoff[b] : doff[b];
+      const uint32_t off = (b < C::BPW_M ? ok_m : ok_n) ? o : kOob;
       const int kb = (int)(b < C::BPW_M ? kb_m : kb_n);
-      if (b < C::BPW_M)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(mrs, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0, 0);
+      if (b < C::BPW_M) {
+        const __amdgpu_buffer_rsrc_t rs = ph2 ? brs : mrs;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t rs = ph2 ? grs : ars;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0, 0);
+      }
     }
   };
 
@@ -361,7 +396,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       }
     }
   };
-  auto mfma_step = [&](const Frag& F) __attribute__((always_inline)) {
+  auto mfma_step = [&](const Frag& F, bool w_stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
@@ -369,11 +404,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     if constexpr (GF) gacc = Mfma<T>::run(F[MB + NB], F[MB + NB + 1], gacc);
     if constexpr (WP) {
       // Every wave squares its row fragments (straight-line code); only the
-      // waves of column group 0 store the sums.
+      // waves of column group 0 store the sums. Rows of B (phase 2) are not
+      // part of the base term.
 #pragma unroll
       for (int a = 0; a < MB; ++a)
 #pragma unroll
-        for (int f = 0; f < FC; ++f) sq[a] += chunk_sumsq(F[a][f], T());
+        for (int f = 0; f < FC; ++f) {
+          const float q = chunk_sumsq(F[a][f], T());
+          sq[a] += (WB && !w_stage) ? 0.f : q;
+        }
     }
   };
   // Pipeline. Stage j lives in ring slot j % NS. In stage i, K16 step s+1's
@@ -384,7 +423,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // i+NS into the slot stage i vacated and read stage i+1's first step. The
   // stage count is rounded up to whole unrolled groups (the extra stages are
   // zeros), so the loop body is straight-line code with fixed load counts.
-  const int n_pad = (n_st + NS - 1) / NS * NS;
+  const int n_pad = (n_tot + NS - 1) / NS * NS;
   Frag H[2];
 #pragma unroll
   for (int j = 0; j < NS; ++j) issue(j, ring(j));
@@ -406,7 +445,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           read_step(ring((j + 1) % NS), 0, H[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(H[s & 1]);
+        mfma_step(H[s & 1], i < n_st);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -794,17 +833,19 @@ __device__ __forceinline__ void store_gram(char* ws, const NormPlan& p, int64_t 
 // increasing x (kSumBatch planes per round trip), reading only blocks on or
 // above the diagonal, which every Gram pass computes. The block is written
 // as G[bi][bj] and, off the diagonal, transposed through LDS as G[bj][bi],
-// so every global access is along a row.
+// so every global access is along a row. The stored matrix is gscale * G
+// (one rounded product per element): s/2 when the W pass runs the Gram term
+// in its own accumulators, 1 otherwise.
 constexpr int kReduceThreads = 1024;
 
 template <typename T>
-__global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws) {
+__global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws, float gscale) {
   constexpr int RG = kReduceThreads / 32;   // row groups; each thread owns 32 / RG rows
   constexpr int RPT = 32 / RG;
   __shared__ float tile[32][33];
   int bi, bj;
   tri_tile(blockIdx.x, (int)(p.rg / 32), &bi, &bj);
-  const int c = threadIdx.x % 32, rg = threadIdx.x / 32;
+  const int c = threadIdx.x % 32, grp = threadIdx.x / 32;
   const float* part_g = reinterpret_cast<const float*>(ws + p.off_g);
   const int64_t plane = p.ga_rows * p.ga_cols;
   const int64_t j = (int64_t)bj * 32 + c;
@@ -813,7 +854,7 @@ __global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p,
   bool live[RPT];
 #pragma unroll
   for (int q = 0; q < RPT; ++q) {
-    const int64_t i = (int64_t)bi * 32 + rg + RG * q;
+    const int64_t i = (int64_t)bi * 32 + grp + RG * q;
     acc[q] = 0.f;
     live[q] = i < p.r && j < p.r;
     src[q] = part_g + i * p.ga_cols + j;
@@ -833,7 +874,8 @@ __global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p,
   }
 #pragma unroll
   for (int q = 0; q < RPT; ++q) {
-    const int row = rg + RG * q;
+    const int row = grp + RG * q;
+    acc[q] = __fmul_rn(acc[q], gscale);
     store_gram<T>(ws, p, (int64_t)bi * 32 + row, j, acc[q]);
     tile[row][c] = acc[q];
   }
@@ -841,7 +883,7 @@ __global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p,
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < RPT; ++q) {
-    const int row = rg + RG * q;   // row of the transposed block: column `row` of the tile
+    const int row = grp + RG * q;   // row of the transposed block: column `row` of the tile
     store_gram<T>(ws, p, (int64_t)bj * 32 + row, (int64_t)bi * 32 + c, tile[c][row]);
   }
 }
@@ -964,11 +1006,15 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
 // assemble: per row, fixed-order sums of the partials, then
 // wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and g = m / max(wnorm, eps),
 // every operation separately rounded (no contraction), sqrt and division
-// correctly rounded. One thread per row; reads are coalesced.
+// correctly rounded. One thread per row; reads are coalesced. n_ba = 0 when
+// the cross partials already hold cross + (s/2) ba (ba is then 0 here).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void assemble_kernel(NormPlan p, const char* __restrict__ ws, int n_ba, float s,
-                                                            const float* m, float eps, float* wnorm, float* g) {
-  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+constexpr int kAsmThreads = 256;   // threads (rows) per assembly workgroup
+
+__global__ __launch_bounds__(kAsmThreads) void assemble_kernel(NormPlan p, const char* __restrict__ ws, int n_ba,
+                                                               float s, const float* m, float eps, float* wnorm,
+                                                               float* g) {
+  const int64_t j = (int64_t)blockIdx.x * kAsmThreads + threadIdx.x;
   if (j >= p.d_out) return;
   const float* pb = reinterpret_cast<const float*>(ws + p.off_base) + j;
   const float* pc = reinterpret_cast<const float*>(ws + p.off_cross) + j;
@@ -1052,6 +1098,32 @@ __global__ __launch_bounds__(kThreads) void widen_kernel(const f16_t* in, int64_
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Launch markers, a benchmark hook (dora_set_launch_events): while events
+// are set, each norm call records event 0 on its stream before its first
+// launch and event i after its i-th launch, for as many events as were
+// given, skipping null entries. Process-wide and unsynchronised, like the
+// hook itself.
+hipEvent_t g_marks[kMaxLaunchEvents];
+int g_n_marks = 0;
+int g_next_mark = 0;
+
+// Records marker i if it exists and is not a null entry.
+hipError_t record_mark(int i, hipStream_t st) {
+  return (i < g_n_marks && g_marks[i] != nullptr) ? hipEventRecord(g_marks[i], st) : hipSuccess;
+}
+
+hipError_t begin_marks(hipStream_t st) {
+  g_next_mark = 1;
+  return record_mark(0, st);
+}
+
+// The status of the launch just made, and its end marker if one is due.
+hipError_t launched(hipStream_t st) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return record_mark(g_next_mark++, st);
+}
+
 template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, int MODE>
 hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const void* B, char* ws,
                        const AssembleArgs& aa, hipStream_t st) {
@@ -1069,7 +1141,7 @@ hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const vo
   }
   hipLaunchKernelGGL((norm_fast_kernel<T, WM, WN, MB, NB, KT, NS, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, st,
                      p, static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws, aa);
-  return hipGetLastError();
+  return launched(st);
 }
 
 template <typename T, int WM, int WN, int MB, int NB, int KT, bool GRAM>
@@ -1080,7 +1152,7 @@ hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const voi
   const int64_t grid = (GRAM ? p.xg : p.xw) * ceil_div64(rows, C::MT) * (cols / C::NTC);
   hipLaunchKernelGGL((norm_gen_kernel<T, WM, WN, MB, NB, KT, GRAM>), dim3((unsigned)grid), dim3(C::NT), 0, st, p,
                      static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws);
-  return hipGetLastError();
+  return launched(st);
 }
 
 // H is the 16-bit storage type (bf16 or fp16); fp32 uses the F* configurations.
@@ -1089,6 +1161,9 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
                        char* ws, hipStream_t st) {
   constexpr bool GRAM = MODE == kPassGram;
   const AssembleArgs aa{};
+  // The Gram term inside the W pass needs the Gram matrix in the storage
+  // type (bf16 hi + lo, or fp32); fp16 keeps it in fp32 and never plans it.
+  if constexpr (MODE == kPassWB && sizeof(H) == 2 && !__is_same(H, bf16_t)) return hipErrorInvalidValue;
   if (p.fast) {
     // The Gram pass only uses the 64- and 128-column configurations.
     switch (fcfg) {
@@ -1110,8 +1185,8 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
     }
     return hipErrorInvalidValue;
   }
-  if constexpr (MODE == kPassWG) {
-    return hipErrorInvalidValue;   // the general kernel never folds the Gram blocks in
+  if constexpr (MODE == kPassWG || MODE == kPassWB) {
+    return hipErrorInvalidValue;   // the general kernel never takes G or the Gram term in
   } else {
     switch (gcfg) {
       case kGenB64: return launch_gen<H, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
@@ -1152,17 +1227,17 @@ hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, cons
       e = launch_fast<float, 2, 4, 1, 1, 32, 2, kPassBG>(p, B, nullptr, B, ws, aa, st);
     }
     if (e != hipSuccess || p.n_bt == 1) return e;
-    hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+    hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads), 0,
                        st, p, ws, p.n_bt, s, m, eps, wnorm, g);
-    return hipGetLastError();
+    return launched(st);
   }
   hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)p.n_cb),
                      dim3(kGramRows * 2), 0, st, p, static_cast<const T*>(B), ws);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launched(st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads), 0, st,
                      p, ws, p.n_cb, s, m, eps, wnorm, g);
-  return hipGetLastError();
+  return launched(st);
 }
 
 }  // namespace
@@ -1172,7 +1247,12 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
                                 hipStream_t st) {
   char* ws = static_cast<char*>(ws_);
   const bool fold = p.fast && p.gfold;
-  hipError_t e;
+  // bf16 and fp32 on the streaming path run the Gram term in the W pass's
+  // accumulators against (s/2) G; fp16 runs its Gram term in fp32 on B
+  // widened, so it keeps the separate pass.
+  const bool fuse = p.fast && !p.gfold && p.dtype != 2;
+  hipError_t e = begin_marks(st);
+  if (e != hipSuccess) return e;
   if (fold) {
     e = launch_pass<kPassWG>(p, p.fcfg, p.gcfg, W, A, B, ws, st);   // W pass with G folded in
   } else {
@@ -1184,9 +1264,18 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   // bf16 keeps G as bf16 hi + lo for the bf16 Gram term; fp32 and fp16 keep
   // it in fp32 (fp16's range cannot hold every G) for the fp32 Gram term.
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
-                     dim3((unsigned)tri_count(p.rg / 32)), dim3(kReduceThreads), 0, st, q, ws);
-  e = hipGetLastError();
+                     dim3((unsigned)tri_count(p.rg / 32)), dim3(kReduceThreads), 0, st, q, ws,
+                     fuse ? 0.5f * s : 1.0f);
+  e = launched(st);
   if (e != hipSuccess) return e;
+  if (fuse) {
+    // W pass with the Gram term; its cross partials hold cross + (s/2) ba.
+    e = launch_pass<kPassWB>(p, p.fcfg, p.gcfg, W, A, B, ws, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads), 0,
+                       st, p, ws, 0, s, m, eps, wnorm, g);
+    return launched(st);
+  }
   if (!fold) {
     e = launch_pass<kPassW>(p, p.fcfg, p.gcfg, W, A, B, ws, st);   // W pass
     if (e != hipSuccess) return e;
@@ -1198,7 +1287,7 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
     const int64_t nB = p.d_out * p.r;
     hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((nB + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
                        static_cast<const f16_t*>(B), nB, Bf);
-    e = hipGetLastError();
+    e = launched(st);
     if (e != hipSuccess) return e;
     return launch_tail<float>(p, Bf, ws, s, m, eps, wnorm, g, st);
   }
@@ -1207,6 +1296,8 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
 
 hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t d_in, bool vec, const float* m,
                                float eps, float* wnorm, float* g, hipStream_t st) {
+  const hipError_t e = begin_marks(st);
+  if (e != hipSuccess) return e;
   if (dtype == 0)
     hipLaunchKernelGGL((norm_rowonly_kernel<bf16_t>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
                        static_cast<const bf16_t*>(W), d_out, d_in, vec, m, eps, wnorm, g);
@@ -1216,7 +1307,12 @@ hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t 
   else
     hipLaunchKernelGGL((norm_rowonly_kernel<float>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
                        static_cast<const float*>(W), d_out, d_in, vec, m, eps, wnorm, g);
-  return hipGetLastError();
+  return launched(st);
+}
+
+void set_launch_events(const hipEvent_t* events, int n) {
+  g_n_marks = n < kMaxLaunchEvents ? n : kMaxLaunchEvents;
+  for (int i = 0; i < g_n_marks; ++i) g_marks[i] = events[i];
 }
 
 hipError_t launch_magnitude(const float* m, const float* wnorm, float eps, int64_t n, float* g, hipStream_t st) {

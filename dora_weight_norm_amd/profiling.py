@@ -63,7 +63,8 @@ def short_name(name: str) -> str:
     m = re.match(r"norm_fast_kernel<(.*)>", n)
     if m:
         args = [a.strip() for a in m.group(1).split(",")]
-        mode = {"0": "W pass", "1": "Gram pass", "2": "Gram term + assembly"}.get(args[-1], args[-1])
+        mode = {"0": "W pass", "1": "Gram pass", "2": "Gram term + assembly", "3": "W pass + G blocks",
+                "4": "W pass + Gram term"}.get(args[-1], args[-1])
         n = f"norm_fast_kernel<{', '.join(args)}> ({mode})"
     return n
 
@@ -132,6 +133,7 @@ def main() -> int:
         part_calls[role] = min(part_calls.get(role, s["calls"]), s["calls"])
     steps = part_calls["compose"]
     traffic = {"norm": 0.0, "compose": 0.0, "compose_bwd": 0.0, "layer_output": 0.0}
+    w_pass_bytes = None   # HBM bytes of one W-pass launch
     lines = []
     for s in sorted(ours, key=lambda s: -s["total_us"]):
         role = kernel_role(s["name"])
@@ -142,6 +144,8 @@ def main() -> int:
         per_step = s["calls"] / part_calls[role]
         if fk and wk:
             traffic[role] += (fb + wb) * per_step
+            if role == "norm" and "(W pass" in short_name(s["name"]):
+                w_pass_bytes = fb + wb
         lines.append(f"| {short_name(s['name'])} | {role} | {s['calls']} | {s['avg_us']:.2f} | {s['min_us']:.2f} | "
                      f"{s['max_us']:.2f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
     def part_us(role):
@@ -159,6 +163,7 @@ def main() -> int:
           "norm_bytes_per_call": traffic["norm"], "compose_bytes_per_call": traffic["compose"],
           "fetch_scale": f_scale, "write_scale": w_scale,
           "compose_bwd_bytes_per_call": traffic["compose_bwd"],
+          "w_pass_bytes_per_launch": w_pass_bytes,
           "norm_us_per_call": norm_us, "compose_us_per_call": comp_us, "compose_bwd_us_per_call": bwd_us,
           "longest_step_kernel": {"name": short_name(longest["name"]), "part": kernel_role(longest["name"]),
                                   "avg_us": longest["avg_us"]},
@@ -175,8 +180,8 @@ def main() -> int:
           f"- compose calls in the trace: {steps}; norm call = sum of its kernels = {norm_us:.2f} µs; "
           f"compose call = {comp_us:.2f} µs",
           f"- longest single launch of a step: {short_name(longest['name'])} ({longest['avg_us']:.2f} µs)",
-          f"- HBM traffic per norm call: {traffic['norm'] / 1e6:.1f} MB; per compose call: "
-          f"{traffic['compose'] / 1e6:.1f} MB",
+          f"- HBM traffic per norm call: {traffic['norm'] / 1e6:.1f} MB (W-pass launch: "
+          f"{(w_pass_bytes or 0) / 1e6:.1f} MB); per compose call: {traffic['compose'] / 1e6:.1f} MB",
           f"- compose backward call (timed on its own after the steps) = {bwd_us:.2f} µs; HBM traffic "
           f"{traffic['compose_bwd'] / 1e6:.1f} MB",
           f"- copy calibration (1 GiB device copy): FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}",

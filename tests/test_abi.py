@@ -66,6 +66,10 @@ def test_plans_of_the_workloads(name):
     # square 128-column Gram tiles are the symmetric ones
     assert info["gram_symmetric"] == (info["gram_tile_cols"] == 128 and w.dtype != "f32")
     assert info["tile_cols"] * info["col_tiles"] >= w.r
+    # the Gram term runs inside the W pass unless G is folded into it (or fp16)
+    assert info["gram_term_fused"] == int(not info["gram_folded"] and w.dtype != "f16")
+    # launch order: [Gram pass, gram_reduce,] W pass, ...
+    assert info["w_launch"] == (0 if info["gram_folded"] else 2)
 
 
 def test_plan_self_check_on_many_shapes():
@@ -184,6 +188,16 @@ def test_norm_to_dtype_argument_errors():
     assert lib.dora_norm_to_dtype(P(0x1000), 8, 0, P(0x2001), None) == 1     # bf16 out misaligned
     assert lib.dora_norm_to_dtype(P(0x1000), 8, 0, P(0x1010), None) == 1     # out overlaps wnorm
     assert lib.dora_norm_to_dtype(None, 0, 0, None, None) == 0               # nothing to do
+
+
+def test_launch_events_hook_arguments():
+    lib = bnd.load()
+    assert lib.dora_set_launch_events(None, -1) == 1
+    assert lib.dora_set_launch_events(None, 2) == 1
+    assert lib.dora_set_launch_events(None, 0) == 0            # clears the hook
+    bnd.dora_set_launch_events([])
+    with pytest.raises(ValueError):
+        bnd.dora_set_launch_events([0])                         # no handle
 
 
 def test_compose_backward_argument_errors_return_before_launch():

@@ -167,15 +167,55 @@ def test_nan_row_propagates_only_to_its_row():
 
 def test_deterministic_and_budget_invariant():
     W, A, B = I.norm_inputs(1500, 4096, 384, "bf16", 23)
-    a, _ = _run(W, A, B, "bf16", 0.5)
-    b, _ = _run(W, A, B, "bf16", 0.5)
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    m = np.full(1500, 1.25, np.float32)
+    a, ga = _run(W, A, B, "bf16", 0.5, m)
+    # Which workgroup of a row tile finishes last (and assembles its rows)
+    # varies from run to run; the result must not.
+    for _ in range(4):
+        b, gb = _run(W, A, B, "bf16", 0.5, m)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert np.array_equal(ga.view(np.uint32), gb.view(np.uint32))
     small = bnd.dora_norm_plan_info(1500, 4096, 384, "bf16", 0.5, 2 << 20)
     big = bnd.dora_norm_plan_info(1500, 4096, 384, "bf16", 0.5, 256 << 20)
     assert (small["gram_ranges"], small["w_ranges"]) != (big["gram_ranges"], big["w_ranges"])
     c, _ = _run(W, A, B, "bf16", 0.5, budget=2 << 20)
     assert np.max(np.abs(c.astype(np.float64) - a) / a) <= 1e-6
     check_norm(c, O.dense_row_norm(W, A, B, 0.5))
+
+
+def test_launch_events_mark_each_launch():
+    W, A, B = I.norm_inputs(2048, 4096, 384, "bf16", 25)
+    info = bnd.dora_norm_plan_info(2048, 4096, 384, "bf16", 0.5)
+    assert info["gram_term_fused"] == 1 and info["w_launch"] == 2
+    plain, _ = _run(W, A, B, "bf16", 0.5)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    bnd.dora_set_launch_events(evs)
+    try:
+        marked, _ = _run(W, A, B, "bf16", 0.5)
+    finally:
+        bnd.dora_set_launch_events([])
+    assert np.array_equal(plain.view(np.uint32), marked.view(np.uint32))
+    # four launches: Gram pass, gram_reduce, W pass with the Gram term,
+    # assembly; the sixth event is past the last launch and stays as it was
+    # recorded before the call
+    ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(4)]
+    assert all(t > 0 for t in ms)
+    assert ms[2] == max(ms)                     # the W pass is the longest launch
+    assert evs[4].elapsed_time(evs[5]) < 0      # event 5 was not re-recorded
+    say(f"    launches (ms): {', '.join(f'{t:.4f}' for t in ms)}")
+    # only the two marks around the W pass (null entries are skipped)
+    before = evs[0].elapsed_time(evs[2])
+    bnd.dora_set_launch_events([None, None, evs[2], evs[3]])
+    try:
+        again, _ = _run(W, A, B, "bf16", 0.5)
+    finally:
+        bnd.dora_set_launch_events([])
+    assert np.array_equal(plain.view(np.uint32), again.view(np.uint32))
+    assert evs[2].elapsed_time(evs[3]) > 0
+    assert evs[0].elapsed_time(evs[2]) > before   # event 0 kept its old time
 
 
 def test_power_of_two_scale_moves_into_B_bitwise():
