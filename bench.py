@@ -40,6 +40,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 F32_MFMA_PEAK_TFLOPS = 157.3
 NSETS = 3                       # input sets the steps rotate through
+ROUNDS = 5                      # rounds of K back-to-back calls for the per-call times
 METRIC = "factored-norm ms/TFLOP/s + compose GB/s (%HBM peak), 8192×8192 r=384 bf16"
 
 
@@ -143,35 +144,30 @@ def time_compose_backward(args, w, lib, bnd, I, based, lorad, g, wnorm, stream, 
         run()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    print(f"# timing {K} compose backward calls", file=sys.stderr, flush=True)
-    for k in range(K):
-        ev[k][0].record(stream)
-        run()
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    times = [e0.elapsed_time(e1) for e0, e1 in ev]
-    ms = float(np.mean(times))
+    print(f"# timing {K} compose backward calls, {ROUNDS} rounds", file=sys.stderr, flush=True)
+    rounds = [_event_ms(run, K, stream) for _ in range(ROUNDS)]
+    ms = float(np.median(rounds))
     nb = compose_bwd_bytes(w.T, w.d_out, esize)
     gbs = nb / (ms * 1e-3) / 1e9
-    return {"ms": ms, "median_ms": float(np.median(times)), "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+    return {"ms": ms, "rounds_ms": rounds, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": nb, "workspace_bytes": ws_bytes,
             "note": "d_base, d_lora, dg and dm in one C-ABI call (row-strip kernel + fixed-order column "
                     "reduction); timed separately, not part of the forward step"}
 
 
 def _event_ms(fn, reps, stream):
-    """Mean milliseconds of fn() over reps calls, HIP events on `stream`."""
-    import numpy as np
+    """Mean milliseconds of fn() over reps back-to-back calls: HIP events on
+    `stream` before the first call and after the last (none in between)."""
     import torch
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for k in range(reps):
-        ev[k][0].record(stream)
-        fn()
-        ev[k][1].record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def comparisons(args, w, bnd, Wd, Ad, Bd, based, lorad, g, md, comp_ms, norm_ms, stream, tdt):
@@ -370,25 +366,44 @@ def main() -> int:
         del src, dst
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    print(f"# timing {K} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        ev[k][0].record(stream)
-        run_norm(k)
-        ev[k][1].record(stream)
-        run_compose(k)
-        ev[k][2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
-    # The W-pass kernel inside the norm call: the same K steps again, with
-    # the library recording one event on the stream before that launch and
-    # one after it (its launch-event hook; launch w_launch lies between
-    # marks w_launch and w_launch + 1). Each recorded event adds about 3 us
-    # between launches, so the steps above, which give the per-call times,
-    # run without them.
+    def span(fn):
+        """Milliseconds per call of fn(k), k = 0 .. K-1, between one event on
+        the stream before the first call and one after the last. (An event
+        recorded between two launches adds about 3 us to the gap between
+        them, so no event is recorded between calls.)"""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for k in range(K):
+            fn(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    def step(k):
+        run_norm(k)
+        run_compose(k)
+
+    # The timed region: K steps, one norm call and one compose call each.
+    print(f"# timing {K} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ms_per_step = span(step)
+    wall = time.perf_counter() - t0
+    # Per-call times: K calls of each back to back, rotating through the
+    # input sets as the steps do, in ROUNDS rounds; the median round counts.
+    print(f"# timing the norm and compose calls: {ROUNDS} rounds of {K} calls each", file=sys.stderr, flush=True)
+    norm_rounds, comp_rounds = [], []
+    for _ in range(ROUNDS):
+        norm_rounds.append(span(run_norm))
+        comp_rounds.append(span(run_compose))
+    norm_ms = float(np.median(norm_rounds))
+    comp_ms = float(np.median(comp_rounds))
+
+    # The W-pass kernel inside the norm call: K more steps, with the library
+    # recording one event on the stream just before that launch and one just
+    # after it (its launch-event hook; launch w_launch lies between marks
+    # w_launch and w_launch + 1).
     plan = bnd.dora_norm_plan_info(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
     wl = plan["w_launch"]
     marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -404,13 +419,8 @@ def main() -> int:
         run_compose(k)
     torch.cuda.synchronize()
     lib.dora_set_launch_events(None, 0)
-    w_ms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
-    norm_ms = float(np.mean([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
-    comp_ms = float(np.mean([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]))
-    norm_med = float(np.median([ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]))
-    comp_med = float(np.median([ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]))
-    span_ms = ev[0][0].elapsed_time(ev[K - 1][2])
-    ms_per_step = span_ms / K
+    w_times = [a.elapsed_time(b) for a, b in marks]
+    w_ms = float(np.median(w_times))
 
     F = norm_flops(w.d_out, w.d_in, w.r)
     nb = norm_bytes(w.d_out, w.d_in, w.r, esize)
@@ -460,7 +470,10 @@ def main() -> int:
     roof_w = {"bound": "mfma", "achieved": w_tflops, "peak": mfma_peak, "unit": "TFLOP/s",
               "frac": w_tflops / mfma_peak, "traffic": traffic.get("w_pass"),
               "kernel": f"norm_fast_kernel ({w_name}; launch {wl} of the norm call)",
-              "algorithmic_flops": Fw, "launch_ms": w_ms, "traffic_source": traffic_note}
+              "algorithmic_flops": Fw, "launch_ms": w_ms, "launch_ms_mean": float(np.mean(w_times)),
+              "timing": "median over the steps of the interval between the events the library records just "
+                        "before and just after the launch (includes its dispatch gap)",
+              "traffic_source": traffic_note}
     # The dominant kernel is the longest single launch of a step, as the
     # committed kernel trace of this workload lists it: the compose kernel,
     # or the norm's W pass. Without a trace, the longer of the compose
@@ -486,11 +499,11 @@ def main() -> int:
         "config": {"workload": w.name, "d_out": w.d_out, "d_in": w.d_in, "r": w.r, "s": w.s, "T": w.T,
                    "budget_MiB": w.budget >> 20, "parallelism": "single-gpu"},
         "norm_ms": norm_ms,
-        "norm_median_ms": norm_med,
+        "norm_rounds_ms": norm_rounds,
         "norm_tflops": norm_tflops,
         "norm_gbs": norm_gbs,
         "compose_ms": comp_ms,
-        "compose_median_ms": comp_med,
+        "compose_rounds_ms": comp_rounds,
         "compose_gbs": comp_gbs,
         "compose_hbm_frac": comp_gbs / HBM_PEAK_GBS,
         "wall_ms_per_step": wall / K * 1e3,
