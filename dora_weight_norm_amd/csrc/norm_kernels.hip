@@ -1009,37 +1009,77 @@ __global__ __launch_bounds__(kGramRows * 2, 1) void gram_term_kernel(NormPlan p,
 // correctly rounded. One thread per row; reads are coalesced. n_ba = 0 when
 // the cross partials already hold cross + (s/2) ba (ba is then 0 here).
 // ---------------------------------------------------------------------------
-constexpr int kAsmThreads = 256;   // threads (rows) per assembly workgroup
+constexpr int kAsmThreads = 256;   // threads per assembly workgroup
 
+// `split` threads per row (a power of two, at most 64): thread q of a row
+// sums planes [n q / split, n (q+1) / split) of each kind in increasing
+// order, the three kinds in lock step (each batch issues all its loads
+// before any addition); then every thread adds its row's split partial sums
+// in the order q = 0, 1, ..., and the row's first thread assembles. With
+// split = 1 this is the plain sum over the planes in order. The host picks
+// the smallest split that leaves each thread one batch of loads, so rows
+// with many partials (many d_in ranges or column tiles) are summed by
+// several threads at once.
 __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(NormPlan p, const char* __restrict__ ws, int n_ba,
                                                                float s, const float* m, float eps, float* wnorm,
-                                                               float* g) {
-  const int64_t j = (int64_t)blockIdx.x * kAsmThreads + threadIdx.x;
-  if (j >= p.d_out) return;
+                                                               float* g, int split) {
+  const int64_t t = (int64_t)blockIdx.x * kAsmThreads + threadIdx.x;
+  const int64_t j = t / split;
+  const int q = (int)(t % split);
+  const bool live = j < p.d_out;
   const float* pb = reinterpret_cast<const float*>(ws + p.off_base) + j;
   const float* pc = reinterpret_cast<const float*>(ws + p.off_cross) + j;
   const float* pa = reinterpret_cast<const float*>(ws + p.off_ba) + j;
   const int nb = p.xw, nc = p.xw * p.n_nt, na = n_ba;
-  const int n = nb > nc ? (nb > na ? nb : na) : (nc > na ? nc : na);
-  // The three sums in lock step: each batch issues all its loads before any
-  // addition, and each sum still adds its planes in increasing order.
+  const int b0 = nb * q / split, b1 = nb * (q + 1) / split;
+  const int c0 = nc * q / split, c1 = nc * (q + 1) / split;
+  const int a0 = na * q / split, a1 = na * (q + 1) / split;
+  const int len = (b1 - b0) > (c1 - c0) ? ((b1 - b0) > (a1 - a0) ? b1 - b0 : a1 - a0)
+                                        : ((c1 - c0) > (a1 - a0) ? c1 - c0 : a1 - a0);
   float base = 0.f, cross = 0.f, ba = 0.f;
-  for (int i = 0; i < n; i += kSumBatch) {
+  for (int i = 0; i < len; i += kSumBatch) {
     float vb[kSumBatch], vc[kSumBatch], va[kSumBatch];
 #pragma unroll
     for (int u = 0; u < kSumBatch; ++u) {
-      vb[u] = (i + u < nb) ? pb[(int64_t)(i + u) * p.ld_w] : 0.f;
-      vc[u] = (i + u < nc) ? pc[(int64_t)(i + u) * p.ld_w] : 0.f;
-      va[u] = (i + u < na) ? pa[(int64_t)(i + u) * p.ld_w] : 0.f;
+      vb[u] = (live && b0 + i + u < b1) ? pb[(int64_t)(b0 + i + u) * p.ld_w] : 0.f;
+      vc[u] = (live && c0 + i + u < c1) ? pc[(int64_t)(c0 + i + u) * p.ld_w] : 0.f;
+      va[u] = (live && a0 + i + u < a1) ? pa[(int64_t)(a0 + i + u) * p.ld_w] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kSumBatch; ++u) {
-      if (i + u < nb) base += vb[u];
-      if (i + u < nc) cross += vc[u];
-      if (i + u < na) ba += va[u];
+      if (b0 + i + u < b1) base += vb[u];
+      if (c0 + i + u < c1) cross += vc[u];
+      if (a0 + i + u < a1) ba += va[u];
     }
   }
-  assemble_sums(base, cross, ba, s, eps, m, wnorm, g, j);
+  if (split > 1) {
+    // The row's threads are consecutive lanes of one wave.
+    const int first = (int)(threadIdx.x & 63) - q;
+    float tb = __shfl(base, first, 64), tc = __shfl(cross, first, 64), ta = __shfl(ba, first, 64);
+    for (int i = 1; i < split; ++i) {
+      tb += __shfl(base, first + i, 64);
+      tc += __shfl(cross, first + i, 64);
+      ta += __shfl(ba, first + i, 64);
+    }
+    base = tb, cross = tc, ba = ta;
+  }
+  if (live && q == 0) assemble_sums(base, cross, ba, s, eps, m, wnorm, g, j);
+}
+
+hipError_t launched(hipStream_t st);
+
+// assemble_kernel over all rows, with the smallest split (threads per row)
+// that leaves each thread at most one batch of kSumBatch planes per kind.
+hipError_t launch_assemble(const NormPlan& p, const char* ws, int n_ba, float s, const float* m, float eps,
+                           float* wnorm, float* g, hipStream_t st) {
+  const int nc = p.xw * p.n_nt;
+  const int n = p.xw > nc ? (p.xw > n_ba ? p.xw : n_ba) : (nc > n_ba ? nc : n_ba);
+  int split = 1;
+  while (split < 64 && (n + split - 1) / split > kSumBatch) split *= 2;
+  const int64_t threads = p.d_out * split;
+  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((threads + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads),
+                     0, st, p, ws, n_ba, s, m, eps, wnorm, g, split);
+  return launched(st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1227,17 +1267,13 @@ hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, cons
       e = launch_fast<float, 2, 4, 1, 1, 32, 2, kPassBG>(p, B, nullptr, B, ws, aa, st);
     }
     if (e != hipSuccess || p.n_bt == 1) return e;
-    hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads), 0,
-                       st, p, ws, p.n_bt, s, m, eps, wnorm, g);
-    return launched(st);
+    return launch_assemble(p, ws, p.n_bt, s, m, eps, wnorm, g, st);
   }
   hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)p.n_cb),
                      dim3(kGramRows * 2), 0, st, p, static_cast<const T*>(B), ws);
   hipError_t e = launched(st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads), 0, st,
-                     p, ws, p.n_cb, s, m, eps, wnorm, g);
-  return launched(st);
+  return launch_assemble(p, ws, p.n_cb, s, m, eps, wnorm, g, st);
 }
 
 }  // namespace
@@ -1272,9 +1308,7 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
     // W pass with the Gram term; its cross partials hold cross + (s/2) ba.
     e = launch_pass<kPassWB>(p, p.fcfg, p.gcfg, W, A, B, ws, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((p.d_out + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads), 0,
-                       st, p, ws, 0, s, m, eps, wnorm, g);
-    return launched(st);
+    return launch_assemble(p, ws, 0, s, m, eps, wnorm, g, st);
   }
   if (!fold) {
     e = launch_pass<kPassW>(p, p.fcfg, p.gcfg, W, A, B, ws, st);   // W pass
