@@ -167,9 +167,11 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
 //   dg[j]       = sum_t dy[t,j] * (base[t,j] + s * lora[t,j])
 // Each thread owns one 16-byte column strip and a fixed set of rows, as in
 // the forward; with DG it also accumulates its rows' dg terms in fp32
-// (fma(dy, fma(s, lora, base), acc), rows in increasing order) and stores
-// one partial per (row block, column). A second kernel adds the row-block
-// partials in a fixed order, so dg is reproducible; no float atomics.
+// (fma(dy, fma(s, lora, base), acc), rows in increasing order; in a narrow
+// workgroup each row lane does so, and the lanes' sums are then added in
+// lane order) and stores one partial per (row block, column). A second
+// kernel adds the row-block partials in a fixed order, so dg is
+// reproducible; no float atomics.
 // With the magnitude frozen (no dg), base and lora are not read at all.
 // ---------------------------------------------------------------------------
 constexpr int kBwdMaxRowBlocks = 256;
@@ -180,18 +182,24 @@ __global__ __launch_bounds__(256) void compose_bwd_kernel(const T* dy, const T* 
                                                           const float* __restrict__ g, float s, int64_t T_rows,
                                                           int64_t d_out, T* d_base, T* d_lora, float* part) {
   using V = typename Strip<T, VEC>::V;
+  // threadIdx.x: column strip; threadIdx.y: row lane. A narrow workgroup
+  // (few column strips) carries blockDim.y row lanes, so that it still has
+  // several waves; lane y of row block b takes rows (b * blockDim.y + y) *
+  // kUnroll + ..., stepping gridDim.y * blockDim.y * kUnroll.
+  __shared__ float lanes[256 * VEC];
+  const int nl = blockDim.y, ly = threadIdx.y;
   const int64_t cg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (cg >= d_out / VEC) return;
-  const int64_t c0 = cg * VEC;
+  const bool col_ok = cg < d_out / VEC;
+  const int64_t c0 = col_ok ? cg * VEC : 0;
   float gv[VEC], gm1[VEC], acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    gv[e] = g[c0 + e];
+    gv[e] = col_ok ? g[c0 + e] : 0.f;
     gm1[e] = gv[e] - 1.0f;
     acc[e] = 0.f;
   }
-  const int64_t step = (int64_t)gridDim.y * kUnroll;
-  for (int64_t t0 = (int64_t)blockIdx.y * kUnroll; t0 < T_rows; t0 += step) {
+  const int64_t step = (int64_t)gridDim.y * nl * kUnroll;
+  for (int64_t t0 = ((int64_t)blockIdx.y * nl + ly) * kUnroll; col_ok && t0 < T_rows; t0 += step) {
     V yv[kUnroll], bv[kUnroll], lv[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -228,8 +236,21 @@ __global__ __launch_bounds__(256) void compose_bwd_kernel(const T* dy, const T* 
     }
   }
   if constexpr (DG) {
+    if (nl > 1) {
+      // The row lanes' sums, added in lane order by lane 0.
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) part[(int64_t)blockIdx.y * d_out + c0 + e] = acc[e];
+      for (int e = 0; e < VEC; ++e) lanes[(ly * blockDim.x + threadIdx.x) * VEC + e] = acc[e];
+      __syncthreads();
+      if (ly == 0) {
+        for (int k = 1; k < nl; ++k)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] += lanes[(k * blockDim.x + threadIdx.x) * VEC + e];
+      }
+    }
+    if (ly == 0 && col_ok) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) part[(int64_t)blockIdx.y * d_out + c0 + e] = acc[e];
+    }
   }
 }
 
@@ -283,8 +304,11 @@ __global__ __launch_bounds__(256) void compose_bwd_reduce_kernel(const float* pa
 // Launch shape of the backward: one thread per 16-byte strip, and about
 // kBwdTargetBlocks workgroups in all (at most max_by row blocks). Fewer,
 // longer row strips stream as fast and leave fewer dg partials to reduce.
+// A workgroup of fewer than 256 strips gets 256 / tpb row lanes (rows of
+// its block taken in turn), so it still has four waves.
 struct Grid2 {
   int64_t tpb, bx, by;
+  int64_t lanes() const { return tpb <= 128 ? 256 / tpb : 1; }
 };
 Grid2 strip_grid(int64_t T_rows, int64_t d_out, int vec, int64_t max_by) {
   const int64_t ncg = d_out / vec;
@@ -308,12 +332,12 @@ hipError_t launch_bwd(const void* dy, const void* base, const void* lora, const 
   if (q.by > 0 && q.bx > 0) {
     if (dg != nullptr)
       hipLaunchKernelGGL((compose_bwd_kernel<T, VEC, true>), dim3((unsigned)q.bx, (unsigned)q.by),
-                         dim3((unsigned)q.tpb), 0, st, static_cast<const T*>(dy), static_cast<const T*>(base),
+                         dim3((unsigned)q.tpb, (unsigned)q.lanes()), 0, st, static_cast<const T*>(dy), static_cast<const T*>(base),
                          static_cast<const T*>(lora), g, s, T_rows, d_out, static_cast<T*>(d_base),
                          static_cast<T*>(d_lora), part);
     else
       hipLaunchKernelGGL((compose_bwd_kernel<T, VEC, false>), dim3((unsigned)q.bx, (unsigned)q.by),
-                         dim3((unsigned)q.tpb), 0, st, static_cast<const T*>(dy), static_cast<const T*>(base),
+                         dim3((unsigned)q.tpb, (unsigned)q.lanes()), 0, st, static_cast<const T*>(dy), static_cast<const T*>(base),
                          static_cast<const T*>(lora), g, s, T_rows, d_out, static_cast<T*>(d_base),
                          static_cast<T*>(d_lora), part);
     const hipError_t e = hipGetLastError();
