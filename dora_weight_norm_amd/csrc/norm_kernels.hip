@@ -291,7 +291,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // Every operand goes through a buffer descriptor spanning the tile's valid
   // rows: rows past the matrix read as zeros.
   const uint32_t m_rowb = (uint32_t)(d_in * ESZ), n_rowb = m_rowb;
-  const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
+  // (In the Gram-term pass a column tile may start past r, since rg pads r;
+  // its A descriptor, never read there, then spans no rows.)
+  const int n_lim = p.r - n0 < NTC ? (p.r > n0 ? (int)(p.r - n0) : 0) : NTC;
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(Msrc + mrow0 * d_in, (uint32_t)m_lim * m_rowb);
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + n0 * d_in, (uint32_t)n_lim * n_rowb);
   const uint32_t b_rowb = (uint32_t)(p.r * ESZ), g_rowb = (uint32_t)((int64_t)NG * p.rg * ESZ);
@@ -634,7 +636,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_gen_kernel(NormPlan p, c
   const int m_lim = m_left < MT ? (int)m_left : MT;   // valid rows of this tile
   const int64_t n0 = (int64_t)n * NTC;
   const T* nsrc = A + n0 * d_in;
-  const int n_lim = p.r - n0 < NTC ? (int)(p.r - n0) : NTC;
+  // (In the Gram-term pass a column tile may start past r, since rg pads r;
+  // its A descriptor, never read there, then spans no rows.)
+  const int n_lim = p.r - n0 < NTC ? (p.r > n0 ? (int)(p.r - n0) : 0) : NTC;
 
   f32x16 acc[MB][NB];
 #pragma unroll
