@@ -1,8 +1,10 @@
 """Summaries of rocprofv3 runs of bench.py, for the profiles/ folder.
 
 Turns the CSV output of three rocprofv3 runs of the same bench command
-(kernel trace with --stats, then --pmc FETCH_SIZE, then --pmc WRITE_SIZE)
-into
+(kernel trace with --stats, then --pmc FETCH_SIZE, then --pmc WRITE_SIZE),
+and optionally a fourth (--pmc MfmaFlopsBF16 MfmaFlopsF32 MfmaUtil: the
+matrix-core work each dispatch executed and the share of cycles the matrix
+cores were busy), into
 
   profiles/<kernel-set>_<workload>.md   per-kernel durations, counters and
                                         the commands that produced them;
@@ -15,7 +17,7 @@ what the same counter reads for a plain device copy of known size (bench.py
 --copy-calibration runs one of 1 GiB), so that the figures are bytes.
 
     python -m dora_weight_norm_amd.profiling --workload NAME --kt DIR --fetch DIR --write DIR \
-        --cmd-kt "..." --cmd-fetch "..." --cmd-write "..." [--out profiles]
+        --cmd-kt "..." --cmd-fetch "..." --cmd-write "..." [--mfma DIR --cmd-mfma "..."] [--out profiles]
 """
 
 from __future__ import annotations
@@ -116,6 +118,8 @@ def main() -> int:
     ap.add_argument("--cmd-kt", required=True)
     ap.add_argument("--cmd-fetch", required=True)
     ap.add_argument("--cmd-write", required=True)
+    ap.add_argument("--mfma", default=None)
+    ap.add_argument("--cmd-mfma", default=None)
     ap.add_argument("--out", default=os.path.join(os.path.dirname(HERE), "profiles"))
     args = ap.parse_args()
 
@@ -123,6 +127,12 @@ def main() -> int:
     fetch = read_counter(args.fetch, "FETCH_SIZE")
     write = read_counter(args.write, "WRITE_SIZE")
     f_scale, w_scale = calibration(fetch), calibration(write)
+    mflops, mutil = {}, {}
+    if args.mfma:
+        for counter in ("MfmaFlopsBF16", "MfmaFlopsF32"):
+            for name, vals in read_counter(args.mfma, counter).items():
+                mflops[name] = mflops.get(name, 0.0) + sum(vals) / len(vals)
+        mutil = {name: sum(v) / len(v) for name, v in read_counter(args.mfma, "MfmaUtil").items()}
 
     ours = [s for s in stats if kernel_role(s["name"])]
     # Calls of each part: every kernel of a part runs at least once per call,
@@ -134,6 +144,7 @@ def main() -> int:
     steps = part_calls["compose"]
     traffic = {"norm": 0.0, "compose": 0.0, "compose_bwd": 0.0, "layer_output": 0.0}
     w_pass_bytes = None   # HBM bytes of one W-pass launch
+    w_pass_mfma = None    # (executed MFMA flops, MFMA busy %) of one W-pass launch
     lines = []
     for s in sorted(ours, key=lambda s: -s["total_us"]):
         role = kernel_role(s["name"])
@@ -146,8 +157,14 @@ def main() -> int:
             traffic[role] += (fb + wb) * per_step
             if role == "norm" and "(W pass" in short_name(s["name"]):
                 w_pass_bytes = fb + wb
+        mcols = ""
+        if args.mfma:
+            mf, mu = mflops.get(s["name"]), mutil.get(s["name"])
+            mcols = (f" {mf / 1e9:.2f} |" if mf is not None else " — |") + (f" {mu:.1f} |" if mu is not None else " — |")
+            if role == "norm" and "(W pass" in short_name(s["name"]) and mf is not None:
+                w_pass_mfma = (mf, mu)
         lines.append(f"| {short_name(s['name'])} | {role} | {s['calls']} | {s['avg_us']:.2f} | {s['min_us']:.2f} | "
-                     f"{s['max_us']:.2f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+                     f"{s['max_us']:.2f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |" + mcols)
     def part_us(role):
         return sum(s["avg_us"] * s["calls"] / part_calls[role] for s in ours if kernel_role(s["name"]) == role)
 
@@ -164,6 +181,8 @@ def main() -> int:
           "fetch_scale": f_scale, "write_scale": w_scale,
           "compose_bwd_bytes_per_call": traffic["compose_bwd"],
           "w_pass_bytes_per_launch": w_pass_bytes,
+          "w_pass_mfma_flops_per_launch": w_pass_mfma[0] if w_pass_mfma else None,
+          "w_pass_mfma_busy_pct": w_pass_mfma[1] if w_pass_mfma else None,
           "norm_us_per_call": norm_us, "compose_us_per_call": comp_us, "compose_bwd_us_per_call": bwd_us,
           "longest_step_kernel": {"name": short_name(longest["name"]), "part": kernel_role(longest["name"]),
                                   "avg_us": longest["avg_us"]},
@@ -171,11 +190,14 @@ def main() -> int:
     with open(os.path.join(args.out, f"traffic_{args.workload}.json"), "w") as f:
         json.dump(tj, f, indent=1)
         f.write("\n")
+    mhead = " MFMA GF | MFMA busy % |" if args.mfma else ""
+    msep = "---|---|" if args.mfma else ""
     md = [f"# Norm and compose kernels, workload {args.workload}", "",
-          "rocprofv3 kernel trace (durations) and two counter passes (HBM bytes) of the same bench.py",
-          "command. Bytes are per dispatch, scaled by the copy calibration below.", "",
-          "| kernel | part | calls | avg µs | min µs | max µs | FETCH MB | WRITE MB |",
-          "|---|---|---|---|---|---|---|---|"] + lines + [
+          "rocprofv3 kernel trace (durations) and counter passes (HBM bytes"
+          + ("; matrix-core work and busy share" if args.mfma else "") + ") of the same bench.py",
+          "command. Bytes and MFMA work are per dispatch; bytes are scaled by the copy calibration below.", "",
+          "| kernel | part | calls | avg µs | min µs | max µs | FETCH MB | WRITE MB |" + mhead,
+          "|---|---|---|---|---|---|---|---|" + msep] + lines + [
           "",
           f"- compose calls in the trace: {steps}; norm call = sum of its kernels = {norm_us:.2f} µs; "
           f"compose call = {comp_us:.2f} µs",
@@ -186,7 +208,8 @@ def main() -> int:
           f"{traffic['compose_bwd'] / 1e6:.1f} MB",
           f"- copy calibration (1 GiB device copy): FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}",
           f"- HIP sources hash: {tj['source_hash']}", "",
-          "Commands:", "", "```", args.cmd_kt, args.cmd_fetch, args.cmd_write, "```", ""]
+          "Commands:", "", "```", args.cmd_kt, args.cmd_fetch, args.cmd_write]
+    md += ([args.cmd_mfma] if args.mfma and args.cmd_mfma else []) + ["```", ""]
     with open(os.path.join(args.out, f"norm_compose_{args.workload}.md"), "w") as f:
         f.write("\n".join(md))
     print("\n".join(md))
