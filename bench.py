@@ -80,35 +80,47 @@ def compose_bwd_bytes(T, d_out, esize, dm=True):
 def cpu_baseline(w, W, A, B, base, lora, g_host):
     """The fp64 CPU oracle, as it stands, on a bounded sample of the workload.
 
-    The whole norm once (dense W + sBA in fp64 through BLAS), and the compose
-    on the first rows only, scaled to all rows.
+    The whole norm (dense W + sBA in fp64 through BLAS): one warm-up, then
+    the median of three runs on every core BLAS uses; the same on one BLAS
+    thread over the first eighth of the rows, scaled to all rows; and the
+    compose over all rows once (elementwise numpy, one thread).
     """
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import dora_oracle as O
 
     blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     threads = max([p.get("num_threads", 1) for p in blas] or [1])
     affinity = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
     O.dense_row_norm(W, A, B, w.s)
-    t_norm = time.perf_counter() - t0
-    rows = min(w.T, 2048)
-    t0 = time.perf_counter()
-    O.round_to_dtype(O.compose(base[:rows], lora[:rows], g_host, w.s), w.dtype)
-    t_comp = (time.perf_counter() - t0) * (w.T / rows)
+    t_norm = float(np.median([timed(lambda: O.dense_row_norm(W, A, B, w.s)) for _ in range(3)]))
+    rows1 = max(1, w.d_out // 8)
+    with threadpool_limits(limits=1, user_api="blas"):
+        O.dense_row_norm(W[:rows1], A, B[:rows1], w.s)
+        t_norm1 = float(np.median([timed(lambda: O.dense_row_norm(W[:rows1], A, B[:rows1], w.s))
+                                   for _ in range(3)])) * (w.d_out / rows1)
+    t_comp = timed(lambda: O.round_to_dtype(O.compose(base, lora, g_host, w.s), w.dtype))
     esize = 2 if w.dtype == "bf16" else 4
-    del np
+    F = norm_flops(w.d_out, w.d_in, w.r)
     return {
-        "value": norm_flops(w.d_out, w.d_in, w.r) / t_norm / 1e12,
+        "value": F / t_norm / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"whole norm once ({w.d_out}x{w.d_in}, r={w.r}) in {t_norm:.2f} s; compose on "
-                   f"{rows} of {w.T} rows scaled to all rows ({t_comp:.2f} s); fp64 numpy, BLAS threads="
-                   f"{threads} of {affinity} cores in the affinity mask, elementwise single-threaded"),
+        "sample": (f"whole norm ({w.d_out}x{w.d_in}, r={w.r}), median of 3 after one warm-up: {t_norm:.2f} s on "
+                   f"{threads} BLAS threads ({affinity} cores in the affinity mask); on 1 thread, rows 0..{rows1 - 1} "
+                   f"scaled to all rows: {t_norm1:.2f} s; compose over all {w.T} rows once, elementwise numpy on "
+                   f"one thread: {t_comp:.2f} s; fp64"),
         "norm_ms": t_norm * 1e3,
+        "value_1thread": F / t_norm1 / 1e12,
+        "norm_ms_1thread": t_norm1 * 1e3,
         "compose_ms": t_comp * 1e3,
         "compose_gbs": compose_bytes(w.T, w.d_out, esize) / t_comp / 1e9,
     }
