@@ -145,9 +145,10 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
   int64_t tpb = ((ncg + 63) / 64) * 64;
   if (tpb > 256) tpb = 256;
   const int64_t bx = (ncg + tpb - 1) / tpb;
-  // About 16 workgroups per compute unit over 256 CUs (8 resident at a
-  // time): more, shorter row strips balance the tail of the grid better.
-  int64_t by = 4096 / bx;
+  // About 32 workgroups per compute unit over 256 CUs (8 resident at a
+  // time; at 8192 columns each workgroup then streams one group of kUnroll
+  // rows): many short row strips balance the tail of the grid best.
+  int64_t by = 8192 / bx;
   if (by < 1) by = 1;
   const int64_t row_iters = (T_rows + kUnroll - 1) / kUnroll;
   if (by > row_iters) by = row_iters;
