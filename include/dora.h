@@ -24,8 +24,9 @@
  *   - Matrices are dense, row-major and contiguous. Layouts follow LoRA:
  *     W [d_out, d_in], A [r, d_in], B [d_out, r]; activations [T, d_out].
  *   - Device pointers are device memory the caller owns (e.g. torch
- *     tensors). The library allocates nothing and keeps no state between
- *     calls; it never frees or retains a pointer.
+ *     tensors). The library allocates nothing and never frees or retains
+ *     a pointer. Its only state between calls is the optional benchmark
+ *     hook of dora_set_launch_events.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is enqueued asynchronously on it; results are valid once
  *     the stream has reached that point.
