@@ -1087,12 +1087,13 @@ hipError_t launch_assemble(const NormPlan& p, const char* ws, int n_ba, float s,
 }
 
 // ---------------------------------------------------------------------------
-// Row sum of squares only (s == 0, r == 0 or d_in == 0).
+// Row sum of squares only (s == 0, r == 0 or d_in == 0): one workgroup per
+// row.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void norm_rowonly_kernel(const T* __restrict__ W, int64_t d_out,
-                                                                int64_t d_in, bool vec, const float* m,
-                                                                float eps, float* wnorm, float* g) {
+__global__ __launch_bounds__(kThreads) void norm_rowonly_kernel(const T* __restrict__ W, int64_t d_in, bool vec,
+                                                                const float* m, float eps, float* wnorm,
+                                                                float* g) {
   constexpr int EPC = Elem<T>::epc;
   __shared__ float wsum[4];
   const int64_t row = blockIdx.x;
@@ -1338,13 +1339,13 @@ hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t 
   if (e != hipSuccess) return e;
   if (dtype == 0)
     hipLaunchKernelGGL((norm_rowonly_kernel<bf16_t>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
-                       static_cast<const bf16_t*>(W), d_out, d_in, vec, m, eps, wnorm, g);
+                       static_cast<const bf16_t*>(W), d_in, vec, m, eps, wnorm, g);
   else if (dtype == 2)
     hipLaunchKernelGGL((norm_rowonly_kernel<f16_t>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
-                       static_cast<const f16_t*>(W), d_out, d_in, vec, m, eps, wnorm, g);
+                       static_cast<const f16_t*>(W), d_in, vec, m, eps, wnorm, g);
   else
     hipLaunchKernelGGL((norm_rowonly_kernel<float>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
-                       static_cast<const float*>(W), d_out, d_in, vec, m, eps, wnorm, g);
+                       static_cast<const float*>(W), d_in, vec, m, eps, wnorm, g);
   return launched(st);
 }
 
