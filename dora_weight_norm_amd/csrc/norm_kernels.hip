@@ -72,7 +72,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Streaming kernel (inputs allow aligned 16-byte loads).
 //
 // Workgroup = WM x WN waves = one (row tile, column tile, d_in range) of MT
-// rows (W, or A in the Gram pass) and NTC columns (rows of A). Wave
+// rows (W; A in the Gram pass; B in the Gram-term stages) and NTC columns
+// (rows of A; rows of the stored Gram matrix in the Gram-term stages). Wave
 // (wm, wn) owns MB x NB blocks of 32x32 accumulators. Each KT-deep stage of
 // both operands (MT + NTC rows) arrives in one of NS LDS ring slots by
 // direct-to-LDS loads (64 lanes x 16 B = 1 KiB per instruction) issued NS-1

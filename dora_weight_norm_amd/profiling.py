@@ -34,13 +34,38 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CALIB_BYTES = 1 << 30   # bench.py --copy-calibration copies this many bytes
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and trailing blanks: a change to the
+    comments alone leaves the kernels, and so the counters, as they were."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                       # string or character literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(line.rstrip() for line in "".join(out).splitlines() if line.strip())
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources: measured traffic is only valid for these."""
+    """Hash of the HIP sources' code (comments excluded): measured traffic is
+    only valid for this code."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
-        with open(path, "rb") as f:
+        with open(path, encoding="utf-8") as f:
             h.update(os.path.basename(path).encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -207,7 +232,7 @@ def main() -> int:
           f"- compose backward call (timed on its own after the steps) = {bwd_us:.2f} µs; HBM traffic "
           f"{traffic['compose_bwd'] / 1e6:.1f} MB",
           f"- copy calibration (1 GiB device copy): FETCH_SIZE x{f_scale:.3f}, WRITE_SIZE x{w_scale:.3f}",
-          f"- HIP sources hash: {tj['source_hash']}", "",
+          f"- HIP sources hash (code without comments): {tj['source_hash']}", "",
           "Commands:", "", "```", args.cmd_kt, args.cmd_fetch, args.cmd_write]
     md += ([args.cmd_mfma] if args.mfma and args.cmd_mfma else []) + ["```", ""]
     with open(os.path.join(args.out, f"norm_compose_{args.workload}.md"), "w") as f:
