@@ -114,13 +114,24 @@ struct FastK {
   static constexpr int WB = NBUF * RW;           // bytes of a wave's region
   static constexpr int WPS = SLOT / WB;          // waves staging B in one ring slot
   static constexpr int WX = NW > WPS * NS ? NW - WPS * NS : 0;   // waves staging B past the ring
+  // The epilogue's per-row sums (WN x MT floats) sit in a small array of
+  // their own, or, when that would not fit beside the ring, in the ring
+  // slot that holds the last wave's B region, right after it (the ring is
+  // free by then).
+  static constexpr int REDB = WN * MT * 4;
+  static constexpr bool RED_IN_RING = NS * SLOT + WX * WB + REDB > 160 * 1024;
+  static constexpr int RED_SLOT = (NW - 1) / WPS;
+  static constexpr int RED_OFF = ((NW - 1) % WPS + 1) * WB;
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(CPR == 8 || CPR == 4, "LDS rows are 64 or 128 bytes");
   static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
   static_assert(SLOT % (1024 * NW) == 0 && MBLK % NW == 0, "a stage splits evenly over the waves");
   static_assert(RW % 1024 == 0 && RBB % 16 == 0, "B stages in whole 1 KiB blocks");
   static_assert(WPS >= 1, "a wave's B fits one ring slot");
-  static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + WN * MT * 4 <= 160 * 1024, "gfx950 has 160 KiB of LDS");
+  static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + (RED_IN_RING ? 0 : REDB) <= 160 * 1024,
+                "gfx950 has 160 KiB of LDS");
+  static_assert(!RED_IN_RING || (WX == 0 && RED_SLOT < NS && RED_OFF + REDB <= SLOT),
+                "the row sums fit in the ring after the B regions");
   static_assert(BPW * (NS - 1) < 64 && LPR < 64, "outstanding loads fit vmcnt");
   static_assert(KSTEPS % 2 == 0, "fragment buffers alternate within a stage");
 };
@@ -242,9 +253,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   __shared__ __attribute__((aligned(1024))) char r2[NS > 2 ? C::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) char r3[NS > 3 ? C::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) char bx[(!GRAM && C::WX > 0) ? C::WX * C::WB : 16];
-  __shared__ float red[GRAM ? 1 : WN * MT];
+  __shared__ float red_arr[(GRAM || C::RED_IN_RING) ? 1 : WN * MT];
+  // Slot j of the ring (j < NS); slots past NS are never named, so their
+  // placeholder arrays take no LDS.
   auto ring = [&](int j) __attribute__((always_inline)) -> char* {
-    return j == 0 ? r0 : (j == 1 ? r1 : (j == 2 ? r2 : r3));
+    if constexpr (NS == 2) {
+      return j == 0 ? r0 : r1;
+    } else if constexpr (NS == 3) {
+      return j == 0 ? r0 : (j == 1 ? r1 : r2);
+    } else {
+      return j == 0 ? r0 : (j == 1 ? r1 : (j == 2 ? r2 : r3));
+    }
   };
 
   const int tid = threadIdx.x;
@@ -490,8 +509,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     // is staged per 32-row block (round) in the wave's own LDS region (the
     // ring is free after the last barrier), the next round's loads in flight
     // while this round is used; then the column groups are added in order.
-    char* bb = wave < C::WPS * NS ? ring(wave / C::WPS) + (wave % C::WPS) * C::WB
-                                  : bx + (wave - C::WPS * NS) * C::WB;
+    char* bb;
+    if constexpr (C::WX > 0) {
+      bb = wave < C::WPS * NS ? ring(wave / C::WPS) + (wave % C::WPS) * C::WB : bx + (wave - C::WPS * NS) * C::WB;
+    } else {
+      bb = ring(wave / C::WPS) + (wave % C::WPS) * C::WB;
+    }
+    float* red;
+    if constexpr (C::RED_IN_RING) {
+      red = reinterpret_cast<float*>(ring(C::RED_SLOT) + C::RED_OFF);
+    } else {
+      red = red_arr;
+    }
     const int64_t w_left = p.d_out - wrow0;
     const int w_lim = w_left <= 0 ? 0 : (w_left < MB * 32 ? (int)w_left : MB * 32);
     const uint32_t brow_bytes = (uint32_t)(p.r * ESZ);
@@ -1225,7 +1254,7 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
         case kFastB384: return launch_fast<H, 2, 4, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
         case kFastB512:
           if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
-          else return launch_fast<H, 2, 4, 2, 4, 32, 3, MODE>(p, M, A, B, ws, aa, st);
+          else return launch_fast<H, 2, 4, 2, 4, 64, 2, MODE>(p, M, A, B, ws, aa, st);
         default: break;
       }
     }
@@ -1379,7 +1408,7 @@ size_t fast_kernel_lds_bytes(int cfg) {
     case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
     case kFastB256: return DORA_LDS(3, bf16_t, 2, 4, 2, 2, 64);
     case kFastB384: return DORA_LDS(2, bf16_t, 2, 4, 2, 3, 64);
-    case kFastB512: return DORA_LDS(3, bf16_t, 2, 4, 2, 4, 32);
+    case kFastB512: return DORA_LDS(2, bf16_t, 2, 4, 2, 4, 64);
     case kFastF32: return DORA_LDS(4, float, 4, 1, 1, 1, 32);
     case kFastF128: return DORA_LDS(4, float, 2, 4, 2, 1, 32);
     default: return 0;

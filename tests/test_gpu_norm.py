@@ -106,10 +106,10 @@ GRAM_ALONE = [
     ("r160_f16", 300, 512, 160, "f16", 0.5),
     ("r40_f32", 300, 512, 40, "f32", 0.5),
     # the Gram term inside the W pass with two column tiles (bf16, fp32) and
-    # with the 512-column, 32-deep tile
+    # with the 512-column tile (its row sums in the ring)
     ("r700_two_col_tiles", 200, 512, 700, "bf16", 0.25),
     ("r200_f32_two_col_tiles", 300, 512, 200, "f32", 0.5),
-    ("r512_kt32", 300, 1024, 512, "bf16", 0.5),
+    ("r512_tile", 300, 1024, 512, "bf16", 0.5),
 ]
 
 
