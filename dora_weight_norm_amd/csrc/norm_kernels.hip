@@ -1402,7 +1402,9 @@ hipError_t launch_cast(const float* wnorm, int64_t n, int dtype, void* out, hipS
 }
 
 size_t fast_kernel_lds_bytes(int cfg) {
-#define DORA_LDS(NS, ...) (size_t)(FastK<__VA_ARGS__, NS>::SLOT * NS + FastK<__VA_ARGS__, NS>::WX * FastK<__VA_ARGS__, NS>::WB)
+#define DORA_LDS(NS, ...)                                                                        \
+  (size_t)(FastK<__VA_ARGS__, NS>::SLOT * NS + FastK<__VA_ARGS__, NS>::WX * FastK<__VA_ARGS__, NS>::WB + \
+           (FastK<__VA_ARGS__, NS>::RED_IN_RING ? 0 : FastK<__VA_ARGS__, NS>::REDB))
   switch (cfg) {
     case kFastB64: return DORA_LDS(4, bf16_t, 4, 2, 1, 1, 64);
     case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
