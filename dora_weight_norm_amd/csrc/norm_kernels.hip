@@ -446,13 +446,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // stage count is rounded up to whole unrolled groups (the extra stages are
   // zeros), so the loop body is straight-line code with fixed load counts.
   const int n_pad = (n_tot + NS - 1) / NS * NS;
+  // With two slots an odd last stage runs after the loop on its own, rather
+  // than as a stage of zeros beside it in the unrolled pair. The extra code
+  // stays within the register budget of tiles of up to 6 blocks per wave;
+  // larger ones keep the zero stage (their tail spilled).
+  constexpr bool PEEL = NS == 2 && MB * NB <= 6;
+  const int n_loop = PEEL ? (n_tot & ~1) : n_pad;   // stages the unrolled loop runs
   Frag H[2];
 #pragma unroll
   for (int j = 0; j < NS; ++j) issue(j, ring(j));
   wait_vm_lgkm0<(NS - 1) * BPW>();   // stage 0 complete; stages 1 .. NS-1 in flight
   barrier_keep_loads();
   read_step(ring(0), 0, H[0]);
-  for (int i0 = 0; i0 < n_pad; i0 += NS) {
+  for (int i0 = 0; i0 < n_loop; i0 += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int i = i0 + j;
@@ -466,6 +472,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           issue(i + NS, ring(j));
           read_step(ring((j + 1) % NS), 0, H[0]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(H[s & 1], i < n_st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if constexpr (PEEL) {
+    if (n_tot & 1) {
+      // The odd last stage (slot 0): its loads landed and its first step's
+      // fragments were read at the loop's last barrier.
+      const int i = n_tot - 1;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        if (s + 1 < KSTEPS) read_step(ring(0), s + 1, H[(s + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(H[s & 1], i < n_st);
         __builtin_amdgcn_sched_barrier(0);
