@@ -48,6 +48,8 @@ CASES = [
     # element loads (d_in % 8 != 0) under a plan with square Gram tiles: the
     # general kernel computes every tile, the reduction reads the upper ones
     ("gen_path_symmetric_gram", 300, 1001, 200, "bf16", 0.5, 19),
+    # negative s through the Gram term inside the W pass: 2s (cross + (s/2) ba)
+    ("neg_s_fused", 600, 1024, 384, "bf16", -0.5, 26),
 ]
 
 
@@ -110,6 +112,7 @@ GRAM_ALONE = [
     ("r700_two_col_tiles", 200, 512, 700, "bf16", 0.25),
     ("r200_f32_two_col_tiles", 300, 512, 200, "f32", 0.5),
     ("r512_tile", 300, 1024, 512, "bf16", 0.5),
+    ("r200_f32_neg_s", 300, 512, 200, "f32", -0.75),
 ]
 
 
@@ -221,6 +224,21 @@ def test_launch_events_mark_each_launch():
     assert np.array_equal(plain.view(np.uint32), again.view(np.uint32))
     assert evs[2].elapsed_time(evs[3]) > 0
     assert evs[0].elapsed_time(evs[2]) > before   # event 0 kept its old time
+
+
+def test_many_partials_per_row_deterministic():
+    # 32 d_in ranges and two column tiles: 32 base and 64 cross partials per
+    # row, summed by several threads per row and then in a fixed order
+    W, A, B = I.norm_inputs(512, 3584, 768, "bf16", 27)
+    info = bnd.dora_norm_plan_info(512, 3584, 768, "bf16", 0.25)
+    assert info["w_ranges"] * info["col_tiles"] > 16
+    m = np.full(512, 0.75, np.float32)
+    a, ga = _run(W, A, B, "bf16", 0.25, m)
+    for _ in range(3):
+        b, gb = _run(W, A, B, "bf16", 0.25, m)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert np.array_equal(ga.view(np.uint32), gb.view(np.uint32))
+    check_norm(a, O.dense_row_norm(W, A, B, 0.25))
 
 
 def test_power_of_two_scale_moves_into_B_bitwise():
