@@ -129,6 +129,39 @@ def test_gram_term_alone(case):
     say(f"    worst rel err {worst:.2e}")
 
 
+def _sweep_shapes():
+    rng = np.random.default_rng(2024)
+    shapes = [(1, 8, 384, "bf16"), (129, 8, 96, "bf16"), (300, 16, 512, "bf16"), (64, 64, 1, "f32"),
+              (257, 24, 200, "f32"), (1, 64, 768, "bf16")]
+    for _ in range(16):
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        q = 8 if dtype == "bf16" else 4
+        d_out = int(rng.integers(1, 400))
+        d_in = int(rng.integers(1, 160)) * q
+        r = int(rng.integers(1, 101)) * q
+        shapes.append((d_out, d_in, r, dtype))
+    return shapes
+
+
+SWEEP = _sweep_shapes()
+
+
+@pytest.mark.parametrize("k", range(len(SWEEP)))
+def test_seeded_shape_sweep(k):
+    # 16-byte-aligned shapes, so the streaming kernels run: the plan's
+    # phases, tiles and d_in ranges at odd sizes (d_in down to one granule,
+    # d_out down to one row), both signs of s
+    d_out, d_in, r, dtype = SWEEP[k]
+    s = (0.5 if k % 2 == 0 else -0.75) * (1.0 if dtype == "bf16" else 2.0)
+    say(f"[norm-sweep] {k}: d_out={d_out} d_in={d_in} r={r} {dtype} s={s}")
+    W, A, B = I.norm_inputs(d_out, d_in, r, dtype, 100 + k)
+    ref = O.dense_row_norm(W, A, B, s)
+    m = magnitude(ref, 100 + k)
+    wn, g = _run(W, A, B, dtype, s, m)
+    check_norm(wn, ref)
+    check_g(g, m, ref, EPS)
+
+
 def test_s_zero_and_zero_sizes():
     W, A, B = I.norm_inputs(130, 300, 12, "bf16", 20)
     wn, _ = _run(W, A, B, "bf16", 0.0)
