@@ -60,6 +60,11 @@ CASES = [
     ("one_row", 1, 8, "bf16", 2.0, 7),
     ("f16", 256, 2048, "f16", 0.5, 8),
     ("f16_ragged", 37, 1001, "f16", 0.75, 9),
+    # narrow workgroups and their row lanes: 128 strips (2 lanes), 192
+    # strips (1 lane), and 64 strips (4 lanes) with fewer rows than lanes
+    ("lanes2_1024", 300, 1024, "bf16", 0.5, 14),
+    ("tpb192_1536", 257, 1536, "bf16", 0.25, 15),
+    ("lanes4_three_rows", 3, 512, "bf16", 2.0, 16),
 ]
 
 
