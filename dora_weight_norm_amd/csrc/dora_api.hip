@@ -37,10 +37,13 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxRank = (int64_t)1 << 16;
 
-// Column tiling over r and the kernel configurations of both passes. The
-// W pass covers as many columns per tile as the streaming kernel holds in
-// its accumulators (so W is read once when r <= 512); the Gram pass uses
-// narrower tiles so that its few rows still spread over many workgroups.
+// Column tiling over r and the kernel configurations of both passes. Up to
+// r = 256 the W pass takes all of r in one column tile of 128-row tiles;
+// above, it takes 256-row tiles of 192 or 256 columns (whichever pads r
+// less; 256-row tiles need fewer loads per MFMA), whose column tiles of
+// one row tile run on one die, so W is still read from HBM about once.
+// The Gram pass uses narrower tiles so that its few rows still spread over
+// many workgroups.
 void choose_tiles(NormPlan& p) {
   const int64_t r = p.r;
   if (p.dtype == DORA_F32) {
@@ -58,10 +61,10 @@ void choose_tiles(NormPlan& p) {
       p.ntc = 128, p.fcfg = dora::kFastB128, p.gcfg = dora::kGenB128;
     } else if (r <= 256) {
       p.ntc = 256, p.fcfg = dora::kFastB256, p.gcfg = dora::kGenB256;
-    } else if (r <= 384 || ceil_div(r, 384) * 384 <= ceil_div(r, 512) * 512) {
-      p.ntc = 384, p.fcfg = dora::kFastB384, p.gcfg = dora::kGenB384;
+    } else if (r <= 384 || ceil_div(r, 192) * 192 <= ceil_div(r, 256) * 256) {
+      p.ntc = 192, p.fcfg = dora::kFastB384, p.gcfg = dora::kGenB384;
     } else {
-      p.ntc = 512, p.fcfg = dora::kFastB512, p.gcfg = dora::kGenB512;
+      p.ntc = 256, p.fcfg = dora::kFastB512, p.gcfg = dora::kGenB512;
     }
     if (p.ntc == 64) {
       p.ntc_g = 64, p.fcfg_g = dora::kFastB64, p.gcfg_g = dora::kGenB64;

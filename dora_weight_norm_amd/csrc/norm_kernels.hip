@@ -276,11 +276,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int X = BG ? 1 : (GRAM ? p.xg : p.xw);
   const int n_nt = BG ? p.n_bt : (GRAM ? (int)(p.ga_cols / NTC) : p.n_nt);
   const int64_t m_rows = GRAM ? p.r : p.d_out;
-  const int x = blockIdx.x % X;
+  int x = blockIdx.x % X;
   const int t = blockIdx.x / X;
   int m = t / n_nt, n = t - m * n_nt;
   if constexpr (GRAM) {
     if (MT == NTC && p.gsym) tri_tile(t, n_nt, &m, &n);   // upper-triangle tiles only
+  }
+  if constexpr (WP) {
+    // Workgroups are dealt to the kDies dies (each with its own L2) in
+    // turn: die = blockIdx mod kDies. Give all column tiles of a (row
+    // tile, d_in range) one die, kDies apart in launch order, so that the
+    // W rows they share come from HBM once and from that die's L2 after.
+    // (A relabelling of the same grid: u runs over the (d_in range, row
+    // tile) pairs, n over the column tiles.)
+    if (n_nt > 1 && gridDim.x % (kDies * n_nt) == 0) {
+      const int lo = blockIdx.x % kDies, g8 = blockIdx.x / kDies;
+      n = g8 % n_nt;
+      const int u = (g8 / n_nt) * kDies + lo;
+      x = u % X;
+      m = u / X;
+    }
   }
   const int64_t mrow0 = (int64_t)m * MT;
   const int64_t n0 = (int64_t)n * NTC;
@@ -1271,10 +1286,10 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
     if constexpr (!GRAM) {
       switch (fcfg) {
         case kFastB256: return launch_fast<H, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
-        case kFastB384: return launch_fast<H, 2, 4, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
+        case kFastB384: return launch_fast<H, 4, 2, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
         case kFastB512:
           if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
-          else return launch_fast<H, 2, 4, 2, 4, 64, 2, MODE>(p, M, A, B, ws, aa, st);
+          else return launch_fast<H, 4, 2, 2, 4, 64, 2, MODE>(p, M, A, B, ws, aa, st);
         default: break;
       }
     }
@@ -1287,8 +1302,8 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
       case kGenB64: return launch_gen<H, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
       case kGenB128: return launch_gen<H, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
       case kGenB256: return launch_gen<H, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB384: return launch_gen<H, 2, 4, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB512: return launch_gen<H, 1, 4, 2, 4, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB384: return launch_gen<H, 4, 2, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenB512: return launch_gen<H, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
       case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st);
       case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st);
       default: return hipErrorInvalidValue;
@@ -1429,8 +1444,8 @@ size_t fast_kernel_lds_bytes(int cfg) {
     case kFastB64: return DORA_LDS(4, bf16_t, 4, 2, 1, 1, 64);
     case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
     case kFastB256: return DORA_LDS(3, bf16_t, 2, 4, 2, 2, 64);
-    case kFastB384: return DORA_LDS(2, bf16_t, 2, 4, 2, 3, 64);
-    case kFastB512: return DORA_LDS(2, bf16_t, 2, 4, 2, 4, 64);
+    case kFastB384: return DORA_LDS(2, bf16_t, 4, 2, 2, 3, 64);
+    case kFastB512: return DORA_LDS(2, bf16_t, 4, 2, 2, 4, 64);
     case kFastF32: return DORA_LDS(4, float, 4, 1, 1, 1, 32);
     case kFastF128: return DORA_LDS(4, float, 2, 4, 2, 1, 32);
     default: return 0;
@@ -1444,8 +1459,8 @@ size_t gen_kernel_lds_bytes(int cfg) {
     case kGenB64: return DORA_LDS(bf16_t, 2, 2, 2, 1, 64);
     case kGenB128: return DORA_LDS(bf16_t, 1, 4, 4, 1, 64);
     case kGenB256: return DORA_LDS(bf16_t, 1, 4, 4, 2, 64);
-    case kGenB384: return DORA_LDS(bf16_t, 2, 4, 2, 3, 64);
-    case kGenB512: return DORA_LDS(bf16_t, 1, 4, 2, 4, 64);
+    case kGenB384: return DORA_LDS(bf16_t, 4, 2, 2, 3, 64);
+    case kGenB512: return DORA_LDS(bf16_t, 1, 4, 4, 2, 64);
     case kGenF32: return DORA_LDS(float, 4, 1, 1, 1, 32);
     case kGenF128: return DORA_LDS(float, 1, 4, 4, 1, 32);
     default: return 0;

@@ -50,6 +50,14 @@ CASES = [
     ("gen_path_symmetric_gram", 300, 1001, 200, "bf16", 0.5, 19),
     # negative s through the Gram term inside the W pass: 2s (cross + (s/2) ba)
     ("neg_s_fused", 600, 1024, 384, "bf16", -0.5, 26),
+    # 256-row tiles whose grid is no multiple of 8 x the column tiles: the
+    # column tiles of a row tile are not grouped per die
+    ("unpaired_r384", 600, 64, 384, "bf16", 0.5, 27),
+    ("unpaired_r512", 300, 128, 512, "bf16", 0.5, 28),
+    # element loads with 192- and 256-column tiles (general kernel)
+    ("gen_r384_tile", 300, 1001, 384, "bf16", 0.5, 29),
+    ("gen_r512_tile", 200, 999, 512, "bf16", 0.25, 30),
+    ("gen_r768_f16", 130, 777, 768, "f16", 0.25, 31),
 ]
 
 
@@ -107,8 +115,8 @@ GRAM_ALONE = [
     ("r160_general", 300, 1001, 160, "bf16", 0.5),
     ("r160_f16", 300, 512, 160, "f16", 0.5),
     ("r40_f32", 300, 512, 40, "f32", 0.5),
-    # the Gram term inside the W pass with two column tiles (bf16, fp32) and
-    # with the 512-column tile (its row sums in the ring)
+    # the Gram term inside the W pass with several column tiles (bf16 256 x 192
+    # tiles, fp32) and with the 256 x 256 tile
     ("r700_two_col_tiles", 200, 512, 700, "bf16", 0.25),
     ("r200_f32_two_col_tiles", 300, 512, 200, "f32", 0.5),
     ("r512_tile", 300, 1024, 512, "bf16", 0.5),
