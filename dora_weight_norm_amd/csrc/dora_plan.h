@@ -30,15 +30,14 @@ enum FastCfg : int {
   kFastB64 = 0,    // bf16, 128 x 64, 8 waves
   kFastB128 = 1,   // bf16, 128 x 128, 8 waves
   kFastB256 = 2,   // bf16, 128 x 256, 8 waves
-  kFastB384 = 3,   // bf16, 256 x 192, 8 waves
-  kFastB512 = 4,   // bf16, 256 x 256, 8 waves
+  kFastT192 = 3,   // bf16, 256 x 192, 8 waves
+  kFastT256 = 4,   // bf16, 256 x 256, 8 waves
   kFastF32 = 5,    // fp32, 128 x 32, 4 waves
   kFastF128 = 6,   // fp32, 128 x 128, 8 waves
-  kNumFastCfg = 7
 };
 // Rows per workgroup tile, and waves per workgroup, of a streaming
 // configuration.
-DORA_HD int fast_rows(int cfg) { return cfg == kFastB384 || cfg == kFastB512 ? 256 : 128; }
+DORA_HD int fast_rows(int cfg) { return cfg == kFastT192 || cfg == kFastT256 ? 256 : 128; }
 DORA_HD int fast_waves(int cfg) { return cfg == kFastF32 ? 4 : 8; }
 constexpr int kGramCols = 64;      // columns of G per Gram-term tile (general kernel)
 constexpr int kGramTile = 128;     // side of the square streaming Gram-pass tile
@@ -65,19 +64,16 @@ enum TileCfg : int {
   kGenB64 = 0,    // bf16, 128 x 64 tiles
   kGenB128 = 1,   // bf16, 128 x 128
   kGenB256 = 2,   // bf16, 128 x 256
-  kGenB384 = 3,   // bf16, 256 x 192
-  kGenB512 = 4,   // bf16, 128 x 256
+  kGenT192 = 3,   // bf16, 256 x 192
   kGenF32 = 5,    // fp32, 128 x 32
   kGenF128 = 6,   // fp32, 128 x 128
-  kNumGenCfg = 7
 };
 DORA_HD TileShape tile_shape(int cfg) {
   switch (cfg) {
     case kGenB64: return TileShape{2, 2, 2, 1, 64};
     case kGenB128: return TileShape{1, 4, 4, 1, 64};
     case kGenB256: return TileShape{1, 4, 4, 2, 64};
-    case kGenB384: return TileShape{4, 2, 2, 3, 64};
-    case kGenB512: return TileShape{1, 4, 4, 2, 64};
+    case kGenT192: return TileShape{4, 2, 2, 3, 64};
     case kGenF32: return TileShape{4, 1, 1, 1, 32};
     default: return TileShape{1, 4, 4, 1, 32};
   }

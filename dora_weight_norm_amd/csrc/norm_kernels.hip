@@ -114,24 +114,14 @@ struct FastK {
   static constexpr int WB = NBUF * RW;           // bytes of a wave's region
   static constexpr int WPS = SLOT / WB;          // waves staging B in one ring slot
   static constexpr int WX = NW > WPS * NS ? NW - WPS * NS : 0;   // waves staging B past the ring
-  // The epilogue's per-row sums (WN x MT floats) sit in a small array of
-  // their own, or, when that would not fit beside the ring, in the ring
-  // slot that holds the last wave's B region, right after it (the ring is
-  // free by then).
-  static constexpr int REDB = WN * MT * 4;
-  static constexpr bool RED_IN_RING = NS * SLOT + WX * WB + REDB > 160 * 1024;
-  static constexpr int RED_SLOT = (NW - 1) / WPS;
-  static constexpr int RED_OFF = ((NW - 1) % WPS + 1) * WB;
+  static constexpr int REDB = WN * MT * 4;      // bytes of the epilogue's per-row sums
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(CPR == 8 || CPR == 4, "LDS rows are 64 or 128 bytes");
   static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
   static_assert(SLOT % (1024 * NW) == 0 && MBLK % NW == 0, "a stage splits evenly over the waves");
   static_assert(RW % 1024 == 0 && RBB % 16 == 0, "B stages in whole 1 KiB blocks");
   static_assert(WPS >= 1, "a wave's B fits one ring slot");
-  static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + (RED_IN_RING ? 0 : REDB) <= 160 * 1024,
-                "gfx950 has 160 KiB of LDS");
-  static_assert(!RED_IN_RING || (WX == 0 && RED_SLOT < NS && RED_OFF + REDB <= SLOT),
-                "the row sums fit in the ring after the B regions");
+  static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + REDB <= 160 * 1024, "gfx950 has 160 KiB of LDS");
   static_assert(BPW * (NS - 1) < 64 && LPR < 64, "outstanding loads fit vmcnt");
   static_assert(KSTEPS % 2 == 0, "fragment buffers alternate within a stage");
 };
@@ -253,7 +243,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   __shared__ __attribute__((aligned(1024))) char r2[NS > 2 ? C::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) char r3[NS > 3 ? C::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) char bx[(!GRAM && C::WX > 0) ? C::WX * C::WB : 16];
-  __shared__ float red_arr[(GRAM || C::RED_IN_RING) ? 1 : WN * MT];
+  __shared__ float red[GRAM ? 1 : WN * MT];
   // Slot j of the ring (j < NS); slots past NS are never named, so their
   // placeholder arrays take no LDS.
   auto ring = [&](int j) __attribute__((always_inline)) -> char* {
@@ -549,12 +539,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       bb = wave < C::WPS * NS ? ring(wave / C::WPS) + (wave % C::WPS) * C::WB : bx + (wave - C::WPS * NS) * C::WB;
     } else {
       bb = ring(wave / C::WPS) + (wave % C::WPS) * C::WB;
-    }
-    float* red;
-    if constexpr (C::RED_IN_RING) {
-      red = reinterpret_cast<float*>(ring(C::RED_SLOT) + C::RED_OFF);
-    } else {
-      red = red_arr;
     }
     const int64_t w_left = p.d_out - wrow0;
     const int w_lim = w_left <= 0 ? 0 : (w_left < MB * 32 ? (int)w_left : MB * 32);
@@ -1286,8 +1270,8 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
     if constexpr (!GRAM) {
       switch (fcfg) {
         case kFastB256: return launch_fast<H, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
-        case kFastB384: return launch_fast<H, 4, 2, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
-        case kFastB512:
+        case kFastT192: return launch_fast<H, 4, 2, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
+        case kFastT256:
           if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
           else return launch_fast<H, 4, 2, 2, 4, 64, 2, MODE>(p, M, A, B, ws, aa, st);
         default: break;
@@ -1302,8 +1286,7 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
       case kGenB64: return launch_gen<H, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
       case kGenB128: return launch_gen<H, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
       case kGenB256: return launch_gen<H, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB384: return launch_gen<H, 4, 2, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB512: return launch_gen<H, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
+      case kGenT192: return launch_gen<H, 4, 2, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
       case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st);
       case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st);
       default: return hipErrorInvalidValue;
@@ -1439,13 +1422,13 @@ hipError_t launch_cast(const float* wnorm, int64_t n, int dtype, void* out, hipS
 size_t fast_kernel_lds_bytes(int cfg) {
 #define DORA_LDS(NS, ...)                                                                        \
   (size_t)(FastK<__VA_ARGS__, NS>::SLOT * NS + FastK<__VA_ARGS__, NS>::WX * FastK<__VA_ARGS__, NS>::WB + \
-           (FastK<__VA_ARGS__, NS>::RED_IN_RING ? 0 : FastK<__VA_ARGS__, NS>::REDB))
+           FastK<__VA_ARGS__, NS>::REDB)
   switch (cfg) {
     case kFastB64: return DORA_LDS(4, bf16_t, 4, 2, 1, 1, 64);
     case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
     case kFastB256: return DORA_LDS(3, bf16_t, 2, 4, 2, 2, 64);
-    case kFastB384: return DORA_LDS(2, bf16_t, 4, 2, 2, 3, 64);
-    case kFastB512: return DORA_LDS(2, bf16_t, 4, 2, 2, 4, 64);
+    case kFastT192: return DORA_LDS(2, bf16_t, 4, 2, 2, 3, 64);
+    case kFastT256: return DORA_LDS(2, bf16_t, 4, 2, 2, 4, 64);
     case kFastF32: return DORA_LDS(4, float, 4, 1, 1, 1, 32);
     case kFastF128: return DORA_LDS(4, float, 2, 4, 2, 1, 32);
     default: return 0;
@@ -1459,8 +1442,7 @@ size_t gen_kernel_lds_bytes(int cfg) {
     case kGenB64: return DORA_LDS(bf16_t, 2, 2, 2, 1, 64);
     case kGenB128: return DORA_LDS(bf16_t, 1, 4, 4, 1, 64);
     case kGenB256: return DORA_LDS(bf16_t, 1, 4, 4, 2, 64);
-    case kGenB384: return DORA_LDS(bf16_t, 4, 2, 2, 3, 64);
-    case kGenB512: return DORA_LDS(bf16_t, 1, 4, 4, 2, 64);
+    case kGenT192: return DORA_LDS(bf16_t, 4, 2, 2, 3, 64);
     case kGenF32: return DORA_LDS(float, 4, 1, 1, 1, 32);
     case kGenF128: return DORA_LDS(float, 1, 4, 4, 1, 32);
     default: return 0;

@@ -58,6 +58,9 @@ CASES = [
     ("gen_r384_tile", 300, 1001, 384, "bf16", 0.5, 29),
     ("gen_r512_tile", 200, 999, 512, "bf16", 0.25, 30),
     ("gen_r768_f16", 130, 777, 768, "f16", 0.25, 31),
+    # 256 x 256 tiles with all of r in one column tile (32 row tiles or
+    # more), the last one ragged
+    ("tall_r200", 8000, 512, 200, "bf16", 0.5, 32),
 ]
 
 
@@ -233,10 +236,14 @@ def test_deterministic_and_budget_invariant():
 
 
 def test_launch_events_mark_each_launch():
-    W, A, B = I.norm_inputs(2048, 4096, 384, "bf16", 25)
-    info = bnd.dora_norm_plan_info(2048, 4096, 384, "bf16", 0.5)
+    # a shape whose W pass (about 33 us) clearly outlasts the other three
+    # launches (each under 10 us, plus a few us per recorded event)
+    W, A, B = I.norm_inputs(4096, 8192, 384, "bf16", 25)
+    info = bnd.dora_norm_plan_info(4096, 8192, 384, "bf16", 0.5)
     assert info["gram_term_fused"] == 1 and info["w_launch"] == 2
     plain, _ = _run(W, A, B, "bf16", 0.5)
+    for _ in range(3):                          # clocks up before the marked call
+        _run(W, A, B, "bf16", 0.5)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for e in evs:
         e.record()
