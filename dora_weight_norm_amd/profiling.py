@@ -78,9 +78,7 @@ def kernel_role(name: str) -> str | None:
     if "compose_kernel" in name:
         # compose_kernel<T, VEC, ADD>: ADD = true is the layer output
         return "layer_output" if re.search(r"compose_kernel<[^>]*true>", name) else "compose"
-    if "widen_kernel" in name or "cast_kernel" in name:
-        return "norm"
-    return "norm"
+    return "norm"   # the norm call's kernels, and the widening and casts around it
 
 
 def short_name(name: str) -> str:
