@@ -38,15 +38,15 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxRank = (int64_t)1 << 16;
 
 // Column tiling over r and the kernel configurations of both passes. Up to
-// r = 256 the W pass takes all of r in one column tile; above, it takes
-// 256-row tiles of 192 or 256 columns (whichever pads r less), whose column
-// tiles of one row tile run on one die, so W is still read from HBM about
-// once. 256-row tiles need fewer loads per MFMA than 128-row ones, but
-// with r <= 256 they halve the workgroups per d_in range: below
-// kTallMinRowTiles row tiles the d_in split would have to go finer than 8
-// ranges to fill the chip, and short ranges cost more than the tall tile
-// saves, so 128-row tiles are kept there. The Gram pass uses narrower
-// tiles so that its few rows still spread over many workgroups.
+// r = 256 the W pass takes all of r in one column tile (64, 128 or 256
+// columns); above, it takes 256-row tiles of 192 or 256 columns (whichever
+// pads r less), whose column tiles of one row tile run on one die, so W is
+// still read from HBM about once. 256-row tiles need fewer loads per MFMA
+// than 128-row ones, but with r <= 256 they halve the workgroups per d_in
+// range: below kTallMinRowTiles row tiles the d_in split would have to go
+// finer than 8 ranges to fill the chip, and short ranges cost more than
+// the tall tile saves, so 128-row tiles are kept there. The Gram pass uses
+// narrower tiles so that its few rows still spread over many workgroups.
 constexpr int64_t kTallMinRowTiles = dora::kGrid / 8;
 void choose_tiles(NormPlan& p) {
   const int64_t r = p.r;
@@ -59,12 +59,12 @@ void choose_tiles(NormPlan& p) {
     p.ntc_g = p.ntc, p.fcfg_g = p.fcfg, p.gcfg_g = p.gcfg;
     p.gran = 32;
   } else {
+    const bool tall = ceil_div(p.d_out, 256) >= kTallMinRowTiles;
     if (r <= 64) {
-      p.ntc = 64, p.fcfg = dora::kFastB64, p.gcfg = dora::kGenB64;
+      p.ntc = 64, p.fcfg = tall ? dora::kFastT64 : dora::kFastB64, p.gcfg = dora::kGenB64;
     } else if (r <= 128) {
-      p.ntc = 128, p.fcfg = dora::kFastB128, p.gcfg = dora::kGenB128;
+      p.ntc = 128, p.fcfg = tall ? dora::kFastT128 : dora::kFastB128, p.gcfg = dora::kGenB128;
     } else if (r <= 256) {
-      const bool tall = ceil_div(p.d_out, 256) >= kTallMinRowTiles;
       p.ntc = 256, p.fcfg = tall ? dora::kFastT256 : dora::kFastB256, p.gcfg = dora::kGenB256;
     } else if (r <= 384 || ceil_div(r, 192) * 192 <= ceil_div(r, 256) * 256) {
       p.ntc = 192, p.fcfg = dora::kFastT192, p.gcfg = dora::kGenT192;

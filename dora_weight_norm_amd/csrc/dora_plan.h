@@ -34,10 +34,14 @@ enum FastCfg : int {
   kFastT256 = 4,   // bf16, 256 x 256, 8 waves
   kFastF32 = 5,    // fp32, 128 x 32, 4 waves
   kFastF128 = 6,   // fp32, 128 x 128, 8 waves
+  kFastT64 = 7,    // bf16, 256 x 64, 8 waves
+  kFastT128 = 8,   // bf16, 256 x 128, 8 waves
 };
 // Rows per workgroup tile, and waves per workgroup, of a streaming
 // configuration.
-DORA_HD int fast_rows(int cfg) { return cfg == kFastT192 || cfg == kFastT256 ? 256 : 128; }
+DORA_HD int fast_rows(int cfg) {
+  return cfg == kFastT64 || cfg == kFastT128 || cfg == kFastT192 || cfg == kFastT256 ? 256 : 128;
+}
 DORA_HD int fast_waves(int cfg) { return cfg == kFastF32 ? 4 : 8; }
 constexpr int kGramCols = 64;      // columns of G per Gram-term tile (general kernel)
 constexpr int kGramTile = 128;     // side of the square streaming Gram-pass tile

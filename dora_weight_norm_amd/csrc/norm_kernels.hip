@@ -1269,6 +1269,8 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
     }
     if constexpr (!GRAM) {
       switch (fcfg) {
+        case kFastT64: return launch_fast<H, 4, 2, 2, 1, 64, 3, MODE>(p, M, A, B, ws, aa, st);
+        case kFastT128: return launch_fast<H, 4, 2, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
         case kFastB256: return launch_fast<H, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
         case kFastT192: return launch_fast<H, 4, 2, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
         case kFastT256:
@@ -1427,6 +1429,8 @@ size_t fast_kernel_lds_bytes(int cfg) {
     case kFastB64: return DORA_LDS(4, bf16_t, 4, 2, 1, 1, 64);
     case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
     case kFastB256: return DORA_LDS(3, bf16_t, 2, 4, 2, 2, 64);
+    case kFastT64: return DORA_LDS(3, bf16_t, 4, 2, 2, 1, 64);
+    case kFastT128: return DORA_LDS(3, bf16_t, 4, 2, 2, 2, 64);
     case kFastT192: return DORA_LDS(2, bf16_t, 4, 2, 2, 3, 64);
     case kFastT256: return DORA_LDS(2, bf16_t, 4, 2, 2, 4, 64);
     case kFastF32: return DORA_LDS(4, float, 4, 1, 1, 1, 32);

@@ -90,7 +90,8 @@ def test_w_pass_tile_shapes():
     # one column tile up to r = 256, in 256-row tiles once there are at
     # least 32 of them; 256-row tiles of 192 or 256 columns above, whichever
     # pads r less
-    expect = {(8192, 64): (128, 64, 1), (8192, 128): (128, 128, 1), (4096, 256): (128, 256, 1),
+    expect = {(8192, 64): (256, 64, 1), (8192, 128): (256, 128, 1), (8192, 8): (256, 64, 1),
+              (4096, 64): (128, 64, 1), (4096, 128): (128, 128, 1), (4096, 256): (128, 256, 1),
               (7936, 256): (128, 256, 1), (7937, 256): (256, 256, 1), (8192, 160): (256, 256, 1),
               (8192, 384): (256, 192, 2), (512, 384): (256, 192, 2), (8192, 512): (256, 256, 2),
               (8192, 768): (256, 192, 4), (8192, 1000): (256, 256, 4), (8192, 1100): (256, 192, 6)}
