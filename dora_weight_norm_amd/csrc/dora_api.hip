@@ -43,11 +43,15 @@ constexpr int64_t kMaxRank = (int64_t)1 << 16;
 // pads r less), whose column tiles of one row tile run on one die, so W is
 // still read from HBM about once. 256-row tiles need fewer loads per MFMA
 // than 128-row ones, but with r <= 256 they halve the workgroups per d_in
-// range: below kTallMinRowTiles row tiles the d_in split would have to go
-// finer than 8 ranges to fill the chip, and short ranges cost more than
-// the tall tile saves, so 128-row tiles are kept there. The Gram pass uses
-// narrower tiles so that its few rows still spread over many workgroups.
+// range, so the d_in split goes twice as fine and each workgroup gets half
+// the stages. Their saving outweighs the fixed cost of the shorter ranges
+// only when there are at least kTallMinRowTiles row tiles (so that 8
+// ranges fill the chip) and d_in is at least kTallMinDepth (so that even
+// 16 ranges leave each workgroup 8 stages of 64); otherwise 128-row tiles
+// are kept. The Gram pass uses narrower tiles so that its few rows still
+// spread over many workgroups.
 constexpr int64_t kTallMinRowTiles = dora::kGrid / 8;
+constexpr int64_t kTallMinDepth = 8192;
 void choose_tiles(NormPlan& p) {
   const int64_t r = p.r;
   if (p.dtype == DORA_F32) {
@@ -59,7 +63,7 @@ void choose_tiles(NormPlan& p) {
     p.ntc_g = p.ntc, p.fcfg_g = p.fcfg, p.gcfg_g = p.gcfg;
     p.gran = 32;
   } else {
-    const bool tall = ceil_div(p.d_out, 256) >= kTallMinRowTiles;
+    const bool tall = ceil_div(p.d_out, 256) >= kTallMinRowTiles && p.d_in >= kTallMinDepth;
     if (r <= 64) {
       p.ntc = 64, p.fcfg = tall ? dora::kFastT64 : dora::kFastB64, p.gcfg = dora::kGenB64;
     } else if (r <= 128) {

@@ -86,18 +86,19 @@ def test_plan_self_check_on_many_shapes():
 
 
 def test_w_pass_tile_shapes():
-    # (d_out, r) -> (tile rows, tile columns, column tiles) of the bf16 W pass:
-    # one column tile up to r = 256, in 256-row tiles once there are at
-    # least 32 of them; 256-row tiles of 192 or 256 columns above, whichever
-    # pads r less
-    expect = {(8192, 64): (256, 64, 1), (8192, 128): (256, 128, 1), (8192, 8): (256, 64, 1),
-              (4096, 64): (128, 64, 1), (4096, 128): (128, 128, 1), (4096, 256): (128, 256, 1),
-              (7936, 256): (128, 256, 1), (7937, 256): (256, 256, 1), (8192, 160): (256, 256, 1),
-              (8192, 384): (256, 192, 2), (512, 384): (256, 192, 2), (8192, 512): (256, 256, 2),
-              (8192, 768): (256, 192, 4), (8192, 1000): (256, 256, 4), (8192, 1100): (256, 192, 6)}
-    for (d_out, r), shape in expect.items():
-        info = bnd.dora_norm_plan_info(d_out, 4096, r, "bf16", 0.5, 256 * MiB)
-        assert (info["tile_rows"], info["tile_cols"], info["col_tiles"]) == shape, (d_out, r)
+    # (d_out, d_in, r) -> (tile rows, tile columns, column tiles) of the bf16
+    # W pass: one column tile up to r = 256, in 256-row tiles once there are
+    # at least 32 of them and d_in >= 8192; 256-row tiles of 192 or 256
+    # columns above, whichever pads r less
+    expect = {(8192, 8192, 64): (256, 64, 1), (8192, 8192, 128): (256, 128, 1), (8192, 8192, 8): (256, 64, 1),
+              (8192, 8191, 64): (128, 64, 1), (8192, 4096, 128): (128, 128, 1), (28672, 2048, 256): (128, 256, 1),
+              (4096, 8192, 64): (128, 64, 1), (4096, 8192, 128): (128, 128, 1), (4096, 8192, 256): (128, 256, 1),
+              (7936, 8192, 256): (128, 256, 1), (7937, 8192, 256): (256, 256, 1), (8192, 8192, 160): (256, 256, 1),
+              (8192, 4096, 384): (256, 192, 2), (512, 3584, 384): (256, 192, 2), (8192, 4096, 512): (256, 256, 2),
+              (8192, 4096, 768): (256, 192, 4), (8192, 4096, 1000): (256, 256, 4), (8192, 4096, 1100): (256, 192, 6)}
+    for (d_out, d_in, r), shape in expect.items():
+        info = bnd.dora_norm_plan_info(d_out, d_in, r, "bf16", 0.5, 256 * MiB)
+        assert (info["tile_rows"], info["tile_cols"], info["col_tiles"]) == shape, (d_out, d_in, r)
 
 
 def test_trivial_modes_need_no_workspace():

@@ -59,12 +59,12 @@ CASES = [
     ("gen_r512_tile", 200, 999, 512, "bf16", 0.25, 30),
     ("gen_r768_f16", 130, 777, 768, "f16", 0.25, 31),
     # 256 x 256 tiles with all of r in one column tile (32 row tiles or
-    # more), the last one ragged
-    ("tall_r200", 8000, 512, 200, "bf16", 0.5, 32),
+    # more and d_in >= 8192), the last one ragged
+    ("tall_r200", 8000, 8192, 200, "bf16", 0.5, 32),
     # 256 x 64 and 256 x 128 tiles with the G blocks folded into the W pass
-    ("tall_r40_folded", 8000, 512, 40, "bf16", 0.5, 33),
-    ("tall_r128_folded", 7950, 640, 128, "bf16", -0.75, 34),
-    ("f16_tall_r64_folded", 8000, 512, 64, "f16", 0.5, 35),
+    ("tall_r40_folded", 8000, 8192, 40, "bf16", 0.5, 33),
+    ("tall_r128_folded", 7950, 8256, 128, "bf16", -0.75, 34),
+    ("f16_tall_r64_folded", 8000, 8192, 64, "f16", 0.5, 35),
 ]
 
 
@@ -129,7 +129,7 @@ GRAM_ALONE = [
     ("r512_tile", 300, 1024, 512, "bf16", 0.5),
     ("r200_f32_neg_s", 300, 512, 200, "f32", -0.75),
     # folded Gram blocks in 256-row tiles (r rounds up to 128 for the Gram term)
-    ("tall_r72_folded", 8000, 512, 72, "bf16", 0.5),
+    ("tall_r72_folded", 8000, 8192, 72, "bf16", 0.5),
 ]
 
 
