@@ -242,7 +242,9 @@ bool plan_self_check(const NormPlan& p) {
     for (int x = 0; x < X; ++x)
       if (dora::range_k0(p, X, x + 1) <= dora::range_k0(p, X, x)) return false;
   }
-  // Row tiles of every kernel (the general 512-column tile has 64 rows).
+  // Row tiles of every kernel: no tile has fewer than 64 rows, and a plan's
+  // general-kernel tile is never taller than its streaming tile (256 rows
+  // only with a 256-row streaming tile), so these bounds cover both.
   const int64_t rows_w = ceil_div(p.d_out, 64) * 64, rows_g = ceil_div(p.r, 64) * 64;
   const int fw = dora::fast_rows(p.fcfg), fg = dora::fast_rows(p.fcfg_g);
   if (ceil_div(p.d_out, fw) * fw > p.ld_w || rows_w > p.ld_w) return false;
