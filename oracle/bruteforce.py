@@ -15,7 +15,8 @@ from __future__ import annotations
 from decimal import Decimal, getcontext
 from fractions import Fraction
 
-__all__ = ["exact_row_sq_norms", "exact_sqrt", "exact_compose", "round_fraction_bf16"]
+__all__ = ["exact_row_sq_norms", "exact_sqrt", "exact_compose", "round_fraction_bf16", "round_fraction_f16",
+           "round_fraction_f32", "exact_compose_f32_stable", "exact_compose_f32_naive"]
 
 
 def _fr(v) -> Fraction:
@@ -106,3 +107,60 @@ def round_fraction_f16(q: Fraction):
     if v > 65504:
         return sign * float("inf")
     return sign * v
+
+
+def round_fraction_f32(q: Fraction):
+    """Round an exact rational to IEEE binary32, ties to even, on integers.
+
+    24 significant bits in the normal range (exponents -126 .. 127), a fixed
+    spacing of 2^-149 below 2^-126 (subnormals), and +-inf once the rounded
+    magnitude reaches 2^128 (the midpoint between the largest finite value
+    2^128 - 2^104 and 2^128 rounds to the even neighbour, 2^128, so to inf).
+    Returns a Fraction, or +-float('inf'). Independent of numpy's casts.
+    """
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = 0
+    while a >= Fraction(2) ** (e + 1):
+        e += 1
+    while a < Fraction(2) ** e:
+        e -= 1
+    spacing = Fraction(2) ** (max(e, -126) - 23)
+    n = a / spacing
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = fl * spacing
+    if v >= Fraction(2) ** 128:
+        return sign * float("inf")
+    return sign * v
+
+
+def _r32(q: Fraction) -> Fraction:
+    v = round_fraction_f32(q)
+    if not isinstance(v, Fraction):
+        raise OverflowError("binary32 overflow in an exact per-operation evaluation")
+    return v
+
+
+def exact_compose_f32_stable(base, lora, g, s) -> Fraction:
+    """The stable compose (g - 1) * base + g * (s * lora) evaluated as binary32
+    arithmetic does it, one element: every input rounded to binary32, then
+    s * lora, g - 1, (g - 1) * base, g * (s * lora) and the final sum, each
+    computed exactly and rounded once to binary32 (round to nearest even)."""
+    b, l, gg, sf = (_r32(_fr(v)) for v in (base, lora, g, s))
+    sl = _r32(sf * l)
+    p1 = _r32(_r32(gg - 1) * b)
+    p2 = _r32(gg * sl)
+    return _r32(p1 + p2)
+
+
+def exact_compose_f32_naive(base, lora, g, s) -> Fraction:
+    """The naive compose g * (s * lora + base) - base in binary32 arithmetic,
+    one element, with the same per-operation rounding as above."""
+    b, l, gg, sf = (_r32(_fr(v)) for v in (base, lora, g, s))
+    t = _r32(_r32(sf * l) + b)
+    return _r32(_r32(gg * t) - b)

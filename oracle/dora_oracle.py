@@ -19,7 +19,7 @@ Pages followed (cited by title and section):
      three-term split into base, cross and Gram terms), §1.2.2 (fp32 norm,
      the clamp at 0, the decoupled magnitude division), §1.3 Table 1 (memory
      closed forms), §2.1 and §2.1.1 (the stable compose and the naive form it
-     replaces), §5.1 Algorithm 1 (chunked factored norm, chunk-size rule).
+     replaces), §5.1 Algorithm 1 (its chunk-size rule).
 [P2] "Scaling DoRA: High-Rank Adaptation via Factored Norms and Fused
      Kernels" (alanhou.org summary of arXiv 2603.22276): "The Problem"
      (W' = m * (W + sBA) / ||W + sBA||_row) and "Factored Norm" (the
@@ -52,7 +52,7 @@ __all__ = [
     "f16_round",
     "dense_row_norm",
     "chunk_size",
-    "algorithm1_row_norm",
+    "factored_row_norm",
     "factored_terms",
     "magnitude_scale",
     "compose",
@@ -104,8 +104,11 @@ def bf16_round(x):
 
 
 def f32_round(x):
-    """Round fp64 values to the nearest binary32 value (numpy casts RNE)."""
-    return _f64(x).astype(np.float32).astype(np.float64)
+    """Round fp64 values once to IEEE binary32, nearest even (numpy's
+    float64 -> float32 conversion, a correctly rounded library routine);
+    returned as fp64. Overflow goes to +-inf, as IEEE rounding does."""
+    with np.errstate(over="ignore"):
+        return _f64(x).astype(np.float32).astype(np.float64)
 
 
 def f16_round(x):
@@ -155,7 +158,7 @@ def dense_row_norm(W, A, B, s, row_block: int = 2048):
 
 
 # --------------------------------------------------------------------------
-# The factored norm, following the chunked algorithm's steps.
+# The factored norm, from the squared-norm identity.
 # --------------------------------------------------------------------------
 
 def chunk_size(d_out: int, d_in: int, budget_bytes: int) -> int:
@@ -164,7 +167,8 @@ def chunk_size(d_out: int, d_in: int, budget_bytes: int) -> int:
     The fp32 chunk buffer [d_out, cs] must fit the byte budget, and the
     width is aligned to 64 elements for the matrix units. Reading: round
     floor(budget / (4 d_out)) down to a multiple of 64, keep it at least 64,
-    and never exceed d_in.
+    and never exceed d_in. (The identity below holds for any split of d_in,
+    so the width decides memory only, never the value.)
     """
     if d_out <= 0 or d_in <= 0:
         return max(d_in, 0)
@@ -173,47 +177,40 @@ def chunk_size(d_out: int, d_in: int, budget_bytes: int) -> int:
     return min(d_in, aligned)
 
 
-def factored_terms(W, A, B, budget_bytes: int = 256 << 20):
-    """The three per-row terms of the factored norm, in fp64.
+def factored_terms(W, A, B):
+    """The three per-row terms of the squared-norm identity, in fp64.
 
-    [P1 §1.2, §1.2.1, §5.1 Algorithm 1; P2 "Factored Norm"]:
-      base[j]  = sum_k W[j,k]^2, accumulated chunk by chunk over d_in;
-      cross[j] = sum_l B[j,l] * U[j,l], U = W A^T, accumulated per chunk
-                 (U_c = W_c A_c^T is used and dropped within each chunk);
-      G        = sum_chunks A_c A_c^T, an r x r Gram matrix;
-      ba[j]    = sum_l (B G)[j,l] * B[j,l], after the loop.
-    Returns (base, cross, ba, G).
+    Expanding ||W_j + s (BA)_j||^2 gives ||W_j||^2 + 2s <W_j, (BA)_j> +
+    s^2 ||(BA)_j||^2 [P2 "Factored Norm"; P1 §1.2, §1.2.1]. Each term is
+    rewritten without forming BA, with U = W A^T [d_out, r] and the Gram
+    matrix G = A A^T [r, r]:
+      base[j]  = sum_k W[j,k]^2
+      cross[j] = <W_j, B_j A> = sum_l B[j,l] U[j,l]
+      ba[j]    = ||B_j A||^2 = B_j G B_j^T = sum_l (B G)[j,l] B[j,l]
+    Whole matrices, one library product each. Returns (base, cross, ba, G).
     """
     W = _f64(W)
     A = _f64(A)
     B = _f64(B)
-    d_out, d_in = W.shape
-    r = A.shape[0]
-    cs = chunk_size(d_out, d_in, budget_bytes)
-    base = np.zeros(d_out)
-    cross = np.zeros(d_out)
-    G = np.zeros((r, r))
-    for c in range(0, d_in, max(cs, 1)):
-        Wc = W[:, c:c + cs]
-        Ac = A[:, c:c + cs]
-        base += np.sum(Wc * Wc, axis=1)
-        G += Ac @ Ac.T
-        Uc = Wc @ Ac.T
-        cross += np.sum(B * Uc, axis=1)
+    base = np.sum(W * W, axis=1)
+    U = W @ A.T
+    cross = np.sum(B * U, axis=1)
+    G = A @ A.T
     ba = np.sum((B @ G) * B, axis=1)
     return base, cross, ba, G
 
 
-def algorithm1_row_norm(W, A, B, s, budget_bytes: int = 256 << 20):
-    """wnorm = sqrt(max(base + 2 s cross + s^2 ba, 0)) [P1 §1.2.2; Algorithm 1 step 6].
+def factored_row_norm(W, A, B, s):
+    """wnorm = sqrt(max(base + 2 s cross + s^2 ba, 0)) [P1 §1.2.2; P2 "Factored Norm"].
 
-    When s == 0 the cross and Gram terms are skipped [P1 §5.1 notes].
+    The clamp at 0 guards the rounding of an exact cancellation. When s == 0
+    the cross and Gram terms vanish and only base remains [P1 §5.1 notes].
     """
     W = _f64(W)
     if s == 0.0:
         v = np.sum(W * W, axis=1)
     else:
-        base, cross, ba, _ = factored_terms(W, A, B, budget_bytes)
+        base, cross, ba, _ = factored_terms(W, A, B)
         v = base + 2.0 * s * cross + s * s * ba
     v = np.where(v < 0.0, 0.0, v)
     return np.sqrt(v)
@@ -310,8 +307,11 @@ def compose_naive(base, lora, g, s):
 def compose_f32_stable(base, lora, g, s):
     """The stable form evaluated in binary32, one rounding per operation.
 
-    Used only to show the cancellation the pages describe [P1 §2.1.1]:
-    with g near 1 this stays close to the fp64 result.
+    Inputs are rounded to binary32 on entry; then s*lora, g-1, (g-1)*base,
+    g*(s*lora) and their sum are each rounded once (numpy float32
+    arithmetic, no fused multiply-add). Used only to show the cancellation
+    the pages describe [P1 §2.1.1]: with g near 1 this stays close to the
+    fp64 result.
     """
     f = np.float32
     base = np.asarray(base, f)
@@ -322,7 +322,9 @@ def compose_f32_stable(base, lora, g, s):
 
 
 def compose_f32_naive(base, lora, g, s):
-    """The naive form in binary32; loses the (g-1) correction near g = 1 [P1 §2.1.1]."""
+    """The naive form in binary32, one rounding per operation (inputs rounded
+    on entry, then s*lora, + base, g*(.), - base); it loses the (g-1)
+    correction near g = 1 [P1 §2.1.1]."""
     f = np.float32
     base = np.asarray(base, f)
     lora = np.asarray(lora, f)

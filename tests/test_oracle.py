@@ -50,7 +50,7 @@ def test_dense_norm_matches_exact_bruteforce(d_out, d_in, r, s, kind):
     B = mk(rng, (d_out, r), 2.0 ** -9)
     exact = bf.exact_row_sq_norms(W.tolist(), A.tolist(), B.tolist(), s)
     got = O.dense_row_norm(W, A, B, s)
-    got_alg = O.algorithm1_row_norm(W, A, B, s, budget_bytes=64 * 4 * max(d_out, 1))
+    got_alg = O.factored_row_norm(W, A, B, s)
     for j in range(d_out):
         ref = float(bf.exact_sqrt(exact[j]))
         assert got[j] == pytest.approx(ref, rel=1e-14, abs=0.0)
@@ -78,16 +78,29 @@ def test_norm_hand_worked_example():
 
 
 @pytest.mark.parametrize("budget_cols", [64, 128, 192, 10_000])
-def test_algorithm1_equals_dense_for_any_chunking(budget_cols):
+def test_factored_terms_add_over_any_split_of_d_in(budget_cols):
+    """base, cross and G are sums over k, so the terms of the chunks of d_in
+    that the pages' chunk rule cuts add up to the whole-matrix terms, and the
+    norm assembled from the summed chunk terms equals the dense norm (ragged
+    last chunk included)."""
     rng = np.random.default_rng(7)
-    d_out, d_in, r, s = 37, 201, 13, 0.75      # ragged last chunk
+    d_out, d_in, r, s = 37, 201, 13, 0.75
     W = rng.standard_normal((d_out, d_in)) / np.sqrt(d_in)
     A = rng.standard_normal((r, d_in)) / np.sqrt(d_in)
     B = rng.standard_normal((d_out, r)) * 0.02
-    budget = budget_cols * 4 * d_out
-    np.testing.assert_allclose(
-        O.algorithm1_row_norm(W, A, B, s, budget), O.dense_row_norm(W, A, B, s), rtol=1e-13
-    )
+    cs = O.chunk_size(d_out, d_in, budget_cols * 4 * d_out)
+    assert cs == min(d_in, max(64, budget_cols // 64 * 64))
+    base, cross, G = np.zeros(d_out), np.zeros(d_out), np.zeros((r, r))
+    for c in range(0, d_in, cs):
+        b_c, x_c, _, G_c = O.factored_terms(W[:, c:c + cs], A[:, c:c + cs], B)
+        base, cross, G = base + b_c, cross + x_c, G + G_c
+    whole = O.factored_terms(W, A, B)
+    np.testing.assert_allclose(base, whole[0], rtol=1e-13)
+    np.testing.assert_allclose(cross, whole[1], rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(G, whole[3], rtol=1e-13, atol=1e-15)
+    ba = np.array([B[j] @ G @ B[j] for j in range(d_out)])
+    np.testing.assert_allclose(np.sqrt(base + 2 * s * cross + s * s * ba), O.dense_row_norm(W, A, B, s), rtol=1e-13)
+    np.testing.assert_allclose(O.factored_row_norm(W, A, B, s), O.dense_row_norm(W, A, B, s), rtol=1e-13)
 
 
 def test_s_zero_is_plain_row_norm():
@@ -97,7 +110,7 @@ def test_s_zero_is_plain_row_norm():
     B = rng.standard_normal((19, 6))
     ref = np.linalg.norm(W, axis=1)
     np.testing.assert_allclose(O.dense_row_norm(W, A, B, 0.0), ref, rtol=1e-15)
-    np.testing.assert_allclose(O.algorithm1_row_norm(W, A, B, 0.0), ref, rtol=1e-15)
+    np.testing.assert_allclose(O.factored_row_norm(W, A, B, 0.0), ref, rtol=1e-15)
 
 
 @pytest.mark.parametrize("zero", ["A", "B"])
@@ -127,7 +140,7 @@ def test_identity_A_closed_form():
     head = W[:, :r] + s * B
     ref = np.sqrt(np.sum(head ** 2, axis=1) + np.sum(W[:, r:] ** 2, axis=1))
     np.testing.assert_allclose(O.dense_row_norm(W, A, B, s), ref, rtol=1e-15)
-    np.testing.assert_allclose(O.algorithm1_row_norm(W, A, B, s), ref, rtol=1e-14)
+    np.testing.assert_allclose(O.factored_row_norm(W, A, B, s), ref, rtol=1e-14)
 
 
 def test_rank_one_and_zero_W_closed_forms():
@@ -143,7 +156,7 @@ def test_rank_one_and_zero_W_closed_forms():
     W0 = np.zeros_like(W)
     ref = abs(s) * np.abs(B[:, 0]) * np.sqrt(nA2)
     np.testing.assert_allclose(O.dense_row_norm(W0, A, B, s), ref, rtol=1e-14)
-    np.testing.assert_allclose(O.algorithm1_row_norm(W0, A, B, s), ref, rtol=1e-13)
+    np.testing.assert_allclose(O.factored_row_norm(W0, A, B, s), ref, rtol=1e-13)
 
 
 def test_rotation_invariance_and_row_permutation():
@@ -155,7 +168,7 @@ def test_rotation_invariance_and_row_permutation():
     Q, _ = np.linalg.qr(rng.standard_normal((d_in, d_in)))
     base = O.dense_row_norm(W, A, B, s)
     np.testing.assert_allclose(O.dense_row_norm(W @ Q, A @ Q, B, s), base, rtol=1e-13)
-    np.testing.assert_allclose(O.algorithm1_row_norm(W @ Q, A @ Q, B, s), base, rtol=1e-13)
+    np.testing.assert_allclose(O.factored_row_norm(W @ Q, A @ Q, B, s), base, rtol=1e-13)
     p = rng.permutation(d_out)
     np.testing.assert_array_equal(O.dense_row_norm(W[p], A, B[p], s), base[p])
 
@@ -165,7 +178,7 @@ def test_factored_terms_are_the_dense_inner_products():
     W = rng.standard_normal((10, 33))
     A = rng.standard_normal((7, 33))
     B = rng.standard_normal((10, 7))
-    base, cross, ba, G = O.factored_terms(W, A, B, budget_bytes=64 * 4 * 10)
+    base, cross, ba, G = O.factored_terms(W, A, B)
     BA = np.zeros((10, 33))
     for j in range(10):              # BA row by row, as explicit sums
         for l in range(7):
@@ -185,7 +198,7 @@ def test_norm_clamp_and_cancellation_to_zero():
     s = 0.5
     W = -s * (B @ A)
     assert np.all(O.dense_row_norm(W, A, B, s) == 0.0)
-    alg = O.algorithm1_row_norm(W, A, B, s)
+    alg = O.factored_row_norm(W, A, B, s)
     assert np.all(np.isfinite(alg)) and np.all(alg >= 0.0) and np.all(alg < 1e-6)
 
 
@@ -292,6 +305,111 @@ def test_f16_round_matches_exact_rounding():
         assert (got == want) if isinstance(want, Fraction) else (got == want), (v, got, want)
     assert O.f16_round(1.0 + 2.0 ** -11) == 1.0 and O.f16_round(1.0 + 3 * 2.0 ** -11) == 1.0 + 2.0 ** -9
     assert O.f16_round(65520.0) == np.inf and O.f16_round(3 * 2.0 ** -25) == 2.0 ** -23
+
+
+def _f32_cases():
+    """Values that exercise every branch of binary32 rounding: random normals,
+    exact midpoints between neighbouring binary32 values (ties), points just
+    off a midpoint, subnormals and their midpoints, the overflow threshold."""
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal(400) * 3.0
+    a = (rng.standard_normal(200) * 5.0).astype(np.float32)
+    nxt = np.nextafter(a, np.float32(np.inf), dtype=np.float32)
+    mids = (a.astype(np.float64) + nxt.astype(np.float64)) / 2.0          # exact in fp64
+    off = mids + np.abs(mids) * 2.0 ** -40
+    tiny = 2.0 ** -149
+    special = [tiny, 3 * tiny / 2, 5 * tiny / 2, 2.0 ** -126 - tiny / 2, 2.0 ** -150, 1.0 + 2.0 ** -24,
+               1.0 + 3 * 2.0 ** -24, -(1.0 + 2.0 ** -24), 1.0 + 2.0 ** -23 + 2.0 ** -24,
+               float(np.finfo(np.float32).max), 2.0 ** 128 - 2.0 ** 103, 2.0 ** 128 - 2.0 ** 103 - 2.0 ** 80,
+               -(2.0 ** 128), 0.1, 1.0 / 3.0, 0.0]
+    return list(x) + list(mids) + list(off) + special
+
+
+def _exact_f32(v):
+    want = bf.round_fraction_f32(Fraction(v))
+    return float(want)
+
+
+def test_f32_round_matches_exact_rounding():
+    """The oracle's binary32 rounding against exact rational rounding on
+    integers: 24 significant bits, ties to even, subnormal spacing 2^-149,
+    overflow to inf at the midpoint above the largest finite value."""
+    for v in _f32_cases():
+        assert O.f32_round(v) == _exact_f32(v), v
+    assert O.f32_round(1.0 + 2.0 ** -24) == 1.0                       # tie to even (down)
+    assert O.f32_round(1.0 + 3 * 2.0 ** -24) == 1.0 + 2.0 ** -22       # tie to even (up)
+    assert O.f32_round(3 * 2.0 ** -150) == 2.0 ** -148                 # subnormal tie to even
+    assert O.f32_round(2.0 ** 128 - 2.0 ** 103) == np.inf              # midpoint past the max
+    assert O.f32_round(2.0 ** 128 - 2.0 ** 103 - 2.0 ** 80) == float(np.finfo(np.float32).max)
+
+
+def _compose_f32_cases():
+    rng = np.random.default_rng(17)
+    n = 400
+    base = O.bf16_round(rng.standard_normal(n))
+    lora = O.bf16_round(0.1 * rng.standard_normal(n))
+    g = O.f32_round(1.0 + 0.0015 * rng.standard_normal(n))
+    # generic fp64 inputs too (they are rounded to binary32 on entry)
+    base2 = rng.standard_normal(n) * 3.0
+    lora2 = rng.standard_normal(n)
+    g2 = 1.0 + 0.3 * rng.standard_normal(n)
+    return [(base, lora, g, 0.5), (base2, lora2, g2, 0.3), (base, lora, g, 16.0 / np.sqrt(384.0))]
+
+
+@pytest.mark.parametrize("form", ["stable", "naive"])
+def test_compose_f32_forms_match_exact_per_operation_rounding(form):
+    """The binary32 compose forms against exact rational arithmetic with one
+    binary32 rounding after each operation (inputs rounded on entry)."""
+    fn = O.compose_f32_stable if form == "stable" else O.compose_f32_naive
+    ex = bf.exact_compose_f32_stable if form == "stable" else bf.exact_compose_f32_naive
+    for base, lora, g, s in _compose_f32_cases():
+        got = np.asarray(fn(base[None], lora[None], g, s), dtype=np.float64)[0]
+        for i in range(len(base)):
+            assert got[i] == float(ex(base[i], lora[i], g[i], s)), (form, i)
+
+
+def test_f32_pins_reject_planted_mistakes():
+    """Plausible mistakes in the binary32 helpers each fail a pin above."""
+    cases = _f32_cases()
+
+    def round_ok(fn):
+        return all(fn(v) == _exact_f32(v) for v in cases)
+
+    def to16(v):
+        with np.errstate(over="ignore"):
+            return float(np.float64(v).astype(np.float16))
+
+    round_mutants = {
+        "fp16 cast": to16,
+        "no rounding": lambda v: float(v),
+        "bf16 rounding": lambda v: float(O.bf16_round(v)),
+        "toward zero": lambda v: (lambda r: float(np.nextafter(np.float32(r), np.float32(0)))
+                                  if abs(r) > abs(v) else r)(float(O.f32_round(v))),
+    }
+    assert round_ok(lambda v: float(O.f32_round(v)))
+    for name, fn in round_mutants.items():
+        assert not round_ok(fn), name
+
+    def compose_ok(fn):
+        for base, lora, g, s in _compose_f32_cases():
+            got = np.asarray(fn(base[None], lora[None], g, s), dtype=np.float64)[0]
+            if not all(got[i] == float(bf.exact_compose_f32_stable(base[i], lora[i], g[i], s))
+                       for i in range(len(base))):
+                return False
+        return True
+
+    f = np.float32
+    compose_mutants = {
+        "fp64 evaluation": lambda b, l, g, s: O.compose(b, l, g, s),
+        "fp16 inputs": lambda b, l, g, s: O.compose_f32_stable(O.f16_round(b), O.f16_round(l), g, s),
+        "fused g*(s*lora) + (g-1)*base": lambda b, l, g, s: O.f32_round(
+            np.asarray(g, f)[None].astype(np.float64) * (f(s) * np.asarray(l, f)).astype(np.float64)
+            + ((np.asarray(g, f) - f(1))[None] * np.asarray(b, f)).astype(np.float64)),
+        "naive form": O.compose_f32_naive,
+    }
+    assert compose_ok(O.compose_f32_stable)
+    for name, fn in compose_mutants.items():
+        assert not compose_ok(fn), name
 
 
 def test_stable_compose_beats_naive_near_one():
@@ -448,7 +566,7 @@ def test_pins_reject_planted_mistakes():
         "s instead of s^2": lambda W, A, B, s: np.sqrt(
             (lambda t: t[0] + 2 * s * t[1] + s * t[2])(O.factored_terms(W, A, B))),
     }
-    assert norm_ok(O.dense_row_norm) and norm_ok(O.algorithm1_row_norm)
+    assert norm_ok(O.dense_row_norm) and norm_ok(O.factored_row_norm)
     for name, fn in norm_mutants.items():
         assert not norm_ok(fn), name
 
