@@ -17,7 +17,9 @@ Prints one JSON line. `value` is the factored norm's algorithmic TFLOP/s;
 the compose's GB/s and fraction of HBM peak, per-call times and the
 roofline objects ride in the same line. Kernel times come from HIP events
 recorded on the stream the kernels run on; the W-pass kernel inside the
-norm call is timed by events the library records around its launches.
+norm call is timed by events dora_factored_norm_marked records around its
+launch. Before the warm-up steps, steps run for PREWARM_S seconds whatever
+--warmup says, so that the timed steps find the clocks up.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-backward]
                     [--no-comparisons] [--no-linear]
@@ -41,6 +43,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 F32_MFMA_PEAK_TFLOPS = 157.3
 NSETS = 3                       # input sets the steps rotate through
 ROUNDS = 5                      # rounds of K back-to-back calls for the per-call times
+PREWARM_S = 0.25                # steps run before the warm-up, whatever --warmup says
 METRIC = "factored-norm ms/TFLOP/s + compose GB/s (%HBM peak), 8192×8192 r=384 bf16"
 
 
@@ -77,13 +80,24 @@ def compose_bwd_bytes(T, d_out, esize, dm=True):
     return 5 * T * d_out * esize + (16 if dm else 8) * d_out
 
 
-def cpu_baseline(w, W, A, B, base, lora, g_host):
-    """The fp64 CPU oracle, as it stands, on a bounded sample of the workload.
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    The whole norm (dense W + sBA in fp64 through BLAS): one warm-up, then
-    the median of three runs on every core BLAS uses; the same on one BLAS
-    thread over the first eighth of the rows, scaled to all rows; and the
-    compose over all rows once (elementwise numpy, one thread).
+
+def cpu_baseline(w, W, A, B, base, lora, g_host):
+    """The fp64 CPU oracle, as it stands, on the same workload.
+
+    Each leg is one untimed run, then the median of three timed runs: the
+    whole norm (dense W + sBA in fp64 through BLAS) on every core BLAS uses
+    and again on one BLAS thread, and the compose over all rows (elementwise
+    numpy, one thread) rounded once to the storage type.
     """
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
@@ -94,30 +108,33 @@ def cpu_baseline(w, W, A, B, base, lora, g_host):
     threads = max([p.get("num_threads", 1) for p in blas] or [1])
     affinity = len(os.sched_getaffinity(0))
 
-    def timed(fn):
-        t0 = time.perf_counter()
+    def median3(fn):
         fn()
-        return time.perf_counter() - t0
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
 
-    O.dense_row_norm(W, A, B, w.s)
-    t_norm = float(np.median([timed(lambda: O.dense_row_norm(W, A, B, w.s)) for _ in range(3)]))
-    rows1 = max(1, w.d_out // 8)
+    t_norm = median3(lambda: O.dense_row_norm(W, A, B, w.s))
     with threadpool_limits(limits=1, user_api="blas"):
-        O.dense_row_norm(W[:rows1], A, B[:rows1], w.s)
-        t_norm1 = float(np.median([timed(lambda: O.dense_row_norm(W[:rows1], A, B[:rows1], w.s))
-                                   for _ in range(3)])) * (w.d_out / rows1)
-    t_comp = timed(lambda: O.round_to_dtype(O.compose(base, lora, g_host, w.s), w.dtype))
+        t_norm1 = median3(lambda: O.dense_row_norm(W, A, B, w.s))
+    t_comp = median3(lambda: O.round_to_dtype(O.compose(base, lora, g_host, w.s), w.dtype))
     esize = 2 if w.dtype == "bf16" else 4
     F = norm_flops(w.d_out, w.d_in, w.r)
+    cpu = _cpu_model()
     return {
         "value": F / t_norm / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"whole norm ({w.d_out}x{w.d_in}, r={w.r}), median of 3 after one warm-up: {t_norm:.2f} s on "
-                   f"{threads} BLAS threads ({affinity} cores in the affinity mask); on 1 thread, rows 0..{rows1 - 1} "
-                   f"scaled to all rows: {t_norm1:.2f} s; compose over all {w.T} rows once, elementwise numpy on "
-                   f"one thread: {t_comp:.2f} s; fp64"),
+        "sample": (f"whole workload, fp64, each leg one untimed run then the median of 3: the norm "
+                   f"({w.d_out}x{w.d_in}, r={w.r}) {t_norm:.3f} s on {threads} BLAS threads and {t_norm1:.3f} s on "
+                   f"one; the compose over all {w.T} rows (elementwise numpy, one thread) {t_comp:.3f} s; "
+                   f"{affinity} cores in the affinity mask, {cpu}"),
+        "cpu_model": cpu,
+        "affinity_cores": affinity,
         "norm_ms": t_norm * 1e3,
         "value_1thread": F / t_norm1 / 1e12,
         "norm_ms_1thread": t_norm1 * 1e3,
@@ -363,7 +380,19 @@ def main() -> int:
         if st:
             raise bnd.DoraError("dora_compose", st)
 
-    print(f"# warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    # Pre-warm: steps for PREWARM_S seconds whatever --warmup says, so that
+    # the timed steps find the GPU's clocks up (a few warm-up steps last only
+    # a millisecond or two, and the first rounds after them run slower).
+    print(f"# pre-warm {PREWARM_S:.2f} s, then warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    t_pw = time.perf_counter()
+    prewarm_steps = 0
+    while time.perf_counter() - t_pw < PREWARM_S:
+        for _ in range(50):
+            run_norm(prewarm_steps)
+            run_compose(prewarm_steps)
+            prewarm_steps += 1
+        torch.cuda.synchronize()
+    prewarm_ms = (time.perf_counter() - t_pw) * 1e3
     for k in range(args.warmup):
         run_norm(k)
         run_compose(k)
@@ -412,10 +441,10 @@ def main() -> int:
     norm_ms = float(np.median(norm_rounds))
     comp_ms = float(np.median(comp_rounds))
 
-    # The W-pass kernel inside the norm call: K more steps, with the library
-    # recording one event on the stream just before that launch and one just
-    # after it (its launch-event hook; launch w_launch lies between marks
-    # w_launch and w_launch + 1).
+    # The W-pass kernel inside the norm call: K more steps whose norm call is
+    # dora_factored_norm_marked, which records one event on the stream just
+    # before that launch and one just after it (launch w_launch lies between
+    # marks w_launch and w_launch + 1).
     plan = bnd.dora_norm_plan_info(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
     wl = plan["w_launch"]
     marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -426,11 +455,11 @@ def main() -> int:
     mark_arrays = [(P * (wl + 2))(*([None] * wl + [a.cuda_event, b.cuda_event])) for a, b in marks]
     print(f"# timing the W-pass launch over {K} more steps", file=sys.stderr, flush=True)
     for k in range(K):
-        lib.dora_set_launch_events(mark_arrays[k], wl + 2)
-        run_norm(k)
+        st = lib.dora_factored_norm_marked(*norm_args[k % NSETS], mark_arrays[k], wl + 2)
+        if st:
+            raise bnd.DoraError("dora_factored_norm_marked", st)
         run_compose(k)
     torch.cuda.synchronize()
-    lib.dora_set_launch_events(None, 0)
     w_times = [a.elapsed_time(b) for a, b in marks]
     w_ms = float(np.median(w_times))
 
@@ -448,11 +477,9 @@ def main() -> int:
 
     tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     traffic, traffic_note = {}, "no counter run for this workload"
-    longest = None
     if os.path.exists(tpath):
         with open(tpath) as f:
             tj = json.load(f)
-        longest = tj.get("longest_step_kernel")
         if tj.get("source_hash") == prof.source_hash():
             traffic = {"norm": tj["norm_bytes_per_call"], "compose": tj["compose_bytes_per_call"],
                        "compose_bwd": tj.get("compose_bwd_bytes_per_call") or None,
@@ -486,14 +513,13 @@ def main() -> int:
               "timing": "median over the steps of the interval between the events the library records just "
                         "before and just after the launch (includes its dispatch gap)",
               "traffic_source": traffic_note}
-    # The dominant kernel is the longest single launch of a step, as the
-    # committed kernel trace of this workload lists it: the compose kernel,
-    # or the norm's W pass. Without a trace, the longer of the compose
-    # launch and the W-pass launch decides.
-    if longest is not None:
-        dominant = roof_compose if longest.get("part") == "compose" else roof_w
-    else:
-        dominant = roof_compose if comp_ms >= w_ms else roof_w
+    # The dominant kernel is the longest single launch of a step, as this
+    # run measured them: the compose kernel (the compose call is that one
+    # launch) against the W-pass launch of the norm call (its event interval,
+    # which also holds its dispatch gap, so a tie goes to the W pass).
+    dominant = roof_compose if comp_ms > w_ms else roof_w
+    dominant = dict(dominant, chosen_by=(f"longest launch of a step in this run: compose {comp_ms * 1e3:.1f} us, "
+                                         f"W pass {w_ms * 1e3:.1f} us"))
 
     res = {
         "metric": METRIC,
@@ -502,6 +528,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "prewarm_ms": prewarm_ms,
+        "prewarm_steps": prewarm_steps,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -11,6 +11,7 @@ The function names match the C entry points.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -36,7 +37,7 @@ __all__ = [
     "PLAN_FIELDS",
     "dora_compose_backward",
     "dora_compose_backward_workspace_size",
-    "dora_set_launch_events",
+    "dora_factored_norm_marked",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdora.so")
@@ -50,7 +51,7 @@ PLAN_FIELDS = (
     "mode", "tile_cols", "col_tiles", "gram_tile_cols", "gram_col_tiles", "fast_cfg", "gen_cfg",
     "gram_fast_cfg", "gram_gen_cfg", "granule", "granules", "w_ranges", "gram_ranges", "workspace_bytes",
     "w_grid", "gram_grid", "lds_bytes", "tile_rows", "gram_folded", "gram_symmetric", "gram_term_fused",
-    "w_launch",
+    "w_launch", "offsets32",
 )
 
 _lib = None
@@ -88,7 +89,8 @@ def load():
         "dora_norm_plan_info": (_c_i, [_c_i64, _c_i64, _c_i64, _c_i, _c_f, _c_sz, ctypes.POINTER(_c_i64), _c_i]),
         "dora_factored_norm": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i64, _c_i64, _c_i64, _c_f, _c_sz, _c_p, _c_sz,
                                       _c_p, _c_p, _c_f, _c_p, _c_p]),
-        "dora_set_launch_events": (_c_i, [ctypes.POINTER(_c_p), _c_i]),
+        "dora_factored_norm_marked": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i64, _c_i64, _c_i64, _c_f, _c_sz, _c_p,
+                                             _c_sz, _c_p, _c_p, _c_f, _c_p, _c_p, ctypes.POINTER(_c_p), _c_i]),
         "dora_magnitude_scale": (_c_i, [_c_p, _c_p, _c_f, _c_i64, _c_p, _c_p]),
         "dora_norm_to_dtype": (_c_i, [_c_p, _c_i64, _c_i, _c_p, _c_p]),
         "dora_compose": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
@@ -148,6 +150,34 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous (row-major)")
 
 
+def _out_like(t, name: str, shape, dtype, device):
+    """A caller-supplied output buffer: on `device`, contiguous, exactly
+    `shape` and `dtype` (the C ABI cannot see allocation sizes, so a short
+    or mistyped buffer is refused here, before any launch)."""
+    _dev(t, name)
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _workspace(t, name: str, need: int, device):
+    """A caller-supplied workspace: on `device`, contiguous, at least `need` bytes."""
+    _dev(t, name)
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes; {need} are needed")
+
+
+def _on(stream):
+    """Allocations made inside belong to `stream` (torch's caching allocator
+    then reuses their memory only after the work queued on `stream`), so
+    temporaries freed on return cannot be handed to other work while the
+    kernels launched on `stream` still use them."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def dora_norm_chunk_size(d_out: int, d_in: int, budget_bytes: int = DEFAULT_BUDGET) -> int:
     cs = _c_i64()
     _call("dora_norm_chunk_size", d_out, d_in, budget_bytes, ctypes.byref(cs))
@@ -169,12 +199,14 @@ def dora_norm_plan_info(d_out: int, d_in: int, r: int, dtype, s: float,
 
 
 def dora_factored_norm(W, A, B, s: float, budget_bytes: int = DEFAULT_BUDGET, m=None, eps: float = 1e-6,
-                       workspace=None, wnorm=None, g=None, stream=None):
+                       workspace=None, wnorm=None, g=None, stream=None, events=None):
     """wnorm = ||W + s B A||_row (fp32) and, if m is given, g = m / max(wnorm, eps).
 
     W [d_out, d_in], A [r, d_in], B [d_out, r], all of one dtype (bfloat16,
-    float16 or float32),
-    on the GPU. Returns (wnorm, g); g is None when m is None.
+    float16 or float32), on the GPU. Returns (wnorm, g); g is None when m is
+    None. `events` (a sequence of recorded torch.cuda.Event objects or None
+    entries) selects dora_factored_norm_marked, which records them between
+    the call's launches.
     """
     for t, nm in ((W, "W"), (A, "A"), (B, "B")):
         _dev(t, nm)
@@ -186,48 +218,59 @@ def dora_factored_norm(W, A, B, s: float, budget_bytes: int = DEFAULT_BUDGET, m=
         raise ValueError(f"shape mismatch: W {tuple(W.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)}")
     if not (W.dtype == A.dtype == B.dtype):
         raise TypeError("W, A, B must share one dtype")
+    if not (W.device == A.device == B.device):
+        raise ValueError("W, A, B must be on one device")
     dt = _dtype_code(W.dtype)
     dev = W.device
     ws_bytes = dora_norm_workspace_size(d_out, d_in, r, dt, s, budget_bytes)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    if wnorm is None:
-        wnorm = torch.empty(d_out, dtype=torch.float32, device=dev)
+    if workspace is not None:
+        _workspace(workspace, "workspace", ws_bytes, dev)
+    if wnorm is not None:
+        _out_like(wnorm, "wnorm", (d_out,), torch.float32, dev)
     if m is not None:
-        _dev(m, "m")
-        if m.dtype != torch.float32 or m.shape != (d_out,):
-            raise ValueError("m must be float32 [d_out]")
-        if g is None:
+        _out_like(m, "m", (d_out,), torch.float32, dev)
+        if g is not None:
+            _out_like(g, "g", (d_out,), torch.float32, dev)
+    with _on(stream):
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        if wnorm is None:
+            wnorm = torch.empty(d_out, dtype=torch.float32, device=dev)
+        if m is not None and g is None:
             g = torch.empty(d_out, dtype=torch.float32, device=dev)
-    _call("dora_factored_norm", _ptr(W), _ptr(A), _ptr(B), dt, d_out, d_in, r, s, budget_bytes,
-          _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-          _ptr(wnorm), _ptr(m), eps, _ptr(g) if m is not None else None, _stream(stream))
+        args = (_ptr(W), _ptr(A), _ptr(B), dt, d_out, d_in, r, s, budget_bytes, _ptr(workspace),
+                0 if workspace is None else workspace.numel() * workspace.element_size(),
+                _ptr(wnorm), _ptr(m), eps, _ptr(g) if m is not None else None, _stream(stream))
+        if events is None:
+            _call("dora_factored_norm", *args)
+        else:
+            handles = [None if e is None else int(getattr(e, "cuda_event", e)) for e in events]
+            if any(h == 0 for h in handles):
+                raise ValueError("an event has no HIP handle yet (record it once first)")
+            arr = (_c_p * max(len(handles), 1))(*handles)
+            _call("dora_factored_norm_marked", *args, arr, len(handles))
     return wnorm, (g if m is not None else None)
 
 
-def dora_set_launch_events(events) -> None:
-    """Events recorded around the launches of later dora_factored_norm calls.
-
-    `events`: a sequence of created torch.cuda.Event objects (record each
-    once before passing it, so that it exists), raw hipEvent_t handles, or
-    None entries (marks that are skipped); an empty sequence or None clears
-    the hook. The caller keeps the events alive while they are set.
-    """
-    events = list(events or [])
-    handles = [None if e is None else int(getattr(e, "cuda_event", e)) for e in events]
-    if any(h == 0 for h in handles):
-        raise ValueError("an event has no HIP handle yet (record it once first)")
-    arr = (_c_p * max(len(handles), 1))(*handles)
-    _call("dora_set_launch_events", arr, len(handles))
+def dora_factored_norm_marked(W, A, B, s: float, events, **kw):
+    """dora_factored_norm with HIP events recorded between its launches
+    (events[0] before the first, events[i] after the i-th; None entries
+    skipped). Same keywords and results as dora_factored_norm."""
+    return dora_factored_norm(W, A, B, s, events=list(events), **kw)
 
 
 def dora_magnitude_scale(m, wnorm, eps: float = 1e-6, g=None, stream=None):
     """g = m / max(wnorm, eps), fp32 [d_out]."""
     _dev(m, "m")
-    _dev(wnorm, "wnorm")
-    if g is None:
-        g = torch.empty_like(m)
-    _call("dora_magnitude_scale", _ptr(m), _ptr(wnorm), eps, m.numel(), _ptr(g), _stream(stream))
+    if m.dtype != torch.float32 or m.dim() != 1:
+        raise ValueError("m must be float32 [d_out]")
+    _out_like(wnorm, "wnorm", m.shape, torch.float32, m.device)
+    if g is not None:
+        _out_like(g, "g", m.shape, torch.float32, m.device)
+    with _on(stream):
+        if g is None:
+            g = torch.empty_like(m)
+        _call("dora_magnitude_scale", _ptr(m), _ptr(wnorm), eps, m.numel(), _ptr(g), _stream(stream))
     return g
 
 
@@ -237,9 +280,12 @@ def dora_norm_to_dtype(wnorm, dtype, out=None, stream=None):
     if wnorm.dtype != torch.float32 or wnorm.dim() != 1:
         raise ValueError("wnorm must be float32 [n]")
     tdt = {DORA_BF16: torch.bfloat16, DORA_F32: torch.float32, DORA_F16: torch.float16}[_dtype_code(dtype)]
-    if out is None:
-        out = torch.empty(wnorm.shape, dtype=tdt, device=wnorm.device)
-    _call("dora_norm_to_dtype", _ptr(wnorm), wnorm.numel(), _dtype_code(dtype), _ptr(out), _stream(stream))
+    if out is not None:
+        _out_like(out, "out", wnorm.shape, tdt, wnorm.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(wnorm.shape, dtype=tdt, device=wnorm.device)
+        _call("dora_norm_to_dtype", _ptr(wnorm), wnorm.numel(), _dtype_code(dtype), _ptr(out), _stream(stream))
     return out
 
 
@@ -253,14 +299,15 @@ def _compose_call(name, base, lora, g, s, out, stream):
     T, d_out = base.shape
     if g.dtype != torch.float32 or g.shape != (d_out,):
         raise ValueError("g must be float32 [d_out]")
+    if not (base.device == lora.device == g.device):
+        raise ValueError("base, lora and g must be on one device")
     dt = _dtype_code(base.dtype)
-    if out is None:
-        out = torch.empty_like(base)
-    else:
-        _dev(out, "out")
-        if out.shape != base.shape or out.dtype != base.dtype:
-            raise ValueError("out must match base")
-    _call(name, _ptr(base), _ptr(lora), _ptr(g), s, dt, T, d_out, _ptr(out), _stream(stream))
+    if out is not None:
+        _out_like(out, "out", base.shape, base.dtype, base.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(base)
+        _call(name, _ptr(base), _ptr(lora), _ptr(g), s, dt, T, d_out, _ptr(out), _stream(stream))
     return out
 
 
@@ -307,14 +354,24 @@ def dora_compose_backward(dy, base, lora, g, s: float, need_dg: bool = True, wno
         if wnorm.dtype != torch.float32 or wnorm.shape != (d_out,):
             raise ValueError("wnorm must be float32 [d_out]")
     dt = _dtype_code(dy.dtype)
-    d_base = torch.empty_like(dy) if d_base is None else d_base
-    d_lora = torch.empty_like(dy) if d_lora is None else d_lora
-    dg = torch.empty(d_out, dtype=torch.float32, device=dy.device) if need_dg else None
-    dm = torch.empty(d_out, dtype=torch.float32, device=dy.device) if wnorm is not None else None
+    dev = dy.device
+    if g.device != dev:
+        raise ValueError("g must be on dy's device")
+    if d_base is not None:
+        _out_like(d_base, "d_base", dy.shape, dy.dtype, dev)
+    if d_lora is not None:
+        _out_like(d_lora, "d_lora", dy.shape, dy.dtype, dev)
     ws_bytes = dora_compose_backward_workspace_size(T, d_out) if need_dg else 0
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dy.device)
-    _call("dora_compose_backward", _ptr(dy), _ptr(base if need_dg else None), _ptr(lora if need_dg else None),
-          _ptr(g), s, dt, T, d_out, _ptr(d_base), _ptr(d_lora), _ptr(dg), _ptr(wnorm), eps, _ptr(dm),
-          _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream))
+    if workspace is not None and ws_bytes > 0:
+        _workspace(workspace, "workspace", ws_bytes, dev)
+    with _on(stream):
+        d_base = torch.empty_like(dy) if d_base is None else d_base
+        d_lora = torch.empty_like(dy) if d_lora is None else d_lora
+        dg = torch.empty(d_out, dtype=torch.float32, device=dev) if need_dg else None
+        dm = torch.empty(d_out, dtype=torch.float32, device=dev) if wnorm is not None else None
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        _call("dora_compose_backward", _ptr(dy), _ptr(base if need_dg else None), _ptr(lora if need_dg else None),
+              _ptr(g), s, dt, T, d_out, _ptr(d_base), _ptr(d_lora), _ptr(dg), _ptr(wnorm), eps, _ptr(dm),
+              _ptr(workspace), ws_bytes if workspace is not None else 0, _stream(stream))
     return d_base, d_lora, dg, dm

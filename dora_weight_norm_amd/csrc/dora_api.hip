@@ -261,6 +261,25 @@ bool plan_self_check(const NormPlan& p) {
   return p.ws_bytes >= p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.r) * 4 : 0);
 }
 
+// The streaming kernel addresses every operand tile through a buffer
+// descriptor with 32-bit byte offsets, and marks masked loads with the
+// offset 2^31 (past every descriptor's range). So each descriptor must span
+// less than 2^31 bytes: the tallest row tile of W or A (the W pass's tile
+// rows, its column tile over A's rows, and the Gram pass's square tiles) by
+// d_in, and the Gram-term operands (B's rows by r, the stored Gram matrix's
+// rows by its width).
+bool offsets_fit_32(const NormPlan& p) {
+  if (p.mode != dora::kModeFactored) return true;
+  const uint64_t es = (uint64_t)esize(p.dtype);
+  uint64_t rows = (uint64_t)dora::fast_rows(p.fcfg);
+  const uint64_t others[] = {(uint64_t)p.ntc, (uint64_t)dora::fast_rows(p.fcfg_g), (uint64_t)p.ntc_g};
+  for (uint64_t o : others) rows = o > rows ? o : rows;
+  const uint64_t tile_span = rows * (uint64_t)p.d_in * es;
+  const uint64_t b_span = rows * (uint64_t)p.r * es;
+  const uint64_t g_span = rows * 2ull * (uint64_t)p.rg * es;
+  return tile_span < (1ull << 31) && b_span < (1ull << 31) && g_span < (1ull << 31);
+}
+
 dora_status hip_status(hipError_t e) { return e == hipSuccess ? DORA_OK : DORA_ERR_HIP; }
 
 dora_status compose_checked(const void* base, const void* lora, const float* g, float s, int dtype, int64_t T,
@@ -338,17 +357,21 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
                           f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0,
                           f ? p.gfold : 0, f ? p.gsym : 0, f ? (int64_t)(!p.gfold && p.dtype != DORA_F16) : 0,
-                          f ? (p.gfold ? 0 : 2) : 0};
+                          f ? (p.gfold ? 0 : 2) : 0, f ? (int64_t)offsets_fit_32(p) : 1};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;
   return DORA_OK;
 }
 
-dora_status dora_factored_norm(const void* W, const void* A, const void* B, int dtype, int64_t d_out,
-                               int64_t d_in, int64_t r, float s, size_t budget_bytes, void* workspace,
-                               size_t workspace_bytes, float* wnorm, const float* m, float eps, float* g,
-                               void* stream) {
+}  // extern "C"
+
+namespace {
+
+dora_status factored_norm(const void* W, const void* A, const void* B, int dtype, int64_t d_out, int64_t d_in,
+                          int64_t r, float s, size_t budget_bytes, void* workspace, size_t workspace_bytes,
+                          float* wnorm, const float* m, float eps, float* g, void* stream, const hipEvent_t* events,
+                          int n_events) {
   if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;
   dora_status st = check_sizes(d_out, d_in, r);
   if (st != DORA_OK) return st;
@@ -358,6 +381,7 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
   st = make_plan(d_out, d_in, r, dtype, s, budget_bytes, &p);
   if (st != DORA_OK) return st;
   if (p.mode == dora::kModeEmpty) return DORA_OK;
+  if (!plan_self_check(p)) return DORA_ERR_INVALID_ARG;
 
   const int64_t es = esize(dtype);
   const int64_t nW = d_out * d_in * es, nA = r * d_in * es, nB = d_out * r * es, nV = d_out * 4;
@@ -386,24 +410,36 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (!factored) {
     const bool vec = aligned(W, 16) && (d_in % epc(dtype)) == 0;
-    return hip_status(dora::launch_norm_rowonly(W, dtype, d_out, d_in, vec, m, eps, wnorm, gout ? g : nullptr, hs));
+    return hip_status(
+        dora::launch_norm_rowonly(W, dtype, d_out, d_in, vec, m, eps, wnorm, gout ? g : nullptr, hs, events, n_events));
   }
   if (workspace_bytes < p.ws_bytes) return DORA_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && (workspace == nullptr || !aligned(workspace, kAlign))) return DORA_ERR_WORKSPACE;
-  // The streaming kernel addresses a tile's rows with 32-bit byte offsets.
-  const int64_t span_rows = p.ntc > 128 ? p.ntc : 128;
-  const uint64_t tile_span = (uint64_t)span_rows * (uint64_t)d_in * (uint64_t)es;
-  const uint64_t b_span = 32ull * (uint64_t)r * (uint64_t)es;
   p.vec_b = aligned(B, 16) && (r % epc(dtype)) == 0;
-  p.fast = aligned(W, 16) && aligned(A, 16) && (d_in % epc(dtype)) == 0 && p.vec_b &&
-           tile_span < (1ull << 31) && b_span < (1ull << 31);
-  return hip_status(dora::launch_norm_factored(p, W, A, B, workspace, s, m, eps, wnorm, g, hs));
+  p.fast = aligned(W, 16) && aligned(A, 16) && (d_in % epc(dtype)) == 0 && p.vec_b && offsets_fit_32(p);
+  return hip_status(dora::launch_norm_factored(p, W, A, B, workspace, s, m, eps, wnorm, g, hs, events, n_events));
 }
 
-dora_status dora_set_launch_events(void* const* events, int n_events) {
+}  // namespace
+
+extern "C" {
+
+dora_status dora_factored_norm(const void* W, const void* A, const void* B, int dtype, int64_t d_out,
+                               int64_t d_in, int64_t r, float s, size_t budget_bytes, void* workspace,
+                               size_t workspace_bytes, float* wnorm, const float* m, float eps, float* g,
+                               void* stream) {
+  return factored_norm(W, A, B, dtype, d_out, d_in, r, s, budget_bytes, workspace, workspace_bytes, wnorm, m, eps,
+                       g, stream, nullptr, 0);
+}
+
+dora_status dora_factored_norm_marked(const void* W, const void* A, const void* B, int dtype, int64_t d_out,
+                                      int64_t d_in, int64_t r, float s, size_t budget_bytes, void* workspace,
+                                      size_t workspace_bytes, float* wnorm, const float* m, float eps, float* g,
+                                      void* stream, void* const* events, int n_events) {
   if (n_events < 0 || (n_events > 0 && events == nullptr)) return DORA_ERR_INVALID_ARG;
-  dora::set_launch_events(reinterpret_cast<const hipEvent_t*>(events), n_events);
-  return DORA_OK;
+  return factored_norm(W, A, B, dtype, d_out, d_in, r, s, budget_bytes, workspace, workspace_bytes, wnorm, m, eps,
+                       g, stream, reinterpret_cast<const hipEvent_t*>(events),
+                       n_events < dora::kMaxLaunchEvents ? n_events : dora::kMaxLaunchEvents);
 }
 
 dora_status dora_magnitude_scale(const float* m, const float* wnorm, float eps, int64_t d_out, float* g,

@@ -1119,12 +1119,12 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(NormPlan p, const
   if (live && q == 0) assemble_sums(base, cross, ba, s, eps, m, wnorm, g, j);
 }
 
-hipError_t launched(hipStream_t st);
+hipError_t launched(hipStream_t st, Marks& mk);
 
 // assemble_kernel over all rows, with the smallest split (threads per row)
 // that leaves each thread at most one batch of kSumBatch planes per kind.
 hipError_t launch_assemble(const NormPlan& p, const char* ws, int n_ba, float s, const float* m, float eps,
-                           float* wnorm, float* g, hipStream_t st) {
+                           float* wnorm, float* g, hipStream_t st, Marks& mk) {
   const int nc = p.xw * p.n_nt;
   const int n = p.xw > nc ? (p.xw > n_ba ? p.xw : n_ba) : (nc > n_ba ? nc : n_ba);
   int split = 1;
@@ -1132,7 +1132,7 @@ hipError_t launch_assemble(const NormPlan& p, const char* ws, int n_ba, float s,
   const int64_t threads = p.d_out * split;
   hipLaunchKernelGGL(assemble_kernel, dim3((unsigned)((threads + kAsmThreads - 1) / kAsmThreads)), dim3(kAsmThreads),
                      0, st, p, ws, n_ba, s, m, eps, wnorm, g, split);
-  return launched(st);
+  return launched(st, mk);
 }
 
 // ---------------------------------------------------------------------------
@@ -1192,35 +1192,28 @@ __global__ __launch_bounds__(kThreads) void widen_kernel(const f16_t* in, int64_
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Launch markers, a benchmark hook (dora_set_launch_events): while events
-// are set, each norm call records event 0 on its stream before its first
-// launch and event i after its i-th launch, for as many events as were
-// given, skipping null entries. Process-wide and unsynchronised, like the
-// hook itself.
-hipEvent_t g_marks[kMaxLaunchEvents];
-int g_n_marks = 0;
-int g_next_mark = 0;
-
-// Records marker i if it exists and is not a null entry.
-hipError_t record_mark(int i, hipStream_t st) {
-  return (i < g_n_marks && g_marks[i] != nullptr) ? hipEventRecord(g_marks[i], st) : hipSuccess;
+// Timing marks of one norm call (dora_factored_norm_marked): event 0 on the
+// stream before the call's first launch, event i after its i-th launch, for
+// as many events as the caller gave, null entries skipped. Local to the call.
+hipError_t record_mark(Marks& mk, int i, hipStream_t st) {
+  return (i < mk.n && mk.ev[i] != nullptr) ? hipEventRecord(mk.ev[i], st) : hipSuccess;
 }
 
-hipError_t begin_marks(hipStream_t st) {
-  g_next_mark = 1;
-  return record_mark(0, st);
+hipError_t begin_marks(Marks& mk, hipStream_t st) {
+  mk.next = 1;
+  return record_mark(mk, 0, st);
 }
 
 // The status of the launch just made, and its end marker if one is due.
-hipError_t launched(hipStream_t st) {
+hipError_t launched(hipStream_t st, Marks& mk) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return record_mark(g_next_mark++, st);
+  return record_mark(mk, mk.next++, st);
 }
 
 template <typename T, int WM, int WN, int MB, int NB, int KT, int NS, int MODE>
 hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const void* B, char* ws,
-                       const AssembleArgs& aa, hipStream_t st) {
+                       const AssembleArgs& aa, hipStream_t st, Marks& mk) {
   using C = FastK<T, WM, WN, MB, NB, KT, NS>;
   int64_t grid;
   if (MODE == kPassBG) {
@@ -1235,24 +1228,24 @@ hipError_t launch_fast(const NormPlan& p, const void* M, const void* A, const vo
   }
   hipLaunchKernelGGL((norm_fast_kernel<T, WM, WN, MB, NB, KT, NS, MODE>), dim3((unsigned)grid), dim3(C::NT), 0, st,
                      p, static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws, aa);
-  return launched(st);
+  return launched(st, mk);
 }
 
 template <typename T, int WM, int WN, int MB, int NB, int KT, bool GRAM>
-hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const void* B, char* ws, hipStream_t st) {
+hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const void* B, char* ws, hipStream_t st, Marks& mk) {
   using C = GenK<T, WM, WN, MB, NB, KT>;
   const int64_t rows = GRAM ? p.r : p.d_out;
   const int64_t cols = GRAM ? p.ga_cols : (int64_t)p.n_nt * p.ntc;
   const int64_t grid = (GRAM ? p.xg : p.xw) * ceil_div64(rows, C::MT) * (cols / C::NTC);
   hipLaunchKernelGGL((norm_gen_kernel<T, WM, WN, MB, NB, KT, GRAM>), dim3((unsigned)grid), dim3(C::NT), 0, st, p,
                      static_cast<const T*>(M), static_cast<const T*>(A), static_cast<const T*>(B), ws);
-  return launched(st);
+  return launched(st, mk);
 }
 
 // H is the 16-bit storage type (bf16 or fp16); fp32 uses the F* configurations.
 template <int MODE, typename H>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
-                       char* ws, hipStream_t st) {
+                       char* ws, hipStream_t st, Marks& mk) {
   constexpr bool GRAM = MODE == kPassGram;
   const AssembleArgs aa{};
   // The Gram term inside the W pass needs the Gram matrix in the storage
@@ -1261,21 +1254,21 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
   if (p.fast) {
     // The Gram pass only uses the 64- and 128-column configurations.
     switch (fcfg) {
-      case kFastB64: return launch_fast<H, 4, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
-      case kFastB128: return launch_fast<H, 2, 4, 2, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st);
-      case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
-      case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st);
+      case kFastB64: return launch_fast<H, 4, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st, mk);
+      case kFastB128: return launch_fast<H, 2, 4, 2, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st, mk);
+      case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st, mk);
+      case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st, mk);
       default: break;
     }
     if constexpr (!GRAM) {
       switch (fcfg) {
-        case kFastT64: return launch_fast<H, 4, 2, 2, 1, 64, 3, MODE>(p, M, A, B, ws, aa, st);
-        case kFastT128: return launch_fast<H, 4, 2, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
-        case kFastB256: return launch_fast<H, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st);
-        case kFastT192: return launch_fast<H, 4, 2, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st);
+        case kFastT64: return launch_fast<H, 4, 2, 2, 1, 64, 3, MODE>(p, M, A, B, ws, aa, st, mk);
+        case kFastT128: return launch_fast<H, 4, 2, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st, mk);
+        case kFastB256: return launch_fast<H, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st, mk);
+        case kFastT192: return launch_fast<H, 4, 2, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st, mk);
         case kFastT256:
           if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
-          else return launch_fast<H, 4, 2, 2, 4, 64, 2, MODE>(p, M, A, B, ws, aa, st);
+          else return launch_fast<H, 4, 2, 2, 4, 64, 2, MODE>(p, M, A, B, ws, aa, st, mk);
         default: break;
       }
     }
@@ -1285,12 +1278,12 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
     return hipErrorInvalidValue;   // the general kernel never takes G or the Gram term in
   } else {
     switch (gcfg) {
-      case kGenB64: return launch_gen<H, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB128: return launch_gen<H, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenB256: return launch_gen<H, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenT192: return launch_gen<H, 4, 2, 2, 3, 64, GRAM>(p, M, A, B, ws, st);
-      case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st);
-      case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st);
+      case kGenB64: return launch_gen<H, 2, 2, 2, 1, 64, GRAM>(p, M, A, B, ws, st, mk);
+      case kGenB128: return launch_gen<H, 1, 4, 4, 1, 64, GRAM>(p, M, A, B, ws, st, mk);
+      case kGenB256: return launch_gen<H, 1, 4, 4, 2, 64, GRAM>(p, M, A, B, ws, st, mk);
+      case kGenT192: return launch_gen<H, 4, 2, 2, 3, 64, GRAM>(p, M, A, B, ws, st, mk);
+      case kGenF32: return launch_gen<float, 4, 1, 1, 1, 32, GRAM>(p, M, A, B, ws, st, mk);
+      case kGenF128: return launch_gen<float, 1, 4, 4, 1, 32, GRAM>(p, M, A, B, ws, st, mk);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1298,14 +1291,14 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
 
 template <int MODE>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
-                       char* ws, hipStream_t st) {
-  return p.dtype == 2 ? launch_pass<MODE, f16_t>(p, fcfg, gcfg, M, A, B, ws, st)
-                      : launch_pass<MODE, bf16_t>(p, fcfg, gcfg, M, A, B, ws, st);
+                       char* ws, hipStream_t st, Marks& mk) {
+  return p.dtype == 2 ? launch_pass<MODE, f16_t>(p, fcfg, gcfg, M, A, B, ws, st, mk)
+                      : launch_pass<MODE, bf16_t>(p, fcfg, gcfg, M, A, B, ws, st, mk);
 }
 
 template <typename T>
 hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, const float* m, float eps,
-                       float* wnorm, float* g, hipStream_t st) {
+                       float* wnorm, float* g, hipStream_t st, Marks& mk) {
   if (p.fast) {
     // Gram term on the matrix cores; with one column tile the assembly is
     // fused in, otherwise a small kernel adds the column-tile partials.
@@ -1313,41 +1306,42 @@ hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, cons
     hipError_t e;
     if constexpr (sizeof(T) == 2) {
       switch (p.bcfg) {
-        case 1: e = launch_fast<bf16_t, 2, 4, 1, 1, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st); break;
-        case 2: e = launch_fast<bf16_t, 2, 4, 1, 2, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st); break;
-        case 3: e = launch_fast<bf16_t, 2, 4, 1, 3, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st); break;
+        case 1: e = launch_fast<bf16_t, 2, 4, 1, 1, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st, mk); break;
+        case 2: e = launch_fast<bf16_t, 2, 4, 1, 2, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st, mk); break;
+        case 3: e = launch_fast<bf16_t, 2, 4, 1, 3, 64, 2, kPassBG>(p, B, nullptr, B, ws, aa, st, mk); break;
         default: return hipErrorInvalidValue;
       }
     } else {
-      e = launch_fast<float, 2, 4, 1, 1, 32, 2, kPassBG>(p, B, nullptr, B, ws, aa, st);
+      e = launch_fast<float, 2, 4, 1, 1, 32, 2, kPassBG>(p, B, nullptr, B, ws, aa, st, mk);
     }
     if (e != hipSuccess || p.n_bt == 1) return e;
-    return launch_assemble(p, ws, p.n_bt, s, m, eps, wnorm, g, st);
+    return launch_assemble(p, ws, p.n_bt, s, m, eps, wnorm, g, st, mk);
   }
   hipLaunchKernelGGL((gram_term_kernel<T>), dim3((unsigned)((p.d_out + kGramRows - 1) / kGramRows), (unsigned)p.n_cb),
                      dim3(kGramRows * 2), 0, st, p, static_cast<const T*>(B), ws);
-  hipError_t e = launched(st);
+  hipError_t e = launched(st, mk);
   if (e != hipSuccess) return e;
-  return launch_assemble(p, ws, p.n_cb, s, m, eps, wnorm, g, st);
+  return launch_assemble(p, ws, p.n_cb, s, m, eps, wnorm, g, st, mk);
 }
 
 }  // namespace
 
 hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A, const void* B, void* ws_,
                                 float s, const float* m, float eps, float* wnorm, float* g,
-                                hipStream_t st) {
+                                hipStream_t st, const hipEvent_t* events, int n_events) {
   char* ws = static_cast<char*>(ws_);
+  Marks mk{events, events != nullptr ? n_events : 0, 0};
   const bool fold = p.fast && p.gfold;
   // bf16 and fp32 on the streaming path run the Gram term in the W pass's
   // accumulators against (s/2) G; fp16 runs its Gram term in fp32 on B
   // widened, so it keeps the separate pass.
   const bool fuse = p.fast && !p.gfold && p.dtype != 2;
-  hipError_t e = begin_marks(st);
+  hipError_t e = begin_marks(mk, st);
   if (e != hipSuccess) return e;
   if (fold) {
-    e = launch_pass<kPassWG>(p, p.fcfg, p.gcfg, W, A, B, ws, st);   // W pass with G folded in
+    e = launch_pass<kPassWG>(p, p.fcfg, p.gcfg, W, A, B, ws, st, mk);   // W pass with G folded in
   } else {
-    e = launch_pass<kPassGram>(p, p.fcfg_g, p.gcfg_g, A, A, B, ws, st);   // Gram pass
+    e = launch_pass<kPassGram>(p, p.fcfg_g, p.gcfg_g, A, A, B, ws, st, mk);   // Gram pass
   }
   if (e != hipSuccess) return e;
   NormPlan q = p;
@@ -1357,35 +1351,37 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
                      dim3((unsigned)tri_count(p.rg / 32)), dim3(kReduceThreads), 0, st, q, ws,
                      fuse ? 0.5f * s : 1.0f);
-  e = launched(st);
+  e = launched(st, mk);
   if (e != hipSuccess) return e;
   if (fuse) {
     // W pass with the Gram term; its cross partials hold cross + (s/2) ba.
-    e = launch_pass<kPassWB>(p, p.fcfg, p.gcfg, W, A, B, ws, st);
+    e = launch_pass<kPassWB>(p, p.fcfg, p.gcfg, W, A, B, ws, st, mk);
     if (e != hipSuccess) return e;
-    return launch_assemble(p, ws, 0, s, m, eps, wnorm, g, st);
+    return launch_assemble(p, ws, 0, s, m, eps, wnorm, g, st, mk);
   }
   if (!fold) {
-    e = launch_pass<kPassW>(p, p.fcfg, p.gcfg, W, A, B, ws, st);   // W pass
+    e = launch_pass<kPassW>(p, p.fcfg, p.gcfg, W, A, B, ws, st, mk);   // W pass
     if (e != hipSuccess) return e;
   }
-  if (p.dtype == 0) return launch_tail<bf16_t>(p, B, ws, s, m, eps, wnorm, g, st);
+  if (p.dtype == 0) return launch_tail<bf16_t>(p, B, ws, s, m, eps, wnorm, g, st, mk);
   if (p.dtype == 2) {
     // fp16: the Gram term runs in fp32 on B widened (exactly) into the workspace.
     float* Bf = reinterpret_cast<float*>(ws + p.off_bf);
     const int64_t nB = p.d_out * p.r;
     hipLaunchKernelGGL(widen_kernel, dim3((unsigned)((nB + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
                        static_cast<const f16_t*>(B), nB, Bf);
-    e = launched(st);
+    e = launched(st, mk);
     if (e != hipSuccess) return e;
-    return launch_tail<float>(p, Bf, ws, s, m, eps, wnorm, g, st);
+    return launch_tail<float>(p, Bf, ws, s, m, eps, wnorm, g, st, mk);
   }
-  return launch_tail<float>(p, B, ws, s, m, eps, wnorm, g, st);
+  return launch_tail<float>(p, B, ws, s, m, eps, wnorm, g, st, mk);
 }
 
 hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t d_in, bool vec, const float* m,
-                               float eps, float* wnorm, float* g, hipStream_t st) {
-  const hipError_t e = begin_marks(st);
+                               float eps, float* wnorm, float* g, hipStream_t st, const hipEvent_t* events,
+                               int n_events) {
+  Marks mk{events, events != nullptr ? n_events : 0, 0};
+  const hipError_t e = begin_marks(mk, st);
   if (e != hipSuccess) return e;
   if (dtype == 0)
     hipLaunchKernelGGL((norm_rowonly_kernel<bf16_t>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
@@ -1396,12 +1392,7 @@ hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t 
   else
     hipLaunchKernelGGL((norm_rowonly_kernel<float>), dim3((unsigned)d_out), dim3(kThreads), 0, st,
                        static_cast<const float*>(W), d_in, vec, m, eps, wnorm, g);
-  return launched(st);
-}
-
-void set_launch_events(const hipEvent_t* events, int n) {
-  g_n_marks = n < kMaxLaunchEvents ? n : kMaxLaunchEvents;
-  for (int i = 0; i < g_n_marks; ++i) g_marks[i] = events[i];
+  return launched(st, mk);
 }
 
 hipError_t launch_magnitude(const float* m, const float* wnorm, float eps, int64_t n, float* g, hipStream_t st) {

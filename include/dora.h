@@ -25,8 +25,7 @@
  *     W [d_out, d_in], A [r, d_in], B [d_out, r]; activations [T, d_out].
  *   - Device pointers are device memory the caller owns (e.g. torch
  *     tensors). The library allocates nothing and never frees or retains
- *     a pointer. Its only state between calls is the optional benchmark
- *     hook of dora_set_launch_events.
+ *     a pointer. It keeps no mutable host state between calls.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is enqueued asynchronously on it; results are valid once
  *     the stream has reached that point.
@@ -108,9 +107,11 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
  * 1 if the streaming Gram pass computes only the tiles on and above the
  * diagonal of G, else 0, and 1 if the streaming W pass also runs the Gram
  * term (B G) . B in its own accumulators (bf16 and fp32 when G is not
- * folded in; no separate Gram-term pass), else 0, and the index of the W
- * pass among the call's launches (see dora_set_launch_events); the
- * streaming fields apply when W, A and B allow aligned 16-byte loads.
+ * folded in; no separate Gram-term pass), else 0, the index of the W
+ * pass among the call's launches (see dora_factored_norm_marked), and 1 if
+ * every operand tile of the streaming kernel spans less than 2^31 bytes
+ * (its 32-bit buffer offsets; otherwise the general kernel runs), else 0;
+ * the streaming fields apply when W, A and B allow aligned 16-byte loads.
  * Entries past the last field are set to -1.
  * Before returning it replays the plan on the host and checks that the
  * d_in ranges tile d_in exactly, every grid fits and every partial sum the
@@ -155,17 +156,16 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
                                void* stream);
 
 /*
- * Benchmark hook: HIP events recorded between the launches of later
- * dora_factored_norm calls, so that a caller can time each kernel of the
- * call on the call's own stream. events[0 .. n_events-1] are hipEvent_t
- * handles created, and later destroyed, by the caller (the library only
- * records them; destroy them only after clearing the hook). While set,
- * every dora_factored_norm call records events[0] on its stream before its
- * first launch and events[i] after its i-th launch, for i < n_events (at
- * most 8 are used); later launches are not marked, and null entries are
- * skipped (each recorded event adds a little time between launches, so a
- * caller that times one launch passes only the two events around it).
- * Launches of one call, in order:
+ * dora_factored_norm with timing marks: the same computation, arguments,
+ * results and errors, and in addition HIP events recorded on `stream`
+ * between the call's launches, so that a caller (a benchmark, a profiler)
+ * can time each kernel of the norm on its own. events[0 .. n_events-1] are
+ * hipEvent_t handles the caller created and owns; the call records
+ * events[0] before its first launch and events[i] after its i-th launch,
+ * for i < n_events (at most 8 are used); null entries are skipped (each
+ * recorded event adds a little time between launches, so a caller that
+ * times one launch passes only the two events around it). Nothing is kept
+ * after the call returns. Launches of one call, in order:
  *   bf16, fp32 (G not folded in): Gram pass, gram_reduce,
  *     W pass with the Gram term, assembly;
  *   G folded into the W pass (plan field gram_folded): W pass with G,
@@ -176,13 +176,14 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
  * (These are the streaming-path launches, used when W, A and B allow
  * aligned 16-byte loads; plan field w_launch is the W pass's index i, which
  * lies between events[i] and events[i+1].)
- * n_events == 0 clears the hook (events may then be NULL). The setting is
- * process-wide and unsynchronised: change it from one thread while no norm
- * call is being issued from another.
- * Errors: DORA_ERR_INVALID_ARG (n_events < 0, or events NULL with
- * n_events > 0).
+ * Errors: those of dora_factored_norm, and DORA_ERR_INVALID_ARG for
+ * n_events < 0 or events NULL with n_events > 0.
  */
-dora_status dora_set_launch_events(void* const* events, int n_events);
+dora_status dora_factored_norm_marked(const void* W, const void* A, const void* B, int dtype,
+                                      int64_t d_out, int64_t d_in, int64_t r, float s,
+                                      size_t budget_bytes, void* workspace, size_t workspace_bytes,
+                                      float* wnorm, const float* m, float eps, float* g,
+                                      void* stream, void* const* events, int n_events);
 
 /*
  * g[j] = m[j] / max(wnorm[j], eps), fp32, on the device (cyqw.cn §1.2.2:

@@ -206,14 +206,33 @@ def test_norm_to_dtype_argument_errors():
     assert lib.dora_norm_to_dtype(None, 0, 0, None, None) == 0               # nothing to do
 
 
-def test_launch_events_hook_arguments():
+def test_marked_norm_event_arguments():
+    """The timing variant refuses a negative event count or a missing event
+    array before doing anything else (argument errors return before launch)."""
     lib = bnd.load()
-    assert lib.dora_set_launch_events(None, -1) == 1
-    assert lib.dora_set_launch_events(None, 2) == 1
-    assert lib.dora_set_launch_events(None, 0) == 0            # clears the hook
-    bnd.dora_set_launch_events([])
-    with pytest.raises(ValueError):
-        bnd.dora_set_launch_events([0])                         # no handle
+    P = ctypes.c_void_p
+    args = (P(0x100000), P(0x200000), P(0x300000), 0, 64, 64, 8, 0.5, 1 << 28, P(0x400000), 1 << 20,
+            P(0x500000), None, 1e-6, None, None)
+    assert lib.dora_factored_norm_marked(*args, None, -1) == 1
+    assert lib.dora_factored_norm_marked(*args, None, 2) == 1
+    bad = list(args)
+    bad[4] = -1                                                 # negative d_out, no events
+    assert lib.dora_factored_norm_marked(*bad, None, 0) == 1
+
+
+def test_streaming_offsets_guard_uses_the_tallest_tile():
+    """The streaming kernel's 32-bit descriptor offsets: every operand tile
+    (the W pass's 256-row tiles included) must span less than 2^31 bytes,
+    else the general kernel runs. 256 rows x 5M bf16 elements is 2.56 GB."""
+    ok = bnd.dora_norm_plan_info(8192, 8192, 64, "bf16", 0.5)
+    assert ok["tile_rows"] == 256 and ok["offsets32"] == 1
+    big = bnd.dora_norm_plan_info(8192, 5 << 20, 64, "bf16", 0.5, budget_bytes=1 << 34)
+    assert big["tile_rows"] == 256 and big["offsets32"] == 0
+    # 128-row tiles: just under 4M elements fit (about 2^30 bytes); 8M (2^31 bytes) do not
+    edge = bnd.dora_norm_plan_info(4096, (1 << 22) - 64, 64, "bf16", 0.5, budget_bytes=1 << 34)
+    assert edge["tile_rows"] == 128 and edge["offsets32"] == 1
+    over = bnd.dora_norm_plan_info(4096, 1 << 23, 64, "bf16", 0.5, budget_bytes=1 << 34)
+    assert over["offsets32"] == 0
 
 
 def test_compose_backward_argument_errors_return_before_launch():

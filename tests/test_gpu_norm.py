@@ -68,9 +68,9 @@ CASES = [
 ]
 
 
-def _run(W, A, B, dtype, s, m=None, budget=256 << 20):
+def _run(W, A, B, dtype, s, m=None, budget=256 << 20, events=None):
     wn, g = bnd.dora_factored_norm(dev(W, dtype), dev(A, dtype), dev(B, dtype), s, budget_bytes=budget,
-                                   m=None if m is None else torch.from_numpy(m).cuda(), eps=EPS)
+                                   m=None if m is None else torch.from_numpy(m).cuda(), eps=EPS, events=events)
     torch.cuda.synchronize()
     return wn.cpu().numpy(), (None if g is None else g.cpu().numpy())
 
@@ -254,11 +254,7 @@ def test_launch_events_mark_each_launch():
     for e in evs:
         e.record()
     torch.cuda.synchronize()
-    bnd.dora_set_launch_events(evs)
-    try:
-        marked, _ = _run(W, A, B, "bf16", 0.5)
-    finally:
-        bnd.dora_set_launch_events([])
+    marked, _ = _run(W, A, B, "bf16", 0.5, events=evs)
     assert np.array_equal(plain.view(np.uint32), marked.view(np.uint32))
     # four launches: Gram pass, gram_reduce, W pass with the Gram term,
     # assembly; the sixth event is past the last launch and stays as it was
@@ -270,14 +266,14 @@ def test_launch_events_mark_each_launch():
     say(f"    launches (ms): {', '.join(f'{t:.4f}' for t in ms)}")
     # only the two marks around the W pass (null entries are skipped)
     before = evs[0].elapsed_time(evs[2])
-    bnd.dora_set_launch_events([None, None, evs[2], evs[3]])
-    try:
-        again, _ = _run(W, A, B, "bf16", 0.5)
-    finally:
-        bnd.dora_set_launch_events([])
+    again, _ = _run(W, A, B, "bf16", 0.5, events=[None, None, evs[2], evs[3]])
     assert np.array_equal(plain.view(np.uint32), again.view(np.uint32))
     assert evs[2].elapsed_time(evs[3]) > 0
     assert evs[0].elapsed_time(evs[2]) > before   # event 0 kept its old time
+    # nothing persists between calls: a later plain call records no event
+    before = evs[2].elapsed_time(evs[3])
+    _run(W, A, B, "bf16", 0.5)
+    assert evs[2].elapsed_time(evs[3]) == before
 
 
 def test_many_partials_per_row_deterministic():
@@ -344,3 +340,72 @@ def test_norm_cast_to_input_dtype():
     assert np.all(np.abs(got - ref) <= 0.5 * bf16_ulp(ref) + 1e-5 * ref)
     with pytest.raises(bnd.DoraError):
         bnd.dora_norm_to_dtype(wn, "bf16", out=wn.view(torch.bfloat16)[:d_out])   # overlaps wnorm
+
+
+def test_caller_buffers_are_checked_before_launch():
+    """Short, mistyped, strided or foreign-device output and workspace
+    buffers are refused by the binding before anything is launched."""
+    d_out, d_in, r = 96, 256, 16
+    W, A, B = (dev(x, "bf16") for x in I.norm_inputs(d_out, d_in, r, "bf16", 31))
+    m = torch.ones(d_out, dtype=torch.float32, device="cuda")
+    good_ws = bnd.dora_norm_workspace_size(d_out, d_in, r, "bf16", 0.5)
+    bad = [
+        dict(wnorm=torch.empty(d_out - 1, dtype=torch.float32, device="cuda")),
+        dict(wnorm=torch.empty(d_out, dtype=torch.bfloat16, device="cuda")),
+        dict(wnorm=torch.empty(2 * d_out, dtype=torch.float32, device="cuda")[::2]),
+        dict(wnorm=torch.empty(d_out, dtype=torch.float32)),
+        dict(m=m, g=torch.empty(d_out - 8, dtype=torch.float32, device="cuda")),
+        dict(m=m[:-1]),
+        dict(workspace=torch.empty(good_ws - 1, dtype=torch.uint8, device="cuda")),
+    ]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)):
+            bnd.dora_factored_norm(W, A, B, 0.5, **kw)
+    wn, _ = bnd.dora_factored_norm(W, A, B, 0.5)
+    with pytest.raises(ValueError):
+        bnd.dora_magnitude_scale(m, wn[:-1])
+    with pytest.raises(ValueError):
+        bnd.dora_magnitude_scale(m, wn, g=torch.empty(d_out, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        bnd.dora_norm_to_dtype(wn, "bf16", out=torch.empty(d_out, dtype=torch.float16, device="cuda"))
+    dy = torch.zeros(8, d_out, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        bnd.dora_compose_backward(dy, dy, dy, m, 0.5, d_base=torch.empty(7, d_out, dtype=torch.bfloat16,
+                                                                           device="cuda"))
+    with pytest.raises(ValueError):
+        bnd.dora_compose_backward(dy, dy, dy, m, 0.5, d_lora=torch.empty(8, d_out, dtype=torch.float32,
+                                                                           device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_side_stream_calls_match_oracle():
+    """The binding on a stream other than the current one: its workspace and
+    outputs belong to that stream, so the results are those of the oracle even
+    while the current stream allocates and writes memory meanwhile."""
+    d_out, d_in, r, s, T = 512, 2048, 384, 0.5, 256
+    W, A, B = I.norm_inputs(d_out, d_in, r, "bf16", 32)
+    ref = O.dense_row_norm(W, A, B, s)
+    m = (ref * (1.0 + I.G_SPREAD * I.m_noise(d_out, 32))).astype(np.float32)
+    Wd, Ad, Bd = dev(W, "bf16"), dev(A, "bf16"), dev(B, "bf16")
+    md = torch.from_numpy(m).cuda()
+    base, lora, _ = I.compose_inputs(T, d_out, "bf16", 32)
+    based, lorad = dev(base, "bf16"), dev(lora, "bf16")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        wn, g = bnd.dora_factored_norm(Wd, Ad, Bd, s, m=md, eps=EPS, stream=side)
+        out = bnd.dora_compose(based, lorad, g, s, stream=side)
+        # the current stream allocates and overwrites memory meanwhile
+        junk = torch.full((1 << 22,), 7.0, device="cuda")
+        junk.mul_(3.0)
+        outs.append((wn, g, out))
+    side.synchronize()
+    torch.cuda.synchronize()
+    for wn, g, out in outs:
+        check_norm(wn.cpu().numpy(), ref)
+        check_g(g.cpu().numpy(), m, wn.cpu().numpy())
+        want = O.bf16_round(O.compose(base, lora, g.cpu().numpy(), s))
+        got = out.float().cpu().numpy().astype(np.float64)
+        ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), 2.0 ** -126))[1] - 8)
+        assert np.all(np.abs(got - want) <= ulp)
