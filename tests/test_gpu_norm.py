@@ -404,7 +404,7 @@ def test_side_stream_calls_match_oracle():
     torch.cuda.synchronize()
     for wn, g, out in outs:
         check_norm(wn.cpu().numpy(), ref)
-        check_g(g.cpu().numpy(), m, wn.cpu().numpy())
+        check_g(g.cpu().numpy(), m, ref, EPS)
         want = O.bf16_round(O.compose(base, lora, g.cpu().numpy(), s))
         got = out.float().cpu().numpy().astype(np.float64)
         ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), 2.0 ** -126))[1] - 8)
