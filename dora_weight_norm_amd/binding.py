@@ -38,6 +38,8 @@ __all__ = [
     "dora_compose_backward",
     "dora_compose_backward_workspace_size",
     "dora_factored_norm_marked",
+    "dora_factored_norm_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdora.so")
@@ -46,6 +48,7 @@ DORA_BF16 = 0
 DORA_F32 = 1
 DORA_F16 = 2
 DEFAULT_BUDGET = 256 << 20
+NOALLOC_SCRATCH_BYTES = 32 << 20   # DORA_NOALLOC_SCRATCH_BYTES
 
 PLAN_FIELDS = (
     "mode", "tile_cols", "col_tiles", "gram_tile_cols", "gram_col_tiles", "fast_cfg", "gen_cfg",
@@ -91,6 +94,8 @@ def load():
                                       _c_p, _c_p, _c_f, _c_p, _c_p]),
         "dora_factored_norm_marked": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i64, _c_i64, _c_i64, _c_f, _c_sz, _c_p,
                                              _c_sz, _c_p, _c_p, _c_f, _c_p, _c_p, ctypes.POINTER(_c_p), _c_i]),
+        "dora_factored_norm_noalloc": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i64, _c_i64, _c_i64, _c_f, _c_sz, _c_p,
+                                              _c_p, _c_f, _c_p, _c_p]),
         "dora_magnitude_scale": (_c_i, [_c_p, _c_p, _c_f, _c_i64, _c_p, _c_p]),
         "dora_norm_to_dtype": (_c_i, [_c_p, _c_i64, _c_i, _c_p, _c_p]),
         "dora_compose": (_c_i, [_c_p, _c_p, _c_p, _c_f, _c_i, _c_i64, _c_i64, _c_p, _c_p]),
@@ -257,6 +262,40 @@ def dora_factored_norm_marked(W, A, B, s: float, events, **kw):
     (events[0] before the first, events[i] after the i-th; None entries
     skipped). Same keywords and results as dora_factored_norm."""
     return dora_factored_norm(W, A, B, s, events=list(events), **kw)
+
+
+def dora_factored_norm_noalloc(W, A, B, s: float, budget_bytes: int = DEFAULT_BUDGET, m=None, eps: float = 1e-6,
+                               wnorm=None, g=None, stream=None):
+    """dora_factored_norm with the library's per-GPU scratch array as its
+    workspace (the C call allocates nothing). wnorm and g may be passed in,
+    so that the call itself allocates nothing either. Returns (wnorm, g)."""
+    for t, nm in ((W, "W"), (A, "A"), (B, "B")):
+        _dev(t, nm)
+    if W.dim() != 2 or A.dim() != 2 or B.dim() != 2:
+        raise ValueError("W, A, B must be 2-D")
+    d_out, d_in = W.shape
+    r = A.shape[0]
+    if A.shape[1] != d_in or tuple(B.shape) != (d_out, r):
+        raise ValueError(f"shape mismatch: W {tuple(W.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if not (W.dtype == A.dtype == B.dtype):
+        raise TypeError("W, A, B must share one dtype")
+    if not (W.device == A.device == B.device):
+        raise ValueError("W, A, B must be on one device")
+    dev = W.device
+    if wnorm is not None:
+        _out_like(wnorm, "wnorm", (d_out,), torch.float32, dev)
+    if m is not None:
+        _out_like(m, "m", (d_out,), torch.float32, dev)
+        if g is not None:
+            _out_like(g, "g", (d_out,), torch.float32, dev)
+    with _on(stream):
+        if wnorm is None:
+            wnorm = torch.empty(d_out, dtype=torch.float32, device=dev)
+        if m is not None and g is None:
+            g = torch.empty(d_out, dtype=torch.float32, device=dev)
+        _call("dora_factored_norm_noalloc", _ptr(W), _ptr(A), _ptr(B), _dtype_code(W.dtype), d_out, d_in, r, s,
+              budget_bytes, _ptr(wnorm), _ptr(m), eps, _ptr(g) if m is not None else None, _stream(stream))
+    return wnorm, (g if m is not None else None)
 
 
 def dora_magnitude_scale(m, wnorm, eps: float = 1e-6, g=None, stream=None):

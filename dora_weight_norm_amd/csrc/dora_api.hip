@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "../../include/dora.h"
@@ -368,10 +369,57 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
 
 namespace {
 
+// Scratch memory of dora_factored_norm_noalloc: the norm's workspace for
+// callers that cannot allocate. Each GPU the library runs on holds its own
+// copy, at its own address, until the process ends. On the host this name
+// is only a stand-in for the symbol; host code uses the device address
+// that hipGetSymbolAddress returns, looked up once per device below.
+static __device__ __align__(256) char scratch[DORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+// Device address of `scratch` on each GPU, set by the first no-alloc call
+// on that GPU and never changed afterwards (concurrent first calls store
+// the same value).
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// The device address of `scratch` on the GPU that `stream` belongs to (the
+// current GPU for the null stream), looked up with that GPU current.
+dora_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return DORA_ERR_HIP;
+    dev = d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return DORA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DORA_ERR_HIP;
+  void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DORA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return DORA_ERR_HIP;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return DORA_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return DORA_ERR_HIP;
+    g_scratch_addr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return DORA_OK;
+}
+
+// The factored norm behind every norm entry point. With use_scratch the
+// workspace is this GPU's `scratch` (workspace and workspace_bytes are
+// ignored), looked up after every argument check has passed.
 dora_status factored_norm(const void* W, const void* A, const void* B, int dtype, int64_t d_out, int64_t d_in,
                           int64_t r, float s, size_t budget_bytes, void* workspace, size_t workspace_bytes,
                           float* wnorm, const float* m, float eps, float* g, void* stream, const hipEvent_t* events,
-                          int n_events) {
+                          int n_events, bool use_scratch = false) {
+  if (use_scratch) {
+    workspace = nullptr;
+    workspace_bytes = DORA_NOALLOC_SCRATCH_BYTES;
+    if (budget_bytes > DORA_NOALLOC_SCRATCH_BYTES) budget_bytes = DORA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;
   dora_status st = check_sizes(d_out, d_in, r);
   if (st != DORA_OK) return st;
@@ -413,6 +461,11 @@ dora_status factored_norm(const void* W, const void* A, const void* B, int dtype
     return hip_status(
         dora::launch_norm_rowonly(W, dtype, d_out, d_in, vec, m, eps, wnorm, gout ? g : nullptr, hs, events, n_events));
   }
+  if (use_scratch && p.ws_bytes > 0) {
+    // (`scratch` is its own allocation: it overlaps no caller buffer.)
+    st = scratch_address(hs, &workspace);
+    if (st != DORA_OK) return st;
+  }
   if (workspace_bytes < p.ws_bytes) return DORA_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && (workspace == nullptr || !aligned(workspace, kAlign))) return DORA_ERR_WORKSPACE;
   p.vec_b = aligned(B, 16) && (r % epc(dtype)) == 0;
@@ -430,6 +483,13 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
                                void* stream) {
   return factored_norm(W, A, B, dtype, d_out, d_in, r, s, budget_bytes, workspace, workspace_bytes, wnorm, m, eps,
                        g, stream, nullptr, 0);
+}
+
+dora_status dora_factored_norm_noalloc(const void* W, const void* A, const void* B, int dtype, int64_t d_out,
+                                       int64_t d_in, int64_t r, float s, size_t budget_bytes, float* wnorm,
+                                       const float* m, float eps, float* g, void* stream) {
+  return factored_norm(W, A, B, dtype, d_out, d_in, r, s, budget_bytes, nullptr, 0, wnorm, m, eps, g, stream, nullptr,
+                       0, true);
 }
 
 dora_status dora_factored_norm_marked(const void* W, const void* A, const void* B, int dtype, int64_t d_out,

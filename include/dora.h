@@ -25,7 +25,9 @@
  *     W [d_out, d_in], A [r, d_in], B [d_out, r]; activations [T, d_out].
  *   - Device pointers are device memory the caller owns (e.g. torch
  *     tensors). The library allocates nothing and never frees or retains
- *     a pointer. It keeps no mutable host state between calls.
+ *     a pointer. Its only host state is the device address of the
+ *     dora_factored_norm_noalloc scratch array on each GPU, looked up once
+ *     per GPU and never changed.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is enqueued asynchronously on it; results are valid once
  *     the stream has reached that point.
@@ -184,6 +186,36 @@ dora_status dora_factored_norm_marked(const void* W, const void* A, const void* 
                                       size_t budget_bytes, void* workspace, size_t workspace_bytes,
                                       float* wnorm, const float* m, float eps, float* g,
                                       void* stream, void* const* events, int n_events);
+
+/*
+ * Bytes of the device scratch array behind dora_factored_norm_noalloc: the
+ * largest norm workspace that entry point can use (32 MiB per GPU).
+ */
+#define DORA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * dora_factored_norm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments, results and errors, except
+ * that there is no workspace argument. The workspace is a library-owned
+ * array of DORA_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, held
+ * until the process ends; the call allocates nothing (no hipMalloc, no
+ * library allocator). The plan is made under min(budget_bytes,
+ * DORA_NOALLOC_SCRATCH_BYTES); a shape whose least parallel plan needs more
+ * returns DORA_ERR_BUDGET before anything is enqueued. With the same plan
+ * the results are bitwise those of dora_factored_norm. The scratch keeps
+ * the last call's partial sums; every call overwrites what it reads, so
+ * nothing needs clearing between calls. All calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (on different streams, or
+ * from different threads without ordering) race and give wrong results;
+ * order them, e.g. on one stream. The first call on each GPU looks up the
+ * array's device address (hipGetSymbolAddress, that GPU current); later
+ * calls reuse it.
+ */
+dora_status dora_factored_norm_noalloc(const void* W, const void* A, const void* B, int dtype,
+                                       int64_t d_out, int64_t d_in, int64_t r, float s,
+                                       size_t budget_bytes, float* wnorm, const float* m, float eps,
+                                       float* g, void* stream);
 
 /*
  * g[j] = m[j] / max(wnorm[j], eps), fp32, on the device (cyqw.cn §1.2.2:
