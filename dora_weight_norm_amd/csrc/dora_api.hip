@@ -40,9 +40,11 @@ constexpr int64_t kMaxRank = (int64_t)1 << 16;
 
 // Column tiling over r and the kernel configurations of both passes. Up to
 // r = 256 the W pass takes all of r in one column tile (64, 128 or 256
-// columns); above, it takes 256-row tiles of 192 or 256 columns (whichever
-// pads r less), whose column tiles of one row tile run on one die, so W is
-// still read from HBM about once. 256-row tiles need fewer loads per MFMA
+// columns); above, tall matrices take 256 x 384 tiles (eight waves of
+// 128 x 96 accumulators) up to r = 768 where they pad r no more than
+// 192-column tiles do, and otherwise 256-row tiles of 192 or 256 columns
+// (whichever pads r less). The column tiles of one row tile run on one die,
+// so W is still read from HBM about once. 256-row tiles need fewer loads per MFMA
 // than 128-row ones, but with r <= 256 they halve the workgroups per d_in
 // range, so the d_in split goes twice as fine and each workgroup gets half
 // the stages. Their saving outweighs the fixed cost of the shorter ranges
@@ -71,6 +73,8 @@ void choose_tiles(NormPlan& p) {
       p.ntc = 128, p.fcfg = tall ? dora::kFastT128 : dora::kFastB128, p.gcfg = dora::kGenB128;
     } else if (r <= 256) {
       p.ntc = 256, p.fcfg = tall ? dora::kFastT256 : dora::kFastB256, p.gcfg = dora::kGenB256;
+    } else if (tall && (r <= 384 || (r <= 768 && ceil_div(r, 384) * 384 <= ceil_div(r, 192) * 192))) {
+      p.ntc = 384, p.fcfg = dora::kFastT384, p.gcfg = dora::kGenT192;
     } else if (r <= 384 || ceil_div(r, 192) * 192 <= ceil_div(r, 256) * 256) {
       p.ntc = 192, p.fcfg = dora::kFastT192, p.gcfg = dora::kGenT192;
     } else {
@@ -83,8 +87,16 @@ void choose_tiles(NormPlan& p) {
     }
     p.gran = 64;
   }
+  p.ntc_gen = p.fcfg == dora::kFastT384 ? 192 : p.ntc;
   p.n_nt = (int)ceil_div(r, p.ntc);
   p.n_nt_g = (int)ceil_div(r, p.ntc_g);
+}
+
+// Column tiles of the W pass on either kernel: the cross partials are laid
+// out for the larger count.
+int64_t cross_tiles(const NormPlan& p) {
+  const int64_t gen = ceil_div(p.r, p.ntc_gen);
+  return p.n_nt > gen ? p.n_nt : gen;
 }
 
 // Gram partial planes the workspace holds: the Gram pass writes xg, the W
@@ -100,7 +112,7 @@ void layout(NormPlan& p) {
   p.off_base = off;
   off = align_up(off + (size_t)((int64_t)p.xw * p.ld_w) * 4, kAlign);
   p.off_cross = off;
-  off = align_up(off + (size_t)((int64_t)p.xw * p.n_nt * p.ld_w) * 4, kAlign);
+  off = align_up(off + (size_t)((int64_t)p.xw * cross_tiles(p) * p.ld_w) * 4, kAlign);
   p.off_ba = off;
   off = align_up(off + (size_t)(ba_planes(p) * p.ld_w) * 4, kAlign);
   p.off_g = off;
@@ -470,6 +482,12 @@ dora_status factored_norm(const void* W, const void* A, const void* B, int dtype
   if (p.ws_bytes > 0 && (workspace == nullptr || !aligned(workspace, kAlign))) return DORA_ERR_WORKSPACE;
   p.vec_b = aligned(B, 16) && (r % epc(dtype)) == 0;
   p.fast = aligned(W, 16) && aligned(A, 16) && (d_in % epc(dtype)) == 0 && p.vec_b && offsets_fit_32(p);
+  if (!p.fast && p.ntc != p.ntc_gen) {
+    // The general kernel's own column tiling (the layout holds its partials).
+    p.ntc = p.ntc_gen;
+    p.n_nt = (int)ceil_div(r, p.ntc);
+    if (!plan_self_check(p)) return DORA_ERR_INVALID_ARG;
+  }
   return hip_status(dora::launch_norm_factored(p, W, A, B, workspace, s, m, eps, wnorm, g, hs, events, n_events));
 }
 

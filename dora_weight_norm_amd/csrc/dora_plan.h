@@ -36,11 +36,13 @@ enum FastCfg : int {
   kFastF128 = 6,   // fp32, 128 x 128, 8 waves
   kFastT64 = 7,    // bf16, 256 x 64, 8 waves
   kFastT128 = 8,   // bf16, 256 x 128, 8 waves
+  kFastT384 = 9,   // bf16, 256 x 384, 8 waves of 128 x 96 (lean register mode)
 };
 // Rows per workgroup tile, and waves per workgroup, of a streaming
 // configuration.
 DORA_HD int fast_rows(int cfg) {
-  return cfg == kFastT64 || cfg == kFastT128 || cfg == kFastT192 || cfg == kFastT256 ? 256 : 128;
+  return cfg == kFastT64 || cfg == kFastT128 || cfg == kFastT192 || cfg == kFastT256 || cfg == kFastT384 ? 256
+                                                                                                       : 128;
 }
 DORA_HD int fast_waves(int cfg) { return cfg == kFastF32 ? 4 : 8; }
 constexpr int kGramCols = 64;      // columns of G per Gram-term tile (general kernel)
@@ -90,6 +92,8 @@ struct NormPlan {
   int dtype;            // 0 = bf16, 1 = fp32, 2 = fp16
   int mode;             // NormMode
   int ntc;              // W pass: columns of one column tile (a multiple of 32)
+  int ntc_gen;          // W pass: column tile width of the general kernel (the streaming
+                        // 384-column tile falls back to 192-column general tiles)
   int n_nt;             // W pass: column tiles over r
   int fcfg;             // W pass: FastCfg used when the inputs allow 16-byte loads
   int gcfg;             // W pass: TileCfg used otherwise

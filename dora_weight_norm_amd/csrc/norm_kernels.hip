@@ -114,14 +114,24 @@ struct FastK {
   static constexpr int WB = NBUF * RW;           // bytes of a wave's region
   static constexpr int WPS = SLOT / WB;          // waves staging B in one ring slot
   static constexpr int WX = NW > WPS * NS ? NW - WPS * NS : 0;   // waves staging B past the ring
-  static constexpr int REDB = WN * MT * 4;      // bytes of the epilogue's per-row sums
+  static constexpr int REDB = 2 * WN * MT * 4;  // bytes of the epilogue's per-row sums (cross, base)
+  // Lean register mode, for waves of 12 or more accumulator blocks (the
+  // 256 x 384 tile: 192 accumulators per lane at two waves per SIMD, so at
+  // most 64 registers for everything else): one set of fragments instead
+  // of two, load offsets formed at each load from one per-lane register per
+  // row length, and the epilogue's row sums kept at the end of the last ring
+  // slot (past the B staging regions of the waves that use that slot).
+  static constexpr bool LEAN = MB * NB >= 12;
+  static constexpr int LAST_WAVES = NW > WPS * (NS - 1) ? NW - WPS * (NS - 1) : 0;   // waves staging B in the last slot
+  static_assert(!LEAN || (WX == 0 && LAST_WAVES * WB + REDB <= SLOT), "lean: row sums fit the last slot");
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(CPR == 8 || CPR == 4, "LDS rows are 64 or 128 bytes");
   static_assert(KSTEPS * 2 * FC == CPR, "K16 steps cover the stage");
   static_assert(SLOT % (1024 * NW) == 0 && MBLK % NW == 0, "a stage splits evenly over the waves");
   static_assert(RW % 1024 == 0 && RBB % 16 == 0, "B stages in whole 1 KiB blocks");
   static_assert(WPS >= 1, "a wave's B fits one ring slot");
-  static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + REDB <= 160 * 1024, "gfx950 has 160 KiB of LDS");
+  static_assert(NS >= 2 && NS <= 4 && NS * SLOT + WX * WB + (LEAN ? 0 : REDB) <= 160 * 1024,
+                "gfx950 has 160 KiB of LDS");
   static_assert(BPW * (NS - 1) < 64 && LPR < 64, "outstanding loads fit vmcnt");
   static_assert(KSTEPS % 2 == 0, "fragment buffers alternate within a stage");
 };
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   __shared__ __attribute__((aligned(1024))) char r2[NS > 2 ? C::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) char r3[NS > 3 ? C::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) char bx[(!GRAM && C::WX > 0) ? C::WX * C::WB : 16];
-  __shared__ float red[GRAM ? 1 : WN * MT];
+  __shared__ float red_arr[(GRAM || C::LEAN) ? 1 : 2 * WN * MT];
   // Slot j of the ring (j < NS); slots past NS are never named, so their
   // placeholder arrays take no LDS.
   auto ring = [&](int j) __attribute__((always_inline)) -> char* {
@@ -255,6 +265,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       return j == 0 ? r0 : (j == 1 ? r1 : (j == 2 ? r2 : r3));
     }
   };
+  // The epilogue's per-row sums of each column group, [WN][MT] for the
+  // cross term and [WN][MT] for the base term: their own array, or in lean
+  // mode the end of the last ring slot.
+  float* const red = C::LEAN ? reinterpret_cast<float*>(ring(NS - 1) + C::SLOT - C::REDB) : red_arr;
+  float* const red_base = red + WN * MT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -335,15 +350,31 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int a_chunk = fswz<CPR>(wave * RPB + l_row, lane % CPR);
   // Blocks b < BPW_M of every wave hold row-operand rows, the rest the
   // column operand's rows; doff for phase 1, eoff for phase 2.
-  uint32_t doff[BPW], eoff[BPW];
+  // (Lean mode keeps only the per-lane parts, one per row length, and adds
+  // each block's first row at the load.)
+  constexpr int BPW_ARR = C::LEAN ? 1 : BPW;
+  uint32_t doff[BPW_ARR], eoff[BPW_ARR];
+  if constexpr (!C::LEAN) {
 #pragma unroll
-  for (int b = 0; b < BPW; ++b) {
-    const int row = (b * NW + wave) * RPB + l_row;
-    doff[b] = b < C::BPW_M ? (uint32_t)row * m_rowb + (uint32_t)(a_chunk * 16)
-                           : (uint32_t)(row - MT) * n_rowb + (uint32_t)(a_chunk * 16);
-    eoff[b] = b < C::BPW_M ? (uint32_t)row * b_rowb + (uint32_t)(a_chunk * 16)
-                           : (uint32_t)(row - MT) * g_rowb + (uint32_t)(a_chunk * 16);
+    for (int b = 0; b < BPW; ++b) {
+      const int row = (b * NW + wave) * RPB + l_row;
+      doff[b] = b < C::BPW_M ? (uint32_t)row * m_rowb + (uint32_t)(a_chunk * 16)
+                             : (uint32_t)(row - MT) * n_rowb + (uint32_t)(a_chunk * 16);
+      eoff[b] = b < C::BPW_M ? (uint32_t)row * b_rowb + (uint32_t)(a_chunk * 16)
+                             : (uint32_t)(row - MT) * g_rowb + (uint32_t)(a_chunk * 16);
+    }
   }
+  // Lean mode: offset of block 0 for this lane, one per row length (W and
+  // A rows in phase 1 share d_in; B rows and Gram rows in phase 2), and the
+  // uniform step from one of the wave's blocks to the next (NW blocks of RPB
+  // rows). Block BPW_M, the column operand's first, starts at the same row
+  // of its operand as block 0 of the row operand (MBLK * RPB == MT).
+  const uint32_t base_m = (uint32_t)(wave * RPB + l_row) * m_rowb + (uint32_t)(a_chunk * 16);
+  const uint32_t base_b = (uint32_t)(wave * RPB + l_row) * b_rowb + (uint32_t)(a_chunk * 16);
+  const uint32_t base_g = (uint32_t)(wave * RPB + l_row) * g_rowb + (uint32_t)(a_chunk * 16);
+  const uint32_t step_m = (uint32_t)(NW * RPB) * m_rowb, step_b = (uint32_t)(NW * RPB) * b_rowb,
+                 step_g = (uint32_t)(NW * RPB) * g_rowb;
+  const int lane_k = a_chunk * EPC;   // this lane's first element within a stage's depth
 
   // Stage i of the tile into a ring slot. Stages past the tile (the loop
   // runs a whole number of unrolled groups) and chunks past the valid depth
@@ -355,6 +386,38 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     const int64_t ks = ph2 ? v0 + (int64_t)j * KT : k0 + (int64_t)i * KT;   // column-operand depth
     const int64_t km = (ph2 && ks >= p.rg) ? ks - p.rg : ks;              // row-operand depth
     const uint32_t kb_m = (uint32_t)((in ? km : 0) * ESZ), kb_n = (uint32_t)((in ? ks : 0) * ESZ);
+    if constexpr (C::LEAN) {
+      // Valid elements left in the operands' rows from this stage's depth
+      // (uniform; 0 past the tile), against which each lane's first element
+      // is compared in 32 bits. Gram rows are never short.
+      const int64_t lm = in ? (ph2 ? p.r : d_in) - km : 0;
+      const int64_t ln = in ? (ph2 ? (int64_t)KT : d_in - ks) : 0;
+      const int32_t rm = (int32_t)(lm < KT ? lm : KT), rn = (int32_t)(ln < KT ? ln : KT);
+      const bool okm = lane_k < rm, okn = lane_k < rn;
+      uint32_t vo = ph2 ? base_b : base_m;
+      asm volatile("" : "+v"(vo));   // formed per stage: no per-block offsets kept across the loop
+#pragma unroll
+      for (int b = 0; b < BPW; ++b) {
+        if (b == C::BPW_M) {
+          vo = ph2 ? base_g : base_m;
+          asm volatile("" : "+v"(vo));
+        }
+        void* dst = slot + (b * NW + wave) * 1024;
+        const uint32_t off = (b < C::BPW_M ? okm : okn) ? vo : kOob;
+        const int kb = (int)(b < C::BPW_M ? kb_m : kb_n);
+        if (b < C::BPW_M) {
+          const __amdgpu_buffer_rsrc_t rs = ph2 ? brs : mrs;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0,
+                                                   0);
+        } else {
+          const __amdgpu_buffer_rsrc_t rs = ph2 ? grs : ars;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0,
+                                                   0);
+        }
+        vo += b < C::BPW_M ? (ph2 ? step_b : step_m) : (ph2 ? step_g : step_m);
+      }
+      return;
+    }
     const bool ok_m = in && km + (int64_t)a_chunk * EPC < (ph2 ? p.r : d_in);
     const bool ok_n = in && (ph2 || ks + (int64_t)a_chunk * EPC < d_in);
 #pragma unroll
@@ -363,7 +426,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       // expression inside its argument list made hipcc's host pass drop the
       // kernel's launch stub.)
       void* dst = slot + (b * NW + wave) * 1024;
-      const uint32_t o = ph2 ? eoff[b] : doff[b];
+      const uint32_t o = ph2 ? eoff[b < BPW_ARR ? b : 0] : doff[b < BPW_ARR ? b : 0];
       const uint32_t off = (b < C::BPW_M ? ok_m : ok_n) ? o : kOob;
       const int kb = (int)(b < C::BPW_M ? kb_m : kb_n);
       if (b < C::BPW_M) {
@@ -406,7 +469,25 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // blocks of A.
   constexpr int NGF = GF ? 2 : 0;
   typedef u32x4 Frag[MB + NB + NGF][FC];
+  // Lean mode: every fragment of a lane sits in rows with the same swizzle
+  // ((lrow >> 1) & 7: the blocks start on multiples of 16 rows), so a step's
+  // addresses are one per-lane offset plus constants; it is formed at each
+  // step rather than kept per step and slot.
+  const uint32_t ysw = (uint32_t)(lgrp ^ ((lrow >> 1) & 7));
   auto read_step = [&](const char* slot, int s, Frag& F) __attribute__((always_inline)) {
+    if constexpr (C::LEAN) {
+      static_assert(FC == 1 && CPR == 8, "lean mode: 16-bit types, 128-byte LDS rows");
+      uint32_t y = ysw;
+      asm volatile("" : "+v"(y));
+      const uint32_t x = (((uint32_t)(2 * s)) ^ y) * 16u + (uint32_t)lrow * RB;
+      const char* rb = slot + wm * MB * 32 * RB + x;
+      const char* cb = slot + (MT + wn * NB * 32) * RB + x;
+#pragma unroll
+      for (int a = 0; a < MB; ++a) F[a][0] = *reinterpret_cast<const u32x4*>(rb + a * 32 * RB);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) F[MB + b][0] = *reinterpret_cast<const u32x4*>(cb + b * 32 * RB);
+      return;
+    }
 #pragma unroll
     for (int f = 0; f < FC; ++f) {
       const int c = s * 2 * FC + lgrp * FC + f;
@@ -423,23 +504,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       }
     }
   };
-  auto mfma_step = [&](const Frag& F, bool w_stage) __attribute__((always_inline)) {
+  auto mfma_step = [&](const Frag& F, bool w_stage, int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<T>::run(F[a], F[MB + b], acc[a][b]);
     if constexpr (GF) gacc = Mfma<T>::run(F[MB + NB], F[MB + NB + 1], gacc);
     if constexpr (WP) {
-      // Every wave squares its row fragments (straight-line code); only the
-      // waves of column group 0 store the sums. Rows of B (phase 2) are not
-      // part of the base term.
+      // The WN waves of a row group hold the same row fragments, so K16 step
+      // s is squared by column group s % WN alone (a wave-uniform branch);
+      // the epilogue adds the groups' sums. Rows of B (phase 2) are not part
+      // of the base term.
+      if (s % WN == wn) {
 #pragma unroll
-      for (int a = 0; a < MB; ++a)
+        for (int a = 0; a < MB; ++a)
 #pragma unroll
-        for (int f = 0; f < FC; ++f) {
-          const float q = chunk_sumsq(F[a][f], T());
-          sq[a] += (WB && !w_stage) ? 0.f : q;
-        }
+          for (int f = 0; f < FC; ++f) {
+            const float q = chunk_sumsq(F[a][f], T());
+            sq[a] += (WB && !w_stage) ? 0.f : q;
+          }
+      }
     }
   };
   // Pipeline. Stage j lives in ring slot j % NS. In stage i, K16 step s+1's
@@ -457,12 +541,39 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // larger ones keep the zero stage (their tail spilled).
   constexpr bool PEEL = NS == 2 && MB * NB <= 6;
   const int n_loop = PEEL ? (n_tot & ~1) : n_pad;   // stages the unrolled loop runs
-  Frag H[2];
+  Frag H[C::LEAN ? 1 : 2];
 #pragma unroll
   for (int j = 0; j < NS; ++j) issue(j, ring(j));
   wait_vm_lgkm0<(NS - 1) * BPW>();   // stage 0 complete; stages 1 .. NS-1 in flight
   barrier_keep_loads();
   read_step(ring(0), 0, H[0]);
+  if constexpr (C::LEAN) {
+    // One fragment set: step s's MFMAs, then step s+1's fragments into the
+    // same registers (the other wave of the SIMD keeps its matrix core busy
+    // meanwhile). After the last step of stage i every wave has read all of
+    // stage i: wait for stage i+1's loads, barrier, reload stage i's slot
+    // with stage i+NS, read stage i+1's first step.
+    for (int i0 = 0; i0 < n_pad; i0 += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int i = i0 + j;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_step(H[0], i < n_st, s);
+          __builtin_amdgcn_sched_barrier(0);
+          if (s + 1 < KSTEPS) {
+            read_step(ring(j), s + 1, H[0]);
+          } else {
+            wait_vm_lgkm0<(NS - 2) * BPW>();
+            barrier_keep_loads();
+            issue(i + NS, ring(j));
+            read_step(ring((j + 1) % NS), 0, H[0]);
+          }
+        }
+      }
+    }
+  } else
   for (int i0 = 0; i0 < n_loop; i0 += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -478,12 +589,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           read_step(ring((j + 1) % NS), 0, H[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(H[s & 1], i < n_st);
+        mfma_step(H[s & 1], i < n_st, s);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
-  if constexpr (PEEL) {
+  if constexpr (PEEL && !C::LEAN) {
     if (n_tot & 1) {
       // The odd last stage (slot 0): its loads landed and its first step's
       // fragments were read at the loop's last barrier.
@@ -492,7 +603,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       for (int s = 0; s < KSTEPS; ++s) {
         if (s + 1 < KSTEPS) read_step(ring(0), s + 1, H[(s + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(H[s & 1], i < n_st);
+        mfma_step(H[s & 1], i < n_st, s);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -521,13 +632,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       }
     }
     if constexpr (WP) {
-      // Base term (waves of column group 0): the two k-halves of each row
-      // live in lanes l and l+32.
-      float* part_base = reinterpret_cast<float*>(ws + p.off_base);
+      // Base term: each column group's sum over its K16 steps (the two
+      // k-halves of a row live in lanes l and l+32); the groups are added in
+      // order with the cross sums below.
 #pragma unroll
       for (int a = 0; a < MB; ++a) {
         const float qs = sq[a] + __shfl_xor(sq[a], 32, 64);
-        if (n == 0 && wn == 0 && lgrp == 0) part_base[(int64_t)x * p.ld_w + wrow0 + a * 32 + lrow] = qs;
+        if (lgrp == 0) red_base[wn * MT + wm * MB * 32 + a * 32 + lrow] = qs;
       }
     }
     // Dot each accumulator row with its B row over this wave's columns. B
@@ -604,6 +715,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
 #pragma unroll
         for (int gi = 0; gi < WN; ++gi) cs += red[gi * MT + tid];
         part[plane * p.ld_w + mrow0 + tid] = cs;
+        if constexpr (WP) {
+          if (n == 0) {
+            float bs = 0.f;
+#pragma unroll
+            for (int gi = 0; gi < WN; ++gi) bs += red_base[gi * MT + tid];
+            reinterpret_cast<float*>(ws + p.off_base)[(int64_t)x * p.ld_w + mrow0 + tid] = bs;
+          }
+        }
       }
     }
   }
@@ -1266,6 +1385,9 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
         case kFastT128: return launch_fast<H, 4, 2, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st, mk);
         case kFastB256: return launch_fast<H, 2, 4, 2, 2, 64, 3, MODE>(p, M, A, B, ws, aa, st, mk);
         case kFastT192: return launch_fast<H, 4, 2, 2, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st, mk);
+        case kFastT384:
+          if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
+          else return launch_fast<H, 2, 4, 4, 3, 64, 2, MODE>(p, M, A, B, ws, aa, st, mk);
         case kFastT256:
           if constexpr (MODE == kPassWG) return hipErrorInvalidValue;   // never planned
           else return launch_fast<H, 4, 2, 2, 4, 64, 2, MODE>(p, M, A, B, ws, aa, st, mk);
@@ -1424,6 +1546,7 @@ size_t fast_kernel_lds_bytes(int cfg) {
     case kFastT128: return DORA_LDS(3, bf16_t, 4, 2, 2, 2, 64);
     case kFastT192: return DORA_LDS(2, bf16_t, 4, 2, 2, 3, 64);
     case kFastT256: return DORA_LDS(2, bf16_t, 4, 2, 2, 4, 64);
+    case kFastT384: return (size_t)FastK<bf16_t, 2, 4, 4, 3, 64, 2>::SLOT * 2;   // row sums inside the ring
     case kFastF32: return DORA_LDS(4, float, 4, 1, 1, 1, 32);
     case kFastF128: return DORA_LDS(4, float, 2, 4, 2, 1, 32);
     default: return 0;

@@ -65,6 +65,18 @@ CASES = [
     ("tall_r40_folded", 8000, 8192, 40, "bf16", 0.5, 33),
     ("tall_r128_folded", 7950, 8256, 128, "bf16", -0.75, 34),
     ("f16_tall_r64_folded", 8000, 8192, 64, "f16", 0.5, 35),
+    # 256 x 384 tiles (all of r = 257 .. 384 in one column tile, eight waves
+    # of 128 x 96 accumulators, eight d_in ranges): whole matrices, with a
+    # ragged last row tile, a ragged d_in and r short of the tile
+    ("tall_r384", 8192, 8192, 384, "bf16", 0.5, 36),
+    ("tall_r296_ragged", 8000, 8256, 296, "bf16", -0.5, 37),
+    ("tall_r264", 7950, 8192, 264, "bf16", 0.25, 38),
+    # the same plans on the general kernel (r % 8 != 0, d_in % 8 != 0): it
+    # keeps its own 192-column tiles, whose partials the layout also holds
+    ("tall_r300_general", 8000, 8256, 300, "bf16", -0.5, 39),
+    ("tall_r384_general", 8000, 8193, 384, "bf16", 0.5, 41),
+    # two 384-column tiles (384 < r <= 768), the second one ragged
+    ("tall_r696_two_col_tiles", 8000, 8192, 696, "bf16", 0.25, 42),
 ]
 
 
@@ -130,6 +142,10 @@ GRAM_ALONE = [
     ("r200_f32_neg_s", 300, 512, 200, "f32", -0.75),
     # folded Gram blocks in 256-row tiles (r rounds up to 128 for the Gram term)
     ("tall_r72_folded", 8000, 8192, 72, "bf16", 0.5),
+    # the 256 x 384 tile: 12 stages of Gram-term depth over 8 d_in ranges
+    ("tall_r384", 8192, 8192, 384, "bf16", 0.5),
+    ("tall_r320_ragged", 7950, 8256, 320, "bf16", -0.25),
+    ("tall_r768_two_col_tiles", 8192, 8192, 768, "bf16", 0.25),
 ]
 
 
