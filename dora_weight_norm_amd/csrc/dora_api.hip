@@ -121,6 +121,8 @@ void layout(NormPlan& p) {
   off = align_up(off + (size_t)(p.rg * p.rg) * 4, kAlign);   // bf16 hi and lo, or fp32
   p.off_bf = off;
   if (p.dtype == DORA_F16) off = align_up(off + (size_t)(p.d_out * p.r) * 4, kAlign);   // B widened to fp32
+  p.off_cnt = off;
+  off = align_up(off + (size_t)ceil_div(p.d_out, dora::fast_rows(p.fcfg)) * 4, kAlign);   // arrival counters
   p.ws_bytes = off;
 }
 
@@ -271,7 +273,8 @@ bool plan_self_check(const NormPlan& p) {
   if (p.off_g < p.off_ba + (size_t)(ba_planes(p) * p.ld_w) * 4) return false;
   if (p.off_gg < p.off_g + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4) return false;
   if (p.off_bf < p.off_gg + (size_t)(p.rg * p.rg) * 4) return false;
-  return p.ws_bytes >= p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.r) * 4 : 0);
+  if (p.off_cnt < p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.r) * 4 : 0)) return false;
+  return p.ws_bytes >= p.off_cnt + (size_t)ceil_div(p.d_out, fw) * 4;
 }
 
 // The streaming kernel addresses every operand tile through a buffer

@@ -125,6 +125,8 @@ struct NormPlan {
   size_t off_g;         // [max(xg, xw if gfold)][ga_rows][ga_cols] fp32 Gram partials
   size_t off_gg;        // reduced Gram matrix: bf16 [rg][Ghi | Glo], fp32 [rg][rg]
   size_t off_bf;        // fp16 inputs only: B widened to fp32 [d_out][r] for the Gram term
+  size_t off_cnt;       // [row tiles of the W pass] uint32 arrival counters (assembly in the W pass)
+  int asm_fused;        // set per call: the W pass with the Gram term also assembles wnorm and g
   size_t ws_bytes;
 };
 

@@ -724,6 +724,32 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           }
         }
       }
+      if constexpr (WB) {
+        if (p.asm_fused) {
+          // The row tile's last workgroup to finish assembles its rows
+          // (nobody waits). Each wave's partial stores complete, then one
+          // thread counts this workgroup in with release ordering at device
+          // scope (the die's L2 is written back, so the partials are visible
+          // on every die); the workgroup that brings the count to the row
+          // tile's total takes an acquire fence and sums every partial of
+          // its rows in the fixed plane order. The counters were zeroed by
+          // the reduction launched before this pass.
+          __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores have completed
+          __syncthreads();
+          int* last = reinterpret_cast<int*>(red);   // the row sums are consumed
+          if (tid == 0) {
+            unsigned* cnt = reinterpret_cast<unsigned*>(ws + p.off_cnt) + m;
+            const unsigned total = (unsigned)(X * n_nt);
+            const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            const int is_last = old + 1u == total;
+            if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            *last = is_last;
+          }
+          __syncthreads();
+          if (*last != 0 && tid < MT && mrow0 + tid < p.d_out)
+            assemble_row(p, ws, aa.s, aa.eps, aa.m, aa.wnorm, aa.g, mrow0 + tid, 0.f);
+        }
+      }
     }
   }
 }
@@ -1015,6 +1041,12 @@ __global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p,
   constexpr int RG = kReduceThreads / 32;   // row groups; each thread owns 32 / RG rows
   constexpr int RPT = 32 / RG;
   __shared__ float tile[32][33];
+  if (p.asm_fused && blockIdx.x == 0) {
+    // arrival counters of the W pass that follows (which assembles)
+    unsigned* cnt = reinterpret_cast<unsigned*>(ws + p.off_cnt);
+    const int64_t n_mt = (p.d_out + fast_rows(p.fcfg) - 1) / fast_rows(p.fcfg);
+    for (int64_t i = threadIdx.x; i < n_mt; i += kReduceThreads) cnt[i] = 0u;
+  }
   int bi, bj;
   tri_tile(blockIdx.x, (int)(p.rg / 32), &bi, &bj);
   const int c = threadIdx.x % 32, grp = threadIdx.x / 32;
@@ -1364,9 +1396,8 @@ hipError_t launch_gen(const NormPlan& p, const void* M, const void* A, const voi
 // H is the 16-bit storage type (bf16 or fp16); fp32 uses the F* configurations.
 template <int MODE, typename H>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
-                       char* ws, hipStream_t st, Marks& mk) {
+                       char* ws, hipStream_t st, Marks& mk, const AssembleArgs& aa = AssembleArgs{}) {
   constexpr bool GRAM = MODE == kPassGram;
-  const AssembleArgs aa{};
   // The Gram term inside the W pass needs the Gram matrix in the storage
   // type (bf16 hi + lo, or fp32); fp16 keeps it in fp32 and never plans it.
   if constexpr (MODE == kPassWB && sizeof(H) == 2 && !__is_same(H, bf16_t)) return hipErrorInvalidValue;
@@ -1413,9 +1444,9 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
 
 template <int MODE>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
-                       char* ws, hipStream_t st, Marks& mk) {
-  return p.dtype == 2 ? launch_pass<MODE, f16_t>(p, fcfg, gcfg, M, A, B, ws, st, mk)
-                      : launch_pass<MODE, bf16_t>(p, fcfg, gcfg, M, A, B, ws, st, mk);
+                       char* ws, hipStream_t st, Marks& mk, const AssembleArgs& aa = AssembleArgs{}) {
+  return p.dtype == 2 ? launch_pass<MODE, f16_t>(p, fcfg, gcfg, M, A, B, ws, st, mk, aa)
+                      : launch_pass<MODE, bf16_t>(p, fcfg, gcfg, M, A, B, ws, st, mk, aa);
 }
 
 template <typename T>
@@ -1468,6 +1499,7 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   if (e != hipSuccess) return e;
   NormPlan q = p;
   if (fold) q.xg = p.xw;   // one Gram partial per W-pass range
+  q.asm_fused = fuse ? 1 : 0;   // the reduction zeroes the W pass's arrival counters
   // bf16 keeps G as bf16 hi + lo for the bf16 Gram term; fp32 and fp16 keep
   // it in fp32 (fp16's range cannot hold every G) for the fp32 Gram term.
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
@@ -1476,10 +1508,11 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   e = launched(st, mk);
   if (e != hipSuccess) return e;
   if (fuse) {
-    // W pass with the Gram term; its cross partials hold cross + (s/2) ba.
-    e = launch_pass<kPassWB>(p, p.fcfg, p.gcfg, W, A, B, ws, st, mk);
-    if (e != hipSuccess) return e;
-    return launch_assemble(p, ws, 0, s, m, eps, wnorm, g, st, mk);
+    // W pass with the Gram term; its cross partials hold cross + (s/2) ba,
+    // and the last workgroup of each row tile assembles wnorm and g.
+    NormPlan pw = p;
+    pw.asm_fused = 1;
+    return launch_pass<kPassWB>(pw, p.fcfg, p.gcfg, W, A, B, ws, st, mk, AssembleArgs{s, eps, m, wnorm, g});
   }
   if (!fold) {
     e = launch_pass<kPassW>(p, p.fcfg, p.gcfg, W, A, B, ws, st, mk);   // W pass
