@@ -178,10 +178,110 @@ def time_compose_backward(args, w, lib, bnd, I, based, lorad, g, wnorm, stream, 
     ms = float(np.median(rounds))
     nb = compose_bwd_bytes(w.T, w.d_out, esize)
     gbs = nb / (ms * 1e-3) / 1e9
+    eager_ms = eager_compose_backward_ms(args, w, based, lorad, g, dy, stream)
     return {"ms": ms, "rounds_ms": rounds, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": nb, "workspace_bytes": ws_bytes,
+            "eager_autograd_ms": eager_ms, "speedup_vs_eager": eager_ms / ms,
             "note": "d_base, d_lora, dg and dm in one C-ABI call (row-strip kernel + fixed-order column "
                     "reduction); timed separately, not part of the forward step"}
+
+
+def eager_compose_backward_ms(args, w, based, lorad, g, dy, stream):
+    """The eager baseline of the fused backward: PyTorch autograd through the
+    eager compose (g - 1) * base + g * (s * lora) in the storage dtype, with
+    base, lora and g (cast to the storage dtype) requiring gradients; only
+    the backward (torch.autograd.grad on a retained graph) is timed, like the
+    fused call it is set beside."""
+    import numpy as np
+    import torch
+
+    base = based.detach().requires_grad_(True)
+    lora = lorad.detach().requires_grad_(True)
+    gg = g.detach().to(based.dtype).requires_grad_(True)
+    out = (gg - 1) * base + gg * (w.s * lora)
+
+    def bwd():
+        return torch.autograd.grad(out, (base, lora, gg), dy, retain_graph=True)
+
+    for _ in range(2):
+        bwd()
+    torch.cuda.synchronize()
+    reps = max(3, min(args.steps, 20))
+    ms = float(np.median([_event_ms(bwd, reps, stream) for _ in range(3)]))
+    del out
+    return ms
+
+
+# The pages' norm-memory comparisons (cyqw.cn §1.3 Table 1 and the measured
+# 768 -> 241 MB under it, at d = 8192, r = 512, fp32, 256 MB budget; §3.3,
+# the 8192 x 28672 MoE-expert shape), as (name, d_out, d_in, r, dtype).
+PAGE_NORM_CONFIGS = [
+    ("square_8192x8192_r512_f32", 8192, 8192, 512, "f32"),
+    ("mlp_28672x8192_r512_bf16", 28672, 8192, 512, "bf16"),
+]
+
+
+def page_norm_comparisons(bnd, stream, seed=7):
+    """Peak allocator memory and time of three ways to get ||W + sBA||_row at
+    the pages' shapes, on synthetic seeded inputs (W, A ~ N(0, 1/d_in),
+    B ~ N(0, 0.02^2); s = 0.5; 256 MiB budget):
+
+    - dense: torch.linalg.norm(W + s * (B @ A), dim=1), the plain form;
+    - identity form: the adapter weight built by running the adapter on an
+      identity matrix, (I A^T) B^T, transposed and added to W, then the row
+      norm, as the pages describe PEFT doing it (cyqw.cn §1.1: an identity
+      matrix of d_in x d_in plus several dense temporaries);
+    - factored: dora_factored_norm (workspace and outputs included).
+
+    Peaks are torch.cuda.max_memory_allocated above what was resident before
+    the call."""
+    import numpy as np
+    import torch
+
+    out = []
+    for name, d_out, d_in, r, dt in PAGE_NORM_CONFIGS:
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        W = (torch.randn(d_out, d_in, device="cuda", generator=gen) / d_in ** 0.5).to(tdt)
+        A = (torch.randn(r, d_in, device="cuda", generator=gen) / d_in ** 0.5).to(tdt)
+        B = (torch.randn(d_out, r, device="cuda", generator=gen) * 0.02).to(tdt)
+        s, budget = 0.5, 256 << 20
+
+        def dense():
+            return torch.linalg.norm(W + s * (B @ A), dim=1)
+
+        def identity_form():
+            eye = torch.eye(d_in, dtype=tdt, device="cuda")
+            lora_w = (eye @ A.t()) @ B.t()            # [d_in, d_out]: the adapter applied to I
+            return torch.linalg.norm(W + s * lora_w.t(), dim=1)
+
+        def factored():
+            return bnd.dora_factored_norm(W, A, B, s, budget_bytes=budget)[0]
+
+        res = {"config": name, "d_out": d_out, "d_in": d_in, "r": r, "dtype": dt, "budget_MiB": budget >> 20}
+        vals = {}
+        for key, fn in (("dense", dense), ("identity_form", identity_form), ("factored", factored)):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base_mem = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            v = fn()
+            torch.cuda.synchronize()
+            res[f"{key}_peak_bytes"] = torch.cuda.max_memory_allocated() - base_mem
+            vals[key] = v.float()
+            del v
+            fn()
+            torch.cuda.synchronize()
+            res[f"{key}_ms"] = float(np.median([_event_ms(fn, 5, stream) for _ in range(3)]))
+        res["dense_over_factored_memory"] = res["dense_peak_bytes"] / max(res["factored_peak_bytes"], 1)
+        res["identity_form_over_factored_memory"] = res["identity_form_peak_bytes"] / max(res["factored_peak_bytes"], 1)
+        res["max_rel_diff_factored_vs_dense"] = float(((vals["factored"] - vals["dense"]).abs()
+                                                        / vals["dense"].abs()).max())
+        out.append(res)
+        del W, A, B, vals
+        torch.cuda.empty_cache()
+    return out
 
 
 def _event_ms(fn, reps, stream):
@@ -560,6 +660,13 @@ def main() -> int:
     if not args.no_comparisons:
         print("# comparisons: eager compose, dense norm", file=sys.stderr, flush=True)
         res["comparisons"] = comparisons(args, w, bnd, Wd, Ad, Bd, based, lorad, g, md, comp_ms, norm_ms, stream, tdt)
+        if "compose_backward" in res:
+            cb = res["compose_backward"]
+            res["comparisons"].update({"eager_compose_backward_ms": cb["eager_autograd_ms"],
+                                       "fused_compose_backward_ms": cb["ms"],
+                                       "compose_backward_speedup_vs_eager": cb["speedup_vs_eager"]})
+        print("# comparisons: norm memory at the pages' shapes", file=sys.stderr, flush=True)
+        res["comparisons"]["page_norm_memory"] = page_norm_comparisons(bnd, stream)
     if not args.no_linear:
         print("# whole DoRA linear layer", file=sys.stderr, flush=True)
         res["linear_forward"] = linear_forward(args, w, I, Wd, Ad, Bd, md, stream, tdt)
