@@ -1499,7 +1499,15 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   if (e != hipSuccess) return e;
   NormPlan q = p;
   if (fold) q.xg = p.xw;   // one Gram partial per W-pass range
-  q.asm_fused = fuse ? 1 : 0;   // the reduction zeroes the W pass's arrival counters
+  // The W pass assembles only when its workgroups run in one round and each
+  // row has at most one batch of partials: every workgroup then pays its
+  // release fence (a write-back of its die's L2, a few us of the CU's time)
+  // once, against the separate assembly launch it saves; over several rounds
+  // the fences add up, and with many partials per row one thread per row
+  // sums them too slowly.
+  const int64_t w_grid = (int64_t)p.xw * ((p.d_out + fast_rows(p.fcfg) - 1) / fast_rows(p.fcfg)) * p.n_nt;
+  const bool asm_in_w = fuse && w_grid <= kGrid && (int64_t)p.xw * p.n_nt <= kSumBatch;
+  q.asm_fused = asm_in_w ? 1 : 0;   // the reduction zeroes the W pass's arrival counters
   // bf16 keeps G as bf16 hi + lo for the bf16 Gram term; fp32 and fp16 keep
   // it in fp32 (fp16's range cannot hold every G) for the fp32 Gram term.
   hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
@@ -1509,10 +1517,13 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   if (e != hipSuccess) return e;
   if (fuse) {
     // W pass with the Gram term; its cross partials hold cross + (s/2) ba,
-    // and the last workgroup of each row tile assembles wnorm and g.
+    // and (asm_in_w) the last workgroup of each row tile assembles wnorm
+    // and g, else the assembly kernel follows.
     NormPlan pw = p;
-    pw.asm_fused = 1;
-    return launch_pass<kPassWB>(pw, p.fcfg, p.gcfg, W, A, B, ws, st, mk, AssembleArgs{s, eps, m, wnorm, g});
+    pw.asm_fused = asm_in_w ? 1 : 0;
+    e = launch_pass<kPassWB>(pw, p.fcfg, p.gcfg, W, A, B, ws, st, mk, AssembleArgs{s, eps, m, wnorm, g});
+    if (e != hipSuccess || asm_in_w) return e;
+    return launch_assemble(p, ws, 0, s, m, eps, wnorm, g, st, mk);
   }
   if (!fold) {
     e = launch_pass<kPassW>(p, p.fcfg, p.gcfg, W, A, B, ws, st, mk);   // W pass

@@ -169,7 +169,9 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
  * times one launch passes only the two events around it). Nothing is kept
  * after the call returns. Launches of one call, in order:
  *   bf16, fp32 (G not folded in): Gram pass, gram_reduce,
- *     W pass with the Gram term and the assembly;
+ *     W pass with the Gram term (and the assembly when the W pass runs
+ *     in one round of at most 256 workgroups with at most 16 partials per
+ *     row), assembly otherwise;
  *   G folded into the W pass (plan field gram_folded): W pass with G,
  *     gram_reduce, Gram term (+ assembly with several Gram-term tiles);
  *   fp16: Gram pass, gram_reduce, W pass, widening of B, Gram term
