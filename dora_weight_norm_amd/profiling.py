@@ -168,6 +168,7 @@ def main() -> int:
     traffic = {"norm": 0.0, "compose": 0.0, "compose_bwd": 0.0, "layer_output": 0.0}
     w_pass_bytes = None   # HBM bytes of one W-pass launch
     w_pass_mfma = None    # (executed MFMA flops, MFMA busy %) of one W-pass launch
+    w_pass_us = None      # the W-pass kernel's average duration
     lines = []
     for s in sorted(ours, key=lambda s: -s["total_us"]):
         role = kernel_role(s["name"])
@@ -180,6 +181,8 @@ def main() -> int:
             traffic[role] += (fb + wb) * per_step
             if role == "norm" and "(W pass" in short_name(s["name"]):
                 w_pass_bytes = fb + wb
+        if role == "norm" and "(W pass" in short_name(s["name"]):
+            w_pass_us = s["avg_us"]
         mcols = ""
         if args.mfma:
             mf, mu = mflops.get(s["name"]), mutil.get(s["name"])
@@ -204,6 +207,7 @@ def main() -> int:
           "fetch_scale": f_scale, "write_scale": w_scale,
           "compose_bwd_bytes_per_call": traffic["compose_bwd"],
           "w_pass_bytes_per_launch": w_pass_bytes,
+          "w_pass_us_per_launch": w_pass_us,
           "w_pass_mfma_flops_per_launch": w_pass_mfma[0] if w_pass_mfma else None,
           "w_pass_mfma_busy_pct": w_pass_mfma[1] if w_pass_mfma else None,
           "norm_us_per_call": norm_us, "compose_us_per_call": comp_us, "compose_bwd_us_per_call": bwd_us,
