@@ -376,10 +376,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
                  step_g = (uint32_t)(NW * RPB) * g_rowb;
   const int lane_k = a_chunk * EPC;   // this lane's first element within a stage's depth
 
-  // Stage i of the tile into a ring slot. Stages past the tile (the loop
-  // runs a whole number of unrolled groups) and chunks past the valid depth
-  // read as zeros, so every step issues the same loads.
-  auto issue = [&](int i, char* slot) __attribute__((always_inline)) {
+  // Blocks [b0, b1) of this wave's share of stage i into a ring slot.
+  // Stages past the tile (the loop runs a whole number of unrolled groups)
+  // and chunks past the valid depth read as zeros, so every step issues the
+  // same loads.
+  auto issue_blocks = [&](int i, char* slot, int b0, int b1) __attribute__((always_inline)) {
     const bool ph2 = BG || (WB && i >= n_st);       // uniform
     const int j = i - n_st;
     const bool in = ph2 ? j < n_bs : i < n_st;
@@ -394,14 +395,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       const int64_t ln = in ? (ph2 ? (int64_t)KT : d_in - ks) : 0;
       const int32_t rm = (int32_t)(lm < KT ? lm : KT), rn = (int32_t)(ln < KT ? ln : KT);
       const bool okm = lane_k < rm, okn = lane_k < rn;
-      uint32_t vo = ph2 ? base_b : base_m;
-      asm volatile("" : "+v"(vo));   // formed per stage: no per-block offsets kept across the loop
 #pragma unroll
       for (int b = 0; b < BPW; ++b) {
-        if (b == C::BPW_M) {
-          vo = ph2 ? base_g : base_m;
-          asm volatile("" : "+v"(vo));
-        }
+        if (b < b0 || b >= b1) continue;
+        // Block b starts whole steps of NW blocks past the operand's first
+        // block; the offset is formed at the load, none is kept across the
+        // loop.
+        uint32_t vo = b < C::BPW_M ? (ph2 ? base_b : base_m) + (uint32_t)b * (ph2 ? step_b : step_m)
+                                   : (ph2 ? base_g : base_m) + (uint32_t)(b - C::BPW_M) * (ph2 ? step_g : step_m);
+        asm volatile("" : "+v"(vo));
         void* dst = slot + (b * NW + wave) * 1024;
         const uint32_t off = (b < C::BPW_M ? okm : okn) ? vo : kOob;
         const int kb = (int)(b < C::BPW_M ? kb_m : kb_n);
@@ -414,7 +416,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, off, kb, 0,
                                                    0);
         }
-        vo += b < C::BPW_M ? (ph2 ? step_b : step_m) : (ph2 ? step_g : step_m);
       }
       return;
     }
@@ -422,6 +423,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     const bool ok_n = in && (ph2 || ks + (int64_t)a_chunk * EPC < d_in);
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
+      if (b < b0 || b >= b1) continue;
       // (Offsets are computed before the builtin call: a conditional
       // expression inside its argument list made hipcc's host pass drop the
       // kernel's launch stub.)
@@ -542,9 +544,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   constexpr bool PEEL = NS == 2 && MB * NB <= 6;
   const int n_loop = PEEL ? (n_tot & ~1) : n_pad;   // stages the unrolled loop runs
   Frag H[C::LEAN ? 1 : 2];
+  // Lean mode (two slots) spreads each stage's loads over the stage before
+  // it: the row-operand blocks (the HBM stream) right after the barrier
+  // that frees their slot, the column-operand blocks a few at a time after
+  // each of the first KSTEPS-1 steps' fragment reads. A wave stalls while
+  // the address unit takes a burst of load instructions, and with one
+  // fragment set the other wave of its SIMD cannot cover the stall.
+  constexpr bool SPREAD = C::LEAN && NS == 2;
+  constexpr int COL_PER_STEP = (BPW - C::BPW_M + KSTEPS - 2) / (KSTEPS - 1);
+  if constexpr (SPREAD) {
+    issue_blocks(0, ring(0), 0, BPW);
+    issue_blocks(1, ring(1), 0, C::BPW_M);
+    wait_vm_lgkm0<C::BPW_M>();   // stage 0 complete; stage 1's row-operand blocks in flight
+  } else {
 #pragma unroll
-  for (int j = 0; j < NS; ++j) issue(j, ring(j));
-  wait_vm_lgkm0<(NS - 1) * BPW>();   // stage 0 complete; stages 1 .. NS-1 in flight
+    for (int j = 0; j < NS; ++j) issue_blocks(j, ring(j), 0, BPW);
+    wait_vm_lgkm0<(NS - 1) * BPW>();   // stage 0 complete; stages 1 .. NS-1 in flight
+  }
   barrier_keep_loads();
   read_step(ring(0), 0, H[0]);
   if constexpr (C::LEAN) {
@@ -564,10 +580,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           __builtin_amdgcn_sched_barrier(0);
           if (s + 1 < KSTEPS) {
             read_step(ring(j), s + 1, H[0]);
+            if constexpr (SPREAD) {
+              // Column-operand blocks of stage i+1 (its slot was freed at
+              // the last barrier; its row-operand blocks went out then).
+              const int c0 = C::BPW_M + s * COL_PER_STEP;
+              const int c1 = c0 + COL_PER_STEP < BPW ? c0 + COL_PER_STEP : BPW;
+              __builtin_amdgcn_sched_barrier(0);
+              issue_blocks(i + 1, ring((j + 1) % NS), c0, c1);
+            }
           } else {
-            wait_vm_lgkm0<(NS - 2) * BPW>();
+            wait_vm_lgkm0<(NS - 2) * BPW>();   // (with two slots: every load issued so far)
             barrier_keep_loads();
-            issue(i + NS, ring(j));
+            if constexpr (SPREAD) {
+              issue_blocks(i + NS, ring(j), 0, C::BPW_M);
+            } else {
+              issue_blocks(i + NS, ring(j), 0, BPW);
+            }
             read_step(ring((j + 1) % NS), 0, H[0]);
           }
         }
@@ -585,7 +613,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
         } else {
           wait_vm_lgkm0<(NS - 2) * BPW>();
           barrier_keep_loads();
-          issue(i + NS, ring(j));
+          issue_blocks(i + NS, ring(j), 0, BPW);
           read_step(ring((j + 1) % NS), 0, H[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -680,15 +708,47 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       float pa[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) pa[v] = 0.f;
+      if constexpr (C::LEAN) {
+        // B's 32x32 block in the accumulator layout (row acc_row(v), column
+        // lrow), made by two MFMAs: the row-operand fragments are B's rows
+        // (16-byte reads of the staged rows, as for W), the column operand
+        // the 0/1 selector E_h with E_h[k][j] = 1 iff j = k + 16h. Each
+        // output is one product by 1.0, so the block is exact; eight 16-byte
+        // reads replace 64 two-byte reads per lane.
+        const uint32_t one = __is_same(T, bf16_t) ? 0x3F80u : 0x3C00u;
+        u32x4 E[2];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int col = b * 32 + lrow;
+        for (int h = 0; h < 2; ++h) {
+          const int e = lrow - 8 * lgrp - 16 * h;   // this lane's 1.0 sits at k-element e, if 0 <= e < 8
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = acc_row(v, lgrp);
-          const T bv = *reinterpret_cast<const T*>(buf + row * C::RBB + (((col / EPC) ^ (row & C::BSW)) * 16) +
-                                                   (col % EPC) * ESZ);
-          pa[v] = fmaf(acc[a][b][v], to_f32(bv), pa[v]);
+          for (int w = 0; w < 4; ++w) E[h][w] = (e == 2 * w ? one : 0u) | ((e == 2 * w + 1 ? one : 0u) << 16);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          u32x4 f[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            f[h] = *reinterpret_cast<const u32x4*>(buf + lrow * C::RBB +
+                                                   (((4 * b + 2 * h + lgrp) ^ (lrow & C::BSW)) * 16));
+          f32x16 bb32;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) bb32[v] = 0.f;
+          bb32 = Mfma<T>::run(&f[0], &E[0], bb32);
+          bb32 = Mfma<T>::run(&f[1], &E[1], bb32);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) pa[v] = fmaf(acc[a][b][v], bb32[v], pa[v]);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int col = b * 32 + lrow;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = acc_row(v, lgrp);
+            const T bv = *reinterpret_cast<const T*>(buf + row * C::RBB + (((col / EPC) ^ (row & C::BSW)) * 16) +
+                                                     (col % EPC) * ESZ);
+            pa[v] = fmaf(acc[a][b][v], to_f32(bv), pa[v]);
+          }
         }
       }
       const float tot = sum32_transpose(pa, lane);
