@@ -163,6 +163,33 @@ int choose_g_ranges(int64_t tiles, int64_t n_gran, int64_t plane_bytes, int max_
   return X;
 }
 
+// Dense mode (see NormMode): 16-bit inputs with r >= d_out, d_in and r in
+// whole 16-byte chunks, and every dense operand within a 32-bit buffer
+// descriptor (A whole, 64 rows of W or of B). Its partials share the
+// workspace with the factored layout, which stays valid as the fallback;
+// the workspace is the larger of the two.
+void plan_dense(NormPlan& p, size_t budget) {
+  if (p.mode != dora::kModeFactored || (p.dtype != DORA_BF16 && p.dtype != DORA_F16)) return;
+  if (p.r < p.d_out || p.d_in % 8 != 0 || p.r % 8 != 0) return;
+  const uint64_t lim = 1ull << 31;
+  if ((uint64_t)p.r * (uint64_t)p.d_in * 2u >= lim || (uint64_t)dora::kDenseRows * (uint64_t)p.d_in * 2u >= lim ||
+      (uint64_t)dora::kDenseRows * (uint64_t)p.r * 2u >= lim)
+    return;
+  const int64_t n_rt = ceil_div(p.d_out, dora::kDenseRows), n_ct = ceil_div(p.d_in, dora::kDenseCols);
+  const int64_t grid = n_rt * ceil_div(n_ct, dora::kDies) * dora::kDies;
+  if (grid >= lim) return;
+  const int64_t ld = ceil_div(p.d_out, 64) * 64;
+  const size_t bytes = (size_t)(ceil_div(n_ct * ld * 4, (int64_t)kAlign) * (int64_t)kAlign);
+  const size_t ws = bytes > p.ws_bytes ? bytes : p.ws_bytes;
+  if (ws > budget) return;
+  p.mode = dora::kModeDense;
+  p.dn_rt = (int)n_rt;
+  p.dn_ct = (int)n_ct;
+  p.ld_d = ld;
+  p.off_dense = 0;
+  p.ws_bytes = ws;
+}
+
 dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s, size_t budget,
                       NormPlan* out) {
   if (!valid_dtype(dtype)) return DORA_ERR_UNSUPPORTED_DTYPE;
@@ -232,6 +259,7 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
     p.xg = xg;
     layout(p);
     if (p.ws_bytes <= budget) {
+      plan_dense(p, budget);
       *out = p;
       return DORA_OK;
     }
@@ -249,7 +277,14 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
 // every grid fits, and every partial the kernels write lies inside its
 // workspace region.
 bool plan_self_check(const NormPlan& p) {
-  if (p.mode != dora::kModeFactored) return true;
+  if (p.mode != dora::kModeFactored && p.mode != dora::kModeDense) return true;
+  if (p.mode == dora::kModeDense) {
+    // Dense tiles cover d_out and d_in; the partials fit the workspace.
+    if (p.dn_rt < 1 || p.dn_ct < 1 || (int64_t)p.dn_rt * dora::kDenseRows < p.d_out ||
+        (int64_t)p.dn_ct * dora::kDenseCols < p.d_in || p.ld_d < p.d_out ||
+        p.ws_bytes < p.off_dense + (size_t)((int64_t)p.dn_ct * p.ld_d) * 4)
+      return false;
+  }
   for (int pass = 0; pass < 2; ++pass) {
     const int X = pass ? p.xg : p.xw;
     if (X < 1 || X > p.n_gran) return false;
@@ -285,7 +320,7 @@ bool plan_self_check(const NormPlan& p) {
 // d_in, and the Gram-term operands (B's rows by r, the stored Gram matrix's
 // rows by its width).
 bool offsets_fit_32(const NormPlan& p) {
-  if (p.mode != dora::kModeFactored) return true;
+  if (p.mode != dora::kModeFactored && p.mode != dora::kModeDense) return true;
   const uint64_t es = (uint64_t)esize(p.dtype);
   uint64_t rows = (uint64_t)dora::fast_rows(p.fcfg);
   const uint64_t others[] = {(uint64_t)p.ntc, (uint64_t)dora::fast_rows(p.fcfg_g), (uint64_t)p.ntc_g};
@@ -364,7 +399,7 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   const dora_status st = make_plan(d_out, d_in, r, dtype, s, budget_bytes, &p);
   if (st != DORA_OK) return st;
   if (!plan_self_check(p)) return DORA_ERR_INVALID_ARG;
-  const bool f = p.mode == dora::kModeFactored;
+  const bool f = p.mode == dora::kModeFactored || p.mode == dora::kModeDense;   // (dense: its fallback)
   const int64_t grid_w = f ? p.xw * ceil_div(p.d_out, dora::fast_rows(p.fcfg)) * p.n_nt : 0;
   const int64_t grid_g = !f ? 0
                              : p.xg * (p.gsym ? dora::tri_count(ceil_div(p.r, dora::kGramTile))
@@ -373,7 +408,8 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
                           f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0,
                           f ? p.gfold : 0, f ? p.gsym : 0, f ? (int64_t)(!p.gfold && p.dtype != DORA_F16) : 0,
-                          f ? (p.gfold ? 0 : 2) : 0, f ? (int64_t)offsets_fit_32(p) : 1};
+                          f ? (p.mode == dora::kModeDense || p.gfold ? 0 : 2) : 0, f ? (int64_t)offsets_fit_32(p) : 1,
+                          p.mode == dora::kModeDense ? p.dn_rt : 0, p.mode == dora::kModeDense ? p.dn_ct : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;
@@ -448,7 +484,7 @@ dora_status factored_norm(const void* W, const void* A, const void* B, int dtype
 
   const int64_t es = esize(dtype);
   const int64_t nW = d_out * d_in * es, nA = r * d_in * es, nB = d_out * r * es, nV = d_out * 4;
-  const bool factored = p.mode == dora::kModeFactored;
+  const bool factored = p.mode == dora::kModeFactored || p.mode == dora::kModeDense;   // (A and B are read)
   if (wnorm == nullptr) return DORA_ERR_INVALID_ARG;
   if (nW > 0 && W == nullptr) return DORA_ERR_INVALID_ARG;
   if (factored && (A == nullptr || B == nullptr)) return DORA_ERR_INVALID_ARG;
@@ -483,6 +519,11 @@ dora_status factored_norm(const void* W, const void* A, const void* B, int dtype
   }
   if (workspace_bytes < p.ws_bytes) return DORA_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && (workspace == nullptr || !aligned(workspace, kAlign))) return DORA_ERR_WORKSPACE;
+  if (p.mode == dora::kModeDense) {
+    if (aligned(W, 16) && aligned(A, 16) && aligned(B, 16))
+      return hip_status(dora::launch_norm_dense(p, W, A, B, workspace, s, m, eps, wnorm, g, hs, events, n_events));
+    p.mode = dora::kModeFactored;   // the 16-byte loads need aligned rows: the factored path, same workspace
+  }
   p.vec_b = aligned(B, 16) && (r % epc(dtype)) == 0;
   p.fast = aligned(W, 16) && aligned(A, 16) && (d_in % epc(dtype)) == 0 && p.vec_b && offsets_fit_32(p);
   if (!p.fast && p.ntc != p.ntc_gen) {

@@ -22,6 +22,9 @@ constexpr int kMaxLaunchEvents = 8;
 hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A, const void* B, void* ws,
                                 float s, const float* m, float eps, float* wnorm, float* g, hipStream_t st,
                                 const hipEvent_t* events, int n_events);
+hipError_t launch_norm_dense(const NormPlan& p, const void* W, const void* A, const void* B, void* ws, float s,
+                             const float* m, float eps, float* wnorm, float* g, hipStream_t st,
+                             const hipEvent_t* events, int n_events);
 hipError_t launch_norm_rowonly(const void* W, int dtype, int64_t d_out, int64_t d_in, bool vec, const float* m,
                                float eps, float* wnorm, float* g, hipStream_t st, const hipEvent_t* events,
                                int n_events);

@@ -85,7 +85,13 @@ DORA_HD TileShape tile_shape(int cfg) {
   }
 }
 
-enum NormMode : int { kModeEmpty = 0, kModeRowOnly = 1, kModeFactored = 2 };
+// kModeDense: the dense fused pass over tiles of W + s B A (16-bit types,
+// r >= d_out); the plan's factored fields stay valid, so a call whose
+// pointers do not allow its 16-byte loads runs the factored path instead,
+// in the same workspace.
+enum NormMode : int { kModeEmpty = 0, kModeRowOnly = 1, kModeFactored = 2, kModeDense = 3 };
+constexpr int kDenseRows = 64;     // rows of W per dense tile
+constexpr int kDenseCols = 128;    // columns of W (d_in) per dense tile
 
 struct NormPlan {
   int64_t d_out, d_in, r;
@@ -127,6 +133,9 @@ struct NormPlan {
   size_t off_bf;        // fp16 inputs only: B widened to fp32 [d_out][r] for the Gram term
   size_t off_cnt;       // [row tiles of the W pass] uint32 arrival counters (assembly in the W pass)
   int asm_fused;        // set per call: the W pass with the Gram term also assembles wnorm and g
+  int dn_rt, dn_ct;     // dense mode: row tiles over d_out, column tiles over d_in
+  int64_t ld_d;         // dense mode: padded rows of the column-tile partials
+  size_t off_dense;     // dense mode: [dn_ct][ld_d] fp32 partial sums of (W + s B A)^2
   size_t ws_bytes;
 };
 

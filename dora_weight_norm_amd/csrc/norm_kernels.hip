@@ -1539,6 +1539,255 @@ hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, cons
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Dense fused row norm, for r >= d_out (16-bit types): per tile of
+// kDenseMT rows by kDenseNT columns of d_in, the tile of W + s B A is formed
+// in the accumulators and squared, and its row sums are stored as one
+// partial per (column tile, row); a second kernel adds each row's partials
+// in column-tile order and takes the root. The definition itself
+// ("DoRA优化技术解析", cyqw.cn, §1.1: ||W + s B A||_row), never materialised:
+// where r >= d_out, the factored form's Gram matrix A A^T (r^2 d_in
+// multiply-adds) outweighs B A (d_out r d_in), so this path does less work
+// and needs no Gram reduction.
+//
+// Workgroup = NW waves (2 x NW/2), each owning 32 rows and 128 / (NW/2)
+// columns of the tile in 32x32 accumulator blocks. The
+// depth r goes through a ring of kDenseNS LDS slots, kDenseKT = 64 deep per
+// stage: B's tile rows (128 bytes each, swizzled like the W pass's rows)
+// and A's k-rows (kDenseNT columns, 16-byte chunks XOR-swizzled by 2 (k & 3)
+// so the transposed reads below hit distinct banks). A row-major A is
+// k-major for B A; each lane's column-operand fragment (8 consecutive k of
+// one column) is read with two ds_read_b64_tr_b16: in each 16-lane group,
+// lane m points at k-row m / 4 and columns 4 (m % 4) + [0, 4), and lane i
+// receives the 4 k-rows of column i. W's tile (64 rows x 256 bytes, chunks
+// XOR-swizzled by row & 15) is loaded first and enters the accumulator
+// layout in the epilogue through selector MFMAs, as B does in the W pass.
+// ---------------------------------------------------------------------------
+typedef short short4v __attribute__((ext_vector_type(4)));
+constexpr int kDenseMT = kDenseRows, kDenseNT = kDenseCols, kDenseKT = 64, kDenseNS = 6;
+constexpr int kDenseWaves = 8;
+constexpr int kDenseBBytes = kDenseMT * kDenseKT * 2;     // B part of a stage (8 KiB)
+constexpr int kDenseABytes = kDenseKT * kDenseNT * 2;     // A part of a stage (16 KiB)
+constexpr int kDenseSlot = kDenseBBytes + kDenseABytes;
+constexpr int kDenseWBytes = kDenseMT * kDenseNT * 2;     // W tile (16 KiB)
+static_assert(kDenseNS * kDenseSlot + kDenseWBytes <= 160 * 1024, "gfx950 has 160 KiB of LDS");
+
+template <typename T, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void norm_dense_kernel(NormPlan p, const T* __restrict__ W,
+                                                                      const T* __restrict__ A,
+                                                                      const T* __restrict__ B, float s,
+                                                                      float* __restrict__ part) {
+  static_assert(sizeof(T) == 2, "16-bit types");
+  // NW waves as 2 x WN; wave (wm, wn) owns rows 32 wm + [0, 32) and NBW
+  // 32-column blocks from column 32 NBW wn.
+  constexpr int WN = NW / 2, NBW = kDenseNT / 32 / WN;
+  constexpr int BPW = kDenseSlot / 1024 / NW;                 // direct-load blocks per wave per stage
+  constexpr int WPW = kDenseWBytes / 1024 / NW;               // W-tile blocks per wave
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(BPW * (kDenseNS - 1) + WPW < 64, "outstanding loads fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char lds[kDenseNS * kDenseSlot + kDenseWBytes];
+  char* const wt = lds + kDenseNS * kDenseSlot;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN, lrow = lane & 31, lgrp = lane >> 5;
+
+  // Tile: all row tiles of one column tile run on one die (die = blockIdx
+  // mod kDies), so A's columns come from memory once per die.
+  const int die = blockIdx.x % kDies, u = blockIdx.x / kDies;
+  const int rt = u % p.dn_rt, ct = (u / p.dn_rt) * kDies + die;
+  if (ct >= p.dn_ct) return;   // (the grid rounds the column tiles up to whole dies)
+  const int64_t i0 = (int64_t)rt * kDenseMT, j0 = (int64_t)ct * kDenseNT;
+  const int64_t d_in = p.d_in, r = p.r;
+  const int rows = p.d_out - i0 < kDenseMT ? (int)(p.d_out - i0) : kDenseMT;   // valid rows of the tile
+  const int64_t cols = d_in - j0;                                              // valid columns past j0
+  // Descriptors over the tile's rows: rows past them read as zeros.
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(B + i0 * r, (uint32_t)(rows * r * 2));
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + j0, (uint32_t)((r * d_in - j0) * 2));
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(W + i0 * d_in + j0, (uint32_t)((rows * d_in - j0) * 2));
+  const int n_st = (int)((r + kDenseKT - 1) / kDenseKT);
+
+  // Stage t into slot `sl`: block q of a stage (q = wave + NW n) is B rows
+  // 8q + [0, 8) for q < 8, else A k-rows 4 (q - 8) + [0, 4). Chunks past r or
+  // d_in, and stages past the depth, read as zeros.
+  auto issue = [&](int t, char* sl) __attribute__((always_inline)) {
+    const int64_t k0 = (int64_t)t * kDenseKT;
+    const bool in = t < n_st;
+#pragma unroll
+    for (int n = 0; n < BPW; ++n) {
+      const int q = wave + NW * n;
+      uint32_t off;
+      if (q < 8) {
+        const int row = q * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t k = k0 + c * 8;
+        off = (in && k < r) ? (uint32_t)(row * r + k) * 2u : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (__attribute__((address_space(3))) void*)(sl + q * 1024), 16,
+                                                 off, 0, 0, 0);
+      } else {
+        const int kr = (q - 8) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ (2 * (kr & 3));
+        off = (in && c * 8 < cols) ? (uint32_t)((k0 + kr) * d_in + c * 8) * 2u : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (__attribute__((address_space(3))) void*)(sl + q * 1024), 16,
+                                                 off, 0, 0, 0);
+      }
+    }
+  };
+  // W's tile: block q = wave + NW n holds rows 4q + [0, 4).
+#pragma unroll
+  for (int n = 0; n < WPW; ++n) {
+    const int q = wave + NW * n;
+    const int row = q * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    const uint32_t off = c * 8 < cols ? (uint32_t)(row * d_in + c * 8) * 2u : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (__attribute__((address_space(3))) void*)(wt + q * 1024), 16, off,
+                                             0, 0, 0);
+  }
+  auto slot = [&](int t) __attribute__((always_inline)) -> char* { return lds + (t % kDenseNS) * kDenseSlot; };
+#pragma unroll
+  for (int t = 0; t < kDenseNS; ++t) issue(t, slot(t));
+  wait_vm_lgkm0<(kDenseNS - 1) * BPW>();   // W's tile and stage 0 complete
+  barrier_keep_loads();
+
+  // Fragments of K16 step st of a stage: X = B rows (16 bytes), Y[b] = A's
+  // columns 32 (NBW wn + b) + (lane mod 32), 8 consecutive k each.
+  struct Frag {
+    u32x4 x, y[NBW];
+  };
+  const int m16 = lane & 15, g16 = lane >> 4;
+  const int kq = 8 * (g16 >> 1) + (m16 >> 2);            // k-row within a step (before + 4 h)
+  const int jq = 16 * (g16 & 1) + 4 * (m16 & 3);         // column within a 32-column block
+  auto read = [&](const char* sl, int st, Frag& F) __attribute__((always_inline)) {
+    const int row = wm * 32 + lrow;
+    F.x = *reinterpret_cast<const u32x4*>(sl + row * 128 + (((2 * st + lgrp) ^ ((row >> 1) & 7)) * 16));
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      const int jj = (wn * NBW + b) * 32 + jq;
+      short4v h[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int kr = 16 * st + kq + 4 * hh;
+        const int phys = (jj >> 3) ^ (2 * (kr & 3));
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v*)(sl + kDenseBBytes + kr * (kDenseNT * 2) + phys * 16 + (jj & 7) * 2));
+      }
+      F.y[b] = u32x4{(uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16),
+                     (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16),
+                     (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16),
+                     (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16)};
+    }
+  };
+  f32x16 acc[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
+  Frag F[2];
+  read(slot(0), 0, F[0]);
+  for (int i = 0; i < n_st; ++i) {
+    char* cur = slot(i);
+#pragma unroll
+    for (int st = 0; st < kDenseKT / 16; ++st) {
+      if (st + 1 < kDenseKT / 16) {
+        read(cur, st + 1, F[(st + 1) & 1]);
+      } else {
+        wait_vm_lgkm0<(kDenseNS - 2) * BPW>();   // stage i+1 landed; later stages in flight
+        barrier_keep_loads();
+        issue(i + kDenseNS, cur);
+        if (i + 1 < n_st) read(slot(i + 1), 0, F[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) acc[b] = Mfma<T>::run(&F[st & 1].x, &F[st & 1].y[b], acc[b]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vm_lgkm0<0>();   // the trailing (zero) stages land before the ring is reused
+  barrier_keep_loads();
+
+  // Epilogue: W's 32x32 blocks in the accumulator layout (two MFMAs each
+  // against 0/1 selectors, exact), then sum over this wave's columns of
+  // (W + s (B A))^2 per row, across the 32 column lanes, then the WN
+  // column waves in order.
+  const uint32_t one = __is_same(T, bf16_t) ? 0x3F80u : 0x3C00u;
+  u32x4 E[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = lrow - 8 * lgrp - 16 * h;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) E[h][w] = (e == 2 * w ? one : 0u) | ((e == 2 * w + 1 ? one : 0u) << 16);
+  }
+  float pa[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) pa[v] = 0.f;
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int row = wm * 32 + lrow;
+    u32x4 f[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = ((wn * NBW + b) * 32 + 16 * h) / 8 + lgrp;
+      f[h] = *reinterpret_cast<const u32x4*>(wt + row * (kDenseNT * 2) + ((c ^ (row & 15)) * 16));
+    }
+    f32x16 wb;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) wb[v] = 0.f;
+    wb = Mfma<T>::run(&f[0], &E[0], wb);
+    wb = Mfma<T>::run(&f[1], &E[1], wb);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float val = fmaf(s, acc[b][v], wb[v]);
+      pa[v] = fmaf(val, val, pa[v]);
+    }
+  }
+  const float tot = sum32_transpose(pa, lane);
+  float* red = reinterpret_cast<float*>(lds);   // (the ring is free)
+  if ((lane & 1) == 0) red[wn * kDenseMT + wm * 32 + acc_row((lane & 31) >> 1, lgrp)] = tot;
+  __syncthreads();
+  if (tid < rows) {
+    float t = red[tid];
+#pragma unroll
+    for (int q = 1; q < WN; ++q) t += red[q * kDenseMT + tid];
+    part[(int64_t)ct * p.ld_d + i0 + tid] = t;
+  }
+}
+
+// wnorm[j] = sqrt of the sum of row j's column-tile partials, added in
+// column-tile order, and g (the same assembly as the factored path's with
+// the cross and Gram terms zero).
+__global__ __launch_bounds__(kThreads) void assemble_dense_kernel(NormPlan p, const float* __restrict__ part,
+                                                                  float s, const float* m, float eps, float* wnorm,
+                                                                  float* g) {
+  const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (j >= p.d_out) return;
+  const float tot = ordered_sum(part + j, p.ld_d, p.dn_ct);
+  assemble_sums(tot, 0.f, 0.f, s, eps, m, wnorm, g, j);
+}
+
+hipError_t launch_norm_dense(const NormPlan& p, const void* W, const void* A, const void* B, void* ws_, float s,
+                             const float* m, float eps, float* wnorm, float* g, hipStream_t st,
+                             const hipEvent_t* events, int n_events) {
+  char* ws = static_cast<char*>(ws_);
+  float* part = reinterpret_cast<float*>(ws + p.off_dense);
+  Marks mk{events, events != nullptr ? n_events : 0, 0};
+  hipError_t e = begin_marks(mk, st);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((int64_t)p.dn_rt * ((p.dn_ct + kDies - 1) / kDies) * kDies);
+  constexpr int NW = kDenseWaves;
+  if (p.dtype == 0)
+    hipLaunchKernelGGL((norm_dense_kernel<bf16_t, NW>), dim3(grid), dim3(NW * 64), 0, st,
+                       p, static_cast<const bf16_t*>(W), static_cast<const bf16_t*>(A),
+                       static_cast<const bf16_t*>(B), s, part);
+  else
+    hipLaunchKernelGGL((norm_dense_kernel<f16_t, NW>), dim3(grid), dim3(NW * 64), 0, st,
+                       p, static_cast<const f16_t*>(W), static_cast<const f16_t*>(A),
+                       static_cast<const f16_t*>(B), s, part);
+  e = launched(st, mk);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(assemble_dense_kernel, dim3((unsigned)((p.d_out + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     st, p, part, s, m, eps, wnorm, g);
+  return launched(st, mk);
+}
+
 hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A, const void* B, void* ws_,
                                 float s, const float* m, float eps, float* wnorm, float* g,
                                 hipStream_t st, const hipEvent_t* events, int n_events) {

@@ -98,7 +98,9 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
 /*
  * The plan dora_factored_norm would use, for diagnostics and benchmarks.
  * Fills info[0 .. n_info-1] with, in order: mode (0 nothing to do, 1 row
- * sum of squares only, 2 factored), W-pass column tile width, W-pass column
+ * sum of squares only, 2 factored, 3 dense fused; in mode 3 the factored
+ * fields describe the fallback used when the pointers do not allow aligned
+ * 16-byte loads), W-pass column tile width, W-pass column
  * tiles, Gram-pass column tile width, Gram-pass column tiles, streaming and
  * general kernel configuration of the W pass, the same of the Gram pass,
  * d_in granule (elements), granules over d_in, d_in ranges of the W pass,
@@ -112,8 +114,10 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
  * folded in; no separate Gram-term pass), else 0, the index of the W
  * pass among the call's launches (see dora_factored_norm_marked), and 1 if
  * every operand tile of the streaming kernel spans less than 2^31 bytes
- * (its 32-bit buffer offsets; otherwise the general kernel runs), else 0;
- * the streaming fields apply when W, A and B allow aligned 16-byte loads.
+ * (its 32-bit buffer offsets; otherwise the general kernel runs), else 0,
+ * and in mode 3 the dense pass's row tiles (64 rows) and column tiles (128
+ * columns of d_in), else 0 and 0; the streaming fields apply when W, A and
+ * B allow aligned 16-byte loads.
  * Entries past the last field are set to -1.
  * Before returning it replays the plan on the host and checks that the
  * d_in ranges tile d_in exactly, every grid fits and every partial sum the
@@ -135,7 +139,16 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
  *
  * Inputs W, A, B are device pointers of storage type `dtype`; all
  * accumulation is fp32. U never leaves the matrix-core accumulators; BA is
- * never formed. wnorm (and g) are fp32 [d_out] device arrays written by the
+ * never formed.
+ *
+ * Where r >= d_out (bf16 and fp16, d_in and r multiples of 8, plan mode 3)
+ * the Gram matrix would cost more than B A itself, and the call computes
+ * the same wnorm by its definition instead: a dense fused pass forms each
+ * 64 x 128 tile of W + s B A in the matrix-core accumulators, squares it
+ * and keeps only its row sums (cyqw.cn §1.1), and a second launch adds each
+ * row's tile sums in a fixed order and takes the root. No tile of B A
+ * leaves the chip; the workspace is the larger of the two paths' (the
+ * factored path runs instead when W, A or B is not 16-byte aligned). wnorm (and g) are fp32 [d_out] device arrays written by the
  * call. m is an fp32 [d_out] device array or NULL (then g is not written
  * and may be NULL). A NaN in the inputs propagates to wnorm and g.
  *
@@ -176,6 +189,7 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
  *     gram_reduce, Gram term (+ assembly with several Gram-term tiles);
  *   fp16: Gram pass, gram_reduce, W pass, widening of B, Gram term
  *     (+ assembly with several Gram-term tiles);
+ *   dense fused (plan mode 3): dense pass, assembly;
  *   s == 0, r == 0 or d_in == 0: one row-sum launch.
  * (These are the streaming-path launches, used when W, A and B allow
  * aligned 16-byte loads; plan field w_launch is the W pass's index i, which

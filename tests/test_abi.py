@@ -50,11 +50,25 @@ def test_chunk_size_matches_oracle_rule(d_out, d_in, budget):
     assert bnd.dora_norm_chunk_size(d_out, d_in, budget) == O.chunk_size(d_out, d_in, budget)
 
 
+def dense_rule(d_out, d_in, r, dtype):
+    """The documented choice of the dense fused pass: 16-bit storage, r >= d_out, d_in and r in whole
+    16-byte chunks, and A (and 64 rows of W or B) under 2^31 bytes."""
+    return (dtype in ("bf16", "f16") and r >= d_out and d_in % 8 == 0 and r % 8 == 0
+            and r * d_in * 2 < 2 ** 31 and 64 * d_in * 2 < 2 ** 31 and 64 * r * 2 < 2 ** 31)
+
+
 @pytest.mark.parametrize("name", sorted(I.WORKLOADS))
 def test_plans_of_the_workloads(name):
     w = I.WORKLOADS[name]
     info = bnd.dora_norm_plan_info(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
-    assert info["mode"] == 2
+    dense = dense_rule(w.d_out, w.d_in, w.r, w.dtype)
+    assert info["mode"] == (3 if dense else 2)
+    if dense:
+        # one 64 x 128 tile per workgroup; the W pass fields describe the factored fallback
+        assert info["dense_row_tiles"] == -(-w.d_out // 64) and info["dense_col_tiles"] == -(-w.d_in // 128)
+        assert info["w_launch"] == 0
+        return
+    assert info["dense_row_tiles"] == 0 and info["dense_col_tiles"] == 0
     assert info["workspace_bytes"] <= w.budget
     assert info["workspace_bytes"] == bnd.dora_norm_workspace_size(w.d_out, w.d_in, w.r, w.dtype, w.s, w.budget)
     assert info["gram_grid"] <= 256 and info["lds_bytes"] <= 160 * 1024
@@ -81,8 +95,10 @@ def test_plan_self_check_on_many_shapes():
     for (d_out, d_in, r) in shapes:
         for dt in ("bf16", "f32"):
             info = bnd.dora_norm_plan_info(d_out, d_in, r, dt, 0.5, 256 * MiB)
-            assert info["mode"] == 2
+            assert info["mode"] == (3 if dense_rule(d_out, d_in, r, dt) else 2), (d_out, d_in, r, dt)
             assert info["tile_cols"] * info["col_tiles"] >= r
+            if info["mode"] == 3:
+                assert info["dense_row_tiles"] * 64 >= d_out and info["dense_col_tiles"] * 128 >= d_in
 
 
 def test_w_pass_tile_shapes():

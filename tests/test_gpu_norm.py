@@ -77,7 +77,21 @@ CASES = [
     ("tall_r384_general", 8000, 8193, 384, "bf16", 0.5, 41),
     # two 384-column tiles (384 < r <= 768), the second one ragged
     ("tall_r696_two_col_tiles", 8000, 8192, 696, "bf16", 0.25, 42),
+    # the dense fused pass (r >= d_out, 16-bit, d_in and r multiples of 8):
+    # ragged row and column tiles, r short of a 64-deep stage, one row, many
+    # column tiles, fp16, r == d_out
+    ("dense_kv_f16", 512, 3584, 768, "f16", 0.25, 43),
+    ("dense_ragged", 100, 1000, 200, "bf16", 0.5, 44),
+    ("dense_r_eq_d_out", 256, 2048, 256, "bf16", -0.5, 45),
+    ("dense_one_row", 1, 8, 8, "bf16", 2.0, 46),
+    ("dense_f16_ragged", 70, 264, 136, "f16", 0.75, 47),
+    ("dense_many_col_tiles", 64, 8192, 64, "bf16", 0.5, 48),
+    ("dense_big_s_neg", 96, 1032, 1024, "bf16", -4.0, 49),
 ]
+
+
+def dense_planned(d_out, d_in, r, dtype):
+    return bnd.dora_norm_plan_info(d_out, d_in, r, dtype, 0.5)["mode"] == 3
 
 
 def _run(W, A, B, dtype, s, m=None, budget=256 << 20, events=None):
@@ -293,18 +307,59 @@ def test_launch_events_mark_each_launch():
 
 
 def test_many_partials_per_row_deterministic():
-    # 32 d_in ranges and two column tiles: 32 base and 64 cross partials per
+    # 16 d_in ranges and four column tiles: 16 base and 64 cross partials per
     # row, summed by several threads per row and then in a fixed order
-    W, A, B = I.norm_inputs(512, 3584, 768, "bf16", 27)
-    info = bnd.dora_norm_plan_info(512, 3584, 768, "bf16", 0.25)
-    assert info["w_ranges"] * info["col_tiles"] > 16
-    m = np.full(512, 0.75, np.float32)
+    W, A, B = I.norm_inputs(800, 3584, 768, "bf16", 27)
+    info = bnd.dora_norm_plan_info(800, 3584, 768, "bf16", 0.25)
+    assert info["mode"] == 2 and info["w_ranges"] * info["col_tiles"] > 16
+    m = np.full(800, 0.75, np.float32)
     a, ga = _run(W, A, B, "bf16", 0.25, m)
     for _ in range(3):
         b, gb = _run(W, A, B, "bf16", 0.25, m)
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
         assert np.array_equal(ga.view(np.uint32), gb.view(np.uint32))
     check_norm(a, O.dense_row_norm(W, A, B, 0.25))
+
+
+def test_dense_pass_deterministic_and_marked():
+    # the dense fused pass and its assembly: two launches, reproducible bits
+    d_out, d_in, r = 512, 3584, 768
+    assert dense_planned(d_out, d_in, r, "bf16")
+    W, A, B = I.norm_inputs(d_out, d_in, r, "bf16", 50)
+    m = np.full(d_out, 1.25, np.float32)
+    a, ga = _run(W, A, B, "bf16", 0.25, m)
+    for _ in range(3):
+        b, gb = _run(W, A, B, "bf16", 0.25, m)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert np.array_equal(ga.view(np.uint32), gb.view(np.uint32))
+    check_norm(a, O.dense_row_norm(W, A, B, 0.25))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    c, _ = _run(W, A, B, "bf16", 0.25, m, events=evs)
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+    assert evs[0].elapsed_time(evs[1]) > 0 and evs[1].elapsed_time(evs[2]) > 0
+    assert evs[2].elapsed_time(evs[3]) < 0      # only two launches: event 3 keeps its old time
+
+
+def test_dense_plan_falls_back_on_unaligned_pointers():
+    # the plan picks the dense pass, but rows that are not 16-byte aligned
+    # run the factored path (element loads) in the same workspace
+    d_out, d_in, r = 200, 1024, 256
+    assert dense_planned(d_out, d_in, r, "bf16")
+    W, A, B = I.norm_inputs(d_out, d_in, r, "bf16", 51)
+    ref = O.dense_row_norm(W, A, B, 0.5)
+
+    def shifted(x):
+        flat = torch.zeros(x.size + 1, dtype=torch.bfloat16, device="cuda")
+        flat[1:] = torch.from_numpy(x.ravel()).cuda().to(torch.bfloat16)
+        return flat[1:].view(*x.shape)
+
+    for args in [(shifted(W), dev(A, "bf16"), dev(B, "bf16")), (dev(W, "bf16"), shifted(A), dev(B, "bf16")),
+                 (dev(W, "bf16"), dev(A, "bf16"), shifted(B))]:
+        wn, _ = bnd.dora_factored_norm(*args, 0.5)
+        check_norm(wn.cpu().numpy(), ref)
 
 
 def test_power_of_two_scale_moves_into_B_bitwise():
