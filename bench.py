@@ -64,6 +64,11 @@ def w_pass_flops(d_out, d_in, r, plan):
     return f
 
 
+def dense_flops(d_out, d_in, r):
+    """The dense fused pass (plan mode 3): B A over r, then W + s (B A) and its square summed per row."""
+    return 2 * d_out * d_in * r + 4 * d_out * d_in
+
+
 def norm_bytes(d_out, d_in, r, esize):
     """W, A, B read once; m read, wnorm and g written (fp32)."""
     return (d_out * d_in + r * d_in + d_out * r) * esize + 12 * d_out
@@ -563,7 +568,8 @@ def main() -> int:
     w_times = [a.elapsed_time(b) for a, b in marks]
     w_ms = float(np.median(w_times))
 
-    F = norm_flops(w.d_out, w.d_in, w.r)
+    # (the algorithm the plan runs: the factored norm, or the dense fused pass)
+    F = dense_flops(w.d_out, w.d_in, w.r) if plan["mode"] == 3 else norm_flops(w.d_out, w.d_in, w.r)
     nb = norm_bytes(w.d_out, w.d_in, w.r, esize)
     cb = compose_bytes(w.T, w.d_out, esize)
     norm_tflops = F / (norm_ms * 1e-3) / 1e12
@@ -594,7 +600,10 @@ def main() -> int:
     roof_compose = {"bound": "hbm", "achieved": comp_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": comp_gbs / HBM_PEAK_GBS, "traffic": traffic.get("compose"),
                     "kernel": "compose_kernel", "algorithmic_bytes": cb, "traffic_source": traffic_note}
-    if plan["gram_folded"]:
+    dense = plan["mode"] == 3
+    if dense:
+        launches = "dense pass over tiles of W + s B A, assembly"
+    elif plan["gram_folded"]:
         launches = "W pass with the G blocks, gram_reduce, Gram term + assembly"
     elif plan["gram_term_fused"]:
         launches = "Gram pass, gram_reduce, W pass with the Gram term, assembly"
@@ -605,13 +614,13 @@ def main() -> int:
                  "kernel": f"dora_factored_norm: {launches} (one C-ABI call, timed as a unit)",
                  "algorithmic_flops": F, "algorithmic_bytes": nb, "hbm_gbs": norm_gbs,
                  "hbm_frac": norm_gbs / HBM_PEAK_GBS, "traffic_source": traffic_note}
-    Fw = w_pass_flops(w.d_out, w.d_in, w.r, plan)
+    Fw = dense_flops(w.d_out, w.d_in, w.r) if dense else w_pass_flops(w.d_out, w.d_in, w.r, plan)
     w_tflops = Fw / (w_ms * 1e-3) / 1e12
-    w_name = ("W pass with the Gram term" if plan["gram_term_fused"]
+    w_name = ("dense pass" if dense else "W pass with the Gram term" if plan["gram_term_fused"]
               else "W pass with the G blocks" if plan["gram_folded"] else "W pass")
     roof_w = {"bound": "mfma", "achieved": w_tflops, "peak": mfma_peak, "unit": "TFLOP/s",
               "frac": w_tflops / mfma_peak, "traffic": traffic.get("w_pass"),
-              "kernel": f"norm_fast_kernel ({w_name}; launch {wl} of the norm call)",
+              "kernel": f"{'norm_dense_kernel' if dense else 'norm_fast_kernel'} ({w_name}; launch {wl} of the norm call)",
               "algorithmic_flops": Fw, "launch_ms": w_ms, "launch_ms_mean": float(np.mean(w_times)),
               "timing": "median over the steps of the interval between the events the library records just "
                         "before and just after the launch (includes its dispatch gap)",

@@ -91,7 +91,16 @@ def short_name(name: str) -> str:
         mode = {"0": "W pass", "1": "Gram pass", "2": "Gram term + assembly", "3": "W pass + G blocks",
                 "4": "W pass + Gram term"}.get(args[-1], args[-1])
         n = f"norm_fast_kernel<{', '.join(args)}> ({mode})"
+    m = re.match(r"norm_dense_kernel<(.*)>", n)
+    if m:
+        n = f"norm_dense_kernel<{m.group(1)}> (dense pass)"
     return n
+
+
+def is_main_pass(name: str) -> bool:
+    """The norm call's main pass: the W pass, or the dense pass where the plan takes it."""
+    short = short_name(name)
+    return "(W pass" in short or "(dense pass)" in short
 
 
 def _one(pattern: str) -> str:
@@ -179,15 +188,15 @@ def main() -> int:
         per_step = s["calls"] / part_calls[role]
         if fk and wk:
             traffic[role] += (fb + wb) * per_step
-            if role == "norm" and "(W pass" in short_name(s["name"]):
+            if role == "norm" and is_main_pass(s["name"]):
                 w_pass_bytes = fb + wb
-        if role == "norm" and "(W pass" in short_name(s["name"]):
+        if role == "norm" and is_main_pass(s["name"]):
             w_pass_us = s["avg_us"]
         mcols = ""
         if args.mfma:
             mf, mu = mflops.get(s["name"]), mutil.get(s["name"])
             mcols = (f" {mf / 1e9:.2f} |" if mf is not None else " — |") + (f" {mu:.1f} |" if mu is not None else " — |")
-            if role == "norm" and "(W pass" in short_name(s["name"]) and mf is not None:
+            if role == "norm" and is_main_pass(s["name"]) and mf is not None:
                 w_pass_mfma = (mf, mu)
         lines.append(f"| {short_name(s['name'])} | {role} | {s['calls']} | {s['avg_us']:.2f} | {s['min_us']:.2f} | "
                      f"{s['max_us']:.2f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |" + mcols)

@@ -41,6 +41,9 @@ def test_kernel_roles_and_short_names():
     assert prof.kernel_role(ns + "compose_kernel<unsigned short, 8, true>(unsigned short const*)") == "layer_output"
     assert prof.kernel_role(ns + "compose_bwd_kernel<unsigned short, 8, true>(unsigned short const*)") == "compose_bwd"
     assert prof.kernel_role("__amd_rocclr_copyBuffer") is None
+    d = ns + "norm_dense_kernel<unsigned short, 8>(dora::NormPlan, unsigned short const*)"
+    assert prof.kernel_role(d) == "norm" and prof.short_name(d) == "norm_dense_kernel<bf16, 8> (dense pass)"
+    assert prof.is_main_pass(d) and prof.is_main_pass(w) and not prof.is_main_pass(g)
 
 
 def test_copy_calibration():
