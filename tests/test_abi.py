@@ -276,3 +276,27 @@ def test_compose_backward_argument_errors_return_before_launch():
     assert call(d_base=0x100000) == 1                  # output is an input
     assert call(ws_bytes=16) == 4                      # workspace too small
     assert call(d_out=0) == 0
+
+
+def test_no_kernel_uses_scratch_or_spills_vector_registers():
+    # build() records the compiler's per-kernel resource use; a scratch array
+    # or spilled vector registers would put every access on memory.
+    from dora_weight_norm_amd import build as B
+    if not os.path.exists(B.RESOURCE_REPORT):
+        pytest.skip("no build report (run build() first)")
+    rows = {}
+    for ln in open(B.RESOURCE_REPORT):
+        name, *fields = ln.split()
+        rows[name] = dict(f.split("=", 1) for f in fields)
+    assert rows
+    for name, d in rows.items():
+        assert d["ScratchSize_[bytes/lane]"] == "0", name
+        assert d["VGPRs_Spill"] == "0", name
+    def find(pat):
+        return [d for n, d in rows.items() if pat in n]
+    # the 256 x 384 W-pass tile (bf16, Gram term inside): 192 accumulators
+    # per lane at two waves per SIMD, so at most 256 registers in all
+    lean = find("norm_fast_kernelItLi2ELi4ELi4ELi3ELi64ELi2ELi4E")
+    assert lean and all(int(d["VGPRs"]) + int(d["AGPRs"]) <= 256 and d["Occupancy_[waves/SIMD]"] == "2"
+                        for d in lean)
+    assert find("norm_dense_kernel") and find("compose_kernel") and find("compose_bwd_kernel")
