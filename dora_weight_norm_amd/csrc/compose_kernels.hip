@@ -178,7 +178,8 @@ hipError_t launch(const void* base, const void* lora, const float* g, float s, i
 // With the magnitude frozen (no dg), base and lora are not read at all.
 // ---------------------------------------------------------------------------
 constexpr int kBwdMaxRowBlocks = 256;
-constexpr int64_t kBwdPlainStoreBytes = (int64_t)64 << 20;   // per output tensor
+constexpr int64_t kBwdPlainMinBytes = (int64_t)64 << 20;     // per output tensor
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;  // MI355X
 constexpr int kBwdTargetBlocks = 256;   // about one workgroup per compute unit
 
 template <typename T, int VEC, bool DG, bool NTS>
@@ -339,10 +340,14 @@ hipError_t launch_bwd(const void* dy, const void* base, const void* lora, const 
                       float* part, hipStream_t st) {
   const Grid2 q = strip_grid(T_rows, d_out, VEC, kBwdMaxRowBlocks);
   if (q.by > 0 && q.bx > 0) {
-    // Non-temporal stores for outputs below kBwdPlainStoreBytes, ordinary
-    // ones above (measured on MI355X: ordinary stores take 6% off the pass
-    // at 8192 x 8192 and add 4-5% at 4096 x 4096 and 8192 x 512).
-    const bool nts = T_rows * d_out * (int64_t)sizeof(T) < kBwdPlainStoreBytes;
+    // Ordinary stores where each output exceeds kBwdPlainMinBytes and both
+    // together fit the 256 MiB Infinity Cache, non-temporal ones otherwise.
+    // Measured on MI355X (bf16, interleaved in one process): ordinary stores
+    // take 6% off the pass at 8192 x 8192 (2 x 128 MiB of output), and add
+    // 4-5% at 4096 x 4096 and 8192 x 512, 5% at 8192 x 12288, 6% at
+    // 16384 x 8192 and 8192 x 28672.
+    const int64_t out_bytes = T_rows * d_out * (int64_t)sizeof(T);
+    const bool nts = !(out_bytes > kBwdPlainMinBytes && 2 * out_bytes <= kInfinityCacheBytes);
     const dim3 grid((unsigned)q.bx, (unsigned)q.by), block((unsigned)q.tpb, (unsigned)q.lanes());
     const T* dy_t = static_cast<const T*>(dy);
     const T* base_t = static_cast<const T*>(base);
