@@ -544,13 +544,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   constexpr bool PEEL = NS == 2 && MB * NB <= 6;
   const int n_loop = PEEL ? (n_tot & ~1) : n_pad;   // stages the unrolled loop runs
   Frag H[C::LEAN ? 1 : 2];
-  // Lean mode (two slots) spreads each stage's loads over the stage before
-  // it: the row-operand blocks (the HBM stream) right after the barrier
-  // that frees their slot, the column-operand blocks a few at a time after
-  // each of the first KSTEPS-1 steps' fragment reads. A wave stalls while
-  // the address unit takes a burst of load instructions, and with one
-  // fragment set the other wave of its SIMD cannot cover the stall.
-  constexpr bool SPREAD = C::LEAN && NS == 2;
+  // With two slots each stage's loads are spread over the stage before it:
+  // the row-operand blocks (the HBM stream) right after the barrier that
+  // frees their slot, the column-operand blocks a few at a time after each
+  // of the first KSTEPS-1 steps' fragment reads. A wave stalls while the
+  // address unit takes a burst of load instructions; spread out, the
+  // stalls fall between MFMA steps (in lean mode, with one fragment set,
+  // the other wave of the SIMD cannot cover them at all).
+  constexpr bool SPREAD = NS == 2;
   constexpr int COL_PER_STEP = (BPW - C::BPW_M + KSTEPS - 2) / (KSTEPS - 1);
   if constexpr (SPREAD) {
     issue_blocks(0, ring(0), 0, BPW);
@@ -610,10 +611,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       for (int s = 0; s < KSTEPS; ++s) {
         if (s + 1 < KSTEPS) {
           read_step(ring(j), s + 1, H[(s + 1) & 1]);
+          if constexpr (SPREAD) {
+            const int c0 = C::BPW_M + s * COL_PER_STEP;
+            const int c1 = c0 + COL_PER_STEP < BPW ? c0 + COL_PER_STEP : BPW;
+            __builtin_amdgcn_sched_barrier(0);
+            issue_blocks(i + 1, ring((j + 1) % NS), c0, c1);
+          }
         } else {
           wait_vm_lgkm0<(NS - 2) * BPW>();
           barrier_keep_loads();
-          issue_blocks(i + NS, ring(j), 0, BPW);
+          if constexpr (SPREAD) {
+            issue_blocks(i + NS, ring(j), 0, C::BPW_M);
+          } else {
+            issue_blocks(i + NS, ring(j), 0, BPW);
+          }
           read_step(ring((j + 1) % NS), 0, H[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
