@@ -719,8 +719,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       float pa[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) pa[v] = 0.f;
-      if constexpr (C::LEAN) {
-        // B's 32x32 block in the accumulator layout (row acc_row(v), column
+      if constexpr (FC == 1) {
+        // (16-bit types) B's 32x32 block in the accumulator layout (row acc_row(v), column
         // lrow), made by two MFMAs: the row-operand fragments are B's rows
         // (16-byte reads of the staged rows, as for W), the column operand
         // the 0/1 selector E_h with E_h[k][j] = 1 iff j = k + 16h. Each
