@@ -120,7 +120,10 @@ void layout(NormPlan& p) {
   p.off_gg = off;
   off = align_up(off + (size_t)(p.rg * p.rg) * 4, kAlign);   // bf16 hi and lo, or fp32
   p.off_bf = off;
-  if (p.dtype == DORA_F16) off = align_up(off + (size_t)(p.d_out * p.r) * 4, kAlign);   // B widened to fp32
+  // fp16: B widened to fp32 [d_out][r] (separate Gram-term pass), or B
+  // split into bf16 [d_out][B_hi | B_lo], rg columns each (Gram term in
+  // the W pass); the region holds the larger.
+  if (p.dtype == DORA_F16) off = align_up(off + (size_t)(p.d_out * p.rg) * 4, kAlign);
   p.off_cnt = off;
   off = align_up(off + (size_t)ceil_div(p.d_out, dora::fast_rows(p.fcfg)) * 4, kAlign);   // arrival counters
   p.ws_bytes = off;
@@ -217,7 +220,7 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   p.ld_w = ceil_div(d_out, dora::kRowPadW) * dora::kRowPadW;
   p.ga_rows = ceil_div(r, dora::kRowPadG) * dora::kRowPadG;
   p.ga_cols = (int64_t)p.n_nt_g * p.ntc_g;
-  const int64_t rq = dtype == DORA_BF16 ? 64 : 32;
+  const int64_t rq = dtype == DORA_F32 ? 32 : 64;   // (16-bit: the Gram term's parts meet on 64-deep stages)
   p.rg = ceil_div(r, rq) * rq;
   // Tiles of the separate Gram-term pass (run when the Gram term is not
   // inside the W pass: G folded into the W pass, fp16, the general path):
@@ -308,7 +311,7 @@ bool plan_self_check(const NormPlan& p) {
   if (p.off_g < p.off_ba + (size_t)(ba_planes(p) * p.ld_w) * 4) return false;
   if (p.off_gg < p.off_g + (size_t)((int64_t)gram_planes(p) * p.ga_rows * p.ga_cols) * 4) return false;
   if (p.off_bf < p.off_gg + (size_t)(p.rg * p.rg) * 4) return false;
-  if (p.off_cnt < p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.r) * 4 : 0)) return false;
+  if (p.off_cnt < p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.rg) * 4 : 0)) return false;
   return p.ws_bytes >= p.off_cnt + (size_t)ceil_div(p.d_out, fw) * 4;
 }
 
@@ -407,7 +410,7 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   const int64_t vals[] = {p.mode, p.ntc, p.n_nt, p.ntc_g, p.n_nt_g, p.fcfg, p.gcfg, p.fcfg_g, p.gcfg_g, p.gran,
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,
                           f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0,
-                          f ? p.gfold : 0, f ? p.gsym : 0, f ? (int64_t)(!p.gfold && p.dtype != DORA_F16) : 0,
+                          f ? p.gfold : 0, f ? p.gsym : 0, f ? (int64_t)(!p.gfold) : 0,
                           f ? (p.mode == dora::kModeDense || p.gfold ? 0 : 2) : 0, f ? (int64_t)offsets_fit_32(p) : 1,
                           p.mode == dora::kModeDense ? p.dn_rt : 0, p.mode == dora::kModeDense ? p.dn_ct : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));

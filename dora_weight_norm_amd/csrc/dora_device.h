@@ -46,6 +46,27 @@ __device__ __forceinline__ bf16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_bits_to_f32(v); }
+
+// Eight fp16 values of a 16-byte chunk split exactly into bf16 hi + lo:
+// hi = the value rounded to bf16, lo = the remainder. fp16 carries 11
+// significant bits and bf16 8 over a wider exponent range, so the
+// remainder (at most 4 bits) is exact in bf16 and hi + lo equals the value.
+// Returns the hi parts, or the lo parts, in the same element order.
+__device__ __forceinline__ u32x4 f16_split_bf16(const u32x4& v, bool lo) {
+  const f16x8 h = __builtin_bit_cast(f16x8, v);   // (by value: no address taken)
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a = (float)h[2 * w], b = (float)h[2 * w + 1];
+    uint32_t ha = f32_to_bf16_rne(a), hb = f32_to_bf16_rne(b);
+    if (lo) {
+      ha = f32_to_bf16_rne(a - bf16_bits_to_f32(ha));
+      hb = f32_to_bf16_rne(b - bf16_bits_to_f32(hb));
+    }
+    r[w] = ha | (hb << 16);
+  }
+  return r;
+}
 __device__ __forceinline__ float to_f32(f16_t v) { return (float)v; }
 __device__ __forceinline__ float to_f32(float v) { return v; }
 

@@ -130,7 +130,7 @@ struct NormPlan {
   size_t off_ba;        // [max(n_bt, n_cb)][ld_w] fp32 Gram-term partials
   size_t off_g;         // [max(xg, xw if gfold)][ga_rows][ga_cols] fp32 Gram partials
   size_t off_gg;        // reduced Gram matrix: bf16 [rg][Ghi | Glo], fp32 [rg][rg]
-  size_t off_bf;        // fp16 inputs only: B widened to fp32 [d_out][r] for the Gram term
+  size_t off_bf;        // fp16 inputs only: B widened to fp32 [d_out][r], or split to bf16 [d_out][B_hi | B_lo]
   size_t off_cnt;       // [row tiles of the W pass] uint32 arrival counters (assembly in the W pass)
   int asm_fused;        // set per call: the W pass with the Gram term also assembles wnorm and g
   int dn_rt, dn_ct;     // dense mode: row tiles over d_out, column tiles over d_in

@@ -61,6 +61,12 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // The memory clobber keeps the compiler from moving LDS accesses across.
 __device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
 
+// Compile-time flag carried into generic lambdas.
+template <bool V>
+struct Tag {
+  static constexpr bool value = V;
+};
+
 // Out-of-range buffer offset: a buffer load at it returns zeros.
 constexpr uint32_t kOob = 0x80000000u;
 
@@ -248,6 +254,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   constexpr bool WP = MODE == kPassW || GF || WB;    // W pass
   static_assert((GRAM ? kRowPadG : kRowPadW) % MT == 0, "row tiles divide the plan's row padding");
   constexpr int NG = sizeof(T) == 2 ? 2 : 1;   // parts of the stored Gram matrix (hi, lo)
+  // fp16 with the Gram term in the W pass: the stored Gram matrix is bf16
+  // hi + lo as for bf16, and B comes split exactly into bf16 hi + lo (by
+  // the Gram reduction, into the workspace as [d_out][B_hi | B_lo], rg
+  // columns each); the virtual depth runs over three parts, [B_hi | B_lo |
+  // B_hi] against [Ghi ; Ghi ; Glo], on the bf16 matrix cores (B_lo Glo,
+  // about 2^-16 of the term, is left out).
+  constexpr bool F16G = WB && __is_same(T, f16_t);
+  constexpr int NV = F16G ? 3 : NG;             // parts of the virtual depth
   __shared__ __attribute__((aligned(1024))) char r0[C::SLOT];
   __shared__ __attribute__((aligned(1024))) char r1[C::SLOT];
   __shared__ __attribute__((aligned(1024))) char r2[NS > 2 ? C::SLOT : 16];
@@ -313,20 +327,27 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   //     against A's rows over this workgroup's d_in range [k0, k1).
   //  2. (kPassBG; kPassWB after phase 1) B's rows against rows of the
   //     stored Gram matrix over the virtual depth [v0, v0 + n_bs KT) of
-  //     [0, NG rg): B's columns against Ghi, then again against Glo. rg is
-  //     a whole number of stages, so no stage straddles the seam.
+  //     [0, NV rg): B's columns against Ghi, then again against Glo (fp16:
+  //     B_hi against Ghi, B_lo against Ghi, B_hi against Glo). rg is a
+  //     whole number of stages, so no stage straddles a seam.
   const int64_t k0 = BG ? 0 : range_k0(p, X, x);
   const int64_t k1 = BG ? 0 : range_k0(p, X, x + 1);
   const int n_st = (int)((k1 - k0 + KT - 1) / KT);   // phase-1 stages (>= 1 unless kPassBG)
   int n_bs = 0;
   int64_t v0 = 0;
   if constexpr (BG || WB) {
-    const int64_t vg = (int64_t)NG * p.rg / KT;     // stages of the whole virtual depth
+    const int64_t vg = (int64_t)NV * p.rg / KT;     // stages of the whole virtual depth
     const int64_t g0 = div_u(vg * x, X);
     n_bs = (int)(div_u(vg * (x + 1), X) - g0);
     v0 = g0 * KT;
   }
-  const int n_tot = n_st + n_bs;
+  // First stage of phase 2: right after phase 1, except for fp16 with the
+  // Gram term, whose phase-2 stages run in a loop of their own (another
+  // MFMA type; a branch between the two inside one loop makes the
+  // compiler spill the accumulators): there phase 1 is padded with zero
+  // stages to a whole group of NS.
+  const int p2s = F16G ? (n_st + NS - 1) / NS * NS : n_st;
+  const int n_tot = p2s + n_bs;
 
   // Every operand goes through a buffer descriptor spanning the tile's valid
   // rows: rows past the matrix read as zeros.
@@ -336,10 +357,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int n_lim = p.r - n0 < NTC ? (p.r > n0 ? (int)(p.r - n0) : 0) : NTC;
   const __amdgpu_buffer_rsrc_t mrs = make_rsrc(Msrc + mrow0 * d_in, (uint32_t)m_lim * m_rowb);
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(A + n0 * d_in, (uint32_t)n_lim * n_rowb);
-  const uint32_t b_rowb = (uint32_t)(p.r * ESZ), g_rowb = (uint32_t)((int64_t)NG * p.rg * ESZ);
+  // (phase-2 row operand: B, or for fp16 its bf16 split, 2 rg wide)
+  const int64_t b_ld = F16G ? 2 * p.rg : p.r;
+  const T* Bp = F16G ? reinterpret_cast<const T*>(ws + p.off_bf) : B;
+  const uint32_t b_rowb = (uint32_t)(b_ld * ESZ), g_rowb = (uint32_t)((int64_t)NG * p.rg * ESZ);
   const int g_lim = p.rg - n0 < NTC ? (int)(p.rg - n0) : NTC;
   const T* Gs = reinterpret_cast<const T*>(ws + p.off_gg);
-  const __amdgpu_buffer_rsrc_t brs = make_rsrc(B + mrow0 * p.r, (uint32_t)m_lim * b_rowb);
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(Bp + mrow0 * b_ld, (uint32_t)m_lim * b_rowb);
   const __amdgpu_buffer_rsrc_t grs = make_rsrc(Gs + n0 * NG * p.rg, (uint32_t)g_lim * g_rowb);
 
   // Direct loads: this wave fills blocks wave, wave + NW, ...; lane l lands at
@@ -379,19 +403,37 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // Blocks [b0, b1) of this wave's share of stage i into a ring slot.
   // Stages past the tile (the loop runs a whole number of unrolled groups)
   // and chunks past the valid depth read as zeros, so every step issues the
-  // same loads.
-  auto issue_blocks = [&](int i, char* slot, int b0, int b1) __attribute__((always_inline)) {
-    const bool ph2 = BG || (WB && i >= n_st);       // uniform
-    const int j = i - n_st;
+  // same loads. (gtag: Tag<true> in the loop over fp16's Gram-term stages,
+  // all of whose loads are of phase 2.)
+  auto issue_blocks = [&](int i, char* slot, int b0, int b1, auto gtag) __attribute__((always_inline)) {
+    const bool ph2 = (F16G && decltype(gtag)::value) || BG || (WB && i >= p2s);   // uniform
+    const int j = i - p2s;
     const bool in = ph2 ? j < n_bs : i < n_st;
-    const int64_t ks = ph2 ? v0 + (int64_t)j * KT : k0 + (int64_t)i * KT;   // column-operand depth
-    const int64_t km = (ph2 && ks >= p.rg) ? ks - p.rg : ks;              // row-operand depth
-    const uint32_t kb_m = (uint32_t)((in ? km : 0) * ESZ), kb_n = (uint32_t)((in ? ks : 0) * ESZ);
+    // Column-operand depth ks (phase 2: into the virtual depth), and the
+    // depths km into the row operand's rows (B's in phase 2) and kc into
+    // the column operand's (phase 2: rows of [Ghi | Glo]).
+    int64_t ks, km, kc;
+    if constexpr (F16G) {
+      // fp16's three parts run over [B_hi | B_lo | B_hi] and [Ghi ; Ghi ;
+      // Glo]: km is the virtual depth k2 in parts 0 and 1 and k2 - 2 rg in
+      // part 2, kc is k2 in part 0 and k2 - rg after. (32-bit: k2 < 3 rg.)
+      const int32_t rg = (int32_t)p.rg, k2 = (int32_t)v0 + j * KT;
+      const int32_t kr = k2 >= rg ? k2 - rg : k2;
+      ks = ph2 ? (int64_t)k2 : k0 + (int64_t)i * KT;
+      km = ph2 ? (int64_t)(kr >= rg ? kr - rg : k2) : ks;
+      kc = ph2 ? (int64_t)kr : ks;
+    } else {
+      ks = ph2 ? v0 + (int64_t)j * KT : k0 + (int64_t)i * KT;
+      km = (ph2 && ks >= p.rg) ? ks - p.rg : ks;   // B's columns against Ghi, then Glo
+      kc = ks;
+    }
+    const uint32_t kb_m = (uint32_t)((in ? km : 0) * ESZ), kb_n = (uint32_t)((in ? kc : 0) * ESZ);
     if constexpr (C::LEAN) {
       // Valid elements left in the operands' rows from this stage's depth
       // (uniform; 0 past the tile), against which each lane's first element
-      // is compared in 32 bits. Gram rows are never short.
-      const int64_t lm = in ? (ph2 ? p.r : d_in) - km : 0;
+      // is compared in 32 bits. Gram rows and fp16's split B rows (zero past
+      // r) are never short.
+      const int64_t lm = in ? ((F16G && ph2) ? (int64_t)KT : (ph2 ? p.r : d_in) - km) : 0;
       const int64_t ln = in ? (ph2 ? (int64_t)KT : d_in - ks) : 0;
       const int32_t rm = (int32_t)(lm < KT ? lm : KT), rn = (int32_t)(ln < KT ? ln : KT);
       const bool okm = lane_k < rm, okn = lane_k < rn;
@@ -419,7 +461,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       }
       return;
     }
-    const bool ok_m = in && km + (int64_t)a_chunk * EPC < (ph2 ? p.r : d_in);
+    const bool ok_m = in && ((F16G && ph2) || km + (int64_t)a_chunk * EPC < (ph2 ? p.r : d_in));
     const bool ok_n = in && (ph2 || ks + (int64_t)a_chunk * EPC < d_in);
 #pragma unroll
     for (int b = 0; b < BPW; ++b) {
@@ -506,7 +548,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       }
     }
   };
-  auto mfma_step = [&](const Frag& F, bool w_stage, int s) __attribute__((always_inline)) {
+  // (gtag: Tag<true> in the loop over fp16's Gram-term stages)
+  auto mfma_step = [&](const Frag& F, bool w_stage, int s, auto gtag) __attribute__((always_inline)) {
+    if constexpr (F16G && decltype(gtag)::value) {
+      // Gram-term stage (fp16): B's bf16 parts against the bf16 Gram rows.
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[a][b] = Mfma<bf16_t>::run(F[a], F[MB + b], acc[a][b]);
+      return;
+    }
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
@@ -541,7 +592,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   // than as a stage of zeros beside it in the unrolled pair. The extra code
   // stays within the register budget of tiles of up to 6 blocks per wave;
   // larger ones keep the zero stage (their tail spilled).
-  constexpr bool PEEL = NS == 2 && MB * NB <= 6;
+  constexpr bool PEEL = NS == 2 && MB * NB <= 6 && !F16G;
   const int n_loop = PEEL ? (n_tot & ~1) : n_pad;   // stages the unrolled loop runs
   Frag H[C::LEAN ? 1 : 2];
   // With two slots each stage's loads are spread over the stage before it:
@@ -554,12 +605,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   constexpr bool SPREAD = NS == 2;
   constexpr int COL_PER_STEP = (BPW - C::BPW_M + KSTEPS - 2) / (KSTEPS - 1);
   if constexpr (SPREAD) {
-    issue_blocks(0, ring(0), 0, BPW);
-    issue_blocks(1, ring(1), 0, C::BPW_M);
+    issue_blocks(0, ring(0), 0, BPW, Tag<false>{});
+    issue_blocks(1, ring(1), 0, C::BPW_M, Tag<false>{});
     wait_vm_lgkm0<C::BPW_M>();   // stage 0 complete; stage 1's row-operand blocks in flight
   } else {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) issue_blocks(j, ring(j), 0, BPW);
+    for (int j = 0; j < NS; ++j) issue_blocks(j, ring(j), 0, BPW, Tag<false>{});
     wait_vm_lgkm0<(NS - 1) * BPW>();   // stage 0 complete; stages 1 .. NS-1 in flight
   }
   barrier_keep_loads();
@@ -570,14 +621,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     // meanwhile). After the last step of stage i every wave has read all of
     // stage i: wait for stage i+1's loads, barrier, reload stage i's slot
     // with stage i+NS, read stage i+1's first step.
-    for (int i0 = 0; i0 < n_pad; i0 += NS) {
+    auto lean_group = [&](int i0, auto gtag) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int i = i0 + j;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
           __builtin_amdgcn_sched_barrier(0);
-          mfma_step(H[0], i < n_st, s);
+          mfma_step(H[0], i < n_st, s, gtag);
           __builtin_amdgcn_sched_barrier(0);
           if (s + 1 < KSTEPS) {
             read_step(ring(j), s + 1, H[0]);
@@ -587,23 +638,27 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
               const int c0 = C::BPW_M + s * COL_PER_STEP;
               const int c1 = c0 + COL_PER_STEP < BPW ? c0 + COL_PER_STEP : BPW;
               __builtin_amdgcn_sched_barrier(0);
-              issue_blocks(i + 1, ring((j + 1) % NS), c0, c1);
+              issue_blocks(i + 1, ring((j + 1) % NS), c0, c1, gtag);
             }
           } else {
             wait_vm_lgkm0<(NS - 2) * BPW>();   // (with two slots: every load issued so far)
             barrier_keep_loads();
             if constexpr (SPREAD) {
-              issue_blocks(i + NS, ring(j), 0, C::BPW_M);
+              issue_blocks(i + NS, ring(j), 0, C::BPW_M, gtag);
             } else {
-              issue_blocks(i + NS, ring(j), 0, BPW);
+              issue_blocks(i + NS, ring(j), 0, BPW, gtag);
             }
             read_step(ring((j + 1) % NS), 0, H[0]);
           }
         }
       }
+    };
+    for (int i0 = 0; i0 < (F16G ? p2s : n_pad); i0 += NS) lean_group(i0, Tag<false>{});
+    if constexpr (F16G) {
+      for (int i0 = p2s; i0 < n_pad; i0 += NS) lean_group(i0, Tag<true>{});
     }
-  } else
-  for (int i0 = 0; i0 < n_loop; i0 += NS) {
+  } else {
+  auto plain_group = [&](int i0, auto gtag) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int i = i0 + j;
@@ -615,23 +670,28 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
             const int c0 = C::BPW_M + s * COL_PER_STEP;
             const int c1 = c0 + COL_PER_STEP < BPW ? c0 + COL_PER_STEP : BPW;
             __builtin_amdgcn_sched_barrier(0);
-            issue_blocks(i + 1, ring((j + 1) % NS), c0, c1);
+            issue_blocks(i + 1, ring((j + 1) % NS), c0, c1, gtag);
           }
         } else {
           wait_vm_lgkm0<(NS - 2) * BPW>();
           barrier_keep_loads();
           if constexpr (SPREAD) {
-            issue_blocks(i + NS, ring(j), 0, C::BPW_M);
+            issue_blocks(i + NS, ring(j), 0, C::BPW_M, gtag);
           } else {
-            issue_blocks(i + NS, ring(j), 0, BPW);
+            issue_blocks(i + NS, ring(j), 0, BPW, gtag);
           }
           read_step(ring((j + 1) % NS), 0, H[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(H[s & 1], i < n_st, s);
+        mfma_step(H[s & 1], i < n_st, s, gtag);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  for (int i0 = 0; i0 < (F16G ? p2s : n_loop); i0 += NS) plain_group(i0, Tag<false>{});
+  if constexpr (F16G) {
+    for (int i0 = p2s; i0 < n_loop; i0 += NS) plain_group(i0, Tag<true>{});
+  }
   }
   if constexpr (PEEL && !C::LEAN) {
     if (n_tot & 1) {
@@ -642,7 +702,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
       for (int s = 0; s < KSTEPS; ++s) {
         if (s + 1 < KSTEPS) read_step(ring(0), s + 1, H[(s + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(H[s & 1], i < n_st, s);
+        mfma_step(H[s & 1], i < n_st, s, Tag<false>{});
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1105,13 +1165,64 @@ __device__ __forceinline__ void store_gram(char* ws, const NormPlan& p, int64_t 
 // so every global access is along a row. The stored matrix is gscale * G
 // (one rounded product per element): s/2 when the W pass runs the Gram term
 // in its own accumulators, 1 otherwise.
+//
+// fp16 with the Gram term in the W pass: the workgroups past the n_red
+// reduction blocks split B exactly into bf16 hi + lo (f16_split_bf16) for
+// it, into the workspace as [d_out][B_hi | B_lo], each part rg columns wide
+// and zero past r.
 constexpr int kReduceThreads = 1024;
 
+// Workgroups of the split of B: each covers whole rows, ppr rows per pass
+// of 1024 threads (one 8-column chunk per thread), at most kSplitBlocks.
+constexpr int kSplitBlocks = 512;
+DORA_HD int split_rows_per_pass(int64_t rg) {
+  const int64_t cpr = rg / 8;
+  return cpr < kReduceThreads ? (int)(kReduceThreads / cpr) : 1;
+}
+int64_t split_blocks(const NormPlan& p) {
+  const int64_t rpp = split_rows_per_pass(p.rg);
+  const int64_t n = (p.d_out + rpp - 1) / rpp;
+  return n < kSplitBlocks ? n : kSplitBlocks;
+}
+
+__device__ void split_b(const NormPlan& p, const f16_t* __restrict__ B, char* __restrict__ ws, int blk, int nblk) {
+  const int cpr = (int)(p.rg / 8);                        // 8-column chunks per part
+  const int cw = cpr < kReduceThreads ? cpr : kReduceThreads;   // threads across a row
+  const int rpp = kReduceThreads / cw;
+  const int ro = (int)threadIdx.x / cw, c0 = (int)threadIdx.x - ro * cw;
+  if (ro >= rpp) return;
+  bf16_t* dst = reinterpret_cast<bf16_t*>(ws + p.off_bf);
+  const bool vec = (p.r & 7) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+  for (int64_t i = (int64_t)blk * rpp + ro; i < p.d_out; i += (int64_t)nblk * rpp) {
+    const f16_t* row = B + i * p.r;
+    bf16_t* out = dst + i * 2 * p.rg;
+    for (int c8 = c0; c8 < cpr; c8 += cw) {
+      const int64_t c = (int64_t)c8 * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (vec) {
+        if (c < p.r) v = *reinterpret_cast<const u32x4*>(row + c);
+      } else {
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = c + e < p.r ? row[c + e] : (f16_t)0;
+        v = __builtin_bit_cast(u32x4, h);
+      }
+      *reinterpret_cast<u32x4*>(out + c) = f16_split_bf16(v, false);
+      *reinterpret_cast<u32x4*>(out + p.rg + c) = f16_split_bf16(v, true);
+    }
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws, float gscale) {
+__global__ __launch_bounds__(kReduceThreads) void gram_reduce_kernel(NormPlan p, char* __restrict__ ws, float gscale,
+                                                                     const f16_t* __restrict__ Bsplit, int n_red) {
   constexpr int RG = kReduceThreads / 32;   // row groups; each thread owns 32 / RG rows
   constexpr int RPT = 32 / RG;
   __shared__ float tile[32][33];
+  if ((int)blockIdx.x >= n_red) {
+    split_b(p, Bsplit, ws, (int)blockIdx.x - n_red, (int)gridDim.x - n_red);
+    return;
+  }
   if (p.asm_fused && blockIdx.x == 0) {
     // arrival counters of the W pass that follows (which assembles)
     unsigned* cnt = reinterpret_cast<unsigned*>(ws + p.off_cnt);
@@ -1469,9 +1580,6 @@ template <int MODE, typename H>
 hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, const void* A, const void* B,
                        char* ws, hipStream_t st, Marks& mk, const AssembleArgs& aa = AssembleArgs{}) {
   constexpr bool GRAM = MODE == kPassGram;
-  // The Gram term inside the W pass needs the Gram matrix in the storage
-  // type (bf16 hi + lo, or fp32); fp16 keeps it in fp32 and never plans it.
-  if constexpr (MODE == kPassWB && sizeof(H) == 2 && !__is_same(H, bf16_t)) return hipErrorInvalidValue;
   if (p.fast) {
     // The Gram pass only uses the 64- and 128-column configurations.
     switch (fcfg) {
@@ -1805,10 +1913,10 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   char* ws = static_cast<char*>(ws_);
   Marks mk{events, events != nullptr ? n_events : 0, 0};
   const bool fold = p.fast && p.gfold;
-  // bf16 and fp32 on the streaming path run the Gram term in the W pass's
-  // accumulators against (s/2) G; fp16 runs its Gram term in fp32 on B
-  // widened, so it keeps the separate pass.
-  const bool fuse = p.fast && !p.gfold && p.dtype != 2;
+  // On the streaming path the Gram term runs in the W pass's accumulators
+  // against (s/2) G: bf16 and fp16 against its bf16 hi + lo parts (fp16
+  // splitting B's fragments into bf16 hi + lo as well), fp32 against fp32.
+  const bool fuse = p.fast && !p.gfold;
   hipError_t e = begin_marks(mk, st);
   if (e != hipSuccess) return e;
   if (fold) {
@@ -1828,11 +1936,17 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   const int64_t w_grid = (int64_t)p.xw * ((p.d_out + fast_rows(p.fcfg) - 1) / fast_rows(p.fcfg)) * p.n_nt;
   const bool asm_in_w = fuse && w_grid <= kGrid && (int64_t)p.xw * p.n_nt <= kSumBatch;
   q.asm_fused = asm_in_w ? 1 : 0;   // the reduction zeroes the W pass's arrival counters
-  // bf16 keeps G as bf16 hi + lo for the bf16 Gram term; fp32 and fp16 keep
-  // it in fp32 (fp16's range cannot hold every G) for the fp32 Gram term.
-  hipLaunchKernelGGL(p.dtype == 0 ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
-                     dim3((unsigned)tri_count(p.rg / 32)), dim3(kReduceThreads), 0, st, q, ws,
-                     fuse ? 0.5f * s : 1.0f);
+  // G is kept as bf16 hi + lo for the bf16 Gram term (bf16, and fp16 with
+  // the Gram term in the W pass), in fp32 otherwise (fp32, and fp16's own
+  // Gram-term pass, which runs in fp32 on B widened: fp16's range cannot
+  // hold every G).
+  // (fp16 with the Gram term in the W pass: B's split rides along.)
+  const bool split = fuse && p.dtype == 2;
+  const int64_t n_red = tri_count(p.rg / 32);
+  const int64_t n_split = split ? split_blocks(p) : 0;
+  hipLaunchKernelGGL((p.dtype == 0 || split) ? gram_reduce_kernel<bf16_t> : gram_reduce_kernel<float>,
+                     dim3((unsigned)(n_red + n_split)), dim3(kReduceThreads), 0, st, q, ws, fuse ? 0.5f * s : 1.0f,
+                     split ? static_cast<const f16_t*>(B) : nullptr, (int)n_red);
   e = launched(st, mk);
   if (e != hipSuccess) return e;
   if (fuse) {

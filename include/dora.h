@@ -61,8 +61,9 @@ typedef enum dora_status {
 typedef enum dora_dtype {
   DORA_BF16 = 0, /* bfloat16 storage, fp32 arithmetic */
   DORA_F32 = 1,  /* binary32 storage and arithmetic   */
-  DORA_F16 = 2   /* binary16 storage, fp32 arithmetic (accumulation and the
-                    Gram term in fp32: G may exceed binary16's range) */
+  DORA_F16 = 2   /* binary16 storage, fp32 arithmetic (accumulation in fp32;
+                    G = A A^T, which may exceed binary16's range, is held as
+                    bf16 hi + lo or in fp32) */
 } dora_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -110,7 +111,7 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
  * separate Gram pass; gram grid and ranges then do not apply), else 0,
  * 1 if the streaming Gram pass computes only the tiles on and above the
  * diagonal of G, else 0, and 1 if the streaming W pass also runs the Gram
- * term (B G) . B in its own accumulators (bf16 and fp32 when G is not
+ * term (B G) . B in its own accumulators (every dtype when G is not
  * folded in; no separate Gram-term pass), else 0, the index of the W
  * pass among the call's launches (see dora_factored_norm_marked), and 1 if
  * every operand tile of the streaming kernel spans less than 2^31 bytes
@@ -181,14 +182,13 @@ dora_status dora_factored_norm(const void* W, const void* A, const void* B, int 
  * recorded event adds a little time between launches, so a caller that
  * times one launch passes only the two events around it). Nothing is kept
  * after the call returns. Launches of one call, in order:
- *   bf16, fp32 (G not folded in): Gram pass, gram_reduce,
- *     W pass with the Gram term (and the assembly when the W pass runs
- *     in one round of at most 256 workgroups with at most 16 partials per
- *     row), assembly otherwise;
+ *   G not folded in: Gram pass, gram_reduce (fp16: which also splits B
+ *     into bf16 hi + lo for the W pass), W pass with the Gram term (and
+ *     the assembly when the W pass runs in one round of at most 256
+ *     workgroups with at most 16 partials per row), assembly otherwise;
  *   G folded into the W pass (plan field gram_folded): W pass with G,
- *     gram_reduce, Gram term (+ assembly with several Gram-term tiles);
- *   fp16: Gram pass, gram_reduce, W pass, widening of B, Gram term
- *     (+ assembly with several Gram-term tiles);
+ *     gram_reduce, (fp16: widening of B,) Gram term (+ assembly with
+ *     several Gram-term tiles);
  *   dense fused (plan mode 3): dense pass, assembly;
  *   s == 0, r == 0 or d_in == 0: one row-sum launch.
  * (These are the streaming-path launches, used when W, A and B allow

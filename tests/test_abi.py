@@ -80,8 +80,8 @@ def test_plans_of_the_workloads(name):
     # square 128-column Gram tiles are the symmetric ones
     assert info["gram_symmetric"] == (info["gram_tile_cols"] == 128 and w.dtype != "f32")
     assert info["tile_cols"] * info["col_tiles"] >= w.r
-    # the Gram term runs inside the W pass unless G is folded into it (or fp16)
-    assert info["gram_term_fused"] == int(not info["gram_folded"] and w.dtype != "f16")
+    # the Gram term runs inside the W pass unless G is folded into it
+    assert info["gram_term_fused"] == int(not info["gram_folded"])
     # launch order: [Gram pass, gram_reduce,] W pass, ...
     assert info["w_launch"] == (0 if info["gram_folded"] else 2)
 

@@ -87,6 +87,14 @@ CASES = [
     ("dense_f16_ragged", 70, 264, 136, "f16", 0.75, 47),
     ("dense_many_col_tiles", 64, 8192, 64, "bf16", 0.5, 48),
     ("dense_big_s_neg", 96, 1032, 1024, "bf16", -4.0, 49),
+    # fp16 with the Gram term inside the W pass (B split into bf16 hi + lo
+    # against G's bf16 hi + lo): the 256 x 384 tile whole, negative s, d_in
+    # ranges of odd stage counts (phase 1 padded with a zero stage), two
+    # column tiles
+    ("f16_tall_r384_fused", 8192, 8192, 384, "f16", 0.5, 65),
+    ("f16_neg_s_fused", 600, 1024, 384, "f16", -0.5, 66),
+    ("f16_odd_stages", 700, 1088, 256, "f16", 0.75, 67),
+    ("f16_r512_two_col_tiles", 700, 1536, 512, "f16", 0.25, 68),
 ]
 
 
@@ -160,6 +168,9 @@ GRAM_ALONE = [
     ("tall_r384", 8192, 8192, 384, "bf16", 0.5),
     ("tall_r320_ragged", 7950, 8256, 320, "bf16", -0.25),
     ("tall_r768_two_col_tiles", 8192, 8192, 768, "bf16", 0.25),
+    # fp16: B's bf16 hi + lo against G's, three parts of the virtual depth
+    ("f16_r384_fused", 1000, 1024, 384, "f16", 0.5),
+    ("f16_tall_r384_fused", 8192, 8192, 384, "f16", -0.5),
 ]
 
 
