@@ -54,7 +54,7 @@ PLAN_FIELDS = (
     "mode", "tile_cols", "col_tiles", "gram_tile_cols", "gram_col_tiles", "fast_cfg", "gen_cfg",
     "gram_fast_cfg", "gram_gen_cfg", "granule", "granules", "w_ranges", "gram_ranges", "workspace_bytes",
     "w_grid", "gram_grid", "lds_bytes", "tile_rows", "gram_folded", "gram_symmetric", "gram_term_fused",
-    "w_launch", "offsets32", "dense_row_tiles", "dense_col_tiles",
+    "w_launch", "offsets32", "dense_row_tiles", "dense_col_tiles", "die_groups",
 )
 
 _lib = None

@@ -262,6 +262,12 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
     p.xg = xg;
     layout(p);
     if (p.ws_bytes <= budget) {
+      // The W pass that carries the Gram term runs in the die grid of two
+      // range groups where its grid allows (B's rows, which its epilogue
+      // reads, then leave memory for two dies instead of one per range).
+      // With G folded in, the plain order was faster.
+      const int64_t n_mt = ceil_div(d_out, dora::fast_rows(p.fcfg));
+      p.die_groups = !p.gfold && dora::die_grid_fits(2, p.xw, n_mt, p.n_nt) ? 2 : 0;
       plan_dense(p, budget);
       *out = p;
       return DORA_OK;
@@ -306,6 +312,7 @@ bool plan_self_check(const NormPlan& p) {
   const int64_t grid_w = p.xw * ceil_div(p.d_out, 64) * p.n_nt;
   const int64_t grid_g = p.xg * ceil_div(p.r, 64) * p.n_nt_g;
   if (grid_w >= ((int64_t)1 << 31) || grid_g >= ((int64_t)1 << 31)) return false;
+  if (p.die_groups != 0 && !dora::die_grid_fits(p.die_groups, p.xw, ceil_div(p.d_out, fw), p.n_nt)) return false;
   if (p.off_cross < p.off_base + (size_t)(p.xw * p.ld_w) * 4) return false;
   if (p.off_ba < p.off_cross + (size_t)(p.xw * p.n_nt * p.ld_w) * 4) return false;
   if (p.off_g < p.off_ba + (size_t)(ba_planes(p) * p.ld_w) * 4) return false;
@@ -313,6 +320,26 @@ bool plan_self_check(const NormPlan& p) {
   if (p.off_bf < p.off_gg + (size_t)(p.rg * p.rg) * 4) return false;
   if (p.off_cnt < p.off_bf + (p.dtype == DORA_F16 ? (size_t)(p.d_out * p.rg) * 4 : 0)) return false;
   return p.ws_bytes >= p.off_cnt + (size_t)ceil_div(p.d_out, fw) * 4;
+}
+
+// Host replay of the streaming W pass's workgroup order (w_tile): every
+// (range, row tile, column tile) exactly once. O(grid) time and memory, so
+// only for plan queries, on grids of up to 2^22 workgroups.
+bool w_order_covers_grid(const NormPlan& p) {
+  if (p.mode != dora::kModeFactored && p.mode != dora::kModeDense) return true;
+  const int64_t n_mt = ceil_div(p.d_out, dora::fast_rows(p.fcfg)), grid = (int64_t)p.xw * n_mt * p.n_nt;
+  if (grid > ((int64_t)1 << 22)) return true;
+  std::vector<bool> seen((size_t)grid, false);
+  for (int64_t b = 0; b < grid; ++b) {
+    int x, n;
+    int64_t m;
+    dora::w_tile(b, p.xw, n_mt, p.n_nt, p.die_groups, &x, &m, &n);
+    if (x < 0 || x >= p.xw || m < 0 || m >= n_mt || n < 0 || n >= p.n_nt) return false;
+    const size_t id = (size_t)((m * p.n_nt + n) * p.xw + x);
+    if (seen[id]) return false;
+    seen[id] = true;
+  }
+  return true;
 }
 
 // The streaming kernel addresses every operand tile through a buffer
@@ -401,7 +428,7 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   NormPlan p;
   const dora_status st = make_plan(d_out, d_in, r, dtype, s, budget_bytes, &p);
   if (st != DORA_OK) return st;
-  if (!plan_self_check(p)) return DORA_ERR_INVALID_ARG;
+  if (!plan_self_check(p) || !w_order_covers_grid(p)) return DORA_ERR_INVALID_ARG;
   const bool f = p.mode == dora::kModeFactored || p.mode == dora::kModeDense;   // (dense: its fallback)
   const int64_t grid_w = f ? p.xw * ceil_div(p.d_out, dora::fast_rows(p.fcfg)) * p.n_nt : 0;
   const int64_t grid_g = !f ? 0
@@ -412,7 +439,8 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
                           f ? (int64_t)dora::fast_kernel_lds_bytes(p.fcfg) : 0, f ? dora::fast_rows(p.fcfg) : 0,
                           f ? p.gfold : 0, f ? p.gsym : 0, f ? (int64_t)(!p.gfold) : 0,
                           f ? (p.mode == dora::kModeDense || p.gfold ? 0 : 2) : 0, f ? (int64_t)offsets_fit_32(p) : 1,
-                          p.mode == dora::kModeDense ? p.dn_rt : 0, p.mode == dora::kModeDense ? p.dn_ct : 0};
+                          p.mode == dora::kModeDense ? p.dn_rt : 0, p.mode == dora::kModeDense ? p.dn_ct : 0,
+                          f ? p.die_groups : 0};
   const int nv = (int)(sizeof(vals) / sizeof(vals[0]));
   for (int i = 0; i < n_info && i < nv; ++i) info[i] = vals[i];
   for (int i = nv; i < n_info; ++i) info[i] = -1;

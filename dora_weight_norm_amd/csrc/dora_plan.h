@@ -118,10 +118,10 @@ struct NormPlan {
   int64_t ld_w;         // padded W rows of the base / cross partials
   int64_t ga_rows;      // padded A rows of the Gram partials
   int64_t ga_cols;      // padded Gram columns: n_nt * ntc
-  int64_t rg;           // side of the reduced Gram matrix: r rounded up to 64 for bf16
-                        // (its Gram term runs over the depth [hi | lo] in 64-deep stages,
-                        // so the seam between the parts must fall on a stage boundary),
-                        // to 32 otherwise
+  int64_t rg;           // side of the reduced Gram matrix: r rounded up to 64 for the
+                        // 16-bit types (their Gram term runs over a depth of several
+                        // parts in 64-deep stages, so the seams between the parts must
+                        // fall on stage boundaries), to 32 for fp32
   int bcfg;             // Gram-term pass (streaming kernel): 128-column blocks per tile (bf16)
   int n_bt;             // Gram-term column tiles of the streaming kernel
   int n_cb;             // Gram-term column tiles of the general kernel (kGramCols columns each)
@@ -133,6 +133,8 @@ struct NormPlan {
   size_t off_bf;        // fp16 inputs only: B widened to fp32 [d_out][r], or split to bf16 [d_out][B_hi | B_lo]
   size_t off_cnt;       // [row tiles of the W pass] uint32 arrival counters (assembly in the W pass)
   int asm_fused;        // set per call: the W pass with the Gram term also assembles wnorm and g
+  int die_groups;       // W pass with the Gram term: d_in range groups of its die grid
+                        // (w_tile), 0 for the plain order
   int dn_rt, dn_ct;     // dense mode: row tiles over d_out, column tiles over d_in
   int64_t ld_d;         // dense mode: padded rows of the column-tile partials
   size_t off_dense;     // dense mode: [dn_ct][ld_d] fp32 partial sums of (W + s B A)^2
@@ -154,6 +156,53 @@ DORA_HD int64_t range_lo(int64_t n_gran, int X, int x) { return div_u(n_gran * x
 DORA_HD int64_t range_k0(const NormPlan& p, int X, int x) {
   const int64_t k = range_lo(p.n_gran, X, x) * p.gran;
   return k < p.d_in ? k : p.d_in;
+}
+
+// Whether the W pass's grid of X d_in ranges x n_mt row tiles x n_nt column
+// tiles takes the die grid of `groups` range groups (see w_tile).
+DORA_HD bool die_grid_fits(int groups, int X, int64_t n_mt, int n_nt) {
+  if (groups < 1 || groups > kDies || kDies % groups != 0) return false;
+  return X % groups == 0 && n_mt % (kDies / groups) == 0;
+}
+
+// Tile (d_in range x, row tile m, column tile n) of W-pass workgroup b, for
+// a grid of X ranges, n_mt row tiles and n_nt column tiles. Workgroups are
+// dealt to the kDies dies in turn (die = b mod kDies), each die with its
+// own L2, and launch in increasing b. In every order the column tiles of
+// one (range, row tile) run on one die, kDies apart in launch order, so
+// the W rows they share come from memory once.
+//  - groups > 0 (die grid): the dies form `groups` range groups by kDies /
+//    groups row groups; a die runs the ranges of its range group with the
+//    row tiles of its row group. A's columns of a range are then fetched by
+//    kDies / groups dies and B's rows of a row tile (read in the epilogue)
+//    by `groups` dies, instead of once and kDies times (groups = kDies, die
+//    = range, the plain order at X = kDies). Needs die_grid_fits.
+//  - groups == 0: x = b mod X, then row tiles and column tiles; with
+//    several column tiles, (range, row tile) pairs in that order by die.
+DORA_HD void w_tile(int64_t b, int X, int64_t n_mt, int n_nt, int groups, int* x, int64_t* m, int* n) {
+  if (groups > 0) {
+    const int lo = (int)(b % kDies);
+    const int64_t g8 = b / kDies;
+    *n = (int)(g8 % n_nt);
+    const int64_t s = g8 / n_nt;   // (range, row tile) pair of this die
+    const int xa = X / groups, rows = kDies / groups;
+    *x = (lo % groups) * xa + (int)(s % xa);
+    *m = (s / xa) * rows + lo / groups;
+    return;
+  }
+  if (n_nt > 1 && (X * n_mt * n_nt) % (kDies * n_nt) == 0) {
+    const int lo = (int)(b % kDies);
+    const int64_t g8 = b / kDies;
+    *n = (int)(g8 % n_nt);
+    const int64_t u = (g8 / n_nt) * kDies + lo;
+    *x = (int)(u % X);
+    *m = u / X;
+    return;
+  }
+  *x = (int)(b % X);
+  const int64_t t = b / X;
+  *m = t / n_nt;
+  *n = (int)(t - *m * n_nt);
 }
 
 }  // namespace dora

@@ -302,19 +302,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     if (MT == NTC && p.gsym) tri_tile(t, n_nt, &m, &n);   // upper-triangle tiles only
   }
   if constexpr (WP) {
-    // Workgroups are dealt to the kDies dies (each with its own L2) in
-    // turn: die = blockIdx mod kDies. Give all column tiles of a (row
-    // tile, d_in range) one die, kDies apart in launch order, so that the
-    // W rows they share come from HBM once and from that die's L2 after.
-    // (A relabelling of the same grid: u runs over the (d_in range, row
-    // tile) pairs, n over the column tiles.)
-    if (n_nt > 1 && gridDim.x % (kDies * n_nt) == 0) {
-      const int lo = blockIdx.x % kDies, g8 = blockIdx.x / kDies;
-      n = g8 % n_nt;
-      const int u = (g8 / n_nt) * kDies + lo;
-      x = u % X;
-      m = u / X;
-    }
+    // W pass: the order of w_tile (by die; the die grid where planned).
+    int64_t mm;
+    w_tile(blockIdx.x, X, (m_rows + MT - 1) / MT, n_nt, p.die_groups, &x, &mm, &n);
+    m = (int)mm;
   }
   const int64_t mrow0 = (int64_t)m * MT;
   const int64_t n0 = (int64_t)n * NTC;

@@ -69,8 +69,49 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# Itanium-ABI codes of the template arguments the library's kernels take.
+_MANGLED_TYPES = {"t": "unsigned short", "DF16_": "_Float16", "f": "float", "b": "bool", "i": "int"}
+
+
+def demangle_ours(name: str) -> str:
+    """A kernel name of this library as rocprofv3 prints it demangled.
+
+    rocprofv3 leaves a name mangled when its demangler does not know a type
+    in it (_Float16, code DF16_). The library's kernels are templates in
+    namespace dora::(anonymous) over types and integers only, so their
+    names are decoded here: identifier, then template arguments (types of
+    _MANGLED_TYPES and integer literals L<type><value>E). Other names are
+    returned as they are."""
+    m = re.match(r"_ZN4dora12_GLOBAL__N_1(\d+)", name)
+    if not m:
+        return name
+    i = m.end()
+    ident = name[i:i + int(m.group(1))]
+    i += len(ident)
+    args = []
+    if name.startswith("I", i):
+        i += 1
+        while i < len(name) and name[i] != "E":
+            lit = re.match(r"L([a-z])(n?\d+)E", name[i:])
+            if lit:
+                val = lit.group(2).replace("n", "-")
+                args.append({"0": "false", "1": "true"}[val] if lit.group(1) == "b" else val)
+                i += lit.end()
+                continue
+            for code, typ in _MANGLED_TYPES.items():
+                if name.startswith(code, i):
+                    args.append(typ)
+                    i += len(code)
+                    break
+            else:
+                return name   # not a form this decoder knows
+    targs = f"<{', '.join(args)}>" if args else ""
+    return f"void dora::(anonymous namespace)::{ident}{targs}()"
+
+
 def kernel_role(name: str) -> str | None:
     """Which part of the hot path a kernel belongs to (None: not ours)."""
+    name = demangle_ours(name)
     if "dora::" not in name:
         return None
     if "compose_bwd" in name:
@@ -82,7 +123,8 @@ def kernel_role(name: str) -> str | None:
 
 
 def short_name(name: str) -> str:
-    n = name.replace("(anonymous namespace)::", "").replace("unsigned short", "bf16")
+    n = demangle_ours(name).replace("(anonymous namespace)::", "").replace("unsigned short", "bf16")
+    n = n.replace("_Float16", "f16")
     n = re.sub(r"\(dora::NormPlan.*$|\(.*$", "", n)
     n = n.replace("void dora::", "").replace("dora::", "")
     m = re.match(r"norm_fast_kernel<(.*)>", n)

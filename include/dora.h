@@ -117,8 +117,11 @@ dora_status dora_norm_workspace_size(int64_t d_out, int64_t d_in, int64_t r, int
  * every operand tile of the streaming kernel spans less than 2^31 bytes
  * (its 32-bit buffer offsets; otherwise the general kernel runs), else 0,
  * and in mode 3 the dense pass's row tiles (64 rows) and column tiles (128
- * columns of d_in), else 0 and 0; the streaming fields apply when W, A and
- * B allow aligned 16-byte loads.
+ * columns of d_in), else 0 and 0, and the d_in range groups of the
+ * streaming W pass's die grid (the dies as range groups by row groups, so
+ * that B's rows of a row tile are fetched by that many dies instead of one
+ * die per range), 0 where it keeps the plain order; the streaming fields
+ * apply when W, A and B allow aligned 16-byte loads.
  * Entries past the last field are set to -1.
  * Before returning it replays the plan on the host and checks that the
  * d_in ranges tile d_in exactly, every grid fits and every partial sum the

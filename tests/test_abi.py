@@ -84,6 +84,12 @@ def test_plans_of_the_workloads(name):
     assert info["gram_term_fused"] == int(not info["gram_folded"])
     # launch order: [Gram pass, gram_reduce,] W pass, ...
     assert info["w_launch"] == (0 if info["gram_folded"] else 2)
+    # the W pass with the Gram term runs in the die grid of two range groups
+    # (by four row groups) where its ranges and row tiles divide evenly; the
+    # plan query has replayed its order on the host (every tile once)
+    n_mt = -(-w.d_out // info["tile_rows"])
+    fits = info["w_ranges"] % 2 == 0 and n_mt % 4 == 0
+    assert info["die_groups"] == (2 if fits and not info["gram_folded"] else 0)
 
 
 def test_plan_self_check_on_many_shapes():
@@ -93,8 +99,11 @@ def test_plan_self_check_on_many_shapes():
     shapes += [tuple(int(v) for v in (rng.integers(1, 5000), rng.integers(1, 9000), rng.integers(1, 1100)))
                for _ in range(40)]
     for (d_out, d_in, r) in shapes:
-        for dt in ("bf16", "f32"):
+        for dt in ("bf16", "f32", "f16"):
+            # (the query replays the W pass's workgroup order on the host and
+            # fails unless it covers every tile exactly once)
             info = bnd.dora_norm_plan_info(d_out, d_in, r, dt, 0.5, 256 * MiB)
+            assert info["die_groups"] in (0, 2)
             assert info["mode"] == (3 if dense_rule(d_out, d_in, r, dt) else 2), (d_out, d_in, r, dt)
             assert info["tile_cols"] * info["col_tiles"] >= r
             if info["mode"] == 3:

@@ -46,6 +46,23 @@ def test_kernel_roles_and_short_names():
     assert prof.is_main_pass(d) and prof.is_main_pass(w) and not prof.is_main_pass(g)
 
 
+def test_names_left_mangled_by_the_profiler():
+    # rocprofv3 prints a name mangled when it holds _Float16 (DF16_); the
+    # library's own names are decoded, others pass through
+    red = "_ZN4dora12_GLOBAL__N_118gram_reduce_kernelItEEvNS_8NormPlanEPcfPKDF16_i"
+    assert prof.demangle_ours(red) == "void dora::(anonymous namespace)::gram_reduce_kernel<unsigned short>()"
+    assert prof.kernel_role(red) == "norm" and prof.short_name(red) == "gram_reduce_kernel<bf16>"
+    w16 = ("_ZN4dora12_GLOBAL__N_116norm_fast_kernelIDF16_Li2ELi4ELi4ELi3ELi64ELi2ELi4EEEvNS_8NormPlanEPKT_S5_S5_"
+           "PcNS0_12AssembleArgsE")
+    assert prof.short_name(w16) == "norm_fast_kernel<f16, 2, 4, 4, 3, 64, 2, 4> (W pass + Gram term)"
+    assert prof.is_main_pass(w16)
+    lay = "_ZN4dora12_GLOBAL__N_114compose_kernelIDF16_Li8ELb1EEEvPKT_S4_PKffllPS2_"
+    assert prof.kernel_role(lay) == "layer_output"
+    assert prof.kernel_role("_ZN4dora12_GLOBAL__N_114compose_kernelIDF16_Li8ELb0EEEvPKT_") == "compose"
+    other = "_ZN2at6native29vectorized_elementwise_kernelILi4EEEvi"
+    assert prof.demangle_ours(other) == other and prof.kernel_role(other) is None
+
+
 def test_copy_calibration():
     # a 1 GiB copy whose counter reads 512 MiB (in KiB) scales by 2
     per = {"__amd_rocclr_copyBuffer": [1024.0, 524288.0],
