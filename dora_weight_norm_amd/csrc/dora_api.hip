@@ -223,9 +223,9 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   const int64_t rq = dtype == DORA_F32 ? 32 : 64;   // (16-bit: the Gram term's parts meet on 64-deep stages)
   p.rg = ceil_div(r, rq) * rq;
   // Tiles of the separate Gram-term pass (run when the Gram term is not
-  // inside the W pass: G folded into the W pass, fp16, the general path):
-  // the streaming kernel covers up to 384 columns of G in one tile (bf16;
-  // 128 for fp32, and for fp16, whose Gram term runs in fp32) and uses
+  // inside the W pass: G folded into the W pass, the general path): the
+  // streaming kernel covers up to 384 columns of G in one tile (bf16; 128
+  // for fp32, and for fp16, whose separate Gram term runs in fp32) and uses
   // 256-column tiles beyond; the general kernel uses kGramCols.
   if (dtype == DORA_BF16) {
     p.bcfg = p.rg <= 384 ? (int)ceil_div(p.rg, 128) : 2;

@@ -13,20 +13,21 @@
 //                 d_in range): U = W A^T on the matrix cores, dotted with B
 //                 row by row at the end (cross term; U is never stored), and
 //                 the W fragments squared on the way (base term). On the
-//                 streaming path (bf16, fp32) each workgroup then runs its
+//                 streaming path (every dtype) each workgroup then runs its
 //                 share of the Gram term's depth, B against (s/2) G, in the
 //                 same accumulators: the dot with B at the end is then
 //                 cross + (s/2) ba, since the Gram term (B G) . B is linear
-//                 in B G.
+//                 in B G. (fp16: B and G as bf16 hi + lo, on the bf16
+//                 matrix cores.)
 //   assemble      fixed-order sums of all partials;
 //                 wnorm = sqrt(max(base + 2s cross + s^2 ba, 0)) and
 //                 g = m / max(wnorm, eps) without contraction, with
 //                 correctly rounded sqrt and division (same page, §1.2.2,
 //                 §5.2, §6.2).
-// Otherwise (fp16, the general kernels, and G folded into the W pass) the
-// Gram term is a pass of its own after the W pass: (B G) on the matrix cores
-// (B Ghi + B Glo for bf16), dotted with B, with the assembly fused in when
-// one tile covers all of G's columns.
+// Otherwise (the general kernels, and G folded into the W pass) the Gram
+// term is a pass of its own after the W pass: (B G) on the matrix cores
+// (B Ghi + B Glo for bf16; fp32 for fp16, on B widened), dotted with B,
+// with the assembly fused in when one tile covers all of G's columns.
 // When the streaming W pass has a single column tile of at most 128 columns
 // (all of A's rows in each stage) it also computes the blocks of G, and the
 // order becomes W pass, gram_reduce, Gram term: the separate Gram pass, and
