@@ -309,3 +309,13 @@ def test_no_kernel_uses_scratch_or_spills_vector_registers():
     assert lean and all(int(d["VGPRs"]) + int(d["AGPRs"]) <= 256 and d["Occupancy_[waves/SIMD]"] == "2"
                         for d in lean)
     assert find("norm_dense_kernel") and find("compose_kernel") and find("compose_bwd_kernel")
+
+
+def test_die_grid_edge_shapes_plan_as_the_gpu_cases_assume():
+    # tests/test_gpu_norm.py runs these shapes for the die grid's edges:
+    # two d_in ranges (one per range group) with several column tiles, and
+    # four ranges with one column tile
+    two = bnd.dora_norm_plan_info(4096, 512, 1536, "bf16", 0.5, 256 * MiB)
+    assert two["mode"] == 2 and two["die_groups"] == 2 and two["w_ranges"] == 2 and two["col_tiles"] > 1
+    four = bnd.dora_norm_plan_info(8192, 512, 192, "bf16", -0.25, 256 * MiB)
+    assert four["mode"] == 2 and four["die_groups"] == 2 and four["w_ranges"] == 4 and four["col_tiles"] == 1

@@ -95,6 +95,11 @@ CASES = [
     ("f16_neg_s_fused", 600, 1024, 384, "f16", -0.5, 66),
     ("f16_odd_stages", 700, 1088, 256, "f16", 0.75, 67),
     ("f16_r512_two_col_tiles", 700, 1536, 512, "f16", 0.25, 68),
+    # the die grid of the W pass with the Gram term at its edges: two d_in
+    # ranges (one per range group) with several column tiles, and four
+    # ranges with one column tile
+    ("die_grid_two_ranges", 4096, 512, 1536, "bf16", 0.5, 69),
+    ("die_grid_four_ranges", 8192, 512, 192, "bf16", -0.25, 70),
 ]
 
 
