@@ -230,13 +230,38 @@ __device__ __forceinline__ void assemble_sums(float base, float cross, float ba,
   }
 }
 
+// ordered_sum over partials that other workgroups of the running kernel
+// stored as device-scope atomics: each load is a device-scope atomic load
+// too, so it reads the value those stores made visible on every die and
+// never a stale line of this die's L2.
+__device__ __forceinline__ float ordered_sum_device(const float* p, int64_t stride, int n) {
+  float acc = 0.f;
+  for (int i = 0; i < n; i += kSumBatch) {
+    float v[kSumBatch];
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u)
+      v[u] = (i + u < n) ? __hip_atomic_load(p + (int64_t)(i + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.f;
+#pragma unroll
+    for (int u = 0; u < kSumBatch; ++u)
+      if (i + u < n) acc += v[u];
+  }
+  return acc;
+}
+
+// Row j's base and cross partials summed in plane order, then assembled.
+// DEVICE: the partials were stored as device-scope atomics by workgroups of
+// the running kernel (the W pass's own assembly); otherwise by an earlier
+// kernel.
+template <bool DEVICE = false>
 __device__ __forceinline__ void assemble_row(const NormPlan& p, const char* ws, float s, float eps, const float* m,
                                              float* wnorm, float* g, int64_t j, float ba) {
   const float* part_base = reinterpret_cast<const float*>(ws + p.off_base);
   const float* part_cross = reinterpret_cast<const float*>(ws + p.off_cross);
   // Cross partials are planes (x, n) in the order x * n_nt + n.
-  const float base = ordered_sum(part_base + j, p.ld_w, p.xw);
-  const float cross = ordered_sum(part_cross + j, p.ld_w, p.xw * p.n_nt);
+  const float base = DEVICE ? ordered_sum_device(part_base + j, p.ld_w, p.xw) : ordered_sum(part_base + j, p.ld_w, p.xw);
+  const float cross = DEVICE ? ordered_sum_device(part_cross + j, p.ld_w, p.xw * p.n_nt)
+                             : ordered_sum(part_cross + j, p.ld_w, p.xw * p.n_nt);
   assemble_sums(base, cross, ba, s, eps, m, wnorm, g, j);
 }
 
@@ -833,29 +858,49 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
     } else {
       float* part = reinterpret_cast<float*>(ws + (BG ? p.off_ba : p.off_cross));
       const int64_t plane = (int64_t)x * n_nt + n;
+      // With the assembly in this pass (asm_fused) the partials are stored
+      // as device-scope atomics: written through to where every die reads
+      // them, so no write-back of the die's L2 is needed before they are
+      // counted in (below).
+      const bool dev = WB && p.asm_fused;
       if (tid < MT) {
         float cs = 0.f;
 #pragma unroll
         for (int gi = 0; gi < WN; ++gi) cs += red[gi * MT + tid];
-        part[plane * p.ld_w + mrow0 + tid] = cs;
+        float* cp = part + plane * p.ld_w + mrow0 + tid;
+        if (dev) {
+          __hip_atomic_store(cp, cs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          *cp = cs;
+        }
         if constexpr (WP) {
           if (n == 0) {
             float bs = 0.f;
 #pragma unroll
             for (int gi = 0; gi < WN; ++gi) bs += red_base[gi * MT + tid];
-            reinterpret_cast<float*>(ws + p.off_base)[(int64_t)x * p.ld_w + mrow0 + tid] = bs;
+            float* bp = reinterpret_cast<float*>(ws + p.off_base) + (int64_t)x * p.ld_w + mrow0 + tid;
+            if (dev) {
+              __hip_atomic_store(bp, bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              *bp = bs;
+            }
           }
         }
       }
       if constexpr (WB) {
         if (p.asm_fused) {
           // The row tile's last workgroup to finish assembles its rows
-          // (nobody waits). Each wave's partial stores complete, then one
-          // thread counts this workgroup in with release ordering at device
-          // scope (the die's L2 is written back, so the partials are visible
-          // on every die); the workgroup that brings the count to the row
-          // tile's total takes an acquire fence and sums every partial of
-          // its rows in the fixed plane order. The counters were zeroed by
+          // (nobody waits). Each wave waits until its device-scope partial
+          // stores are acknowledged (vmcnt(0): the device has them), then
+          // one thread counts the workgroup in with a device-scope atomic
+          // add; the workgroup that brings the count to the row tile's
+          // total sums every partial of its rows in the fixed plane order,
+          // with device-scope loads. Every access to the partials and the
+          // counter is a device-scope atomic and the count is taken only
+          // after the stores completed, so the last workgroup reads every
+          // partial; no fence is needed (a release fence would write back
+          // the die's whole L2, an acquire fence would invalidate it under
+          // the workgroups still streaming W). The counters were zeroed by
           // the reduction launched before this pass.
           __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores have completed
           __syncthreads();
@@ -863,14 +908,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
           if (tid == 0) {
             unsigned* cnt = reinterpret_cast<unsigned*>(ws + p.off_cnt) + m;
             const unsigned total = (unsigned)(X * n_nt);
-            const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            const int is_last = old + 1u == total;
-            if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            *last = is_last;
+            const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *last = old + 1u == total;
           }
           __syncthreads();
           if (*last != 0 && tid < MT && mrow0 + tid < p.d_out)
-            assemble_row(p, ws, aa.s, aa.eps, aa.m, aa.wnorm, aa.g, mrow0 + tid, 0.f);
+            assemble_row<true>(p, ws, aa.s, aa.eps, aa.m, aa.wnorm, aa.g, mrow0 + tid, 0.f);
         }
       }
     }
@@ -1920,11 +1963,11 @@ hipError_t launch_norm_factored(const NormPlan& p, const void* W, const void* A,
   NormPlan q = p;
   if (fold) q.xg = p.xw;   // one Gram partial per W-pass range
   // The W pass assembles only when its workgroups run in one round and each
-  // row has at most one batch of partials: every workgroup then pays its
-  // release fence (a write-back of its die's L2, a few us of the CU's time)
-  // once, against the separate assembly launch it saves; over several rounds
-  // the fences add up, and with many partials per row one thread per row
-  // sums them too slowly.
+  // row has at most one batch of partials: every workgroup then waits once
+  // for its partial stores to reach the device and for its count, against
+  // the separate assembly launch that saves; over several rounds those
+  // waits add up, and with many partials per row one thread per row sums
+  // them too slowly.
   const int64_t w_grid = (int64_t)p.xw * ((p.d_out + fast_rows(p.fcfg) - 1) / fast_rows(p.fcfg)) * p.n_nt;
   const bool asm_in_w = fuse && w_grid <= kGrid && (int64_t)p.xw * p.n_nt <= kSumBatch;
   q.asm_fused = asm_in_w ? 1 : 0;   // the reduction zeroes the W pass's arrival counters
