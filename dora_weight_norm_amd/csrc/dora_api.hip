@@ -80,8 +80,17 @@ void choose_tiles(NormPlan& p) {
     } else {
       p.ntc = 256, p.fcfg = dora::kFastT256, p.gcfg = dora::kGenB256;
     }
+    // Gram pass: square tiles of 64 where their upper triangle times 8 d_in
+    // ranges fits the chip (r <= 384): with half the rows per tile each
+    // workgroup loads half as much, against 128-row tiles (measured: 70.2
+    // against 68.6 us for the norm call at 8192 x 8192, r = 384; slower at
+    // r = 768, where 64-row tiles make 78 of them). Their column count is
+    // kept a multiple of 128, the general kernel's tile (which runs the Gram
+    // pass when the inputs do not allow 16-byte loads).
     if (p.ntc == 64) {
       p.ntc_g = 64, p.fcfg_g = dora::kFastB64, p.gcfg_g = dora::kGenB64;
+    } else if (dora::tri_count(2 * ceil_div(r, 128)) * 8 <= dora::kGrid) {
+      p.ntc_g = 64, p.fcfg_g = dora::kFastG64, p.gcfg_g = dora::kGenB128;
     } else {
       p.ntc_g = 128, p.fcfg_g = dora::kFastB128, p.gcfg_g = dora::kGenB128;
     }
@@ -89,7 +98,7 @@ void choose_tiles(NormPlan& p) {
   }
   p.ntc_gen = p.fcfg == dora::kFastT384 ? 192 : p.ntc;
   p.n_nt = (int)ceil_div(r, p.ntc);
-  p.n_nt_g = (int)ceil_div(r, p.ntc_g);
+  p.n_nt_g = p.fcfg_g == dora::kFastG64 ? (int)(2 * ceil_div(r, 128)) : (int)ceil_div(r, p.ntc_g);
 }
 
 // Column tiles of the W pass on either kernel: the cross partials are laid
@@ -244,11 +253,12 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
   const int64_t nbc = p.rg / 32;
   p.gfold = p.n_nt == 1 && p.ntc <= 128 &&
             nbc * nbc <= (int64_t)dora::fast_waves(p.fcfg) * ceil_div(d_out, dora::fast_rows(p.fcfg));
-  // The 128 x 128 Gram tiles are square, so only those on and above the
-  // diagonal are computed (the reduction reads the rest transposed); with a
-  // third less work per range, the Gram pass can split d_in further.
-  p.gsym = p.fcfg_g == dora::kFastB128;
-  const int64_t ntg = ceil_div(r, dora::kGramTile);
+  // The 128 x 128 and 64 x 64 Gram tiles are square, so only those on and
+  // above the diagonal are computed (the reduction reads the rest
+  // transposed); with a third less work per range, the Gram pass can split
+  // d_in further.
+  p.gsym = p.fcfg_g == dora::kFastB128 || p.fcfg_g == dora::kFastG64;
+  const int64_t ntg = p.n_nt_g;
   const int64_t tiles_g = p.gsym ? dora::tri_count(ntg) : ceil_div(r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g;
   const int64_t plane = p.ga_rows * p.ga_cols * 4;
   const int64_t written = p.gsym ? plane * dora::tri_count(ntg) / (ntg * ntg) : plane;
@@ -432,7 +442,7 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
   const bool f = p.mode == dora::kModeFactored || p.mode == dora::kModeDense;   // (dense: its fallback)
   const int64_t grid_w = f ? p.xw * ceil_div(p.d_out, dora::fast_rows(p.fcfg)) * p.n_nt : 0;
   const int64_t grid_g = !f ? 0
-                             : p.xg * (p.gsym ? dora::tri_count(ceil_div(p.r, dora::kGramTile))
+                             : p.xg * (p.gsym ? dora::tri_count(p.n_nt_g)
                                               : ceil_div(p.r, dora::fast_rows(p.fcfg_g)) * p.n_nt_g);
   const int64_t vals[] = {p.mode, p.ntc, p.n_nt, p.ntc_g, p.n_nt_g, p.fcfg, p.gcfg, p.fcfg_g, p.gcfg_g, p.gran,
                           p.n_gran, p.xw, p.xg, (int64_t)p.ws_bytes, grid_w, grid_g,

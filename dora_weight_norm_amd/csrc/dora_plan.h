@@ -37,16 +37,17 @@ enum FastCfg : int {
   kFastT64 = 7,    // bf16, 256 x 64, 8 waves
   kFastT128 = 8,   // bf16, 256 x 128, 8 waves
   kFastT384 = 9,   // bf16, 256 x 384, 8 waves of 128 x 96 (lean register mode)
+  kFastG64 = 10,   // bf16, 64 x 64, 4 waves (Gram pass, square tiles)
 };
 // Rows per workgroup tile, and waves per workgroup, of a streaming
 // configuration.
 DORA_HD int fast_rows(int cfg) {
+  if (cfg == kFastG64) return 64;
   return cfg == kFastT64 || cfg == kFastT128 || cfg == kFastT192 || cfg == kFastT256 || cfg == kFastT384 ? 256
                                                                                                        : 128;
 }
-DORA_HD int fast_waves(int cfg) { return cfg == kFastF32 ? 4 : 8; }
+DORA_HD int fast_waves(int cfg) { return cfg == kFastF32 || cfg == kFastG64 ? 4 : 8; }
 constexpr int kGramCols = 64;      // columns of G per Gram-term tile (general kernel)
-constexpr int kGramTile = 128;     // side of the square streaming Gram-pass tile
 
 // Number of tiles on and above the diagonal of an nt x nt tile grid, and
 // the (row, column) tile of upper-triangle tile t in row-major order.
@@ -112,7 +113,7 @@ struct NormPlan {
   int xw;               // d_in ranges of the W pass
   int xg;               // d_in ranges of the Gram pass
   int gsym;             // the streaming Gram pass computes only the tiles on and above
-                        // the diagonal (square kGramTile tiles; G is symmetric)
+                        // the diagonal (square kFastB128 or kFastG64 tiles; G is symmetric)
   int gfold;            // the streaming W pass also computes G (no Gram pass); its
                         // Gram partials are then per W-pass range (xw planes)
   int64_t ld_w;         // padded W rows of the base / cross partials

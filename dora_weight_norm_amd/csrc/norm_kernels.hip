@@ -337,7 +337,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void norm_fast_kernel(NormPlan p, 
   const int64_t n0 = (int64_t)n * NTC;
   const int64_t d_in = p.d_in;
   const int64_t m_left = m_rows - mrow0;
-  const int m_lim = m_left < MT ? (int)m_left : MT;   // valid rows of the tile
+  // Valid rows of the tile (none for a square Gram tile past r: the Gram
+  // columns are padded to 128, so 64-row tiles can start at or past r).
+  const int m_lim = m_left <= 0 ? 0 : (m_left < MT ? (int)m_left : MT);
 
   // Stages of the tile, in two phases.
   //  1. (every mode but kPassBG) Msrc rows (W, or A in the Gram pass)
@@ -1616,10 +1618,11 @@ hipError_t launch_pass(const NormPlan& p, int fcfg, int gcfg, const void* M, con
                        char* ws, hipStream_t st, Marks& mk, const AssembleArgs& aa = AssembleArgs{}) {
   constexpr bool GRAM = MODE == kPassGram;
   if (p.fast) {
-    // The Gram pass only uses the 64- and 128-column configurations.
+    // The Gram pass only uses these configurations (64 and 128 columns).
     switch (fcfg) {
       case kFastB64: return launch_fast<H, 4, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st, mk);
       case kFastB128: return launch_fast<H, 2, 4, 2, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st, mk);
+      case kFastG64: return launch_fast<H, 2, 2, 1, 1, 64, 4, MODE>(p, M, A, B, ws, aa, st, mk);
       case kFastF32: return launch_fast<float, 4, 1, 1, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st, mk);
       case kFastF128: return launch_fast<float, 2, 4, 2, 1, 32, 4, MODE>(p, M, A, B, ws, aa, st, mk);
       default: break;
@@ -2054,6 +2057,7 @@ size_t fast_kernel_lds_bytes(int cfg) {
   switch (cfg) {
     case kFastB64: return DORA_LDS(4, bf16_t, 4, 2, 1, 1, 64);
     case kFastB128: return DORA_LDS(4, bf16_t, 2, 4, 2, 1, 64);
+    case kFastG64: return DORA_LDS(4, bf16_t, 2, 2, 1, 1, 64);
     case kFastB256: return DORA_LDS(3, bf16_t, 2, 4, 2, 2, 64);
     case kFastT64: return DORA_LDS(3, bf16_t, 4, 2, 2, 1, 64);
     case kFastT128: return DORA_LDS(3, bf16_t, 4, 2, 2, 2, 64);

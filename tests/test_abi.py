@@ -74,11 +74,19 @@ def test_plans_of_the_workloads(name):
     assert info["gram_grid"] <= 256 and info["lds_bytes"] <= 160 * 1024
     # the W pass: one workgroup per (row tile, d_in range)
     assert info["w_grid"] == -(-w.d_out // info["tile_rows"]) * info["col_tiles"] * info["w_ranges"]
-    nt = -(-w.r // 128)
-    tiles_g = nt * (nt + 1) // 2 if info["gram_symmetric"] else nt * info["gram_col_tiles"]
+    # square Gram tiles (128 x 128, or 64 x 64 where 8 ranges of their upper
+    # triangle fit the chip) are the symmetric ones
+    square = info["gram_fast_cfg"] in (1, 10)
+    assert info["gram_symmetric"] == (square and w.dtype != "f32")
+    if info["gram_symmetric"]:
+        nt = info["gram_col_tiles"]
+        assert nt * info["gram_tile_cols"] == -(-w.r // 128) * 128
+        tiles_g = nt * (nt + 1) // 2
+        n64 = 2 * -(-w.r // 128)
+        assert (info["gram_tile_cols"] == 64) == (w.r > 64 and n64 * (n64 + 1) // 2 * 8 <= 256)
+    else:
+        tiles_g = -(-w.r // 128) * info["gram_col_tiles"]
     assert info["gram_grid"] == tiles_g * info["gram_ranges"]
-    # square 128-column Gram tiles are the symmetric ones
-    assert info["gram_symmetric"] == (info["gram_tile_cols"] == 128 and w.dtype != "f32")
     assert info["tile_cols"] * info["col_tiles"] >= w.r
     # the Gram term runs inside the W pass unless G is folded into it
     assert info["gram_term_fused"] == int(not info["gram_folded"])

@@ -75,6 +75,9 @@ CASES = [
     # keeps its own 192-column tiles, whose partials the layout also holds
     ("tall_r300_general", 8000, 8256, 300, "bf16", -0.5, 39),
     ("tall_r384_general", 8000, 8193, 384, "bf16", 0.5, 41),
+    # 64 x 64 square Gram tiles over columns padded to 128: the last tiles
+    # start past r and read nothing
+    ("gram64_tiles_past_r", 500, 1024, 136, "bf16", 0.5, 43),
     # two 384-column tiles (384 < r <= 768), the second one ragged
     ("tall_r696_two_col_tiles", 8000, 8192, 696, "bf16", 0.25, 42),
     # the dense fused pass (r >= d_out, 16-bit, d_in and r multiples of 8):
