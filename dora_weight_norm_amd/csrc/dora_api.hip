@@ -275,9 +275,21 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
       // The W pass that carries the Gram term runs in the die grid of two
       // range groups where its grid allows (B's rows, which its epilogue
       // reads, then leave memory for two dies instead of one per range).
-      // With G folded in, the plain order was faster.
+      // A grid of several rounds takes four range groups where they fit:
+      // between rounds each die's L2 sees its share of W go through and
+      // loses A, so every round fetches the die's ranges of A again, and
+      // two ranges per die halve that against four ranges (B's rows then
+      // leave memory for four dies). With G folded in, the plain order was
+      // faster.
       const int64_t n_mt = ceil_div(d_out, dora::fast_rows(p.fcfg));
-      p.die_groups = !p.gfold && dora::die_grid_fits(2, p.xw, n_mt, p.n_nt) ? 2 : 0;
+      const bool rounds = (int64_t)p.xw * n_mt * p.n_nt > dora::kGrid;
+      if (p.gfold) {
+        p.die_groups = 0;
+      } else if (rounds && dora::die_grid_fits(4, p.xw, n_mt, p.n_nt)) {
+        p.die_groups = 4;
+      } else {
+        p.die_groups = dora::die_grid_fits(2, p.xw, n_mt, p.n_nt) ? 2 : 0;
+      }
       plan_dense(p, budget);
       *out = p;
       return DORA_OK;

@@ -93,11 +93,20 @@ def test_plans_of_the_workloads(name):
     # launch order: [Gram pass, gram_reduce,] W pass, ...
     assert info["w_launch"] == (0 if info["gram_folded"] else 2)
     # the W pass with the Gram term runs in the die grid of two range groups
-    # (by four row groups) where its ranges and row tiles divide evenly; the
-    # plan query has replayed its order on the host (every tile once)
+    # (by four row groups) where its ranges and row tiles divide evenly, of
+    # four range groups (by two row groups) when its grid runs in several
+    # rounds and they fit; the plan query has replayed its order on the host
+    # (every tile once)
     n_mt = -(-w.d_out // info["tile_rows"])
-    fits = info["w_ranges"] % 2 == 0 and n_mt % 4 == 0
-    assert info["die_groups"] == (2 if fits and not info["gram_folded"] else 0)
+    assert info["die_groups"] == die_groups_rule(info["w_ranges"], n_mt, info["col_tiles"], info["gram_folded"])
+
+
+def die_groups_rule(xw, n_mt, n_nt, folded):
+    if folded:
+        return 0
+    if xw * n_mt * n_nt > 256 and xw % 4 == 0 and n_mt % 2 == 0:
+        return 4
+    return 2 if xw % 2 == 0 and n_mt % 4 == 0 else 0
 
 
 def test_plan_self_check_on_many_shapes():
@@ -111,7 +120,11 @@ def test_plan_self_check_on_many_shapes():
             # (the query replays the W pass's workgroup order on the host and
             # fails unless it covers every tile exactly once)
             info = bnd.dora_norm_plan_info(d_out, d_in, r, dt, 0.5, 256 * MiB)
-            assert info["die_groups"] in (0, 2)
+            assert info["die_groups"] in (0, 2, 4)
+            if info["mode"] in (2, 3):
+                n_mt = -(-d_out // info["tile_rows"])
+                assert info["die_groups"] == die_groups_rule(info["w_ranges"], n_mt, info["col_tiles"],
+                                                             info["gram_folded"]), (d_out, d_in, r, dt)
             assert info["mode"] == (3 if dense_rule(d_out, d_in, r, dt) else 2), (d_out, d_in, r, dt)
             assert info["tile_cols"] * info["col_tiles"] >= r
             if info["mode"] == 3:
@@ -327,3 +340,15 @@ def test_die_grid_edge_shapes_plan_as_the_gpu_cases_assume():
     assert two["mode"] == 2 and two["die_groups"] == 2 and two["w_ranges"] == 2 and two["col_tiles"] > 1
     four = bnd.dora_norm_plan_info(8192, 512, 192, "bf16", -0.25, 256 * MiB)
     assert four["mode"] == 2 and four["die_groups"] == 2 and four["w_ranges"] == 4 and four["col_tiles"] == 1
+    # grids of several rounds, the last one partial, in four range groups
+    # (by two row groups), with 192- and 256-column tiles; the 28672 x 8192,
+    # r = 512 workload plans the same way
+    multi = bnd.dora_norm_plan_info(4608, 1024, 384, "bf16", 0.5, 256 * MiB)
+    assert multi["mode"] == 2 and multi["die_groups"] == 4 and multi["col_tiles"] == 2
+    assert multi["w_grid"] % 256 != 0 and multi["w_grid"] > 512 and multi["w_ranges"] == 16
+    assert multi["tile_cols"] == 192
+    wide = bnd.dora_norm_plan_info(8704, 512, 448, "bf16", -0.5, 256 * MiB)
+    assert wide["mode"] == 2 and wide["die_groups"] == 4 and wide["col_tiles"] == 2
+    assert wide["tile_cols"] == 256 and wide["w_grid"] > 256 and wide["w_ranges"] == 8
+    mlp = bnd.dora_norm_plan_info(28672, 8192, 512, "bf16", 0.5, 256 * MiB)
+    assert mlp["die_groups"] == 4 and mlp["w_grid"] > 256

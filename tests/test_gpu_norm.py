@@ -103,6 +103,11 @@ CASES = [
     # ranges with one column tile
     ("die_grid_two_ranges", 4096, 512, 1536, "bf16", 0.5, 69),
     ("die_grid_four_ranges", 8192, 512, 192, "bf16", -0.25, 70),
+    # grids of several rounds (the last one partial) in the die grid of four
+    # range groups: 192-column tiles over 16 d_in ranges, and 256-column
+    # tiles (r past the last tile's edge) over 8
+    ("die_grid_four_groups_rounds", 4608, 1024, 384, "bf16", 0.5, 71),
+    ("die_grid_four_groups_256_cols", 8704, 512, 448, "bf16", -0.5, 72),
 ]
 
 
