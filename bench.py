@@ -370,17 +370,51 @@ def comparisons(args, w, bnd, Wd, Ad, Bd, based, lorad, g, md, comp_ms, norm_ms,
     }
 
 
+def eager_factored_norm(W, A, B, s, chunk):
+    """||W + s B A||_row by the three-term identity in eager PyTorch, fp32
+    ("DoRA优化技术解析：从内存瓶颈到高效实现", cyqw.cn, §1.2, §1.2.1): the
+    row sums of W^2 and U = W A^T built over d_in chunks of `chunk` columns
+    (the pages' budget rule bounds the fp32 copy of a chunk), then
+    cross = rowsum(B * U) and ba = rowsum((B G) * B) with G = A A^T. The
+    comparison baseline for the whole layer; not the library's path."""
+    import torch
+
+    d_out, d_in = W.shape
+    sq = torch.zeros(d_out, dtype=torch.float32, device=W.device)
+    U = torch.zeros(d_out, A.shape[0], dtype=torch.float32, device=W.device)
+    for c0 in range(0, d_in, chunk):
+        Wc = W[:, c0:c0 + chunk].float()
+        sq += Wc.square().sum(dim=1)
+        U += torch.mm(Wc, A[:, c0:c0 + chunk].float().t().contiguous())
+    Bf = B.float()
+    Af = A.float()
+    G = torch.mm(Af, Af.t().contiguous())
+    cross = (Bf * U).sum(dim=1)
+    ba = (torch.mm(Bf, G) * Bf).sum(dim=1)
+    return torch.sqrt(torch.clamp_min(sq + 2 * s * cross + s * s * ba, 0))
+
+
 def linear_forward(args, w, I, Wd, Ad, Bd, md, stream, tdt):
     """The whole DoRA linear layer at this workload's T (not part of a step):
     x W^T and (x A^T) B^T by hipBLASLt, the factored norm and the single-pass
-    layer output by libdora; beside it the plain LoRA layer (the same two
-    products, then base + s * lora) to show what DoRA's magnitude costs."""
+    layer output by libdora. Beside it:
+    - the plain LoRA layer (the same two products, then base + s * lora), to
+      show what DoRA's magnitude costs;
+    - the same layer in eager PyTorch in the pages' standard form (the
+      factored norm in fp32 over d_in chunks, g = m / max(wnorm, eps), the
+      stable compose (g-1) base + g (s lora) in fp32 added to base), the
+      baseline of the pages' end-to-end speed-ups (cyqw.cn, §3.1, §6.1
+      Table 9);
+    - and in PEFT's form (the dense norm of W + s (B @ A), then the compose
+      in the storage dtype, cyqw.cn, §1.1)."""
     import torch
 
+    from dora_weight_norm_amd import binding as bnd
     from dora_weight_norm_amd.layer import dora_linear
 
     x = torch.from_numpy(I.activations(w.T, w.d_in, w.dtype, w.seed)).cuda().to(tdt)
     reps = max(3, min(args.steps, 20))
+    chunk = bnd.dora_norm_chunk_size(w.d_out, w.d_in, w.budget)
 
     def dora():
         return dora_linear(x, Wd, Ad, Bd, md, w.s, eps=w.eps, budget_bytes=w.budget)
@@ -388,11 +422,33 @@ def linear_forward(args, w, I, Wd, Ad, Bd, md, stream, tdt):
     def lora():
         return torch.mm(x, Wd.t()) + w.s * torch.mm(torch.mm(x, Ad.t()), Bd.t())
 
-    for fn in (dora, lora):
+    def standard():
+        base = torch.mm(x, Wd.t())
+        lora_out = torch.mm(torch.mm(x, Ad.t()), Bd.t())
+        g = md / torch.clamp_min(eager_factored_norm(Wd, Ad, Bd, w.s, chunk), w.eps)
+        bf = base.float()
+        delta = (g - 1) * bf + g * (w.s * lora_out.float())
+        return (bf + delta).to(tdt)
+
+    def peft():
+        base = torch.mm(x, Wd.t())
+        lora_out = torch.mm(torch.mm(x, Ad.t()), Bd.t())
+        wnorm = torch.linalg.norm(Wd + w.s * (Bd @ Ad), dim=1).float()
+        g = (md / torch.clamp_min(wnorm, w.eps)).to(tdt)
+        return base + ((g - 1) * base + g * (w.s * lora_out))
+
+    y_fused = dora()
+    y_std = standard()
+    for fn in (lora, peft):
         fn()
     torch.cuda.synchronize()
+    # the fused layer against the standard form: both round y once from fp32
+    agree = ((y_fused.float() - y_std.float()).abs().max() / y_std.float().abs().max().clamp_min(1e-30)).item()
+    del y_fused, y_std
     dora_ms = _event_ms(dora, reps, stream)
     lora_ms = _event_ms(lora, reps, stream)
+    std_ms = _event_ms(standard, reps, stream)
+    peft_ms = _event_ms(peft, reps, stream)
     flops = 2 * w.T * w.d_out * w.d_in + 2 * w.T * w.r * (w.d_in + w.d_out)
     return {
         "T": w.T,
@@ -401,8 +457,15 @@ def linear_forward(args, w, I, Wd, Ad, Bd, md, stream, tdt):
         "gemm_tflops": flops / (dora_ms * 1e-3) / 1e12,
         "lora_linear_ms": lora_ms,
         "dora_overhead_vs_lora": dora_ms / lora_ms,
+        "eager_standard_dora_ms": std_ms,
+        "speedup_vs_eager_standard": std_ms / dora_ms,
+        "eager_peft_dora_ms": peft_ms,
+        "speedup_vs_eager_peft": peft_ms / dora_ms,
+        "max_rel_diff_vs_standard": agree,
         "note": "y = x (m V/||V||)^T with V = W + sBA; projections by torch.mm (hipBLASLt), norm and "
-                "output by libdora; lora_linear is torch.mm(x, W^T) + s * (x A^T) B^T",
+                "output by libdora; lora_linear is torch.mm(x, W^T) + s * (x A^T) B^T; eager_standard: "
+                "factored norm in fp32 torch over the budget's d_in chunks and the fp32 stable compose; "
+                "eager_peft: dense norm of W + s (B @ A) and the compose in the storage dtype",
     }
 
 

@@ -31,3 +31,21 @@ def test_headline_work_figures():
     for fused, folded in [(1, 0), (0, 1), (0, 0)]:
         p = {"gram_term_fused": fused, "gram_folded": folded}
         assert bench.w_pass_flops(4096, 4096, 64, p) <= bench.norm_flops(4096, 4096, 64)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 1000])
+def test_eager_factored_norm_baseline_is_the_row_norm(chunk):
+    # The eager baseline of the whole-layer comparison (fp32 torch on the
+    # CPU here) against the dense row norm of W + s B A formed in fp64:
+    # chunks that split d_in unevenly, one chunk past d_in, and s < 0.
+    import numpy as np
+    import torch
+
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((37, 300))
+    A = rng.standard_normal((11, 300)) * 0.2
+    B = rng.standard_normal((37, 11)) * 0.2
+    for s in (0.7, -1.3):
+        ref = np.linalg.norm(W + s * (B @ A), axis=1)
+        got = bench.eager_factored_norm(*(torch.tensor(v, dtype=torch.float32) for v in (W, A, B)), s, chunk)
+        assert np.abs(got.numpy() - ref).max() <= 1e-5 * ref.max()
