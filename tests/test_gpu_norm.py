@@ -14,7 +14,7 @@ from dora_weight_norm_amd import binding as bnd
 from dora_weight_norm_amd import inputs as I
 from oracle import dora_oracle as O
 
-from gpu_helpers import check_g, check_norm, dev, magnitude, say
+from gpu_helpers import check_g, check_norm, check_norm_conditioned, dev, magnitude, say
 
 pytestmark = pytest.mark.gpu
 
@@ -231,6 +231,68 @@ def test_seeded_shape_sweep(k):
     wn, g = _run(W, A, B, dtype, s, m)
     check_norm(wn, ref)
     check_g(g, m, ref, EPS)
+
+
+def _plan_branches():
+    """One shape per branch of the planner: storage type, mode (factored or
+    dense), streaming or general kernel, W-pass and Gram-pass
+    configurations, die grid (plain, two or four range groups), Gram blocks
+    folded in or not, one round of workgroups or several, and whether the W
+    pass may assemble (at most 8 partials per row). Shapes are drawn from a
+    seeded generator (aligned for the streaming kernels 85% of the time),
+    planned on the host, and the cheapest shape of each branch is kept, with
+    d_out * d_in * r at most 3e9 so that the oracle stays fast."""
+    rng = np.random.default_rng(77)
+    best = {}
+    for _ in range(6000):
+        dtype = ["bf16", "bf16", "f16", "f32"][int(rng.integers(0, 4))]
+        q = 4 if dtype == "f32" else 8
+        aligned = rng.random() < 0.85
+        d_out = int(rng.choice([rng.integers(1, 600), rng.integers(600, 3000), rng.integers(3000, 12000)]))
+        d_in = int(rng.choice([rng.integers(1, 128), rng.integers(128, 1024), rng.integers(1024, 9000)]))
+        r = int(rng.choice([rng.integers(1, 128), rng.integers(128, 400), rng.integers(400, 900)]))
+        if aligned:
+            d_in, r = max(q, d_in // q * q), max(q, r // q * q)
+        cost = d_out * d_in * r
+        if cost > 3e9:
+            continue
+        info = bnd.dora_norm_plan_info(d_out, d_in, r, dtype, 0.5, bnd.DEFAULT_BUDGET)
+        fast = d_in % q == 0 and r % q == 0
+        key = (dtype, info["mode"], "fast" if fast else "gen",
+               info["fast_cfg"] if fast else info["gen_cfg"],
+               info["gram_fast_cfg"] if fast else info["gram_gen_cfg"],
+               info["die_groups"] if fast else 0, info["gram_folded"] if fast else 0,
+               "rounds" if info["w_grid"] > 256 else "one", info["w_ranges"] * info["col_tiles"] <= 8)
+        if key not in best or cost < best[key][0]:
+            best[key] = (cost, d_out, d_in, r)
+    out = []
+    for key in sorted(best, key=str):
+        dtype, mode, kind, cfg, gcfg, dg, fold, rounds, few = key
+        name = f"{dtype}-m{mode}-{kind}-c{cfg}-g{gcfg}-dg{dg}-f{fold}-{rounds}-{'few' if few else 'many'}"
+        out.append((name,) + best[key][1:] + (dtype,))
+    return out
+
+
+BRANCHES = _plan_branches()
+
+
+@pytest.mark.parametrize("case", BRANCHES, ids=[c[0] for c in BRANCHES])
+def test_plan_branch_sweep(case):
+    name, d_out, d_in, r, dtype = case
+    k = BRANCHES.index(case)
+    s = 0.5 if k % 2 == 0 else -0.75
+    say(f"[norm-branch] {name}: d_out={d_out} d_in={d_in} r={r} {dtype} s={s}")
+    W, A, B = I.norm_inputs(d_out, d_in, r, dtype, 300 + k)
+    ref = O.dense_row_norm(W, A, B, s)
+    m = magnitude(ref, 300 + k)
+    wn, g = _run(W, A, B, dtype, s, m)
+    # d_in down to 1 and r up to 900: rows where W_j nearly cancels s (BA)_j,
+    # or B G B^T cancels (G of rank d_in < r), are held to the bound of the
+    # fp32 evaluation of the identity; the rest to 1e-5
+    worst, n_ill = check_norm_conditioned(wn, ref, W, A, B, s)
+    well = np.abs(wn.astype(np.float64) - ref) <= 1e-5 * ref
+    check_g(g[well], m[well], ref[well], EPS)
+    say(f"    worst rel err {worst:.2e} on well-conditioned rows; {n_ill} ill-conditioned rows")
 
 
 def test_s_zero_and_zero_sizes():

@@ -1,0 +1,74 @@
+"""The conditioning-aware norm bound of the GPU parity sweep, on the CPU:
+it must accept what an fp32 evaluation of the three-term identity gives on
+ill-conditioned rows, and reject the plausible mistakes (a dropped or
+mis-scaled term, a wrong sign, an error on a well-conditioned row)."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+sys.path.insert(0, os.path.dirname(HERE))
+
+from dora_weight_norm_amd import inputs as I  # noqa: E402
+from gpu_helpers import check_norm_conditioned  # noqa: E402
+from oracle import dora_oracle as O  # noqa: E402
+
+
+def fp32_identity(W, A, B, s, split_g=False, cross_sign=1.0, ba_scale=1.0, s2=None):
+    """wnorm by the identity with every product and sum in fp32 (numpy's
+    float32 matmul and sums), G kept as bf16 hi + lo when split_g (as the
+    kernels keep it for the 16-bit types), optionally with a planted
+    mistake."""
+    f = np.float32
+    W32, A32, B32 = (np.asarray(v, f) for v in (W, A, B))
+    base = (W32 * W32).sum(1, dtype=f)
+    cross = (B32 * (W32 @ A32.T)).sum(1, dtype=f)
+    G = A32 @ A32.T
+    if split_g:
+        hi = O.bf16_round(G).astype(f)
+        G = hi + O.bf16_round(G - hi).astype(f)
+    ba = ((B32 @ G) * B32).sum(1, dtype=f)
+    s2 = f(s * s) if s2 is None else f(s2)
+    n2 = base + f(2 * s) * f(cross_sign) * cross + s2 * f(ba_scale) * ba
+    return np.sqrt(np.maximum(n2, f(0))).astype(f)
+
+
+# d_in of 1 or 2 against r in the hundreds: W_j often nearly cancels
+# s (BA)_j, and G = A A^T has rank d_in, so B G B^T cancels.
+CASES = [(400, 1, 300, "f32", 0.5, 1), (324, 2, 760, "bf16", 0.5, 2), (500, 1, 200, "bf16", -0.75, 3)]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_fp32_identity_meets_the_bound(case):
+    d_out, d_in, r, dtype, s, seed = case
+    W, A, B = I.norm_inputs(d_out, d_in, r, dtype, seed)
+    ref = O.dense_row_norm(W, A, B, s)
+    wn = fp32_identity(W, A, B, s, split_g=dtype != "f32")
+    _, n_ill = check_norm_conditioned(wn, ref, W, A, B, s)
+    assert n_ill > 0   # the case does exercise the ill-conditioned branch
+
+
+@pytest.mark.parametrize("mistake", [dict(ba_scale=0.0), dict(cross_sign=-1.0), dict(s2=0.5), dict(ba_scale=1.01)],
+                         ids=["gram_term_dropped", "cross_sign", "s_for_s_squared", "gram_term_1pct"])
+@pytest.mark.parametrize("case", CASES)
+def test_planted_mistakes_are_rejected(case, mistake):
+    d_out, d_in, r, dtype, s, seed = case
+    W, A, B = I.norm_inputs(d_out, d_in, r, dtype, seed)
+    ref = O.dense_row_norm(W, A, B, s)
+    wn = fp32_identity(W, A, B, s, split_g=dtype != "f32", **mistake)
+    with pytest.raises(AssertionError):
+        check_norm_conditioned(wn, ref, W, A, B, s)
+
+
+def test_well_conditioned_row_keeps_the_strict_bound():
+    W, A, B = I.norm_inputs(64, 512, 32, "bf16", 4)
+    ref = O.dense_row_norm(W, A, B, 0.5)
+    wn = ref.astype(np.float32)
+    check_norm_conditioned(wn, ref, W, A, B, 0.5)
+    wn[7] *= 1 + 2e-5
+    with pytest.raises(AssertionError):
+        check_norm_conditioned(wn, ref, W, A, B, 0.5)
