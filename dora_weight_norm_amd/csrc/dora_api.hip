@@ -175,14 +175,21 @@ int choose_g_ranges(int64_t tiles, int64_t n_gran, int64_t plane_bytes, int max_
   return X;
 }
 
-// Dense mode (see NormMode): 16-bit inputs with r >= d_out, d_in and r in
-// whole 16-byte chunks, and every dense operand within a 32-bit buffer
-// descriptor (A whole, 64 rows of W or of B). Its partials share the
+// Dense mode (see NormMode): 16-bit inputs where B A costs less than the
+// factored terms, d_in and r in whole 16-byte chunks, and every dense
+// operand within a 32-bit buffer descriptor (A whole, 64 rows of W or of
+// B). B A costs d_out d_in r multiply-adds: less than G = A A^T (r^2 d_in)
+// when r >= d_out, and less than the Gram term B G (d_out r^2) when
+// r > d_in. The first rule always holds; the second only where the dense
+// pass measured faster, up to 4096 rows (taller matrices keep the W pass,
+// whose tiles reuse their operands more). Its partials share the
 // workspace with the factored layout, which stays valid as the fallback;
 // the workspace is the larger of the two.
+constexpr int64_t kDenseMaxRowsRankAboveDin = 4096;
 void plan_dense(NormPlan& p, size_t budget) {
   if (p.mode != dora::kModeFactored || (p.dtype != DORA_BF16 && p.dtype != DORA_F16)) return;
-  if (p.r < p.d_out || p.d_in % 8 != 0 || p.r % 8 != 0) return;
+  const bool cheaper = p.r >= p.d_out || (p.r > p.d_in && p.d_out <= kDenseMaxRowsRankAboveDin);
+  if (!cheaper || p.d_in % 8 != 0 || p.r % 8 != 0) return;
   const uint64_t lim = 1ull << 31;
   if ((uint64_t)p.r * (uint64_t)p.d_in * 2u >= lim || (uint64_t)dora::kDenseRows * (uint64_t)p.d_in * 2u >= lim ||
       (uint64_t)dora::kDenseRows * (uint64_t)p.r * 2u >= lim)

@@ -87,7 +87,8 @@ DORA_HD TileShape tile_shape(int cfg) {
 }
 
 // kModeDense: the dense fused pass over tiles of W + s B A (16-bit types,
-// r >= d_out); the plan's factored fields stay valid, so a call whose
+// r >= d_out, or r > d_in with at most 4096 rows); the plan's factored
+// fields stay valid, so a call whose
 // pointers do not allow its 16-byte loads runs the factored path instead,
 // in the same workspace.
 enum NormMode : int { kModeEmpty = 0, kModeRowOnly = 1, kModeFactored = 2, kModeDense = 3 };

@@ -1697,15 +1697,16 @@ hipError_t launch_tail(const NormPlan& p, const void* B, char* ws, float s, cons
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Dense fused row norm, for r >= d_out (16-bit types): per tile of
+// Dense fused row norm, for r >= d_out or r > d_in (16-bit types): per tile of
 // kDenseMT rows by kDenseNT columns of d_in, the tile of W + s B A is formed
 // in the accumulators and squared, and its row sums are stored as one
 // partial per (column tile, row); a second kernel adds each row's partials
 // in column-tile order and takes the root. The definition itself
 // ("DoRA优化技术解析", cyqw.cn, §1.1: ||W + s B A||_row), never materialised:
 // where r >= d_out, the factored form's Gram matrix A A^T (r^2 d_in
-// multiply-adds) outweighs B A (d_out r d_in), so this path does less work
-// and needs no Gram reduction.
+// multiply-adds) outweighs B A (d_out r d_in), and where r > d_in its Gram
+// term B G (d_out r^2) does, so this path does less work and needs no Gram
+// reduction.
 //
 // Workgroup = NW waves (2 x NW/2), each owning 32 rows and 128 / (NW/2)
 // columns of the tile in 32x32 accumulator blocks. The

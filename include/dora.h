@@ -145,8 +145,9 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
  * accumulation is fp32. U never leaves the matrix-core accumulators; BA is
  * never formed.
  *
- * Where r >= d_out (bf16 and fp16, d_in and r multiples of 8, plan mode 3)
- * the Gram matrix would cost more than B A itself, and the call computes
+ * Where r >= d_out, or r > d_in with d_out <= 4096 (bf16 and fp16, d_in
+ * and r multiples of 8, plan mode 3), the Gram matrix or the Gram term
+ * would cost more than B A itself, and the call computes
  * the same wnorm by its definition instead: a dense fused pass forms each
  * 64 x 128 tile of W + s B A in the matrix-core accumulators, squares it
  * and keeps only its row sums (cyqw.cn §1.1), and a second launch adds each

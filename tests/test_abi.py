@@ -51,9 +51,11 @@ def test_chunk_size_matches_oracle_rule(d_out, d_in, budget):
 
 
 def dense_rule(d_out, d_in, r, dtype):
-    """The documented choice of the dense fused pass: 16-bit storage, r >= d_out, d_in and r in whole
-    16-byte chunks, and A (and 64 rows of W or B) under 2^31 bytes."""
-    return (dtype in ("bf16", "f16") and r >= d_out and d_in % 8 == 0 and r % 8 == 0
+    """The documented choice of the dense fused pass: 16-bit storage, r >= d_out (or r > d_in with
+    at most 4096 rows), d_in and r in whole 16-byte chunks, and A (and 64 rows of W or B) under
+    2^31 bytes."""
+    cheaper = r >= d_out or (r > d_in and d_out <= 4096)
+    return (dtype in ("bf16", "f16") and cheaper and d_in % 8 == 0 and r % 8 == 0
             and r * d_in * 2 < 2 ** 31 and 64 * d_in * 2 < 2 ** 31 and 64 * r * 2 < 2 ** 31)
 
 
@@ -336,7 +338,7 @@ def test_die_grid_edge_shapes_plan_as_the_gpu_cases_assume():
     # tests/test_gpu_norm.py runs these shapes for the die grid's edges:
     # two d_in ranges (one per range group) with several column tiles, and
     # four ranges with one column tile
-    two = bnd.dora_norm_plan_info(4096, 512, 1536, "bf16", 0.5, 256 * MiB)
+    two = bnd.dora_norm_plan_info(7168, 512, 768, "bf16", 0.5, 256 * MiB)
     assert two["mode"] == 2 and two["die_groups"] == 2 and two["w_ranges"] == 2 and two["col_tiles"] > 1
     four = bnd.dora_norm_plan_info(8192, 512, 192, "bf16", -0.25, 256 * MiB)
     assert four["mode"] == 2 and four["die_groups"] == 2 and four["w_ranges"] == 4 and four["col_tiles"] == 1

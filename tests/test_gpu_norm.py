@@ -52,7 +52,7 @@ CASES = [
     ("neg_s_fused", 600, 1024, 384, "bf16", -0.5, 26),
     # 256-row tiles whose grid is no multiple of 8 x the column tiles: the
     # column tiles of a row tile are not grouped per die
-    ("unpaired_r384", 600, 64, 384, "bf16", 0.5, 27),
+    ("unpaired_r384", 600, 384, 384, "bf16", 0.5, 27),
     ("unpaired_r512", 300, 128, 512, "bf16", 0.5, 28),
     # element loads with 192- and 256-column tiles (general kernel)
     ("gen_r384_tile", 300, 1001, 384, "bf16", 0.5, 29),
@@ -80,10 +80,13 @@ CASES = [
     ("gram64_tiles_past_r", 500, 1024, 136, "bf16", 0.5, 43),
     # two 384-column tiles (384 < r <= 768), the second one ragged
     ("tall_r696_two_col_tiles", 8000, 8192, 696, "bf16", 0.25, 42),
-    # the dense fused pass (r >= d_out, 16-bit, d_in and r multiples of 8):
-    # ragged row and column tiles, r short of a 64-deep stage, one row, many
-    # column tiles, fp16, r == d_out
+    # the dense fused pass (r >= d_out, or r > d_in with at most 4096 rows;
+    # 16-bit, d_in and r multiples of 8): ragged row and column tiles, r
+    # short of a 64-deep stage, one row, many column tiles, fp16,
+    # r == d_out, r just above d_in with d_out at the 4096 limit and above r
     ("dense_kv_f16", 512, 3584, 768, "f16", 0.25, 43),
+    ("dense_r_above_d_in", 4096, 504, 512, "bf16", 0.5, 48),
+    ("dense_r_above_d_in_f16", 2000, 256, 384, "f16", -0.5, 49),
     ("dense_ragged", 100, 1000, 200, "bf16", 0.5, 44),
     ("dense_r_eq_d_out", 256, 2048, 256, "bf16", -0.5, 45),
     ("dense_one_row", 1, 8, 8, "bf16", 2.0, 46),
@@ -101,7 +104,7 @@ CASES = [
     # the die grid of the W pass with the Gram term at its edges: two d_in
     # ranges (one per range group) with several column tiles, and four
     # ranges with one column tile
-    ("die_grid_two_ranges", 4096, 512, 1536, "bf16", 0.5, 69),
+    ("die_grid_two_ranges", 7168, 512, 768, "bf16", 0.5, 69),
     ("die_grid_four_ranges", 8192, 512, 192, "bf16", -0.25, 70),
     # grids of several rounds (the last one partial) in the die grid of four
     # range groups: 192-column tiles over 16 d_in ranges, and 256-column
