@@ -147,15 +147,17 @@ dora_status dora_norm_plan_info(int64_t d_out, int64_t d_in, int64_t r, int dtyp
  *
  * Where r >= d_out, or r > d_in with d_out <= 4096 (bf16 and fp16, d_in
  * and r multiples of 8, plan mode 3), the Gram matrix or the Gram term
- * would cost more than B A itself, and the call computes
- * the same wnorm by its definition instead: a dense fused pass forms each
- * 64 x 128 tile of W + s B A in the matrix-core accumulators, squares it
- * and keeps only its row sums (cyqw.cn §1.1), and a second launch adds each
- * row's tile sums in a fixed order and takes the root. No tile of B A
- * leaves the chip; the workspace is the larger of the two paths' (the
- * factored path runs instead when W, A or B is not 16-byte aligned). wnorm (and g) are fp32 [d_out] device arrays written by the
- * call. m is an fp32 [d_out] device array or NULL (then g is not written
- * and may be NULL). A NaN in the inputs propagates to wnorm and g.
+ * would cost more than B A itself, and the call computes the same wnorm
+ * by its definition instead: a dense fused pass forms each 64 x 128 tile
+ * of W + s B A in the matrix-core accumulators, squares it and keeps only
+ * its row sums (cyqw.cn §1.1), and a second launch adds each row's tile
+ * sums in a fixed order and takes the root. No tile of B A leaves the
+ * chip; the workspace is the larger of the two paths' (the factored path
+ * runs instead when W, A or B is not 16-byte aligned).
+ *
+ * wnorm (and g) are fp32 [d_out] device arrays written by the call. m is
+ * an fp32 [d_out] device array or NULL (then g is not written and may be
+ * NULL). A NaN in the inputs propagates to wnorm and g.
  *
  * `workspace` must hold at least dora_norm_workspace_size(...) bytes
  * (256-byte aligned) for the same (d_out, d_in, r, dtype, s, budget);
