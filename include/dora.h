@@ -30,7 +30,11 @@
  *     per GPU and never changed.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is enqueued asynchronously on it; results are valid once
- *     the stream has reached that point.
+ *     the stream has reached that point. Calls enqueue kernels only (no
+ *     memset, copy, allocation or host synchronisation; counters a call
+ *     needs are cleared by one of its own kernels), so a sequence of calls
+ *     can be captured into a HIP graph and replayed; a replay depends on
+ *     nothing an earlier call left in the workspace.
  *   - Errors: arguments are checked on the host before any launch. A
  *     failed check returns a non-zero dora_status and enqueues nothing.
  *     A HIP launch error returns DORA_ERR_HIP. No exception crosses this
