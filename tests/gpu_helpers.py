@@ -121,13 +121,23 @@ def check_compose(out_gpu: torch.Tensor, base, lora, g, s, dtype):
     bf16, f16: |out - RNE(ref)| <= 1 ulp of the storage type.
     f32 : additionally the bound the evaluation order implies,
           fma(g, RN(s*lora), RN((g-1)*base)): half an ulp of each rounded
-          operand plus one ulp of the result. Returns the worst error in ulps.
+          operand plus one ulp of the result.
+    Where the two terms nearly cancel (the output is a tiny difference of
+    terms thousands of times larger), their fp32 roundings alone exceed an
+    ulp of the output, so there the bar widens by those roundings,
+    2^-23 (|(g-1) base| + |g s lora|); it stays 1 ulp wherever that is at
+    most a sixteenth of an ulp. Returns the worst error in ulps.
     """
     ref = O.compose(base, lora, g, s)
     got = out_gpu.float().cpu().numpy().astype(np.float64)
     err = np.abs(got - O.round_to_dtype(ref, dtype))
     ub = storage_ulp(ref, dtype)
-    assert np.all(err <= ub), f"max err {np.max(err / ub):.2f} ulp"
+    g64 = np.asarray(g, np.float64)[None, :]
+    terms = np.abs((g64 - 1.0) * np.asarray(base, np.float64)) + np.abs(g64 * s * np.asarray(lora, np.float64))
+    rounding = 2.0 ** -23 * terms
+    strict = rounding <= ub / 16
+    assert np.all(err[strict] <= ub[strict]), f"max err {np.max(err[strict] / ub[strict]):.2f} ulp"
+    assert np.all(err <= ub + rounding), f"cancelling element off by {np.max(err / (ub + rounding)):.2f}x its bound"
     if dtype == "f32":
         g2 = np.asarray(g, np.float64)[None, :]
         t = np.abs((g2 - 1.0) * base)
@@ -135,4 +145,4 @@ def check_compose(out_gpu: torch.Tensor, base, lora, g, s, dtype):
         tol = 0.5 * ulp32(t) + 0.5 * ulp32(sl) * np.abs(g2) + ulp32(np.maximum(np.abs(ref), np.abs(got)))
         e32 = np.abs(got - ref)
         assert np.all(e32 <= tol), f"fp32 bound exceeded by {np.max(e32 / tol):.2f}x"
-    return float(np.max(err / ub))
+    return float(np.max(err[strict] / ub[strict])) if strict.any() else 0.0

@@ -130,3 +130,36 @@ def test_compose_stable_vs_naive_error():
     say(f"    mean rel err: stable {np.mean(e_stable):.3e}, naive {np.mean(e_naive):.3e} "
         f"(ratio {ratio:.1f}); max: stable {np.max(e_stable):.3e}, naive {np.max(e_naive):.3e}")
     assert np.mean(e_stable) < np.mean(e_naive) and np.max(e_stable) <= np.max(e_naive)
+
+
+def _compose_sweep():
+    """Seeded shapes across the compose kernel's paths: widths that are and
+    are not multiples of the 16-byte vector (8 elements for the 16-bit
+    types, 4 for fp32, else the element path), widths below one 64-lane
+    wave and across several 256-lane blocks, row counts around the 4-row
+    unroll, both signs of s."""
+    rng = np.random.default_rng(909)
+    out = []
+    for k in range(24):
+        dtype = ["bf16", "bf16", "f16", "f32"][k % 4]
+        q = 4 if dtype == "f32" else 8
+        d_out = int(rng.integers(1, 5000))
+        if k % 3 != 2:
+            d_out = max(q, d_out // q * q)
+        T = int(rng.choice([rng.integers(1, 9), rng.integers(9, 700), rng.integers(700, 3000)]))
+        s = float(rng.choice([0.5, -0.75, 2.0, 0.125]))
+        out.append((T, d_out, dtype, s))
+    return out
+
+
+COMPOSE_SWEEP = _compose_sweep()
+
+
+@pytest.mark.parametrize("k", range(len(COMPOSE_SWEEP)))
+def test_compose_seeded_sweep(k):
+    T, d_out, dtype, s = COMPOSE_SWEEP[k]
+    say(f"[compose-sweep] {k}: T={T} d_out={d_out} {dtype} s={s}")
+    base, lora, g = I.compose_inputs(T, d_out, dtype, 500 + k)
+    out = bnd.dora_compose(dev(base, dtype), dev(lora, dtype), torch.from_numpy(g).cuda(), s)
+    torch.cuda.synchronize()
+    check_compose(out, base, lora, g, s, dtype)

@@ -162,3 +162,51 @@ def test_compose_backward_argument_errors():
         bnd.dora_compose_backward(dy, dy, dy, g, 0.5, d_base=dy)   # output aliases an input
     with pytest.raises(bnd.DoraError):
         bnd.dora_compose_backward(dy, dy, dy, g, float("nan"))
+
+
+def _backward_sweep():
+    """Seeded shapes across the backward's strip grid: widths giving 1 to
+    several column blocks, narrow workgroups with 2 and 4 row lanes, widths
+    off the 16-byte vector (the element path), row counts from one row to
+    thousands, trained and frozen magnitude."""
+    rng = np.random.default_rng(919)
+    out = []
+    for k in range(20):
+        dtype = ["bf16", "f16", "f32", "bf16"][k % 4]
+        q = 4 if dtype == "f32" else 8
+        d_out = int(rng.choice([rng.integers(1, 520), rng.integers(520, 5000)]))
+        if k % 4 != 3:
+            d_out = max(q, d_out // q * q)
+        T = int(rng.choice([rng.integers(1, 9), rng.integers(9, 600), rng.integers(600, 2500)]))
+        s = float(rng.choice([0.5, -0.75, 2.0]))
+        out.append((T, d_out, dtype, s, k % 5 == 4))
+    return out
+
+
+BWD_SWEEP = _backward_sweep()
+
+
+@pytest.mark.parametrize("k", range(len(BWD_SWEEP)))
+def test_compose_backward_seeded_sweep(k):
+    T, d_out, dtype, s, frozen = BWD_SWEEP[k]
+    say(f"[compose-bwd-sweep] {k}: T={T} d_out={d_out} {dtype} s={s} frozen={frozen}")
+    dy, base, lora, g = _inputs(T, d_out, dtype, 600 + k)
+    _, wnorm = I.grad_inputs(T, d_out, dtype, 600 + k)
+    if frozen:
+        d_base, d_lora, dg, dm = bnd.dora_compose_backward(dev(dy, dtype), dev(base, dtype), dev(lora, dtype),
+                                                           torch.from_numpy(g).cuda(), s, need_dg=False)
+    else:
+        d_base, d_lora, dg, dm = bnd.dora_compose_backward(dev(dy, dtype), dev(base, dtype), dev(lora, dtype),
+                                                           torch.from_numpy(g).cuda(), s,
+                                                           wnorm=torch.from_numpy(wnorm).cuda(), eps=1e-6)
+    torch.cuda.synchronize()
+    rb, rl, rg, rm = O.compose_backward(dy, base, lora, g, s, wnorm=wnorm, eps=1e-6)
+    _check_elem(d_base, rb, dtype, "d_base")
+    _check_elem(d_lora, rl, dtype, "d_lora")
+    if frozen:
+        assert dg is None and dm is None
+    else:
+        _check_dg(dg, dy, base, lora, s, rg)
+        got_dm = dm.cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(got_dm, O.magnitude_scale(dg.cpu().numpy().astype(np.float64), wnorm, 1e-6),
+                                   rtol=2 * U32, atol=0)

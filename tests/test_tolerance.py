@@ -72,3 +72,67 @@ def test_well_conditioned_row_keeps_the_strict_bound():
     wn[7] *= 1 + 2e-5
     with pytest.raises(AssertionError):
         check_norm_conditioned(wn, ref, W, A, B, 0.5)
+
+
+# ---------------------------------------------------------------------------
+# The compose bar (check_compose): 1 ulp of the output, widened only where the
+# two terms cancel by their fp32 roundings.
+
+from gpu_helpers import check_compose  # noqa: E402
+
+
+def fp32_compose(base, lora, g, s, first=None, second=None):
+    """The kernels' evaluation order in fp32, fma(g, RN(s*lora), RN((g-1)*base))
+    rounded once (the fma done in fp64 and rounded: exact for fp32 operands),
+    optionally with a planted mistake in either term."""
+    f = np.float32
+    g32 = np.asarray(g, f)[None, :]
+    sl = (f(s) * np.asarray(lora, f)).astype(f) if second is None else second
+    t = ((g32 - f(1)) * np.asarray(base, f)).astype(f) if first is None else first
+    return (g32.astype(np.float64) * sl.astype(np.float64) + t.astype(np.float64)).astype(f)
+
+
+def _cancelling_inputs(dtype):
+    """Ordinary compose inputs with a few columns whose g makes one element's
+    two terms cancel: g = base / (base + s lora), rounded to fp32, leaves
+    (g - 1) base + g s lora at about 1e-7 of the terms."""
+    base, lora, g = I.compose_inputs(64, 512, dtype, 77)
+    s = 0.5
+    for i, j in [(3, 10), (17, 200), (40, 511)]:
+        b_, l_ = float(base[i, j]), float(lora[i, j])
+        g[j] = np.float32(b_ / (b_ + s * l_))
+    return base, lora, g, s
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compose_bar_accepts_the_fp32_evaluation_where_terms_cancel(dtype):
+    import torch
+
+    base, lora, g, s = _cancelling_inputs(dtype)
+    ref = O.compose(base, lora, g, s)
+    terms = np.abs((g[None, :] - 1.0) * base) + np.abs(g[None, :] * s * lora)
+    assert (np.abs(ref) / terms).min() < 1e-5   # the constructed elements do cancel
+    out = fp32_compose(base, lora, g, s)
+    if dtype == "bf16":
+        out = O.bf16_round(out.astype(np.float64)).astype(np.float32)
+    check_compose(torch.from_numpy(out), base, lora, g, s, dtype)
+
+
+@pytest.mark.parametrize("mistake", ["g_for_g_minus_1", "s_dropped", "s_on_base", "two_ulp"])
+def test_compose_bar_rejects_planted_mistakes(mistake):
+    import torch
+
+    base, lora, g, s = _cancelling_inputs("f32")
+    f = np.float32
+    g32 = np.asarray(g, f)[None, :]
+    if mistake == "g_for_g_minus_1":
+        out = fp32_compose(base, lora, g, s, first=(g32 * np.asarray(base, f)).astype(f))
+    elif mistake == "s_dropped":
+        out = fp32_compose(base, lora, g, s, second=np.asarray(lora, f))
+    elif mistake == "s_on_base":
+        out = fp32_compose(base, lora, g, s, first=((g32 - f(1)) * f(s) * np.asarray(base, f)).astype(f))
+    else:
+        out = fp32_compose(base, lora, g, s)
+        out[5, 5] = out[5, 5] + 2 * np.ldexp(1.0, np.frexp(abs(float(out[5, 5])))[1] - 8)   # 2 bf16 ulps
+    with pytest.raises(AssertionError):
+        check_compose(torch.from_numpy(out), base, lora, g, s, "f32")
