@@ -474,6 +474,26 @@ def test_unaligned_inputs_use_element_loads():
     check_norm(wn.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("d_out,d_in,r,mode", [(2, (1 << 24) + 64, 8, 2), (1, 1 << 23, 8, 3)],
+                         ids=["general_kernel_16M", "dense_pass_8M"])
+def test_long_d_in_past_32_bit_tile_offsets(d_out, d_in, r, mode):
+    # A W-pass tile of 128 rows at these lengths spans 2^31 bytes or more,
+    # so the plan leaves the streaming kernel's 32-bit buffer offsets: two
+    # rows of 16M + 64 columns run the general kernel (element loads, 64-bit
+    # addressing, 32 d_in ranges); one row of 8M columns takes the dense
+    # pass (r >= d_out), whose operands still fit 32-bit descriptors.
+    info = bnd.dora_norm_plan_info(d_out, d_in, r, "bf16", 0.5)
+    assert info["offsets32"] == 0 and info["mode"] == mode
+    say(f"[norm-long] d_out={d_out} d_in={d_in} r={r} mode {mode}")
+    W, A, B = I.norm_inputs(d_out, d_in, r, "bf16", 26)
+    ref = O.dense_row_norm(W, A, B, 0.5)
+    m = magnitude(ref, 26)
+    wn, g = _run(W, A, B, "bf16", 0.5, m)
+    worst = check_norm(wn, ref)
+    check_g(g, m, ref, EPS)
+    say(f"    worst rel err {worst:.2e}")
+
+
 def test_budget_too_small_raises():
     W, A, B = I.norm_inputs(512, 512, 64, "bf16", 26)
     with pytest.raises(bnd.DoraError) as e:
