@@ -43,7 +43,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 F32_MFMA_PEAK_TFLOPS = 157.3
 NSETS = 3                       # input sets the steps rotate through
 ROUNDS = 5                      # rounds of K back-to-back calls for the per-call times
-PREWARM_S = 0.25                # steps run before the warm-up, whatever --warmup says
+PREWARM_S = 1.0                 # steps run before the warm-up, whatever --warmup says
 METRIC = "factored-norm ms/TFLOP/s + compose GB/s (%HBM peak), 8192×8192 r=384 bf16"
 
 
