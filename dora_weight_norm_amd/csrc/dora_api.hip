@@ -180,9 +180,9 @@ int choose_g_ranges(int64_t tiles, int64_t n_gran, int64_t plane_bytes, int max_
 // operand within a 32-bit buffer descriptor (A whole, 64 rows of W or of
 // B). B A costs d_out d_in r multiply-adds: less than G = A A^T (r^2 d_in)
 // when r >= d_out, and less than the Gram term B G (d_out r^2) when
-// r > d_in. The first rule always holds; the second only where the dense
-// pass measured faster, up to 4096 rows (taller matrices keep the W pass,
-// whose tiles reuse their operands more). Its partials share the
+// r > d_in. The first rule applies at every size, the second up to 4096
+// rows, where the dense pass measured faster (taller matrices keep the W
+// pass, whose tiles reuse their operands more). Its partials share the
 // workspace with the factored layout, which stays valid as the fallback;
 // the workspace is the larger of the two.
 constexpr int64_t kDenseMaxRowsRankAboveDin = 4096;
@@ -285,9 +285,9 @@ dora_status make_plan(int64_t d_out, int64_t d_in, int64_t r, int dtype, float s
       // A grid of several rounds takes four range groups where they fit:
       // between rounds each die's L2 sees its share of W go through and
       // loses A, so every round fetches the die's ranges of A again, and
-      // two ranges per die halve that against four ranges (B's rows then
-      // leave memory for four dies). With G folded in, the plain order was
-      // faster.
+      // four groups give each die half as many ranges as two do, halving
+      // those bytes (B's rows then leave memory for four dies instead of
+      // two). With G folded in, the plain order was faster.
       const int64_t n_mt = ceil_div(d_out, dora::fast_rows(p.fcfg));
       const bool rounds = (int64_t)p.xw * n_mt * p.n_nt > dora::kGrid;
       if (p.gfold) {

@@ -88,9 +88,8 @@ DORA_HD TileShape tile_shape(int cfg) {
 
 // kModeDense: the dense fused pass over tiles of W + s B A (16-bit types,
 // r >= d_out, or r > d_in with at most 4096 rows); the plan's factored
-// fields stay valid, so a call whose
-// pointers do not allow its 16-byte loads runs the factored path instead,
-// in the same workspace.
+// fields stay valid, so a call whose pointers do not allow its 16-byte
+// loads runs the factored path instead, in the same workspace.
 enum NormMode : int { kModeEmpty = 0, kModeRowOnly = 1, kModeFactored = 2, kModeDense = 3 };
 constexpr int kDenseRows = 64;     // rows of W per dense tile
 constexpr int kDenseCols = 128;    // columns of W (d_in) per dense tile
